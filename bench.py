@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark: paged decode attention on one MI355X.
+
+Default workload: 32 requests, 12 layers, H=12, d_h=64, 16-token pages,
+attended lengths uniform in [1, 1024], a 4096-page pool with a seeded shuffled
+free list, float32.  One step is the whole decode path: begin_token on every
+request (lazy page lease), then per layer one batched append_and_attend (K/V
+row append, paged attention, split-K merge, plan upload on the first layer),
+then commit_token on every request.  Lengths grow by one per committed step;
+bytes are counted per step from the actual lengths.
+
+Prints one JSON line.  ``value`` is K/V GB/s over the timed steps (wall clock
+between device synchronisations); ``roofline`` reports the attention kernel
+alone: the library records HIP events on the launch stream immediately around
+every attention kernel of the timed steps (PKV_OPT_PROFILING) and sums its
+algorithmic bytes.
+
+Other workloads (--workload): batch256_bf16, skewed64_bf16 (single-layer
+batched decode over existing rows) and fullstep128_bf16_l32 (32 layers, 128
+requests, bf16, 1% seeded aborts).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="batch32_fp32_l12")
+    ap.add_argument("--split-blocks", type=int, default=0)
+    ap.add_argument("--merge-mode", type=int, default=0,
+                    help="0: separate merge kernel, 2: last-arriving chunk merges")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="bound on the oracle's timed CPU work")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this decode path has no multi-GPU mode "
+              "(requests and heads shard without communication; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_attention_amd as pkv
+    from synth import gpu as sgpu
+    from synth import workloads as W
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    maker = W.WORKLOADS[args.workload]
+    w = maker(extra_steps=args.steps + args.warmup + 2) if args.workload.startswith("fullstep") \
+        else maker()
+    transactional = w.appends
+    dt = sgpu.torch_dtype(w.dtype)
+    H, D, L, n = w.heads, w.head_width, w.layers, w.n
+    elt = w.elt
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---- pool and inputs, filled on the device by the seeded generator ----
+    shape = (L, w.num_pages, H, w.page_size, D)
+    kp = torch.empty(shape, dtype=dt, device="cuda")
+    vp = torch.empty(shape, dtype=dt, device="cuda")
+    for layer in range(L):
+        sgpu.fill_normal(kp[layer], w.kpool_key(layer), w.dtype)
+        sgpu.fill_normal(vp[layer], w.vpool_key(layer), w.dtype)
+    rows = (L, n, H, D)
+    q_all = torch.empty(rows, dtype=dt, device="cuda")
+    k_all = torch.empty(rows, dtype=dt, device="cuda")
+    v_all = torch.empty(rows, dtype=dt, device="cuda")
+    for layer in range(L):
+        sgpu.fill_normal(q_all[layer], w.q_key(layer), w.dtype)
+        sgpu.fill_normal(k_all[layer], w.k_key(layer), w.dtype)
+        sgpu.fill_normal(v_all[layer], w.v_key(layer), w.dtype)
+    out = torch.empty((n, H, D), dtype=torch.float32, device="cuda")
+
+    max_context = int(w.lengths.max()) + args.steps + args.warmup + 32
+    d = pkv.pkv_pool_desc_init()
+    d.num_layers, d.num_heads, d.head_width = L, H, D
+    d.page_size, d.num_pages, d.max_context = w.page_size, w.num_pages, max_context
+    d.max_caches = max(n, 1)
+    d.kv_dtype = pkv.PKV_DTYPE_F32 if w.dtype == "f32" else pkv.PKV_DTYPE_BF16
+    d.split_blocks = args.split_blocks
+    d.k_storage, d.v_storage = kp.data_ptr(), vp.data_ptr()
+    d.free_list_seed = w.seed
+    pool = pkv.pkv_pool_create(d)
+    pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_MERGE_MODE, args.merge_mode)
+
+    step_kv_bytes = []
+
+    if transactional:
+        caches = [pkv.pkv_cache_create(pool, max_context) for _ in range(n)]
+        for c, t in zip(caches, w.lengths.tolist()):
+            pkv.pkv_cache_grow(c, t - 1)
+        lens = [t - 1 for t in w.lengths.tolist()]   # committed lengths
+        step_no = [0]
+
+        def step(timed: bool):
+            s = step_no[0]
+            step_no[0] += 1
+            abort = w.abort_layer(s)
+            for c in caches:
+                pkv.pkv_begin_token(c)
+            live = list(range(n))
+            kv_bytes = 0
+            for layer in range(L):
+                for r in [r for r in live if abort[r] == layer]:
+                    pkv.pkv_abort_token(caches[r])
+                live = [r for r in live if abort[r] != layer]
+                if len(live) == n:
+                    q, k, v, o = q_all[layer], k_all[layer], v_all[layer], out
+                else:
+                    idx = torch.tensor(live, device="cuda")
+                    q, k, v = q_all[layer][idx], k_all[layer][idx], v_all[layer][idx]
+                    o = out[:len(live)]
+                t_sum = sum(lens[r] + 1 for r in live)
+                kv_bytes += t_sum * H * 2 * D * elt
+                pkv.pkv_append_and_attend_batched([caches[r] for r in live], layer, q, k, v, o,
+                                                  stream=stream)
+            for r in live:
+                pkv.pkv_commit_token(caches[r])
+                lens[r] += 1
+            if timed:
+                step_kv_bytes.append(kv_bytes)
+    else:
+        plan = pkv.pkv_plan_create(pool)
+        pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride, stream=stream)
+        pt = torch.from_numpy(w.page_tables.copy()).to("cuda")
+        kv_once = int(w.lengths.sum()) * H * 2 * D * elt
+
+        def step(timed: bool):
+            pkv.pkv_plan_decode_attention(plan, 0, q_all[0], pt, out, stream=stream)
+            if timed:
+                step_kv_bytes.append(kv_once)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    pkv.pkv_pool_get_profile(pool, reset=True)
+    pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_PROFILING, 1)   # events around each kernel
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_PROFILING, 0)
+    prof = pkv.pkv_pool_get_profile(pool, reset=True)
+    avg_kern_s = prof.attention_ms / max(1, prof.attention_launches) / 1e3
+    bytes_per_launch = prof.algorithmic_bytes / max(1, prof.attention_launches)
+    achieved = bytes_per_launch / avg_kern_s / 1e9
+    kv_total = float(sum(step_kv_bytes))
+    value = kv_total / elapsed / 1e9
+    chunks = None
+    if not transactional:
+        chunks = pkv.pkv_plan_num_chunks(plan)
+
+    result = {
+        "metric": "paged decode attention KV GB/s (% of HBM peak) + decode-attention steps/sec",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "steps_per_sec": round(args.steps / elapsed, 2),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "requests": n, "layers": L, "heads": H, "head_width": D,
+            "page_size": w.page_size, "pool_pages": w.num_pages,
+            "mean_attended_len": round(kv_total / args.steps / L / (H * 2 * D * elt) /
+                                       max(1, n), 1),
+            "kv_bytes_per_step": int(kv_total / args.steps),
+            "split_blocks": args.split_blocks,
+            "merge_mode": args.merge_mode,
+            "plan_chunks": chunks,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": ("attend_fast_kernel<float,64>" if w.dtype == "f32" else
+                       "attend_fast_kernel<bf16,128>"),
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "avg_launch_us": round(avg_kern_s * 1e6, 2),
+            "bytes_per_launch": int(bytes_per_launch),
+            "launches_timed": int(prof.attention_launches),
+            "merge_launches": int(prof.merge_launches),
+            "merge_avg_us": round(prof.merge_ms / max(1, prof.merge_launches) * 1e3, 2),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The oracle as it is, single-threaded, on a bounded sample of the same
+    workload: layer 0, requests in order until the time budget is spent.
+    Page generation is done before timing; only the oracle is timed."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+
+    pages_k, pages_v = {}, {}
+    q = w.q(0)
+    kn, vn = w.k_new(0), w.v_new(0)
+    order = list(range(w.n))
+    prepared = []
+    t_prep = time.perf_counter()
+    pt_all = w.page_tables if w.page_tables.shape[1] else None
+    for r in order:
+        t = int(w.lengths[r])
+        npg = -(-t // w.page_size)
+        pt = pt_all[r, :npg] if pt_all is not None else np.arange(r * npg, (r + 1) * npg)
+        for p in pt.tolist():
+            if p not in pages_k:
+                pages_k[p] = w.pool_page("k", 0, p)
+                pages_v[p] = w.pool_page("v", 0, p)
+        prepared.append((r, t, pt))
+        if time.perf_counter() - t_prep > budget_s:
+            break
+    limiter = threadpool_limits(limits=1) if threadpool_limits else None
+    done_bytes = 0
+    done = 0
+    t0 = time.perf_counter()
+    try:
+        for r, t, pt in prepared:
+            if w.appends:
+                oracle.append_and_attend(q[r], kn[r], vn[r], pages_k, pages_v, pt, t - 1,
+                                         w.page_size)
+            else:
+                oracle.paged_decode_attention(q[r], pages_k, pages_v, pt, t, w.page_size)
+            done_bytes += t * w.heads * 2 * w.head_width * w.elt
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
+    el = time.perf_counter() - t0
+    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"layer 0 of {w.name}: {done} of {w.n} requests, all {w.heads} heads, "
+                      f"{done_bytes} K/V bytes in {el:.2f} s (float64, one thread)"}
+
+
+if __name__ == "__main__":
+    main()

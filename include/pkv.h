@@ -1,0 +1,290 @@
+/*
+ * pkv.h — paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpkv.  Plain C types only: sizes are int32_t/size_t, device
+ * memory is passed as `void*` / typed pointers obtained from the HIP runtime
+ * (for example from torch tensors' data_ptr()), and a stream is a `void*`
+ * holding a hipStream_t (NULL = the default stream).
+ *
+ * What the library computes (sources cited by page title and section):
+ *
+ *  - riftco-transformer "Incremental Serving", section "Paged KV-cache layout":
+ *    a pool owns, for every layer, key pages and value pages laid out
+ *    [physical_page, head, page_offset, head_width]; a request owns a logical
+ *    page table; one physical page ID addresses the matching page in every
+ *    layer; pages are leased lazily as a sequence grows and returned on reset
+ *    or destroy; the default page holds 16 tokens; a block count of 0 sizes
+ *    the pool for one maximum-length context.
+ *  - same page, section "Request flow": per token, begin reserves the next
+ *    position, each layer appends its K/V row and attends with a [1,H,1,d_h]
+ *    query, commit makes the position visible, abort leaves the visible
+ *    length unchanged.
+ *  - learn_llm ch.38 "cached generation", section "Prepare every block, then
+ *    commit every cache together": the newest query scores the retained rows
+ *    and the new row (len+1 rows) with dot(q,k)/sqrt(d_h), applies a stable
+ *    softmax and mixes the value rows.
+ *
+ * Conventions
+ *  - Every function returning pkv_status returns PKV_OK (0) on success.  On
+ *    any error the library state is unchanged and pkv_last_error() describes
+ *    the failure (a thread-local string owned by the library).
+ *  - Not thread-safe: the caller serialises all calls on one pool and its
+ *    caches (as the pages require external synchronisation of the raw C ABI,
+ *    section "Stable C and Python sessions").
+ *  - Host state changes take effect when the call returns.  Device work is
+ *    enqueued on the given stream; results are valid once it completes.  All
+ *    device work for one pool must be issued on one stream, or ordered by the
+ *    caller.
+ *  - Device outputs are float32; K/V, q, k and v use the pool dtype.  Every
+ *    device pointer must be 16-byte aligned (INVALID_ARGUMENT otherwise).
+ *  - Gathered K/V tensors are never exposed; only the pool and the context.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARGUMENT = 1, /* bad pointer, size, index or geometry       */
+  PKV_ERR_BAD_STATE = 2,        /* call not allowed in the current state      */
+  PKV_ERR_OUT_OF_PAGES = 3,     /* the pool has no free page                  */
+  PKV_ERR_CAPACITY_EXHAUSTED = 4, /* the cache is at its maximum context      */
+  PKV_ERR_ALLOC = 5,            /* host or device allocation failed           */
+  PKV_ERR_DEVICE = 6            /* a HIP runtime call failed                  */
+} pkv_status;
+
+typedef enum pkv_dtype {
+  PKV_DTYPE_F32 = 0,  /* IEEE binary32                                      */
+  PKV_DTYPE_BF16 = 1  /* bfloat16, the upper half of a binary32             */
+} pkv_dtype;
+
+/* Pool flag: host state only.  No device memory is allocated or touched and
+ * no work is enqueued; device-facing calls validate their arguments, update
+ * the host state exactly as usual and leave every output buffer unwritten.
+ * For exercising the page allocator and the token transaction without a GPU;
+ * storage pointers are recorded, never dereferenced. */
+#define PKV_POOL_HOST_ONLY 1u
+
+typedef struct pkv_pool pkv_pool;
+typedef struct pkv_cache pkv_cache;
+typedef struct pkv_plan pkv_plan;
+
+/* Pool geometry and storage.
+ * k_storage and v_storage are caller-owned device buffers, each holding
+ * num_layers * num_pages * num_heads * page_size * head_width elements of
+ * kv_dtype, laid out [layer][physical_page][head][page_offset][head_width]
+ * and 16-byte aligned.  They must stay alive until pkv_pool_destroy. */
+typedef struct pkv_pool_desc {
+  int32_t num_layers;     /* L >= 1                                           */
+  int32_t num_heads;      /* H >= 1                                           */
+  int32_t head_width;     /* d_h, 1..1024                                     */
+  int32_t page_size;      /* tokens per page; default 16                      */
+  int32_t num_pages;      /* P; 0 = ceil(max_context / page_size)             */
+  int32_t max_context;    /* largest context of any cache of this pool        */
+  int32_t max_caches;     /* live caches at once (device page-table rows); 0 = 256 */
+  int32_t kv_dtype;       /* pkv_dtype                                        */
+  int32_t split_blocks;   /* split-K chunk in 16-row blocks; 0 = automatic,
+                             -1 = never split                                  */
+  int32_t flags;          /* PKV_POOL_* bits; 0 by default                     */
+  void* k_storage;
+  void* v_storage;
+  uint64_t free_list_seed; /* seeds the shuffle of the initial free list      */
+} pkv_pool_desc;
+
+/* Work counters of a pool, summed over its committed tokens.
+ * score_cells: one per (layer, head, attended row) of each committed token —
+ * the cached newest-query score row of learn_llm ch.38, section "Count
+ * attention-score cells, not total runtime". */
+typedef struct pkv_counters {
+  uint64_t committed_tokens;
+  uint64_t aborted_tokens;
+  uint64_t cache_appends;     /* layer rows appended by committed tokens     */
+  uint64_t score_cells;
+  uint64_t kv_bytes_read;     /* algorithmic K/V bytes read by attention launches */
+  int32_t pages_free;
+  int32_t pages_leased;
+} pkv_counters;
+
+/* Kernel timing of one pool, collected while PKV_OPT_PROFILING is on: HIP
+ * events recorded on the launch stream immediately before and after each
+ * attention kernel (and each separate merge kernel).  algorithmic_bytes sums
+ * what the attention launches must move: the K/V rows read from the pool,
+ * q, the appended rows (read and written) and the float32 context. */
+typedef struct pkv_profile {
+  uint64_t attention_launches;
+  double attention_ms;
+  uint64_t merge_launches;
+  double merge_ms;
+  uint64_t algorithmic_bytes;
+} pkv_profile;
+
+/* Tunables of a pool (pkv_pool_set_option). */
+typedef enum pkv_option {
+  PKV_OPT_SPLIT_BLOCKS = 1, /* as pkv_pool_desc.split_blocks                   */
+  PKV_OPT_MERGE_MODE = 2,   /* 0: separate merge kernel; 2: last-arriving
+                               chunk merges inside the attention kernel        */
+  PKV_OPT_PROFILING = 3     /* 1: record kernel timing events; 0: stop         */
+} pkv_option;
+
+/* Library version "major.minor.patch"; static string. */
+const char* pkv_version(void);
+
+/* Message for the last error on this thread ("" if none); owned by the library. */
+const char* pkv_last_error(void);
+
+/* ------------------------------------------------------------------ pool -- */
+
+/* Defaults: page_size 16, num_pages 0, max_caches 0 (=256), dtype F32,
+ * split_blocks 0, flags 0, seed 0, null storage.  Mirrors the session-options init of
+ * "Incremental Serving", section "Stable C and Python sessions". */
+void pkv_pool_desc_init(pkv_pool_desc* desc);
+
+/* Creates a pool over caller storage.  The free list holds every page ID in
+ * a seeded random order.  Touches no device: device resources are created on
+ * the first device call, on the device current at that moment.
+ * Errors: INVALID_ARGUMENT (null desc/out/storage, storage not 16-byte
+ * aligned, non-positive sizes, head_width > 1024, unknown dtype or flags);
+ * ALLOC. */
+pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out);
+
+/* Destroys the pool.  Errors: BAD_STATE while any cache or plan of the pool
+ * is alive or any raw page is leased. */
+pkv_status pkv_pool_destroy(pkv_pool* pool);
+
+/* The resolved geometry (num_pages, max_caches filled in). */
+pkv_status pkv_pool_get_desc(const pkv_pool* pool, pkv_pool_desc* out);
+
+pkv_status pkv_pool_get_counters(const pkv_pool* pool, pkv_counters* out);
+
+/* Sets one pkv_option.  Errors: INVALID_ARGUMENT (unknown option or value). */
+pkv_status pkv_pool_set_option(pkv_pool* pool, int32_t option, int64_t value);
+
+/* Waits for the recorded timing events, sums them into *out and, if reset,
+ * clears the record.  Errors: DEVICE. */
+pkv_status pkv_pool_get_profile(pkv_pool* pool, pkv_profile* out, int32_t reset);
+
+/* Raw page lease/release, for callers that keep their own page tables and
+ * use the batched calls below.  Errors: OUT_OF_PAGES; INVALID_ARGUMENT for a
+ * page that is out of range or not raw-leased. */
+pkv_status pkv_page_lease(pkv_pool* pool, int32_t* page);
+pkv_status pkv_page_release(pkv_pool* pool, int32_t page);
+
+/* ------------------------------------------------------- request caches -- */
+
+/* Creates an empty request cache (length 0, no pages).  max_context <= the
+ * pool's.  Errors: INVALID_ARGUMENT; BAD_STATE when max_caches caches live. */
+pkv_status pkv_cache_create(pkv_pool* pool, int32_t max_context, pkv_cache** out);
+
+/* Returns every page (a pending token's included) and frees the handle. */
+pkv_status pkv_cache_destroy(pkv_cache* cache);
+
+/* Length back to 0, every page returned, handle kept.  Pages return in the
+ * reverse of their lease order, so replaying the same tokens leases the same
+ * pages again.  Errors: BAD_STATE while a token is pending. */
+pkv_status pkv_cache_reset(pkv_cache* cache);
+
+/* Committed length, maximum context, page size (tokens). -1 for a null cache. */
+int32_t pkv_cache_size(const pkv_cache* cache);
+int32_t pkv_cache_capacity(const pkv_cache* cache);
+int32_t pkv_cache_block_size(const pkv_cache* cache);
+
+/* Copies the logical page table (pages held, a pending token's included) into
+ * out[0..cap); *n_out receives the number of entries.  Errors:
+ * INVALID_ARGUMENT when cap is too small (nothing written). */
+pkv_status pkv_cache_page_table(const pkv_cache* cache, int32_t* out, int32_t cap,
+                                int32_t* n_out);
+
+/* Extends the committed length by n_tokens rows whose K/V bytes the caller
+ * writes itself (a bulk prefill writer), leasing the pages they need.
+ * Errors: BAD_STATE (token pending), CAPACITY_EXHAUSTED, OUT_OF_PAGES. */
+pkv_status pkv_cache_grow(pkv_cache* cache, int32_t n_tokens);
+
+/* --------------------------------------------------- token transaction -- */
+
+/* Reserves position = length; leases a page when the position starts one.
+ * Errors: BAD_STATE (already pending), CAPACITY_EXHAUSTED, OUT_OF_PAGES. */
+pkv_status pkv_begin_token(pkv_cache* cache, int32_t* position);
+
+/* One layer of the pending token: writes k and v ([1,H,1,d_h], pool dtype,
+ * device) into the pool at the pending position, then attends with q over
+ * the length+1 rows, writing out ([1,H,1,d_h] float32, device).
+ * Errors: BAD_STATE (no pending token, layer already appended),
+ * INVALID_ARGUMENT (layer out of range, null pointer), DEVICE. */
+pkv_status pkv_append_and_attend(pkv_cache* cache, int32_t layer, const void* q,
+                                 const void* k, const void* v, float* out, void* stream);
+
+/* Makes the pending position visible.  Errors: BAD_STATE (nothing pending,
+ * or some layer not appended; the caller may then abort). */
+pkv_status pkv_commit_token(pkv_cache* cache);
+
+/* Drops the pending token: length unchanged, a page leased by its begin
+ * returned.  Errors: BAD_STATE (nothing pending). */
+pkv_status pkv_abort_token(pkv_cache* cache);
+
+/* The same layer step for n pending caches of one pool in one launch:
+ * q, k, v are [n,H,d_h] (pool dtype), out is [n,H,d_h] float32, row i
+ * belonging to caches[i].  All caches are validated before any work is
+ * enqueued.  Errors: as pkv_append_and_attend, per cache; INVALID_ARGUMENT
+ * for a repeated cache or caches of different pools. */
+pkv_status pkv_append_and_attend_batched(pkv_cache* const* caches, int32_t n, int32_t layer,
+                                         const void* q, const void* k, const void* v,
+                                         float* out, void* stream);
+
+/* ------------------------------------------- batched calls on page tables -- */
+
+/* A split plan: per-request attended lengths turned into a device work list
+ * (split-K chunks, longest first) plus partial buffers.  Build it once per
+ * decode step and reuse it for every layer. */
+pkv_status pkv_plan_create(pkv_pool* pool, pkv_plan** out);
+pkv_status pkv_plan_destroy(pkv_plan* plan);
+
+/* seq_lens: host array of n attended lengths t_r >= 1 (the newest row
+ * included), each at most pt_stride * page_size.  Uploads the plan on the
+ * stream.  Errors: INVALID_ARGUMENT (n < 1, t_r < 1 or too long); ALLOC. */
+pkv_status pkv_plan_build(pkv_plan* plan, int32_t n, const int32_t* seq_lens,
+                          int32_t pt_stride, void* stream);
+
+/* Number of split chunks of the built plan (0 if not built). */
+int32_t pkv_plan_num_chunks(const pkv_plan* plan);
+
+/* Batched decode attention: for each request r, q[r] ([H,d_h], pool dtype)
+ * attends to rows 0..t_r-1 of its pages; page_table is a device int32
+ * array [n][pt_stride] of physical page IDs (request r's logical page i at
+ * page_table[r*pt_stride + i]).  out: [n,H,d_h] float32, device. */
+pkv_status pkv_plan_decode_attention(pkv_plan* plan, int32_t layer, const void* q,
+                                     const int32_t* page_table, float* out, void* stream);
+
+/* Batched append: writes k[r], v[r] ([n,H,d_h], pool dtype) into row t_r-1
+ * of each request's pages (a byte copy). */
+pkv_status pkv_plan_kv_append(pkv_plan* plan, int32_t layer, const int32_t* page_table,
+                              const void* k, const void* v, void* stream);
+
+/* Both in one launch: append row t_r-1, then attend over rows 0..t_r-1. */
+pkv_status pkv_plan_append_and_attend(pkv_plan* plan, int32_t layer,
+                                      const int32_t* page_table, const void* q,
+                                      const void* k, const void* v, float* out,
+                                      void* stream);
+
+/* One-call forms that build an internal plan from host seq_lens. */
+pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, int32_t n, const void* q,
+                                const int32_t* page_table, int32_t pt_stride,
+                                const int32_t* seq_lens, float* out, void* stream);
+
+/* positions: host array of n row indices; row positions[r] of request r is
+ * written, so positions[r] < pt_stride * page_size. */
+pkv_status pkv_kv_append(pkv_pool* pool, int32_t layer, int32_t n,
+                         const int32_t* page_table, int32_t pt_stride,
+                         const int32_t* positions, const void* k, const void* v,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -16,7 +16,8 @@ Sources, by page and section:
 Readings where the pages are silent: abort also returns a page that this
 token's begin leased (so pool and page table equal their state before begin);
 reset while a token is pending is rejected; destroy always succeeds and
-returns every page, the pending one included.
+returns every page, the pending one included; a call with an invalid argument
+is rejected as such before the state is consulted.
 """
 from __future__ import annotations
 
@@ -75,10 +76,10 @@ class CacheModel:
         return Status.OK
 
     def append(self, layer: int) -> Status:
-        if self.pending is None:
-            return Status.BAD_STATE
         if not 0 <= layer < self.layers:
             return Status.INVALID_ARGUMENT
+        if self.pending is None:
+            return Status.BAD_STATE
         if layer in self.pending[2]:
             return Status.BAD_STATE
         self.pending[2].add(layer)

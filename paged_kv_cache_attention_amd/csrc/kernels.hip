@@ -1,0 +1,567 @@
+// gfx950 kernels of libpkv: paged decode attention (fast and generic paths),
+// the log-sum-exp merge of split-K partials, the K/V row append and the
+// page-table patch.
+//
+// What is computed (learn_llm ch.38 "cached generation", section "Prepare
+// every block, then commit every cache together"): for one request, layer and
+// head, the newest query q scores each attended row j with dot(q, k_j)/sqrt(d_h),
+// a stable softmax turns the scores into weights and the context is the
+// weighted sum of the value rows.  Rows are found through the request's page
+// table in pages laid out [physical_page, head, page_offset, head_width]
+// ("Incremental Serving", section "Paged KV-cache layout").
+//
+// Arithmetic: float32 throughout (bf16 K/V widen exactly).  Scores are kept in
+// log2 units (q is pre-multiplied by log2(e)/sqrt(d_h)) so every exponential is
+// one v_exp_f32.  Softmax is online: each lane group keeps a running maximum m,
+// a running sum l of 2^(s-m) and an accumulator of 2^(s-m) v; groups, waves and
+// split-K chunks combine by rescaling to the larger maximum.
+#include <cfloat>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBF16 = 1;
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <typename T>
+struct KVTraits;
+
+template <>
+struct KVTraits<float> {
+  static constexpr int kPerVec = 4;  // elements in 16 bytes
+  __device__ static inline void unpack(const uint4& u, float* f) {
+    f[0] = __uint_as_float(u.x);
+    f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z);
+    f[3] = __uint_as_float(u.w);
+  }
+  __device__ static inline float load1(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+};
+
+template <>
+struct KVTraits<bf16_t> {
+  static constexpr int kPerVec = 8;
+  __device__ static inline void unpack(const uint4& u, float* f) {
+    f[0] = __uint_as_float(u.x << 16);
+    f[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    f[2] = __uint_as_float(u.y << 16);
+    f[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    f[4] = __uint_as_float(u.z << 16);
+    f[5] = __uint_as_float(u.z & 0xFFFF0000u);
+    f[6] = __uint_as_float(u.w << 16);
+    f[7] = __uint_as_float(u.w & 0xFFFF0000u);
+  }
+  __device__ static inline float load1(const void* p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+  }
+};
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Rotate within a 16-lane DPP row (row_ror:N has control 0x120 + N).
+template <int CTRL>
+__device__ inline float dpp_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the total.
+__device__ inline float row16_sum(float x) {
+  x += dpp_ror<0x128>(x);
+  x += dpp_ror<0x124>(x);
+  x += dpp_ror<0x122>(x);
+  x += dpp_ror<0x121>(x);
+  return x;
+}
+
+__device__ inline float wave_max(float x) {
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+__device__ inline float wave_sum(float x) {
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ inline uint4 select4(bool c, const uint4& a, const uint4& b) {
+  return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
+// Ends one (chunk, head).  A request with one chunk writes its context; a
+// split request writes a partial (m, l, acc).  In kMergeLastArriver mode the
+// chunk that arrives last at the (request, head) counter then merges all
+// partials (merge_partials) and returns the counter to zero for the next
+// launch; in kMergeSeparate mode merge_kernel does that afterwards.
+// Called once per chunk by one whole wave.  Lane-held column e is
+// col0 + e * CSTRIDE, present when own_cols and below the head width.
+template <int NCOL, int CSTRIDE>
+__device__ inline void merge_partials(const AttnArgs& a, int req, const ReqEntry& rq, int h,
+                                      bool own_cols, int col0) {
+  // Second pass: o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, in split
+  // order, so the result does not depend on which chunk finished last.
+  const int D = a.head_width;
+  const int H = a.num_heads;
+  if (!own_cols) return;
+  const int64_t stride = (int64_t)H * (D + 2);
+  const float* base = a.partials + ((int64_t)rq.partial_base * H + h) * (D + 2);
+  float mx = -FLT_MAX;
+  for (int s = 0; s < rq.nsplit; ++s) mx = fmaxf(mx, base[s * stride]);
+  float lsum = 0.f;
+  float o[NCOL];
+#pragma unroll
+  for (int e = 0; e < NCOL; ++e) o[e] = 0.f;
+  for (int s = 0; s < rq.nsplit; ++s) {
+    const float* ps = base + s * stride;
+    const float wgt = fast_exp2(ps[0] - mx);
+    lsum = fmaf(ps[1], wgt, lsum);
+#pragma unroll
+    for (int e = 0; e < NCOL; ++e)
+      if (col0 + e * CSTRIDE < D) o[e] = fmaf(ps[2 + col0 + e * CSTRIDE], wgt, o[e]);
+  }
+  const float inv = 1.0f / lsum;
+  float* out = a.out + ((int64_t)req * H + h) * D + col0;
+#pragma unroll
+  for (int e = 0; e < NCOL; ++e)
+    if (col0 + e * CSTRIDE < D) out[e * CSTRIDE] = o[e] * inv;
+}
+
+__device__ inline void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int NCOL, int CSTRIDE>
+__device__ inline void finish_chunk(const AttnArgs& a, const WorkItem& it, const ReqEntry& rq,
+                                    int h, int lane, bool own_cols, int col0, float m, float l,
+                                    const float* acc) {
+  const int D = a.head_width;
+  const int H = a.num_heads;
+  auto has = [&](int e) { return own_cols && col0 + e * CSTRIDE < D; };
+  if (rq.nsplit == 1) {
+    const float inv = 1.0f / l;
+    float* o = a.out + ((int64_t)it.req * H + h) * D + col0;
+#pragma unroll
+    for (int e = 0; e < NCOL; ++e)
+      if (has(e)) o[e * CSTRIDE] = acc[e] * inv;
+    return;
+  }
+  float* part = a.partials + ((int64_t)(rq.partial_base + it.split) * H + h) * (D + 2);
+  if (a.merge_mode == kMergeSeparate) {
+#pragma unroll
+    for (int e = 0; e < NCOL; ++e)
+      if (has(e)) part[2 + col0 + e * CSTRIDE] = acc[e];
+    if (lane == 0) {
+      part[0] = m;
+      part[1] = l;
+    }
+    return;
+  }
+  // Last-arriver merge.  Agent-scope stores write through to the
+  // device-coherent level; waiting for every outstanding memory operation
+  // orders them before the counter increment that publishes them.
+#pragma unroll
+  for (int e = 0; e < NCOL; ++e)
+    if (has(e)) store_agent(part + 2 + col0 + e * CSTRIDE, acc[e]);
+  if (lane == 0) {
+    store_agent(part, m);
+    store_agent(part + 1, l);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  int* counter = a.merge_count + (int64_t)it.req * H + h;
+  int prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __shfl(prev, 0);
+  if (prev != rq.nsplit - 1) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (lane == 0) (void)__hip_atomic_exchange(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  merge_partials<NCOL, CSTRIDE>(a, it.req, rq, h, own_cols, col0);
+}
+
+// ---------------------------------------------------------------------------
+// Fast path: rows of exactly 256 bytes (bf16 d_h=128, f32 d_h=64), pages a
+// multiple of 16 rows.  Workgroup = 4 waves on one (chunk, head).  A wave
+// takes every 4th 16-row block of the chunk; a block is one contiguous 4 KiB
+// slab of K and one of V.  Lane (g, c): row i*4+g of each of the 4 loads, 16
+// bytes at column c, so one load instruction reads 1 KiB contiguous and the
+// 16 lanes of a DPP row hold one K/V row.  Each 16-lane group keeps its own
+// online-softmax state over its rows; groups merge in-wave, waves in LDS.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attend_fast_kernel(AttnArgs a) {
+  using KV = KVTraits<T>;
+  constexpr int EPL = KV::kPerVec;
+  constexpr int LPR = D / EPL;
+  static_assert(LPR == 16, "fast path needs 256-byte rows");
+  constexpr int RPI = 64 / LPR;            // rows per load instruction
+  constexpr int NI = kBlockRows / RPI;     // load instructions per block
+  constexpr int ROW_BYTES = D * (int)sizeof(T);
+  constexpr int WAVES = 4;
+
+  const WorkItem it = a.items[blockIdx.x];
+  const ReqEntry rq = a.reqs[it.req];
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane / LPR;
+  const int c = lane % LPR;
+  const int t = rq.seq_len;
+  const int S = a.page_size;
+  const int32_t* pt = a.page_table + (int64_t)rq.pt_row * a.pt_stride;
+  const int64_t qrow_bytes = (((int64_t)it.req * a.num_heads + h) * D) * (int64_t)sizeof(T);
+  const int64_t head_off = (int64_t)h * a.head_bytes;
+  const int last_blk = (t - 1) / kBlockRows;
+  const bool fused = a.fuse_append != 0 && it.blk_end > last_blk;
+
+  float qf[EPL];
+  {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + qrow_bytes +
+                                                    c * 16);
+    KV::unpack(u, qf);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[e] *= a.scale_log2e;
+  }
+
+  uint4 knew = make_uint4(0, 0, 0, 0), vnew = make_uint4(0, 0, 0, 0);
+  if (fused) {
+    knew = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + qrow_bytes + c * 16);
+    vnew = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + qrow_bytes + c * 16);
+    if (wave == 0 && g == 0) {
+      const int pos = t - 1;
+      const int64_t slot = (int64_t)pt[pos / S] * a.page_bytes + head_off +
+                           (int64_t)(pos % S) * ROW_BYTES + c * 16;
+      *reinterpret_cast<uint4*>(a.k_layer + slot) = knew;
+      *reinterpret_cast<uint4*>(a.v_layer + slot) = vnew;
+    }
+  }
+
+  auto load_block = [&](int b, uint4* kk, uint4* vv) {
+    const int row0 = b * kBlockRows;
+    const int64_t base = (int64_t)pt[row0 / S] * a.page_bytes + head_off +
+                         (int64_t)(row0 % S) * ROW_BYTES;
+    const char* kb = a.k_layer + base;
+    const char* vb = a.v_layer + base;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int off = (i * RPI + g) * ROW_BYTES + c * 16;
+      kk[i] = *reinterpret_cast<const uint4*>(kb + off);
+      vv[i] = *reinterpret_cast<const uint4*>(vb + off);
+    }
+  };
+
+  float m = -FLT_MAX, l = 0.f;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+
+  auto step = [&](int b, uint4* kk, uint4* vv, bool edge) {
+    bool valid[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) valid[i] = true;
+    if (edge) {
+      // The request's last block: rows >= t are masked (their bytes may be
+      // anything), and with a fused append row t-1 comes from k_new/v_new.
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int row = b * kBlockRows + i * RPI + g;
+        const bool is_new = fused && row == t - 1;
+        valid[i] = row < t;
+        kk[i] = select4(is_new, knew, kk[i]);
+        vv[i] = select4(valid[i], select4(is_new, vnew, vv[i]), make_uint4(0, 0, 0, 0));
+      }
+    }
+    float s[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float kf[EPL];
+      KV::unpack(kk[i], kf);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) d = fmaf(qf[e], kf[e], d);
+      s[i] = row16_sum(d);
+      if (edge && !valid[i]) s[i] = -INFINITY;
+    }
+    float mb = s[0];
+#pragma unroll
+    for (int i = 1; i < NI; ++i) mb = fmaxf(mb, s[i]);
+    const float mn = fmaxf(m, mb);
+    const float alpha = fast_exp2(m - mn);
+    float p[NI];
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      p[i] = fast_exp2(s[i] - mn);
+      ps += p[i];
+    }
+    l = fmaf(l, alpha, ps);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float vf[EPL];
+      KV::unpack(vv[i], vf);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p[i], vf[e], acc[e]);
+    }
+    m = mn;
+  };
+
+  {
+    uint4 k0[NI], v0[NI], k1[NI], v1[NI];
+    const int end = it.blk_end;
+    int b = it.blk_begin + wave;
+    if (b < end) load_block(b, k0, v0);
+    for (; b < end; b += 2 * WAVES) {
+      const int b1 = b + WAVES;
+      if (b1 < end) load_block(b1, k1, v1);
+      step(b, k0, v0, b == last_blk);
+      if (b1 >= end) break;
+      if (b1 + WAVES < end) load_block(b1 + WAVES, k0, v0);
+      step(b1, k1, v1, b1 == last_blk);
+    }
+  }
+
+  // Merge the four 16-lane groups of the wave (lanes differing in bits 4, 5).
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    const float mo = __shfl_xor(m, off);
+    const float lo = __shfl_xor(l, off);
+    const float mx = fmaxf(m, mo);
+    const float wa = fast_exp2(m - mx), wb = fast_exp2(mo - mx);
+    l = l * wa + lo * wb;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float ao = __shfl_xor(acc[e], off);
+      acc[e] = acc[e] * wa + ao * wb;
+    }
+    m = mx;
+  }
+
+  // Merge the waves through LDS.
+  __shared__ float s_m[WAVES], s_l[WAVES];
+  __shared__ float s_acc[WAVES][D];
+  if (lane < LPR) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s_acc[wave][c * EPL + e] = acc[e];
+    if (lane == 0) {
+      s_m[wave] = m;
+      s_l[wave] = l;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float mx = s_m[0];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) mx = fmaxf(mx, s_m[w]);
+    float wt[WAVES];
+    float lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      wt[w] = fast_exp2(s_m[w] - mx);
+      lsum = fmaf(s_l[w], wt[w], lsum);
+    }
+    float o[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float x = 0.f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) x = fmaf(s_acc[w][c * EPL + e], wt[w], x);
+      o[e] = x;
+    }
+    finish_chunk<EPL, 1>(a, it, rq, h, lane, lane < LPR, c * EPL, mx, lsum, o);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Generic path: any head width up to 1024, any page size.  One wave per
+// (chunk, head).  Tiles of 64 rows: lane j scores row j of the tile, the wave
+// reduces max and sum, then lanes sweep head-width columns accumulating the
+// weighted value rows.
+template <typename T>
+__global__ __launch_bounds__(64) void attend_generic_kernel(AttnArgs a) {
+  using KV = KVTraits<T>;
+  constexpr int MAXV = 16;  // columns per lane: head_width <= 64 * MAXV
+  extern __shared__ float smem[];
+  const int D = a.head_width;
+  float* qs = smem;         // [D]
+  float* ps = smem + D;     // [64]
+
+  const WorkItem it = a.items[blockIdx.x];
+  const ReqEntry rq = a.reqs[it.req];
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int t = rq.seq_len;
+  const int S = a.page_size;
+  const int32_t* pt = a.page_table + (int64_t)rq.pt_row * a.pt_stride;
+  const int64_t qrow = ((int64_t)it.req * a.num_heads + h) * D;
+  const int64_t head_off = (int64_t)h * a.head_bytes;
+  const int64_t row_bytes = (int64_t)D * sizeof(T);
+  const int row_begin = it.blk_begin * kBlockRows;
+  const int row_end = min(it.blk_end * kBlockRows, t);
+  const bool fused = a.fuse_append != 0 && row_end == t;
+
+  for (int d = lane; d < D; d += 64) qs[d] = KV::load1(a.q, qrow + d) * a.scale_log2e;
+  if (fused) {
+    const int pos = t - 1;
+    const int64_t slot = (int64_t)pt[pos / S] * a.page_bytes + head_off + (int64_t)(pos % S) * row_bytes;
+    for (int d = lane; d < D; d += 64) {
+      reinterpret_cast<T*>(a.k_layer + slot)[d] = static_cast<const T*>(a.k_new)[qrow + d];
+      reinterpret_cast<T*>(a.v_layer + slot)[d] = static_cast<const T*>(a.v_new)[qrow + d];
+    }
+  }
+  __syncthreads();
+
+  auto row_ptr = [&](const char* layer, int row) -> const void* {
+    return layer + (int64_t)pt[row / S] * a.page_bytes + head_off + (int64_t)(row % S) * row_bytes;
+  };
+
+  float m = -FLT_MAX, l = 0.f;
+  float acc[MAXV];
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v) acc[v] = 0.f;
+
+  for (int row0 = row_begin; row0 < row_end; row0 += 64) {
+    const int row = row0 + lane;
+    const bool valid = row < row_end;
+    float s = -INFINITY;
+    if (valid) {
+      const bool is_new = fused && row == t - 1;
+      const void* kp = is_new ? static_cast<const void*>(static_cast<const T*>(a.k_new) + qrow)
+                              : row_ptr(a.k_layer, row);
+      float dot = 0.f;
+      for (int d = 0; d < D; ++d) dot = fmaf(qs[d], KV::load1(kp, d), dot);
+      s = dot;
+    }
+    const float mn = fmaxf(m, wave_max(s));
+    const float alpha = fast_exp2(m - mn);
+    const float p = valid ? fast_exp2(s - mn) : 0.f;
+    l = l * alpha + wave_sum(p);
+    m = mn;
+    ps[lane] = p;
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) acc[v] *= alpha;
+    const int nrows = min(64, row_end - row0);
+    for (int j = 0; j < nrows; ++j) {
+      const int rj = row0 + j;
+      const void* vp = (fused && rj == t - 1)
+                           ? static_cast<const void*>(static_cast<const T*>(a.v_new) + qrow)
+                           : row_ptr(a.v_layer, rj);
+      const float pj = ps[j];
+#pragma unroll
+      for (int v = 0; v < MAXV; ++v) {
+        const int d = lane + 64 * v;
+        if (d < D) acc[v] = fmaf(pj, KV::load1(vp, d), acc[v]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // This lane holds columns lane, lane + 64, ...
+  finish_chunk<MAXV, 64>(a, it, rq, h, lane, true, lane, m, l, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Second pass of kMergeSeparate: one wave per (split request, head); lanes
+// hold columns lane, lane + 64, ...
+__global__ __launch_bounds__(64) void merge_kernel(AttnArgs a) {
+  const int req = a.merge_reqs[blockIdx.x];
+  const ReqEntry rq = a.reqs[req];
+  merge_partials<16, 64>(a, req, rq, blockIdx.y, true, threadIdx.x);
+}
+
+// ---------------------------------------------------------------------------
+// Append: row t-1 of request r, head h <- k[r][h][:], v[r][h][:] (bit copy).
+template <typename W>
+__global__ __launch_bounds__(64) void kv_append_kernel(AttnArgs a) {
+  const int r = blockIdx.x;
+  const int h = blockIdx.y;
+  const ReqEntry rq = a.reqs[r];
+  const int pos = rq.seq_len - 1;
+  const int S = a.page_size;
+  const int D = a.head_width;
+  const int32_t* pt = a.page_table + (int64_t)rq.pt_row * a.pt_stride;
+  const int64_t dst = (int64_t)pt[pos / S] * a.page_bytes + (int64_t)h * a.head_bytes +
+                      (int64_t)(pos % S) * D * (int64_t)sizeof(W);
+  const int64_t src = ((int64_t)r * a.num_heads + h) * D;
+  W* kd = reinterpret_cast<W*>(a.k_layer + dst);
+  W* vd = reinterpret_cast<W*>(a.v_layer + dst);
+  const W* ks = static_cast<const W*>(a.k_new) + src;
+  const W* vs = static_cast<const W*>(a.v_new) + src;
+  for (int d = threadIdx.x; d < D; d += 64) {
+    kd[d] = ks[d];
+    vd[d] = vs[d];
+  }
+}
+
+__global__ __launch_bounds__(256) void patch_kernel(int32_t* arena, PatchBatch b) {
+  const int i = threadIdx.x;
+  if (i < b.count) arena[b.offset[i]] = b.value[i];
+}
+
+template <typename T, int D>
+hipError_t launch_fast(const AttnArgs& a, int num_items, hipStream_t stream) {
+  hipLaunchKernelGGL((attend_fast_kernel<T, D>), dim3(num_items, a.num_heads), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_generic(const AttnArgs& a, int num_items, hipStream_t stream) {
+  const size_t lds = (size_t)(a.head_width + 64) * sizeof(float);
+  hipLaunchKernelGGL((attend_generic_kernel<T>), dim3(num_items, a.num_heads), dim3(64), lds,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool fast_path_supported(int dtype, int head_width, int page_size) {
+  if (page_size % kBlockRows != 0) return false;
+  if (dtype == kDtypeF32) return head_width == 64;
+  if (dtype == kDtypeBF16) return head_width == 128;
+  return false;
+}
+
+hipError_t launch_attention(const AttnArgs& a, int dtype, int num_items, hipStream_t stream,
+                            KernelPath* path_out) {
+  const bool fast = fast_path_supported(dtype, a.head_width, a.page_size);
+  if (path_out) *path_out = fast ? KernelPath::kFast : KernelPath::kGeneric;
+  if (fast)
+    return dtype == kDtypeF32 ? launch_fast<float, 64>(a, num_items, stream)
+                              : launch_fast<bf16_t, 128>(a, num_items, stream);
+  return dtype == kDtypeF32 ? launch_generic<float>(a, num_items, stream)
+                            : launch_generic<bf16_t>(a, num_items, stream);
+}
+
+hipError_t launch_merge(const AttnArgs& a, int num_split_reqs, hipStream_t stream) {
+  hipLaunchKernelGGL(merge_kernel, dim3(num_split_reqs, a.num_heads), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const AttnArgs& a, int dtype, int num_reqs, hipStream_t stream) {
+  if (dtype == kDtypeF32) {
+    hipLaunchKernelGGL(kv_append_kernel<uint32_t>, dim3(num_reqs, a.num_heads), dim3(64), 0,
+                       stream, a);
+  } else {
+    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, dim3(num_reqs, a.num_heads), dim3(64), 0,
+                       stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_patches(int32_t* arena, const PatchBatch& b, hipStream_t stream) {
+  hipLaunchKernelGGL(patch_kernel, dim3(1), dim3(256), 0, stream, arena, b);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

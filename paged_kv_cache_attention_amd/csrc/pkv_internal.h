@@ -1,0 +1,86 @@
+// Internal types shared by the host runtime and the gfx950 kernels of libpkv.
+#pragma once
+
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+namespace pkv {
+
+// Rows per block: the unit of the split-K work list.  A 16-row block of one
+// head is one contiguous 16 x d_h slab when page_size is a multiple of 16.
+constexpr int kBlockRows = 16;
+
+// One request of a plan.  pt_row selects the request's row of the page-table
+// array the launch receives; seq_len is the attended length t (newest row
+// included).  nsplit > 1 means the request's chunks write partials starting at
+// slot partial_base, and a merge produces the output.
+struct ReqEntry {
+  int32_t pt_row;
+  int32_t seq_len;
+  int32_t nsplit;
+  int32_t partial_base;
+};
+
+// One split-K chunk: blocks [blk_begin, blk_end) of request req, split index split.
+struct WorkItem {
+  int32_t req;
+  int32_t blk_begin;
+  int32_t blk_end;
+  int32_t split;
+};
+
+struct AttnArgs {
+  const void* q;          // [n][H][D] pool dtype
+  const void* k_new;      // [n][H][D] rows to append at t-1 (fused append), or null
+  const void* v_new;
+  float* out;             // [n][H][D]
+  char* k_layer;          // K pool of this layer: [P][H][S][D]
+  char* v_layer;
+  const int32_t* page_table;
+  int64_t pt_stride;      // entries per page-table row
+  const ReqEntry* reqs;
+  const WorkItem* items;
+  float* partials;        // [slots][H][D + 2]: (m, l, acc[D]); m in log2 units
+  int32_t* merge_count;   // [n][H] arrival counters of split requests (self-resetting)
+  const int32_t* merge_reqs;  // requests with nsplit > 1 (separate merge kernel)
+  int32_t num_heads;
+  int32_t page_size;
+  int32_t head_width;
+  int32_t fuse_append;    // 1: write k_new/v_new at row t-1 and attend with them
+  int32_t merge_mode;     // MergeMode
+  int64_t page_bytes;     // H * S * D * elt
+  int64_t head_bytes;     // S * D * elt
+  float scale_log2e;      // log2(e) / sqrt(D)
+};
+
+struct PatchBatch {
+  static constexpr int kMax = 248;
+  int32_t count;
+  int32_t pad;
+  int32_t offset[kMax];
+  int32_t value[kMax];
+};
+
+enum class KernelPath { kFast, kGeneric };
+
+// How split requests are merged.
+//  kSeparate: chunks store partials; a second kernel merges (the kernel
+//             boundary orders the partial stores before the merge reads).
+//  kLastArriver: the chunk that arrives last at a (request, head) counter
+//             merges.  Partials are stored with agent-scope atomic stores,
+//             which write through to the device-coherent level; the writer
+//             waits for them to complete before its relaxed counter
+//             increment, and the last arriver runs an agent-scope acquire
+//             fence before reading.
+enum MergeMode : int32_t { kMergeSeparate = 0, kMergeLastArriver = 2 };
+
+// Launchers (kernels.hip).  Each returns the hipError_t of the launch.
+hipError_t launch_attention(const AttnArgs& a, int dtype, int num_items, hipStream_t stream,
+                            KernelPath* path_out);
+hipError_t launch_merge(const AttnArgs& a, int num_split_reqs, hipStream_t stream);
+hipError_t launch_kv_append(const AttnArgs& a, int dtype, int num_reqs, hipStream_t stream);
+hipError_t launch_patches(int32_t* arena, const PatchBatch& b, hipStream_t stream);
+bool fast_path_supported(int dtype, int head_width, int page_size);
+
+}  // namespace pkv

@@ -1,0 +1,946 @@
+// Host runtime and C ABI of libpkv: page pool and free list, request caches
+// and their per-token transaction, split-K plans, device page-table mirror.
+//
+// Sources (by page and section):
+//  - riftco-transformer "Incremental Serving", "Paged KV-cache layout": shared
+//    pool of per-layer key/value pages, request-local logical page tables, one
+//    page ID valid in every layer, lazy lease, return on reset/destroy, 16-token
+//    default pages, block count 0 = one maximum context.
+//  - same page, "Request flow": begin / append_and_attend per layer / commit,
+//    abort leaves the visible length unchanged.
+//  - same page, "Stable C and Python sessions": options init with defaults,
+//    capacity exhaustion reported to the caller, external synchronisation.
+//  - learn_llm ch.38 "cached generation": every layer prepares before any
+//    commit; rejected operations leave committed state unchanged; reset keeps
+//    the allocation; work counters (appends, score values).
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <new>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/pkv.h"
+#include "pkv_internal.h"
+
+using pkv::AttnArgs;
+using pkv::PatchBatch;
+using pkv::ReqEntry;
+using pkv::WorkItem;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pkv_status ok() {
+  g_last_error.clear();
+  return PKV_OK;
+}
+
+#define PKV_HIP_TRY(expr)                                                                  \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess)                                                                  \
+      return fail(PKV_ERR_DEVICE, "%s failed: %s", #expr, hipGetErrorString(e_));          \
+  } while (0)
+
+// SplitMix64, used only to shuffle the initial free list.
+uint64_t splitmix_next(uint64_t& s) {
+  s += 0x9E3779B97F4A7C15ull;
+  uint64_t z = s;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+size_t elt_bytes(int32_t dtype) { return dtype == PKV_DTYPE_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+enum PageOwner : uint8_t { kFree = 0, kCache = 1, kRaw = 2 };
+
+struct pkv_plan {
+  pkv_pool* pool = nullptr;
+  bool internal = false;
+  bool built = false;
+  int32_t n = 0;
+  int32_t pt_stride = 0;
+  int32_t num_items = 0;
+  int32_t total_splits = 0;
+  int32_t num_split_reqs = 0;
+  bool any_split = false;
+  uint64_t rows_attended = 0;  // sum of t_r
+  std::vector<ReqEntry> reqs;
+  std::vector<WorkItem> items;
+  std::vector<int64_t> key;  // (pt_row, seq_len) pairs of the last build
+  char* d_meta = nullptr;
+  size_t d_meta_cap = 0;
+  float* d_partials = nullptr;
+  size_t partials_cap = 0;  // floats
+  int32_t* d_counters = nullptr;  // [n][H] merge arrival counters, zero between launches
+  size_t counters_cap = 0;
+  char* h_stage = nullptr;
+  size_t h_stage_cap = 0;
+  hipEvent_t ev = nullptr;
+  bool ev_pending = false;
+};
+
+struct pkv_cache {
+  pkv_pool* pool = nullptr;
+  int32_t max_context = 0;
+  int32_t slot = -1;
+  int32_t len = 0;
+  std::vector<int32_t> pages;
+  bool pending = false;
+  int32_t pending_pos = 0;
+  bool pending_new_page = false;
+  std::vector<uint8_t> appended;
+  int32_t appended_count = 0;
+};
+
+struct pkv_pool {
+  pkv_pool_desc desc{};
+  size_t elt = 4;
+  int64_t head_bytes = 0, page_bytes = 0, layer_bytes = 0;
+  std::vector<int32_t> free_stack;  // lease pops from the back
+  std::vector<uint8_t> owner;
+  int32_t raw_leased = 0;
+  int32_t live_caches = 0;
+  int32_t live_plans = 0;
+  std::vector<int32_t> free_slots;
+  int32_t arena_stride = 0;  // page-table entries per cache slot
+  // device side (created lazily)
+  bool host_only = false;
+  int device = -1;
+  int32_t* d_arena = nullptr;
+  std::vector<std::pair<int32_t, int32_t>> patches;  // (arena offset, page)
+  pkv_plan txn_plan;   // transactional steps
+  pkv_plan call_plan;  // one-call batched forms
+  pkv_counters counters{};
+  int32_t merge_mode = pkv::kMergeSeparate;
+  bool profiling = false;
+  struct Timed {
+    hipEvent_t start, end;
+    bool merge;
+  };
+  std::vector<Timed> timed;         // recorded, not yet summed
+  std::vector<hipEvent_t> spare;    // reusable events
+  pkv_profile profile{};
+};
+
+namespace {
+
+int32_t lease_page(pkv_pool* p, uint8_t who) {
+  const int32_t page = p->free_stack.back();
+  p->free_stack.pop_back();
+  p->owner[page] = who;
+  return page;
+}
+
+void release_page(pkv_pool* p, int32_t page) {
+  p->owner[page] = kFree;
+  p->free_stack.push_back(page);
+}
+
+void record_patch(pkv_cache* c, int32_t logical, int32_t page) {
+  pkv_pool* p = c->pool;
+  p->patches.emplace_back(c->slot * p->arena_stride + logical, page);
+}
+
+pkv_status ensure_device(pkv_pool* p) {
+  if (p->host_only) return PKV_OK;
+  int dev = 0;
+  PKV_HIP_TRY(hipGetDevice(&dev));
+  if (p->device >= 0) {
+    if (dev != p->device)
+      return fail(PKV_ERR_INVALID_ARGUMENT, "pool lives on device %d, current device is %d",
+                  p->device, dev);
+    return PKV_OK;
+  }
+  const size_t bytes = (size_t)p->desc.max_caches * (size_t)p->arena_stride * sizeof(int32_t);
+  void* arena = nullptr;
+  if (hipMalloc(&arena, bytes) != hipSuccess)
+    return fail(PKV_ERR_ALLOC, "device page-table arena of %zu bytes", bytes);
+  if (hipMemset(arena, 0, bytes) != hipSuccess) {
+    (void)hipFree(arena);
+    return fail(PKV_ERR_DEVICE, "hipMemset of the page-table arena failed");
+  }
+  p->d_arena = static_cast<int32_t*>(arena);
+  p->device = dev;
+  return PKV_OK;
+}
+
+pkv_status flush_patches(pkv_pool* p, hipStream_t stream) {
+  if (p->host_only) {
+    p->patches.clear();
+    return PKV_OK;
+  }
+  size_t i = 0;
+  while (i < p->patches.size()) {
+    PatchBatch b{};
+    b.count = 0;
+    for (; i < p->patches.size() && b.count < PatchBatch::kMax; ++i, ++b.count) {
+      b.offset[b.count] = p->patches[i].first;
+      b.value[b.count] = p->patches[i].second;
+    }
+    PKV_HIP_TRY(pkv::launch_patches(p->d_arena, b, stream));
+  }
+  p->patches.clear();
+  return PKV_OK;
+}
+
+int32_t choose_split_blocks(const pkv_pool* p, int64_t total_blocks) {
+  if (p->desc.split_blocks > 0) return p->desc.split_blocks;
+  if (p->desc.split_blocks < 0) return std::numeric_limits<int32_t>::max();
+  // Aim for enough (chunk, head) workgroups to fill 256 CUs several times,
+  // with chunks of 8..64 blocks (128..1024 rows).
+  const int64_t work = total_blocks * p->desc.num_heads;
+  int64_t c = 8;
+  while (c < 64 && work / (c * 2) >= 4096) c *= 2;
+  return static_cast<int32_t>(c);
+}
+
+void plan_release(pkv_plan* pl) {
+  if (pl->ev) {
+    (void)hipEventSynchronize(pl->ev);
+    (void)hipEventDestroy(pl->ev);
+  }
+  if (pl->d_meta) (void)hipFree(pl->d_meta);
+  if (pl->d_partials) (void)hipFree(pl->d_partials);
+  if (pl->d_counters) (void)hipFree(pl->d_counters);
+  if (pl->h_stage) (void)hipHostFree(pl->h_stage);
+  pl->ev = nullptr;
+  pl->d_counters = nullptr;
+  pl->counters_cap = 0;
+  pl->d_meta = nullptr;
+  pl->d_partials = nullptr;
+  pl->h_stage = nullptr;
+  pl->d_meta_cap = pl->partials_cap = pl->h_stage_cap = 0;
+  pl->built = false;
+}
+
+// Builds the split plan for n requests (rows[r] selects the page-table row,
+// lens[r] the attended length) and uploads it on the stream.
+pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_t* lens,
+                      int32_t pt_stride, hipStream_t stream) {
+  pkv_pool* p = pl->pool;
+  const int64_t max_len = (int64_t)pt_stride * p->desc.page_size;
+  int64_t total_blocks = 0;
+  for (int32_t r = 0; r < n; ++r) {
+    if (lens[r] < 1 || lens[r] > max_len)
+      return fail(PKV_ERR_INVALID_ARGUMENT, "seq_lens[%d]=%d outside [1, %lld]", r, lens[r],
+                  (long long)max_len);
+    total_blocks += (lens[r] + pkv::kBlockRows - 1) / pkv::kBlockRows;
+  }
+  std::vector<int64_t> key(2 * (size_t)n + 1);
+  key[0] = pt_stride;
+  for (int32_t r = 0; r < n; ++r) {
+    key[1 + 2 * r] = rows[r];
+    key[2 + 2 * r] = lens[r];
+  }
+  if (pl->built && key == pl->key) return PKV_OK;  // identical plan already on the device
+  pkv_status st = ensure_device(p);
+  if (st != PKV_OK) return st;
+
+  const int32_t chunk = choose_split_blocks(p, total_blocks);
+  const bool upload = !p->host_only;
+  std::vector<ReqEntry> reqs(n);
+  std::vector<WorkItem> items;
+  items.reserve((size_t)n * 2);
+  int32_t slots = 0;
+  uint64_t rows_attended = 0;
+  for (int32_t r = 0; r < n; ++r) {
+    const int32_t blocks = (lens[r] + pkv::kBlockRows - 1) / pkv::kBlockRows;
+    const int32_t nsplit = (int32_t)(((int64_t)blocks + chunk - 1) / chunk);
+    reqs[r] = ReqEntry{rows[r], lens[r], nsplit, nsplit > 1 ? slots : -1};
+    if (nsplit > 1) slots += nsplit;
+    for (int32_t s = 0; s < nsplit; ++s) {
+      const int32_t b0 = (int32_t)((int64_t)s * chunk);
+      const int32_t b1 = (int32_t)std::min<int64_t>((int64_t)(s + 1) * chunk, blocks);
+      items.push_back(WorkItem{r, b0, b1, s});
+    }
+    rows_attended += (uint64_t)lens[r];
+  }
+  std::vector<int32_t> merge_list;
+  for (int32_t r = 0; r < n; ++r)
+    if (reqs[r].nsplit > 1) merge_list.push_back(r);
+  // Longest chunks first, so the short tail chunks fill in at the end.
+  std::stable_sort(items.begin(), items.end(), [](const WorkItem& a, const WorkItem& b) {
+    return (a.blk_end - a.blk_begin) > (b.blk_end - b.blk_begin);
+  });
+
+  const size_t meta_bytes = reqs.size() * sizeof(ReqEntry) + items.size() * sizeof(WorkItem) +
+                            merge_list.size() * sizeof(int32_t);
+  if (upload) {
+  if (pl->ev_pending) {
+    PKV_HIP_TRY(hipEventSynchronize(pl->ev));
+    pl->ev_pending = false;
+  }
+  if (!pl->ev) PKV_HIP_TRY(hipEventCreateWithFlags(&pl->ev, hipEventDisableTiming));
+  if (meta_bytes > pl->d_meta_cap) {
+    const size_t cap = std::max(meta_bytes, pl->d_meta_cap * 2);
+    void* d = nullptr;
+    if (hipMalloc(&d, cap) != hipSuccess) return fail(PKV_ERR_ALLOC, "plan buffer %zu bytes", cap);
+    if (pl->d_meta) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(pl->d_meta);
+    }
+    pl->d_meta = static_cast<char*>(d);
+    pl->d_meta_cap = cap;
+  }
+  if (meta_bytes > pl->h_stage_cap) {
+    const size_t cap = std::max(meta_bytes, pl->h_stage_cap * 2);
+    void* h = nullptr;
+    if (hipHostMalloc(&h, cap, hipHostMallocDefault) != hipSuccess)
+      return fail(PKV_ERR_ALLOC, "pinned staging %zu bytes", cap);
+    if (pl->h_stage) (void)hipHostFree(pl->h_stage);
+    pl->h_stage = static_cast<char*>(h);
+    pl->h_stage_cap = cap;
+  }
+  const size_t part_floats = (size_t)slots * p->desc.num_heads * (p->desc.head_width + 2);
+  if (part_floats > pl->partials_cap) {
+    const size_t cap = std::max(part_floats, pl->partials_cap * 2);
+    void* d = nullptr;
+    if (hipMalloc(&d, cap * sizeof(float)) != hipSuccess)
+      return fail(PKV_ERR_ALLOC, "partials %zu floats", cap);
+    if (pl->d_partials) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(pl->d_partials);
+    }
+    pl->d_partials = static_cast<float*>(d);
+    pl->partials_cap = cap;
+  }
+  const size_t counters = (size_t)n * p->desc.num_heads;
+  if (counters > pl->counters_cap) {
+    const size_t cap = std::max(counters, pl->counters_cap * 2);
+    void* d = nullptr;
+    if (hipMalloc(&d, cap * sizeof(int32_t)) != hipSuccess)
+      return fail(PKV_ERR_ALLOC, "merge counters %zu", cap);
+    if (hipMemset(d, 0, cap * sizeof(int32_t)) != hipSuccess) {
+      (void)hipFree(d);
+      return fail(PKV_ERR_DEVICE, "hipMemset of merge counters failed");
+    }
+    if (pl->d_counters) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(pl->d_counters);
+    }
+    pl->d_counters = static_cast<int32_t*>(d);
+    pl->counters_cap = cap;
+  }
+  std::memcpy(pl->h_stage, reqs.data(), reqs.size() * sizeof(ReqEntry));
+  std::memcpy(pl->h_stage + reqs.size() * sizeof(ReqEntry), items.data(),
+              items.size() * sizeof(WorkItem));
+  if (!merge_list.empty())
+    std::memcpy(pl->h_stage + reqs.size() * sizeof(ReqEntry) + items.size() * sizeof(WorkItem),
+                merge_list.data(), merge_list.size() * sizeof(int32_t));
+  PKV_HIP_TRY(hipMemcpyAsync(pl->d_meta, pl->h_stage, meta_bytes, hipMemcpyHostToDevice, stream));
+  PKV_HIP_TRY(hipEventRecord(pl->ev, stream));
+  pl->ev_pending = true;
+  }  // upload
+
+  pl->reqs = std::move(reqs);
+  pl->items = std::move(items);
+  pl->key = std::move(key);
+  pl->n = n;
+  pl->pt_stride = pt_stride;
+  pl->num_items = (int32_t)pl->items.size();
+  pl->total_splits = slots;
+  pl->num_split_reqs = (int32_t)merge_list.size();
+  pl->any_split = slots > 0;
+  pl->rows_attended = rows_attended;
+  pl->built = true;
+  return PKV_OK;
+}
+
+AttnArgs make_args(const pkv_plan* pl, int32_t layer, const int32_t* page_table,
+                   const void* q, const void* k, const void* v, float* out, bool fuse) {
+  const pkv_pool* p = pl->pool;
+  AttnArgs a{};
+  a.q = q;
+  a.k_new = k;
+  a.v_new = v;
+  a.out = out;
+  a.k_layer = static_cast<char*>(p->desc.k_storage) + (int64_t)layer * p->layer_bytes;
+  a.v_layer = static_cast<char*>(p->desc.v_storage) + (int64_t)layer * p->layer_bytes;
+  a.page_table = page_table;
+  a.pt_stride = pl->pt_stride;
+  a.reqs = reinterpret_cast<const ReqEntry*>(pl->d_meta);
+  a.items = reinterpret_cast<const WorkItem*>(pl->d_meta + pl->reqs.size() * sizeof(ReqEntry));
+  a.partials = pl->d_partials;
+  a.merge_count = pl->d_counters;
+  a.merge_reqs = reinterpret_cast<const int32_t*>(pl->d_meta + pl->reqs.size() * sizeof(ReqEntry) +
+                                                  pl->items.size() * sizeof(WorkItem));
+  a.merge_mode = p->merge_mode;
+  a.num_heads = p->desc.num_heads;
+  a.page_size = p->desc.page_size;
+  a.head_width = p->desc.head_width;
+  a.fuse_append = fuse ? 1 : 0;
+  a.page_bytes = p->page_bytes;
+  a.head_bytes = p->head_bytes;
+  a.scale_log2e = (float)(1.4426950408889634 / std::sqrt((double)p->desc.head_width));
+  return a;
+}
+
+pkv_status check_ptr(const void* ptr, const char* name) {
+  if (!ptr) return fail(PKV_ERR_INVALID_ARGUMENT, "%s is null", name);
+  if (!aligned16(ptr)) return fail(PKV_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  return PKV_OK;
+}
+
+hipEvent_t take_event(pkv_pool* p) {
+  if (!p->spare.empty()) {
+    hipEvent_t e = p->spare.back();
+    p->spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Algorithmic bytes of one attention launch: pool rows read, q, the appended
+// rows (read from the inputs and written to the pool) and the context.
+uint64_t launch_bytes(const pkv_plan* pl, bool fuse) {
+  const pkv_pool* p = pl->pool;
+  const uint64_t row = (uint64_t)p->desc.num_heads * p->desc.head_width;  // per request
+  const uint64_t kv_rows = pl->rows_attended - (fuse ? (uint64_t)pl->n : 0);
+  uint64_t b = kv_rows * row * 2 * p->elt;          // K and V rows from the pool
+  b += (uint64_t)pl->n * row * (p->elt + 4);        // q in, context out
+  if (fuse) b += (uint64_t)pl->n * row * 2 * p->elt * 2;  // new K/V rows in and out
+  return b;
+}
+
+pkv_status run_attention(pkv_plan* pl, int32_t layer, const int32_t* page_table, const void* q,
+                         const void* k, const void* v, float* out, bool fuse, hipStream_t stream) {
+  pkv_pool* p = pl->pool;
+  p->counters.kv_bytes_read += pl->rows_attended * (uint64_t)p->desc.num_heads * 2ull *
+                               (uint64_t)p->desc.head_width * p->elt;
+  if (p->host_only) return PKV_OK;
+  AttnArgs a = make_args(pl, layer, page_table, q, k, v, out, fuse);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (p->profiling) {
+    e0 = take_event(p);
+    e1 = take_event(p);
+    if (!e0 || !e1) return fail(PKV_ERR_DEVICE, "hipEventCreate failed");
+    PKV_HIP_TRY(hipEventRecord(e0, stream));
+  }
+  PKV_HIP_TRY(pkv::launch_attention(a, p->desc.kv_dtype, pl->num_items, stream, nullptr));
+  if (p->profiling) {
+    PKV_HIP_TRY(hipEventRecord(e1, stream));
+    p->timed.push_back({e0, e1, false});
+    p->profile.algorithmic_bytes += launch_bytes(pl, fuse);
+  }
+  if (pl->any_split && p->merge_mode == pkv::kMergeSeparate) {
+    if (p->profiling) {
+      e0 = take_event(p);
+      e1 = take_event(p);
+      if (!e0 || !e1) return fail(PKV_ERR_DEVICE, "hipEventCreate failed");
+      PKV_HIP_TRY(hipEventRecord(e0, stream));
+    }
+    PKV_HIP_TRY(pkv::launch_merge(a, pl->num_split_reqs, stream));
+    if (p->profiling) {
+      PKV_HIP_TRY(hipEventRecord(e1, stream));
+      p->timed.push_back({e0, e1, true});
+    }
+  }
+  return PKV_OK;
+}
+
+pkv_status check_layer(const pkv_pool* p, int32_t layer) {
+  if (layer < 0 || layer >= p->desc.num_layers)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", layer, p->desc.num_layers);
+  return PKV_OK;
+}
+
+// Shared body of the single and batched transactional layer step.
+pkv_status txn_step(pkv_cache* const* caches, int32_t n, int32_t layer, const void* q,
+                    const void* k, const void* v, float* out, void* stream) {
+  if (!caches || n < 1) return fail(PKV_ERR_INVALID_ARGUMENT, "need at least one cache");
+  for (int32_t i = 0; i < n; ++i)
+    if (!caches[i]) return fail(PKV_ERR_INVALID_ARGUMENT, "caches[%d] is null", i);
+  pkv_pool* p = caches[0]->pool;
+  pkv_status st;
+  if ((st = check_layer(p, layer)) != PKV_OK) return st;
+  if ((st = check_ptr(q, "q")) != PKV_OK || (st = check_ptr(k, "k")) != PKV_OK ||
+      (st = check_ptr(v, "v")) != PKV_OK || (st = check_ptr(out, "out")) != PKV_OK)
+    return st;
+  std::vector<int32_t> rows(n), lens(n);
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_cache* c = caches[i];
+    if (c->pool != p) return fail(PKV_ERR_INVALID_ARGUMENT, "caches[%d] belongs to another pool", i);
+    if (!c->pending) return fail(PKV_ERR_BAD_STATE, "caches[%d] has no pending token", i);
+    if (c->appended[layer])
+      return fail(PKV_ERR_BAD_STATE, "caches[%d] already appended layer %d", i, layer);
+    rows[i] = c->slot;
+    lens[i] = c->pending_pos + 1;
+  }
+  if (n > 1) {
+    std::vector<int32_t> sorted(rows);
+    std::sort(sorted.begin(), sorted.end());
+    if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
+      return fail(PKV_ERR_INVALID_ARGUMENT, "a cache appears twice in the batch");
+  }
+  if ((st = ensure_device(p)) != PKV_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = flush_patches(p, s)) != PKV_OK) return st;
+  if ((st = plan_build(&p->txn_plan, n, rows.data(), lens.data(), p->arena_stride, s)) != PKV_OK)
+    return st;
+  if ((st = run_attention(&p->txn_plan, layer, p->d_arena, q, k, v, out, true, s)) != PKV_OK)
+    return st;
+  for (int32_t i = 0; i < n; ++i) {
+    caches[i]->appended[layer] = 1;
+    caches[i]->appended_count += 1;
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_version(void) { return "0.1.0"; }
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+void pkv_pool_desc_init(pkv_pool_desc* d) {
+  if (!d) return;
+  std::memset(d, 0, sizeof *d);
+  d->page_size = 16;
+  d->num_pages = 0;
+  d->max_caches = 0;
+  d->kv_dtype = PKV_DTYPE_F32;
+  d->split_blocks = 0;
+}
+
+pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out) {
+  if (!desc || !out) return fail(PKV_ERR_INVALID_ARGUMENT, "null desc or out");
+  pkv_pool_desc d = *desc;
+  if (d.num_layers < 1 || d.num_heads < 1 || d.head_width < 1 || d.page_size < 1 ||
+      d.max_context < 1 || d.num_pages < 0 || d.max_caches < 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "sizes must be positive");
+  if (d.head_width > 1024) return fail(PKV_ERR_INVALID_ARGUMENT, "head_width %d > 1024", d.head_width);
+  if (d.kv_dtype != PKV_DTYPE_F32 && d.kv_dtype != PKV_DTYPE_BF16)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "unknown kv_dtype %d", d.kv_dtype);
+  if (d.flags & ~PKV_POOL_HOST_ONLY) return fail(PKV_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", d.flags);
+  if (!d.k_storage || !d.v_storage) return fail(PKV_ERR_INVALID_ARGUMENT, "null storage");
+  if (!aligned16(d.k_storage) || !aligned16(d.v_storage))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "storage not 16-byte aligned");
+  if (d.num_pages == 0) d.num_pages = (d.max_context + d.page_size - 1) / d.page_size;
+  if (d.max_caches == 0) d.max_caches = 256;
+  const int64_t pages_per_cache = ((int64_t)d.max_context + d.page_size - 1) / d.page_size;
+  if ((int64_t)d.max_caches * pages_per_cache > std::numeric_limits<int32_t>::max())
+    return fail(PKV_ERR_INVALID_ARGUMENT, "max_caches * pages per context overflows");
+  const size_t elt = elt_bytes(d.kv_dtype);
+  const double layer_bytes =
+      (double)d.num_pages * d.num_heads * d.page_size * d.head_width * (double)elt;
+  if (layer_bytes * d.num_layers > 9.0e18)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "pool larger than 2^63 bytes");
+  pkv_pool* p = new (std::nothrow) pkv_pool();
+  if (!p) return fail(PKV_ERR_ALLOC, "pool");
+  try {
+    p->desc = d;
+    p->host_only = (d.flags & PKV_POOL_HOST_ONLY) != 0;
+    p->elt = elt;
+    p->head_bytes = (int64_t)d.page_size * d.head_width * (int64_t)elt;
+    p->page_bytes = p->head_bytes * d.num_heads;
+    p->layer_bytes = p->page_bytes * d.num_pages;
+    p->arena_stride = (int32_t)pages_per_cache;
+    p->free_stack.resize(d.num_pages);
+    for (int32_t i = 0; i < d.num_pages; ++i) p->free_stack[i] = i;
+    uint64_t s = d.free_list_seed;
+    for (int32_t i = d.num_pages - 1; i > 0; --i) {
+      const uint64_t j = ((splitmix_next(s) >> 32) * (uint64_t)(i + 1)) >> 32;
+      std::swap(p->free_stack[i], p->free_stack[(size_t)j]);
+    }
+    std::reverse(p->free_stack.begin(), p->free_stack.end());  // first lease = first shuffled ID
+    p->owner.assign(d.num_pages, kFree);
+    p->free_slots.resize(d.max_caches);
+    for (int32_t i = 0; i < d.max_caches; ++i) p->free_slots[i] = d.max_caches - 1 - i;
+    p->txn_plan.pool = p;
+    p->txn_plan.internal = true;
+    p->call_plan.pool = p;
+    p->call_plan.internal = true;
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(PKV_ERR_ALLOC, "pool metadata");
+  }
+  *out = p;
+  return ok();
+}
+
+pkv_status pkv_pool_destroy(pkv_pool* p) {
+  if (!p) return fail(PKV_ERR_INVALID_ARGUMENT, "null pool");
+  if (p->live_caches > 0 || p->live_plans > 0 || p->raw_leased > 0)
+    return fail(PKV_ERR_BAD_STATE, "pool still has %d caches, %d plans, %d raw pages",
+                p->live_caches, p->live_plans, p->raw_leased);
+  plan_release(&p->txn_plan);
+  plan_release(&p->call_plan);
+  for (const auto& t : p->timed) {
+    (void)hipEventSynchronize(t.end);
+    p->spare.push_back(t.start);
+    p->spare.push_back(t.end);
+  }
+  for (hipEvent_t e : p->spare) (void)hipEventDestroy(e);
+  if (p->d_arena) (void)hipFree(p->d_arena);
+  delete p;
+  return ok();
+}
+
+pkv_status pkv_pool_get_desc(const pkv_pool* p, pkv_pool_desc* out) {
+  if (!p || !out) return fail(PKV_ERR_INVALID_ARGUMENT, "null argument");
+  *out = p->desc;
+  return ok();
+}
+
+pkv_status pkv_pool_get_counters(const pkv_pool* p, pkv_counters* out) {
+  if (!p || !out) return fail(PKV_ERR_INVALID_ARGUMENT, "null argument");
+  *out = p->counters;
+  out->pages_free = (int32_t)p->free_stack.size();
+  out->pages_leased = p->desc.num_pages - out->pages_free;
+  return ok();
+}
+
+pkv_status pkv_pool_set_option(pkv_pool* p, int32_t option, int64_t value) {
+  if (!p) return fail(PKV_ERR_INVALID_ARGUMENT, "null pool");
+  switch (option) {
+    case PKV_OPT_SPLIT_BLOCKS:
+      if (value < -1 || value > (1 << 24)) return fail(PKV_ERR_INVALID_ARGUMENT, "split_blocks");
+      p->desc.split_blocks = (int32_t)value;
+      p->txn_plan.key.clear();
+      p->call_plan.key.clear();
+      return ok();
+    case PKV_OPT_MERGE_MODE:
+      if (value != pkv::kMergeSeparate && value != pkv::kMergeLastArriver)
+        return fail(PKV_ERR_INVALID_ARGUMENT, "merge mode %lld", (long long)value);
+      p->merge_mode = (int32_t)value;
+      return ok();
+    case PKV_OPT_PROFILING:
+      if (value != 0 && value != 1) return fail(PKV_ERR_INVALID_ARGUMENT, "profiling %lld", (long long)value);
+      p->profiling = value == 1;
+      return ok();
+    default:
+      return fail(PKV_ERR_INVALID_ARGUMENT, "unknown option %d", option);
+  }
+}
+
+pkv_status pkv_pool_get_profile(pkv_pool* p, pkv_profile* out, int32_t reset) {
+  if (!p || !out) return fail(PKV_ERR_INVALID_ARGUMENT, "null argument");
+  for (const auto& t : p->timed) {
+    PKV_HIP_TRY(hipEventSynchronize(t.end));
+    float ms = 0.f;
+    PKV_HIP_TRY(hipEventElapsedTime(&ms, t.start, t.end));
+    if (t.merge) {
+      p->profile.merge_launches += 1;
+      p->profile.merge_ms += ms;
+    } else {
+      p->profile.attention_launches += 1;
+      p->profile.attention_ms += ms;
+    }
+    p->spare.push_back(t.start);
+    p->spare.push_back(t.end);
+  }
+  p->timed.clear();
+  *out = p->profile;
+  if (reset) p->profile = pkv_profile{};
+  return ok();
+}
+
+pkv_status pkv_page_lease(pkv_pool* p, int32_t* page) {
+  if (!p || !page) return fail(PKV_ERR_INVALID_ARGUMENT, "null argument");
+  if (p->free_stack.empty()) return fail(PKV_ERR_OUT_OF_PAGES, "no free page");
+  *page = lease_page(p, kRaw);
+  p->raw_leased += 1;
+  return ok();
+}
+
+pkv_status pkv_page_release(pkv_pool* p, int32_t page) {
+  if (!p) return fail(PKV_ERR_INVALID_ARGUMENT, "null pool");
+  if (page < 0 || page >= p->desc.num_pages)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "page %d out of range", page);
+  if (p->owner[page] != kRaw) return fail(PKV_ERR_INVALID_ARGUMENT, "page %d is not raw-leased", page);
+  release_page(p, page);
+  p->raw_leased -= 1;
+  return ok();
+}
+
+pkv_status pkv_cache_create(pkv_pool* p, int32_t max_context, pkv_cache** out) {
+  if (!p || !out) return fail(PKV_ERR_INVALID_ARGUMENT, "null argument");
+  if (max_context < 1 || max_context > p->desc.max_context)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "max_context %d outside [1, %d]", max_context,
+                p->desc.max_context);
+  if (p->free_slots.empty())
+    return fail(PKV_ERR_BAD_STATE, "all %d cache slots in use", p->desc.max_caches);
+  pkv_cache* c = new (std::nothrow) pkv_cache();
+  if (!c) return fail(PKV_ERR_ALLOC, "cache");
+  try {
+    c->pages.reserve((max_context + p->desc.page_size - 1) / p->desc.page_size);
+    c->appended.assign(p->desc.num_layers, 0);
+  } catch (const std::bad_alloc&) {
+    delete c;
+    return fail(PKV_ERR_ALLOC, "cache");
+  }
+  c->pool = p;
+  c->max_context = max_context;
+  c->slot = p->free_slots.back();
+  p->free_slots.pop_back();
+  p->live_caches += 1;
+  *out = c;
+  return ok();
+}
+
+static void cache_return_pages(pkv_cache* c) {
+  for (auto it = c->pages.rbegin(); it != c->pages.rend(); ++it) release_page(c->pool, *it);
+  c->pages.clear();
+}
+
+pkv_status pkv_cache_destroy(pkv_cache* c) {
+  if (!c) return fail(PKV_ERR_INVALID_ARGUMENT, "null cache");
+  pkv_pool* p = c->pool;
+  if (c->pending) p->counters.aborted_tokens += 1;
+  cache_return_pages(c);
+  p->free_slots.push_back(c->slot);
+  p->live_caches -= 1;
+  p->txn_plan.key.clear();  // slot may be reused: never reuse a plan keyed on it
+  delete c;
+  return ok();
+}
+
+pkv_status pkv_cache_reset(pkv_cache* c) {
+  if (!c) return fail(PKV_ERR_INVALID_ARGUMENT, "null cache");
+  if (c->pending) return fail(PKV_ERR_BAD_STATE, "reset with a pending token; abort it first");
+  cache_return_pages(c);
+  c->len = 0;
+  return ok();
+}
+
+int32_t pkv_cache_size(const pkv_cache* c) { return c ? c->len : -1; }
+int32_t pkv_cache_capacity(const pkv_cache* c) { return c ? c->max_context : -1; }
+int32_t pkv_cache_block_size(const pkv_cache* c) { return c ? c->pool->desc.page_size : -1; }
+
+pkv_status pkv_cache_page_table(const pkv_cache* c, int32_t* out, int32_t cap, int32_t* n_out) {
+  if (!c || !n_out) return fail(PKV_ERR_INVALID_ARGUMENT, "null argument");
+  const int32_t n = (int32_t)c->pages.size();
+  if (n > 0 && (!out || cap < n))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "page table has %d entries, cap %d", n, cap);
+  if (n > 0) std::memcpy(out, c->pages.data(), n * sizeof(int32_t));
+  *n_out = n;
+  return ok();
+}
+
+pkv_status pkv_cache_grow(pkv_cache* c, int32_t n_tokens) {
+  if (!c) return fail(PKV_ERR_INVALID_ARGUMENT, "null cache");
+  if (n_tokens < 0) return fail(PKV_ERR_INVALID_ARGUMENT, "negative n_tokens");
+  if (c->pending) return fail(PKV_ERR_BAD_STATE, "grow with a pending token");
+  if ((int64_t)c->len + n_tokens > c->max_context)
+    return fail(PKV_ERR_CAPACITY_EXHAUSTED, "length %d + %d exceeds capacity %d", c->len,
+                n_tokens, c->max_context);
+  pkv_pool* p = c->pool;
+  const int32_t S = p->desc.page_size;
+  const int32_t need = (c->len + n_tokens + S - 1) / S - (int32_t)c->pages.size();
+  if (need > (int32_t)p->free_stack.size())
+    return fail(PKV_ERR_OUT_OF_PAGES, "need %d pages, %zu free", need, p->free_stack.size());
+  for (int32_t i = 0; i < need; ++i) {
+    const int32_t page = lease_page(p, kCache);
+    record_patch(c, (int32_t)c->pages.size(), page);
+    c->pages.push_back(page);
+  }
+  c->len += n_tokens;
+  return ok();
+}
+
+pkv_status pkv_begin_token(pkv_cache* c, int32_t* position) {
+  if (!c) return fail(PKV_ERR_INVALID_ARGUMENT, "null cache");
+  if (c->pending) return fail(PKV_ERR_BAD_STATE, "a token is already pending");
+  if (c->len >= c->max_context)
+    return fail(PKV_ERR_CAPACITY_EXHAUSTED, "cache is at its capacity %d", c->max_context);
+  pkv_pool* p = c->pool;
+  const bool new_page = c->len % p->desc.page_size == 0;
+  if (new_page && p->free_stack.empty()) return fail(PKV_ERR_OUT_OF_PAGES, "no free page");
+  if (new_page) {
+    const int32_t page = lease_page(p, kCache);
+    record_patch(c, (int32_t)c->pages.size(), page);
+    c->pages.push_back(page);
+  }
+  c->pending = true;
+  c->pending_pos = c->len;
+  c->pending_new_page = new_page;
+  std::fill(c->appended.begin(), c->appended.end(), 0);
+  c->appended_count = 0;
+  if (position) *position = c->pending_pos;
+  return ok();
+}
+
+pkv_status pkv_append_and_attend(pkv_cache* c, int32_t layer, const void* q, const void* k,
+                                 const void* v, float* out, void* stream) {
+  if (!c) return fail(PKV_ERR_INVALID_ARGUMENT, "null cache");
+  return txn_step(&c, 1, layer, q, k, v, out, stream);
+}
+
+pkv_status pkv_append_and_attend_batched(pkv_cache* const* caches, int32_t n, int32_t layer,
+                                         const void* q, const void* k, const void* v,
+                                         float* out, void* stream) {
+  return txn_step(caches, n, layer, q, k, v, out, stream);
+}
+
+pkv_status pkv_commit_token(pkv_cache* c) {
+  if (!c) return fail(PKV_ERR_INVALID_ARGUMENT, "null cache");
+  if (!c->pending) return fail(PKV_ERR_BAD_STATE, "no pending token");
+  pkv_pool* p = c->pool;
+  if (c->appended_count != p->desc.num_layers)
+    return fail(PKV_ERR_BAD_STATE, "only %d of %d layers appended", c->appended_count,
+                p->desc.num_layers);
+  c->len = c->pending_pos + 1;
+  c->pending = false;
+  p->counters.committed_tokens += 1;
+  p->counters.cache_appends += (uint64_t)p->desc.num_layers;
+  p->counters.score_cells += (uint64_t)p->desc.num_layers * p->desc.num_heads * (uint64_t)c->len;
+  return ok();
+}
+
+pkv_status pkv_abort_token(pkv_cache* c) {
+  if (!c) return fail(PKV_ERR_INVALID_ARGUMENT, "null cache");
+  if (!c->pending) return fail(PKV_ERR_BAD_STATE, "no pending token");
+  if (c->pending_new_page) {
+    release_page(c->pool, c->pages.back());
+    c->pages.pop_back();
+  }
+  c->pending = false;
+  c->pool->counters.aborted_tokens += 1;
+  return ok();
+}
+
+pkv_status pkv_plan_create(pkv_pool* p, pkv_plan** out) {
+  if (!p || !out) return fail(PKV_ERR_INVALID_ARGUMENT, "null argument");
+  pkv_plan* pl = new (std::nothrow) pkv_plan();
+  if (!pl) return fail(PKV_ERR_ALLOC, "plan");
+  pl->pool = p;
+  p->live_plans += 1;
+  *out = pl;
+  return ok();
+}
+
+pkv_status pkv_plan_destroy(pkv_plan* pl) {
+  if (!pl || pl->internal) return fail(PKV_ERR_INVALID_ARGUMENT, "null or internal plan");
+  pl->pool->live_plans -= 1;
+  plan_release(pl);
+  delete pl;
+  return ok();
+}
+
+pkv_status pkv_plan_build(pkv_plan* pl, int32_t n, const int32_t* seq_lens, int32_t pt_stride,
+                          void* stream) {
+  if (!pl || !seq_lens || n < 1 || pt_stride < 1)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "null plan/seq_lens or non-positive n/pt_stride");
+  std::vector<int32_t> rows(n);
+  for (int32_t r = 0; r < n; ++r) rows[r] = r;
+  pkv_status st = plan_build(pl, n, rows.data(), seq_lens, pt_stride,
+                             static_cast<hipStream_t>(stream));
+  return st == PKV_OK ? ok() : st;
+}
+
+int32_t pkv_plan_num_chunks(const pkv_plan* pl) {
+  return (pl && pl->built) ? pl->num_items : 0;
+}
+
+static pkv_status plan_ready(const pkv_plan* pl, int32_t layer, const int32_t* page_table) {
+  if (!pl) return fail(PKV_ERR_INVALID_ARGUMENT, "null plan");
+  if (!pl->built) return fail(PKV_ERR_BAD_STATE, "plan not built");
+  pkv_status st = check_layer(pl->pool, layer);
+  if (st != PKV_OK) return st;
+  if (!page_table) return fail(PKV_ERR_INVALID_ARGUMENT, "page_table is null");
+  return ensure_device(pl->pool);
+}
+
+pkv_status pkv_plan_decode_attention(pkv_plan* pl, int32_t layer, const void* q,
+                                     const int32_t* page_table, float* out, void* stream) {
+  pkv_status st = plan_ready(pl, layer, page_table);
+  if (st != PKV_OK) return st;
+  if ((st = check_ptr(q, "q")) != PKV_OK || (st = check_ptr(out, "out")) != PKV_OK) return st;
+  st = run_attention(pl, layer, page_table, q, nullptr, nullptr, out, false,
+                     static_cast<hipStream_t>(stream));
+  return st == PKV_OK ? ok() : st;
+}
+
+pkv_status pkv_plan_kv_append(pkv_plan* pl, int32_t layer, const int32_t* page_table,
+                              const void* k, const void* v, void* stream) {
+  pkv_status st = plan_ready(pl, layer, page_table);
+  if (st != PKV_OK) return st;
+  if ((st = check_ptr(k, "k")) != PKV_OK || (st = check_ptr(v, "v")) != PKV_OK) return st;
+  if (pl->pool->host_only) return ok();
+  AttnArgs a = make_args(pl, layer, page_table, nullptr, k, v, nullptr, false);
+  PKV_HIP_TRY(pkv::launch_kv_append(a, pl->pool->desc.kv_dtype, pl->n,
+                                    static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+pkv_status pkv_plan_append_and_attend(pkv_plan* pl, int32_t layer, const int32_t* page_table,
+                                      const void* q, const void* k, const void* v, float* out,
+                                      void* stream) {
+  pkv_status st = plan_ready(pl, layer, page_table);
+  if (st != PKV_OK) return st;
+  if ((st = check_ptr(q, "q")) != PKV_OK || (st = check_ptr(k, "k")) != PKV_OK ||
+      (st = check_ptr(v, "v")) != PKV_OK || (st = check_ptr(out, "out")) != PKV_OK)
+    return st;
+  st = run_attention(pl, layer, page_table, q, k, v, out, true, static_cast<hipStream_t>(stream));
+  return st == PKV_OK ? ok() : st;
+}
+
+pkv_status pkv_decode_attention(pkv_pool* p, int32_t layer, int32_t n, const void* q,
+                                const int32_t* page_table, int32_t pt_stride,
+                                const int32_t* seq_lens, float* out, void* stream) {
+  if (!p || !seq_lens || n < 1 || pt_stride < 1)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "null pool/seq_lens or non-positive n/pt_stride");
+  pkv_status st = check_layer(p, layer);
+  if (st != PKV_OK) return st;
+  if (!page_table) return fail(PKV_ERR_INVALID_ARGUMENT, "page_table is null");
+  if ((st = check_ptr(q, "q")) != PKV_OK || (st = check_ptr(out, "out")) != PKV_OK) return st;
+  std::vector<int32_t> rows(n);
+  for (int32_t r = 0; r < n; ++r) rows[r] = r;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = plan_build(&p->call_plan, n, rows.data(), seq_lens, pt_stride, s)) != PKV_OK) return st;
+  st = run_attention(&p->call_plan, layer, page_table, q, nullptr, nullptr, out, false, s);
+  return st == PKV_OK ? ok() : st;
+}
+
+pkv_status pkv_kv_append(pkv_pool* p, int32_t layer, int32_t n, const int32_t* page_table,
+                         int32_t pt_stride, const int32_t* positions, const void* k,
+                         const void* v, void* stream) {
+  if (!p || !positions || n < 1 || pt_stride < 1)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "null pool/positions or non-positive n/pt_stride");
+  pkv_status st = check_layer(p, layer);
+  if (st != PKV_OK) return st;
+  if (!page_table) return fail(PKV_ERR_INVALID_ARGUMENT, "page_table is null");
+  if ((st = check_ptr(k, "k")) != PKV_OK || (st = check_ptr(v, "v")) != PKV_OK) return st;
+  std::vector<int32_t> rows(n), lens(n);
+  for (int32_t r = 0; r < n; ++r) {
+    if (positions[r] < 0) return fail(PKV_ERR_INVALID_ARGUMENT, "positions[%d] < 0", r);
+    rows[r] = r;
+    lens[r] = positions[r] + 1;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = plan_build(&p->call_plan, n, rows.data(), lens.data(), pt_stride, s)) != PKV_OK)
+    return st;
+  if (p->host_only) return ok();
+  AttnArgs a = make_args(&p->call_plan, layer, page_table, nullptr, k, v, nullptr, false);
+  PKV_HIP_TRY(pkv::launch_kv_append(a, p->desc.kv_dtype, n, s));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,283 @@
+"""CPU tests of the C-ABI library: exports, argument checks and the host state
+machine (page allocator, request caches, token transaction), driven through
+the C ABI on host-only pools and compared with the oracle's transaction model."""
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import Status
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+pkv = pytest.importorskip("paged_kv_cache_attention_amd")
+
+FAKE = 0x10000  # 16-byte aligned placeholder: host-only pools never dereference it
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported_and_bound():
+    import ctypes
+    names = header_functions()
+    assert len(names) >= 30
+    lib = ctypes.CDLL(pkv.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in pkv.h but not exported"
+        assert n in pkv.SIGNATURES, f"{n} has no Python binding"
+        assert callable(getattr(pkv, n)), f"{n} missing from the Python package"
+
+
+def make_pool(layers=2, heads=2, width=2, page=16, pages=8, ctx=64, caches=8, seed=1,
+              dtype=0, split=0):
+    d = pkv.pkv_pool_desc_init()
+    d.num_layers, d.num_heads, d.head_width = layers, heads, width
+    d.page_size, d.num_pages, d.max_context = page, pages, ctx
+    d.max_caches, d.kv_dtype, d.split_blocks = caches, dtype, split
+    d.flags = pkv.PKV_POOL_HOST_ONLY
+    d.k_storage = d.v_storage = FAKE
+    d.free_list_seed = seed
+    return pkv.pkv_pool_create(d)
+
+
+def status_of(fn, *args):
+    try:
+        fn(*args)
+        return Status.OK
+    except pkv.PkvError as e:
+        return Status(e.status)
+
+
+def test_desc_defaults():
+    d = pkv.pkv_pool_desc_init()
+    assert d.page_size == 16 and d.num_pages == 0 and d.kv_dtype == 0 and d.flags == 0
+    d.num_layers, d.num_heads, d.head_width, d.max_context = 1, 1, 8, 100
+    d.flags = pkv.PKV_POOL_HOST_ONLY
+    d.k_storage = d.v_storage = FAKE
+    p = pkv.pkv_pool_create(d)
+    got = pkv.pkv_pool_get_desc(p)
+    assert got.num_pages == 7 and got.max_caches == 256   # ceil(100/16): one full context
+    pkv.pkv_pool_destroy(p)
+
+
+@pytest.mark.parametrize("field,value", [("num_layers", 0), ("num_heads", -1), ("head_width", 0),
+                                         ("head_width", 1025), ("page_size", 0),
+                                         ("max_context", 0), ("kv_dtype", 7), ("flags", 2),
+                                         ("k_storage", None), ("v_storage", FAKE + 4)])
+def test_pool_create_rejects(field, value):
+    d = pkv.pkv_pool_desc_init()
+    d.num_layers, d.num_heads, d.head_width, d.max_context = 1, 1, 8, 64
+    d.flags = pkv.PKV_POOL_HOST_ONLY
+    d.k_storage = d.v_storage = FAKE
+    setattr(d, field, value)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_pool_create(d)
+    assert e.value.status == pkv.PKV_ERR_INVALID_ARGUMENT
+
+
+def test_free_list_is_seeded_permutation_and_raw_lease():
+    p = make_pool(pages=64, seed=11)
+    got = [pkv.pkv_page_lease(p) for _ in range(64)]
+    assert sorted(got) == list(range(64)) and got != list(range(64))
+    assert status_of(pkv.pkv_page_lease, p) == Status.OUT_OF_PAGES
+    assert status_of(pkv.pkv_pool_destroy, p) == Status.BAD_STATE
+    assert status_of(pkv.pkv_page_release, p, 64) == Status.INVALID_ARGUMENT
+    for g in got:
+        pkv.pkv_page_release(p, g)
+    assert status_of(pkv.pkv_page_release, p, got[0]) == Status.INVALID_ARGUMENT
+    p2 = make_pool(pages=64, seed=11)
+    assert [pkv.pkv_page_lease(p2) for _ in range(64)] == got  # same seed, same order
+    for g in got:
+        pkv.pkv_page_release(p2, g)
+    pkv.pkv_pool_destroy(p)
+    pkv.pkv_pool_destroy(p2)
+
+
+def step(cache, layers, q=FAKE):
+    pos = pkv.pkv_begin_token(cache)
+    for layer in range(layers):
+        pkv.pkv_append_and_attend(cache, layer, q, q, q, q, stream=0)
+    pkv.pkv_commit_token(cache)
+    return pos
+
+
+def test_tiny_fixture_schedule_on_host():
+    # 2 layers, 2 heads, context 4, 16-token pages, 8 pages: the pages' fixture
+    p = make_pool(layers=2, heads=2, ctx=4, pages=8)
+    c = pkv.pkv_cache_create(p, 4)
+    assert (pkv.pkv_cache_size(c), pkv.pkv_cache_capacity(c), pkv.pkv_cache_block_size(c)) == \
+        (0, 4, 16)
+    assert [step(c, 2) for _ in range(3)] == [0, 1, 2]
+    cnt = pkv.pkv_pool_get_counters(p)
+    # counters after prompt (2 rows) + 1 decoded row: 6 appends, 24 score cells
+    assert cnt.cache_appends == 6 and cnt.score_cells == 24 and cnt.committed_tokens == 3
+    assert len(pkv.pkv_cache_page_table(c)) == 1 and cnt.pages_leased == 1
+    step(c, 2)
+    assert status_of(pkv.pkv_begin_token, c) == Status.CAPACITY_EXHAUSTED
+    assert pkv.pkv_cache_size(c) == 4
+    pkv.pkv_cache_destroy(c)
+    assert pkv.pkv_pool_get_counters(p).pages_free == 8
+    pkv.pkv_pool_destroy(p)
+
+
+def test_lazy_lease_abort_and_reset_replay():
+    p = make_pool(layers=3, page=4, pages=16, ctx=40)
+    c = pkv.pkv_cache_create(p, 40)
+    for _ in range(5):
+        step(c, 3)
+    pt = pkv.pkv_cache_page_table(c)
+    assert len(pt) == 2                           # 5 rows in 4-row pages
+    for _ in range(3):
+        step(c, 3)
+    assert len(pkv.pkv_cache_page_table(c)) == 2  # rows 0..7 fill two pages exactly
+    free_before = pkv.pkv_pool_get_counters(p).pages_free
+    pkv.pkv_begin_token(c)                        # position 8 starts a page: leased
+    assert pkv.pkv_pool_get_counters(p).pages_free == free_before - 1
+    pkv.pkv_append_and_attend(c, 0, FAKE, FAKE, FAKE, FAKE, stream=0)
+    pkv.pkv_abort_token(c)
+    assert pkv.pkv_cache_size(c) == 8
+    assert pkv.pkv_pool_get_counters(p).pages_free == free_before
+    table = pkv.pkv_cache_page_table(c)
+    assert len(table) == 2
+    pkv.pkv_cache_reset(c)
+    assert pkv.pkv_cache_size(c) == 0 and pkv.pkv_pool_get_counters(p).pages_free == 16
+    for _ in range(8):
+        step(c, 3)
+    assert pkv.pkv_cache_page_table(c) == table   # replay leases the same pages
+    pkv.pkv_cache_destroy(c)
+    pkv.pkv_pool_destroy(p)
+
+
+def test_rejected_calls_change_nothing():
+    p = make_pool(layers=2, pages=2, page=4, ctx=16)
+    c = pkv.pkv_cache_create(p, 16)
+    d = pkv.pkv_cache_create(p, 16)
+
+    def snap():
+        cnt = pkv.pkv_pool_get_counters(p)
+        return (pkv.pkv_cache_size(c), tuple(pkv.pkv_cache_page_table(c)), cnt.pages_free,
+                cnt.committed_tokens, pkv.pkv_cache_size(d))
+
+    s0 = snap()
+    assert status_of(pkv.pkv_commit_token, c) == Status.BAD_STATE
+    assert status_of(pkv.pkv_abort_token, c) == Status.BAD_STATE
+    assert status_of(pkv.pkv_append_and_attend, c, 0, FAKE, FAKE, FAKE, FAKE, 0) == Status.BAD_STATE
+    assert snap() == s0
+    pkv.pkv_begin_token(c)
+    s1 = snap()
+    assert status_of(pkv.pkv_begin_token, c) == Status.BAD_STATE
+    assert status_of(pkv.pkv_append_and_attend, c, 2, FAKE, FAKE, FAKE, FAKE, 0) == \
+        Status.INVALID_ARGUMENT
+    assert status_of(pkv.pkv_append_and_attend, c, 0, None, FAKE, FAKE, FAKE, 0) == \
+        Status.INVALID_ARGUMENT
+    assert status_of(pkv.pkv_append_and_attend, c, 0, FAKE + 8, FAKE, FAKE, FAKE, 0) == \
+        Status.INVALID_ARGUMENT
+    pkv.pkv_append_and_attend(c, 0, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert status_of(pkv.pkv_append_and_attend, c, 0, FAKE, FAKE, FAKE, FAKE, 0) == Status.BAD_STATE
+    assert status_of(pkv.pkv_commit_token, c) == Status.BAD_STATE   # layer 1 missing
+    assert status_of(pkv.pkv_cache_reset, c) == Status.BAD_STATE
+    assert status_of(pkv.pkv_cache_grow, c, 1) == Status.BAD_STATE
+    # batched: d not pending -> whole call rejected, c's layer 1 stays unappended
+    assert status_of(pkv.pkv_append_and_attend_batched, [c, d], 1, FAKE, FAKE, FAKE, FAKE, 0) == \
+        Status.BAD_STATE
+    assert status_of(pkv.pkv_append_and_attend_batched, [c, c], 1, FAKE, FAKE, FAKE, FAKE, 0) == \
+        Status.INVALID_ARGUMENT
+    assert snap() == s1
+    pkv.pkv_append_and_attend(c, 1, FAKE, FAKE, FAKE, FAKE, stream=0)
+    pkv.pkv_commit_token(c)
+    # pool exhaustion: 2 pages of 4 rows
+    pkv.pkv_cache_grow(c, 3)                       # c holds rows 0..3: page 1 full
+    pkv.pkv_cache_grow(d, 1)                       # d takes the second page
+    s2 = snap()
+    assert status_of(pkv.pkv_begin_token, c) == Status.OUT_OF_PAGES
+    assert status_of(pkv.pkv_cache_grow, c, 1) == Status.OUT_OF_PAGES
+    assert status_of(pkv.pkv_cache_grow, c, 13) == Status.CAPACITY_EXHAUSTED
+    assert snap() == s2
+    pkv.pkv_cache_destroy(c)
+    pkv.pkv_cache_destroy(d)
+    pkv.pkv_pool_destroy(p)
+
+
+def test_cache_slots_and_geometry_checks():
+    p = make_pool(caches=2, ctx=32)
+    assert status_of(pkv.pkv_cache_create, p, 33) == Status.INVALID_ARGUMENT
+    a = pkv.pkv_cache_create(p, 32)
+    b = pkv.pkv_cache_create(p, 8)
+    assert status_of(pkv.pkv_cache_create, p, 8) == Status.BAD_STATE
+    assert status_of(pkv.pkv_pool_destroy, p) == Status.BAD_STATE
+    pkv.pkv_cache_destroy(a)
+    pkv.pkv_cache_destroy(b)
+    pkv.pkv_pool_destroy(p)
+
+
+def test_plan_and_batched_call_validation():
+    p = make_pool(pages=64, ctx=256)
+    plan = pkv.pkv_plan_create(p)
+    assert pkv.pkv_plan_num_chunks(plan) == 0
+    assert status_of(pkv.pkv_plan_decode_attention, plan, 0, FAKE, FAKE, FAKE, 0) == Status.BAD_STATE
+    assert status_of(pkv.pkv_plan_build, plan, [3, 0], 4, 0) == Status.INVALID_ARGUMENT
+    assert status_of(pkv.pkv_plan_build, plan, [3, 65], 4, 0) == Status.INVALID_ARGUMENT
+    pkv.pkv_plan_build(plan, [3, 64, 17], 4, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 3
+    assert status_of(pkv.pkv_plan_decode_attention, plan, 2, FAKE, FAKE, FAKE, 0) == \
+        Status.INVALID_ARGUMENT
+    assert status_of(pkv.pkv_decode_attention, p, 0, FAKE, FAKE, 4, [0], FAKE, 0) == \
+        Status.INVALID_ARGUMENT
+    assert status_of(pkv.pkv_kv_append, p, 0, FAKE, 4, [64], FAKE, FAKE, 0) == \
+        Status.INVALID_ARGUMENT
+    assert status_of(pkv.pkv_pool_destroy, p) == Status.BAD_STATE
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(p)
+
+
+def test_split_plan_chunking():
+    # fixed 2-block chunks: a 100-row request (7 blocks) splits into 4 chunks
+    p = make_pool(pages=64, ctx=1024, split=2)
+    plan = pkv.pkv_plan_create(p)
+    pkv.pkv_plan_build(plan, [100, 16, 33], 64, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 4 + 1 + 2
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(p)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_state_machine_matches_oracle_model(seed):
+    rnd = random.Random(seed)
+    layers, page, pages, ctx = 2, 4, 12, 24
+    p = make_pool(layers=layers, page=page, pages=pages, ctx=ctx)
+    pool_model = oracle.PoolModel(pages)
+    caches = [(pkv.pkv_cache_create(p, ctx), oracle.CacheModel(pool_model, layers, ctx, page))
+              for _ in range(3)]
+    ops = ["begin", "append", "commit", "abort", "reset"]
+    for _ in range(600):
+        c, m = rnd.choice(caches)
+        op = rnd.choices(ops, weights=[4, 6, 3, 1, 0.3])[0]
+        if op == "begin":
+            got, want = status_of(pkv.pkv_begin_token, c), m.begin()
+        elif op == "append":
+            layer = rnd.randrange(layers + 1)
+            got = status_of(pkv.pkv_append_and_attend, c, layer, FAKE, FAKE, FAKE, FAKE, 0)
+            want = m.append(layer)
+        elif op == "commit":
+            got, want = status_of(pkv.pkv_commit_token, c), m.commit()
+        elif op == "abort":
+            got, want = status_of(pkv.pkv_abort_token, c), m.abort()
+        else:
+            got, want = status_of(pkv.pkv_cache_reset, c), m.reset()
+        assert got == want, (op, got, want)
+        assert pkv.pkv_cache_size(c) == m.length
+        assert len(pkv.pkv_cache_page_table(c)) == m.pages_held
+        assert pkv.pkv_pool_get_counters(p).pages_free == pool_model.free
+    tables = [pkv.pkv_cache_page_table(c) for c, _ in caches]
+    flat = [x for t in tables for x in t]
+    assert len(flat) == len(set(flat)) and all(0 <= x < pages for x in flat)
+    for c, _ in caches:
+        pkv.pkv_cache_destroy(c)
+    assert pkv.pkv_pool_get_counters(p).pages_free == pages
+    pkv.pkv_pool_destroy(p)

@@ -1,0 +1,469 @@
+"""GPU parity: the HIP library through its C ABI against the float64 oracle.
+
+Inputs are drawn by ``synth``; the device pools are filled by the generator's
+device kernel and the oracle regenerates the same pages on the host.  Bars:
+max abs error 1e-5 (float32 K/V) and 2e-2 (bfloat16 K/V, float32
+accumulate); page writes bit-exact; page-table permutation and page-size
+changes bit-identical on the device.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import workloads as W
+from tests.gpu_support import (TOL, HostPages, device_pool, max_err, rows_to_device, to_bits)
+
+pytestmark = pytest.mark.gpu
+pkv = pytest.importorskip("paged_kv_cache_attention_amd")
+
+
+def _pool(w, kp, vp, split=0, seed=0, max_caches=0, max_context=None, merge=0):
+    d = pkv.pkv_pool_desc_init()
+    d.num_layers, d.num_heads, d.head_width = w.layers, w.heads, w.head_width
+    d.page_size, d.num_pages = w.page_size, w.num_pages
+    d.max_context = max_context or w.pt_stride * w.page_size
+    d.max_caches = max_caches
+    d.kv_dtype = pkv.PKV_DTYPE_F32 if w.dtype == "f32" else pkv.PKV_DTYPE_BF16
+    d.split_blocks = split
+    d.k_storage, d.v_storage = kp.data_ptr(), vp.data_ptr()
+    d.free_list_seed = seed
+    pool = pkv.pkv_pool_create(d)
+    pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_MERGE_MODE, merge)
+    return pool
+
+
+def _small(name, dtype, D, S, lengths, heads=3, layers=2, seed=17, extra_pages=5):
+    lengths = np.asarray(lengths, dtype=np.int64)
+    P = int(W.pages_needed(lengths, S).sum()) + extra_pages
+    w = W.Workload(name, seed, len(lengths), layers, heads, D, S, P, dtype, lengths,
+                   appends=True)
+    return W._finish(w)
+
+
+def _oracle_decode(w, layer, r, q_host, appended=None):
+    """Oracle context of request r: over the generator pages, or with the
+    newest row supplied as a candidate when the step appended it."""
+    kp, vp = HostPages(w, "k", layer), HostPages(w, "v", layer)
+    t = int(w.lengths[r])
+    pt = w.page_tables[r]
+    if appended is None:
+        return oracle.paged_decode_attention(q_host[r], kp, vp, pt, t, w.page_size)
+    k_new, v_new = appended
+    return oracle.append_and_attend(q_host[r], k_new[r], v_new[r], kp, vp, pt, t - 1, w.page_size)
+
+
+def _pt_device(w):
+    return torch.from_numpy(w.page_tables.copy()).to("cuda")
+
+
+# --------------------------------------------------------------- generator --
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_device_fill_matches_host_generator(dtype):
+    from synth import gpu as sgpu
+    key = synth.stream_key(99, synth.TAG_MISC, 1)
+    t = torch.empty(1 << 20, dtype=sgpu.torch_dtype(dtype), device="cuda")
+    sgpu.fill_normal(t, key, dtype, start=12345)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(t, dtype), synth.normals(key, 12345, 1 << 20, dtype))
+
+
+# ------------------------------------------------------------ tiny fixture --
+def _tiny_run(page_size, num_pages, seed=3, abort_at=None):
+    """Token-at-a-time through begin / append_and_attend x L / commit on one
+    request: L=2, H=2, d_h=2, lengths 1..4.  Returns the outputs per step."""
+    g = W.tiny_geometry()
+    L, H, D, C = g["layers"], g["heads"], g["head_width"], g["max_len"]
+    shape = (L, num_pages, H, page_size, D)
+    kp = torch.full(shape, float("nan"), device="cuda")
+    vp = torch.full(shape, float("nan"), device="cuda")
+    d = pkv.pkv_pool_desc_init()
+    d.num_layers, d.num_heads, d.head_width = L, H, D
+    d.page_size, d.num_pages, d.max_context = page_size, num_pages, C
+    d.k_storage, d.v_storage, d.free_list_seed = kp.data_ptr(), vp.data_ptr(), seed
+    pool = pkv.pkv_pool_create(d)
+    cache = pkv.pkv_cache_create(pool, C)
+    hist_k = np.zeros((L, 1, H, C, D), dtype=np.float32)   # contiguous strategy
+    hist_v = np.zeros((L, 1, H, C, D), dtype=np.float32)
+    outs = []
+    for pos in range(C):
+        for attempt in range(2 if abort_at == pos else 1):
+            assert pkv.pkv_begin_token(cache) == pos
+            step_out = []
+            layers = range(L) if attempt == 1 or abort_at != pos else range(1)
+            for layer in layers:
+                # the aborted attempt uses different rows than the retried one
+                qh, kh, vh = W.tiny_rows(g["seed"] + 100 * (attempt == 0 and abort_at == pos),
+                                         layer, pos, H, D)
+                q, k, v = (rows_to_device(x, "f32") for x in (qh, kh, vh))
+                out = torch.empty((H, D), device="cuda")
+                pkv.pkv_append_and_attend(cache, layer, q, k, v, out)
+                torch.cuda.synchronize()
+                step_out.append(out.cpu().numpy().copy())
+                if attempt == 0 and abort_at == pos:
+                    continue
+                ref = oracle.append_and_attend(qh, kh, vh, hist_k[layer], hist_v[layer], [0],
+                                               pos, C)
+                assert max_err(out, ref) <= TOL["f32"]
+                pt = pkv.pkv_cache_page_table(cache)
+                page, slot = pt[pos // page_size], pos % page_size
+                assert np.array_equal(to_bits(kp[layer, page, :, slot, :], "f32"), kh)
+                assert np.array_equal(to_bits(vp[layer, page, :, slot, :], "f32"), vh)
+                hist_k[layer, 0, :, pos, :] = kh
+                hist_v[layer, 0, :, pos, :] = vh
+            if attempt == 0 and abort_at == pos:
+                pkv.pkv_abort_token(cache)
+                assert pkv.pkv_cache_size(cache) == pos
+                continue
+            pkv.pkv_commit_token(cache)
+            outs.append(np.stack(step_out))
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_begin_token(cache)
+    assert e.value.status == pkv.PKV_ERR_CAPACITY_EXHAUSTED
+    cnt = pkv.pkv_pool_get_counters(pool)
+    assert cnt.cache_appends == L * C and cnt.score_cells == L * H * sum(range(1, C + 1))
+    pkv.pkv_cache_destroy(cache)
+    pkv.pkv_pool_destroy(pool)
+    return outs
+
+
+def test_tiny_fixture_transactions():
+    base = _tiny_run(16, 8)
+    assert len(base) == 4 and base[0].shape == (2, 2, 2)
+    # lengths 1: the context is the newest value row itself, exactly
+    for layer in range(2):
+        _, _, vh = W.tiny_rows(W.tiny_geometry()["seed"], layer, 0, 2, 2)
+        assert np.array_equal(base[0][layer], vh)
+    # page size 1 and 2 (rows cross pages), and the contiguous strategy (one
+    # page of the full context): bit-identical on the device
+    for S, P in ((1, 8), (2, 8), (4, 2)):
+        other = _tiny_run(S, P, seed=S + 7)
+        for a, b in zip(base, other):
+            assert np.array_equal(a, b), f"page size {S} differs"
+    # an aborted token leaves no trace: the retried step equals the plain run
+    aborted = _tiny_run(16, 8, abort_at=2)
+    for a, b in zip(base, aborted):
+        assert np.array_equal(a, b)
+
+
+# -------------------------------------------------------- batched, small --
+SMALL_CASES = [
+    ("f32", 64, 16), ("bf16", 128, 16), ("bf16", 128, 32),   # fast path
+    ("f32", 40, 16), ("bf16", 256, 16), ("f32", 64, 5), ("bf16", 128, 7),  # generic path
+]
+LENGTHS = [1, 15, 16, 17, 100, 333, 1000]
+
+
+MERGES = [pkv.PKV_MERGE_SEPARATE, pkv.PKV_MERGE_LAST_ARRIVER]
+
+
+@pytest.mark.parametrize("dtype,D,S", SMALL_CASES)
+@pytest.mark.parametrize("split,merge", [(0, 0), (2, 0), (2, 2), (-1, 0)])
+def test_batched_decode_small(dtype, D, S, split, merge):
+    w = _small(f"small_{dtype}_{D}_{S}", dtype, D, S, LENGTHS)
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp, split=split, merge=merge)
+    plan = pkv.pkv_plan_create(pool)
+    pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
+    if split == 2:
+        assert pkv.pkv_plan_num_chunks(plan) > w.n
+    pt = _pt_device(w)
+    for layer in range(w.layers):
+        qh = w.q(layer)
+        q = rows_to_device(qh, dtype)
+        out = torch.empty((w.n, w.heads, D), device="cuda")
+        pkv.pkv_plan_decode_attention(plan, layer, q, pt, out)
+        torch.cuda.synchronize()
+        for r in range(w.n):
+            ref = _oracle_decode(w, layer, r, qh)
+            assert max_err(out[r], ref) <= TOL[dtype], (layer, r, int(w.lengths[r]))
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(pool)
+
+
+@pytest.mark.parametrize("dtype,D,S", SMALL_CASES)
+@pytest.mark.parametrize("merge", MERGES)
+def test_append_and_attend_small(dtype, D, S, merge):
+    w = _small(f"append_{dtype}_{D}_{S}", dtype, D, S, LENGTHS, seed=23)
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp, split=2, merge=merge)
+    plan = pkv.pkv_plan_create(pool)
+    pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
+    pt = _pt_device(w)
+    layer = 1
+    qh, kh, vh = w.q(layer), w.k_new(layer), w.v_new(layer)
+    q, k, v = (rows_to_device(x, dtype) for x in (qh, kh, vh))
+    out = torch.empty((w.n, w.heads, D), device="cuda")
+    pkv.pkv_plan_append_and_attend(plan, layer, pt, q, k, v, out)
+    torch.cuda.synchronize()
+    for r in range(w.n):
+        t = int(w.lengths[r])
+        page, slot = w.page_tables[r][(t - 1) // S], (t - 1) % S
+        assert np.array_equal(to_bits(kp[layer, page, :, slot, :], dtype), kh[r])
+        assert np.array_equal(to_bits(vp[layer, page, :, slot, :], dtype), vh[r])
+        ref = _oracle_decode(w, layer, r, qh, appended=(kh, vh))
+        assert max_err(out[r], ref) <= TOL[dtype], (r, t)
+    # the unfused pair (append, then attend) gives bit-identical contexts
+    kp2, vp2 = device_pool(w, layers=[layer])
+    pool2 = _pool(w, kp2, vp2, split=2, merge=merge)
+    pkv.pkv_kv_append(pool2, layer, pt, w.pt_stride, (w.lengths - 1).tolist(), k, v)
+    out2 = torch.empty_like(out)
+    pkv.pkv_decode_attention(pool2, layer, q, pt, w.pt_stride, w.lengths.tolist(), out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    assert torch.equal(kp[layer], kp2[layer]) and torch.equal(vp[layer], vp2[layer])
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(pool)
+    pkv.pkv_pool_destroy(pool2)
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128), ("f32", 24)])
+@pytest.mark.parametrize("merge", MERGES)
+def test_page_table_permutation_is_bit_identical(dtype, D, merge):
+    w = _small("perm", dtype, D, 16, [1, 31, 300, 777], heads=2, layers=1, extra_pages=40)
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp, split=4, merge=merge)
+    q = rows_to_device(w.q(0), dtype)
+    out_a = torch.empty((w.n, w.heads, D), device="cuda")
+    pt_a = _pt_device(w)
+    pkv.pkv_decode_attention(pool, 0, q, pt_a, w.pt_stride, w.lengths.tolist(), out_a)
+    # move every used page to a new physical ID (a permutation of the pool)
+    perm = torch.from_numpy(synth.shuffle(synth.stream_key(5, synth.TAG_SHUFFLE), w.num_pages)
+                            .astype(np.int64)).to("cuda")
+    kp_b = torch.empty_like(kp)
+    vp_b = torch.empty_like(vp)
+    kp_b[0, perm] = kp[0]
+    vp_b[0, perm] = vp[0]
+    pt_b = torch.where(pt_a >= 0, perm[pt_a.clamp(min=0).long()].int(), pt_a)
+    pool_b = _pool(w, kp_b, vp_b, split=4, merge=merge)
+    out_b = torch.empty_like(out_a)
+    pkv.pkv_decode_attention(pool_b, 0, q, pt_b.contiguous(), w.pt_stride, w.lengths.tolist(),
+                             out_b)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    pkv.pkv_pool_destroy(pool)
+    pkv.pkv_pool_destroy(pool_b)
+
+
+def test_split_and_unsplit_agree_and_degenerate_cases():
+    w = _small("deg", "f32", 64, 16, [1, 2, 4000], heads=2, layers=1, extra_pages=0)
+    kp, vp = device_pool(w)
+    q = rows_to_device(w.q(0), "f32")
+    pt = _pt_device(w)
+    outs = []
+    for split, merge in ((-1, 0), (1, 0), (3, 0), (64, 0), (1, 2), (3, 2)):
+        pool = _pool(w, kp, vp, split=split, merge=merge)
+        out = torch.empty((w.n, w.heads, 64), device="cuda")
+        pkv.pkv_decode_attention(pool, 0, q, pt, w.pt_stride, w.lengths.tolist(), out)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+        pkv.pkv_pool_destroy(pool)
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= TOL["f32"]
+    # t = 1: the context is the single value row, exactly
+    page = int(w.page_tables[0][0])
+    v0 = vp[0, page, :, 0, :].cpu().numpy()
+    assert np.array_equal(outs[0][0], v0)
+    # zero query: the mean of the value rows
+    pool = _pool(w, kp, vp)
+    out = torch.empty((w.n, w.heads, 64), device="cuda")
+    pkv.pkv_decode_attention(pool, 0, torch.zeros_like(q), pt, w.pt_stride,
+                             w.lengths.tolist(), out)
+    torch.cuda.synchronize()
+    for r in range(w.n):
+        V = np.stack([oracle.gather_prefix(HostPages(w, "v", 0), w.page_tables[r],
+                                           int(w.lengths[r]), 16, h) for h in range(2)])
+        assert np.max(np.abs(out[r].cpu().numpy() - V.astype(np.float64).mean(axis=1))) <= 1e-5
+    # a dominant score (q equal to one key, scaled up): finite, that value row
+    big = np.zeros((w.n, w.heads, 64), dtype=np.float32)
+    kpages = HostPages(w, "k", 0)
+    target = 1234
+    for h in range(2):
+        K = oracle.gather_prefix(kpages, w.page_tables[2], 4000, 16, h)
+        big[2, h] = K[target] * 40.0
+    out = torch.empty((w.n, w.heads, 64), device="cuda")
+    pkv.pkv_decode_attention(pool, 0, rows_to_device(big, "f32"), pt, w.pt_stride,
+                             w.lengths.tolist(), out)
+    torch.cuda.synchronize()
+    got = out[2].cpu().numpy()
+    assert np.all(np.isfinite(got))
+    ref = oracle.paged_decode_attention(big[2], kpages, HostPages(w, "v", 0), w.page_tables[2],
+                                        4000, 16)
+    assert np.max(np.abs(got - ref)) <= 1e-5
+    pkv.pkv_pool_destroy(pool)
+
+
+def test_empty_and_oversized_inputs_rejected():
+    w = _small("rej", "f32", 64, 16, [5], heads=1, layers=1)
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp)
+    q = torch.zeros((1, 1, 64), device="cuda")
+    out = torch.empty_like(q)
+    pt = _pt_device(w)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_decode_attention(pool, 0, q, pt, w.pt_stride, [], out)
+    assert e.value.status == pkv.PKV_ERR_INVALID_ARGUMENT
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_decode_attention(pool, 0, q, pt, w.pt_stride, [w.pt_stride * 16 + 1], out)
+    assert e.value.status == pkv.PKV_ERR_INVALID_ARGUMENT
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_decode_attention(pool, 0, q[..., 1:], pt, w.pt_stride, [5], out)  # misaligned
+    pkv.pkv_pool_destroy(pool)
+
+
+def test_maximum_head_width_generic():
+    w = _small("wide", "f32", 1024, 16, [1, 70, 129], heads=2, layers=1)
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp, split=2)
+    qh = w.q(0)
+    out = torch.empty((w.n, w.heads, 1024), device="cuda")
+    pkv.pkv_decode_attention(pool, 0, rows_to_device(qh, "f32"), _pt_device(w), w.pt_stride,
+                             w.lengths.tolist(), out)
+    torch.cuda.synchronize()
+    for r in range(w.n):
+        assert max_err(out[r], _oracle_decode(w, 0, r, qh)) <= TOL["f32"]
+    pkv.pkv_pool_destroy(pool)
+
+
+# ------------------------------------------------------ full-size configs --
+def _sampled(n, extra=()):
+    idx = sorted(set(list(range(0, n, max(1, n // 6))) + [n - 1] + list(extra)))
+    return idx
+
+
+@pytest.mark.parametrize("merge", MERGES)
+def test_batch32_fp32_l12_full_step(merge):
+    """32 requests x 12 layers, H=12, d_h=64, fp32, 4096-page pool: one decode
+    step (fused append + attend per layer) under the launch the bench times."""
+    w = W.batch32_fp32()
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp, merge=merge, split=4)
+    plan = pkv.pkv_plan_create(pool)
+    pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
+    pt = _pt_device(w)
+    outs = []
+    for layer in range(w.layers):
+        q, k, v = (rows_to_device(x, "f32") for x in (w.q(layer), w.k_new(layer), w.v_new(layer)))
+        out = torch.empty((w.n, w.heads, w.head_width), device="cuda")
+        pkv.pkv_plan_append_and_attend(plan, layer, pt, q, k, v, out)
+        outs.append(out)
+    torch.cuda.synchronize()
+    rows = np.arange(w.n)
+    last = w.lengths - 1
+    pages = w.page_tables[rows, last // 16]
+    for layer in range(w.layers):
+        kh, vh = w.k_new(layer), w.v_new(layer)
+        got_k = to_bits(kp[layer][torch.from_numpy(pages).long(), :, torch.from_numpy(last % 16)
+                                  .long(), :], "f32")
+        got_v = to_bits(vp[layer][torch.from_numpy(pages).long(), :, torch.from_numpy(last % 16)
+                                  .long(), :], "f32")
+        assert np.array_equal(got_k, kh) and np.array_equal(got_v, vh)
+    longest = int(np.argmax(w.lengths))
+    for layer in (0, 5, 11):
+        qh = w.q(layer)
+        for r in _sampled(w.n, extra=[longest, int(np.argmin(w.lengths))]):
+            ref = _oracle_decode(w, layer, r, qh, appended=(w.k_new(layer), w.v_new(layer)))
+            assert max_err(outs[layer][r], ref) <= TOL["f32"], (layer, r)
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(pool)
+
+
+@pytest.mark.parametrize("maker", [W.batch256_bf16, W.skewed64_bf16])
+@pytest.mark.parametrize("merge", MERGES)
+def test_bf16_single_layer_full(maker, merge):
+    w = maker()
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp, merge=merge)
+    plan = pkv.pkv_plan_create(pool)
+    pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
+    if w.lengths.max() > 4096:
+        assert pkv.pkv_plan_num_chunks(plan) > w.n   # long contexts are split
+    qh = w.q(0)
+    out = torch.empty((w.n, w.heads, w.head_width), device="cuda")
+    pkv.pkv_plan_decode_attention(plan, 0, rows_to_device(qh, "bf16"), _pt_device(w), out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    longest, shortest = int(np.argmax(w.lengths)), int(np.argmin(w.lengths))
+    for r in _sampled(w.n, extra=[longest, shortest])[:12]:
+        ref = _oracle_decode(w, 0, r, qh)
+        assert max_err(out[r], ref) <= TOL["bf16"], (r, int(w.lengths[r]))
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(pool)
+
+
+def test_fullstep128_bf16_l32_transactional():
+    """128 caches x 32 layers, H=32, d_h=128, bf16: begin, batched
+    append_and_attend per layer, commit; seeded aborts; then the aborted
+    requests retry and match a run that never saw the aborted token."""
+    w = W.fullstep128_bf16(extra_steps=4)
+    checked_layers = [0, 13, 31]
+    kp, vp = device_pool(w, layers=checked_layers)
+    pool = _pool(w, kp, vp, seed=55, max_caches=w.n, max_context=4096)
+    caches = [pkv.pkv_cache_create(pool, 4096) for _ in range(w.n)]
+    prefix = w.lengths - 1
+    for c, n in zip(caches, prefix.tolist()):
+        pkv.pkv_cache_grow(c, n)
+    tables = [pkv.pkv_cache_page_table(c) for c in caches]
+    flat = [p for t in tables for p in t]
+    assert len(flat) == len(set(flat))
+    # find a step with at least one abort
+    step = next(s for s in range(100) if (w.abort_layer(s) >= 0).any())
+    abort = w.abort_layer(step)
+    for c in caches:
+        pkv.pkv_begin_token(c)
+    tables = [pkv.pkv_cache_page_table(c) for c in caches]
+    outs = {}
+    live = list(range(w.n))
+    for layer in range(w.layers):
+        for r in [r for r in live if abort[r] == layer]:
+            pkv.pkv_abort_token(caches[r])
+        live = [r for r in live if abort[r] != layer]
+        qa, ka, va = w.q(layer, step), w.k_new(layer, step), w.v_new(layer, step)
+        q, k, v = (rows_to_device(x[live], "bf16") for x in (qa, ka, va))
+        out = torch.empty((len(live), w.heads, w.head_width), device="cuda")
+        pkv.pkv_append_and_attend_batched([caches[r] for r in live], layer, q, k, v, out)
+        if layer in checked_layers:
+            outs[layer] = (list(live), out)
+    torch.cuda.synchronize()
+    for r in live:
+        pkv.pkv_commit_token(caches[r])
+    aborted = [r for r in range(w.n) if abort[r] >= 0]
+    assert aborted
+    for r in range(w.n):
+        assert pkv.pkv_cache_size(caches[r]) == prefix[r] + (0 if r in aborted else 1)
+    for layer in checked_layers:
+        lv, out = outs[layer]
+        qa, ka, va = w.q(layer, step), w.k_new(layer, step), w.v_new(layer, step)
+        kpg, vpg = HostPages(w, "k", layer), HostPages(w, "v", layer)
+        for i in _sampled(len(lv))[:5]:
+            r = lv[i]
+            ref = oracle.append_and_attend(qa[r], ka[r], va[r], kpg, vpg, tables[r],
+                                           int(prefix[r]), 16)
+            assert max_err(out[i], ref) <= TOL["bf16"], (layer, r)
+    # the aborted requests retry with the next step's rows
+    retry = step + 1
+    for r in aborted:
+        assert pkv.pkv_begin_token(caches[r]) == prefix[r]
+    layer_outs = {}
+    for layer in range(w.layers):
+        qa, ka, va = w.q(layer, retry), w.k_new(layer, retry), w.v_new(layer, retry)
+        q, k, v = (rows_to_device(x[aborted], "bf16") for x in (qa, ka, va))
+        out = torch.empty((len(aborted), w.heads, w.head_width), device="cuda")
+        pkv.pkv_append_and_attend_batched([caches[r] for r in aborted], layer, q, k, v, out)
+        layer_outs[layer] = out
+    torch.cuda.synchronize()
+    for r in aborted:
+        pkv.pkv_commit_token(caches[r])
+    for layer in checked_layers:
+        qa, ka, va = w.q(layer, retry), w.k_new(layer, retry), w.v_new(layer, retry)
+        for i, r in enumerate(aborted):
+            ref = oracle.append_and_attend(qa[r], ka[r], va[r], HostPages(w, "k", layer),
+                                           HostPages(w, "v", layer),
+                                           pkv.pkv_cache_page_table(caches[r]), int(prefix[r]), 16)
+            assert max_err(layer_outs[layer][i], ref) <= TOL["bf16"]
+    cnt = pkv.pkv_pool_get_counters(pool)
+    assert cnt.committed_tokens == w.n and cnt.aborted_tokens == len(aborted)
+    for c in caches:
+        pkv.pkv_cache_destroy(c)
+    pkv.pkv_pool_destroy(pool)
