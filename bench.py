@@ -29,6 +29,30 @@ import time
 
 HBM_PEAK_GBS = 8000.0
 
+# Calibrated HBM traffic per attention launch from rocprofv3 PMC runs:
+# FETCH_SIZE and WRITE_SIZE in KiB per dispatch, scaled by what the same
+# counters read for one kernel that reads and writes exactly 1 GiB
+# (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000 on MI355X).  Valid only for the
+# kernel source they were taken from (sha256 prefix of csrc/kernels.hip).
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+MEASURED_TRAFFIC = {
+    "batch32_fp32_l12": {"kernels_sha256_16": "00cbe2a2e504533e",
+                         "fetch_kib": 44375.5, "write_kib": 2004.4},
+}
+
+
+def measured_traffic(workload: str):
+    import hashlib
+    m = MEASURED_TRAFFIC.get(workload)
+    if m is None:
+        return None
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_attention_amd",
+                       "csrc", "kernels.hip")
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != m["kernels_sha256_16"]:
+            return None
+    return int((m["fetch_kib"] * FETCH_SCALE + m["write_kib"] * WRITE_SCALE) * 1024)
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -37,13 +61,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="batch32_fp32_l12")
     ap.add_argument("--split-blocks", type=int, default=0)
-    ap.add_argument("--merge-mode", type=int, default=0,
-                    help="0: separate merge kernel, 2: last-arriving chunk merges")
+    ap.add_argument("--merge-mode", type=int, default=2,
+                    help="2: last-arriving chunk merges (default), 0: separate merge kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's timed CPU work")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run one 1 GiB device copy (HBM counter calibration)")
+                    help="also run one kernel that reads and writes 1 GiB (HBM counter "
+                         "calibration)")
     return ap.parse_args()
 
 
@@ -77,9 +102,10 @@ def main():
     elt = w.elt
 
     if args.calibrate_copy:
-        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        # one elementwise kernel that reads 1 GiB and writes 1 GiB
+        src = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -118,33 +144,37 @@ def main():
         caches = [pkv.pkv_cache_create(pool, max_context) for _ in range(n)]
         for c, t in zip(caches, w.lengths.tolist()):
             pkv.pkv_cache_grow(c, t - 1)
+        all_caches = pkv.pkv_cache_array(caches)
         lens = [t - 1 for t in w.lengths.tolist()]   # committed lengths
+        sh = stream.cuda_stream
         step_no = [0]
 
         def step(timed: bool):
             s = step_no[0]
             step_no[0] += 1
             abort = w.abort_layer(s)
-            for c in caches:
-                pkv.pkv_begin_token(c)
+            pkv.pkv_begin_token_batched(all_caches)
             live = list(range(n))
+            live_arr = all_caches
             kv_bytes = 0
+            t_sum = sum(lens) + n
             for layer in range(L):
-                for r in [r for r in live if abort[r] == layer]:
-                    pkv.pkv_abort_token(caches[r])
-                live = [r for r in live if abort[r] != layer]
+                if (abort == layer).any():
+                    for r in [r for r in live if abort[r] == layer]:
+                        pkv.pkv_abort_token(caches[r])
+                    live = [r for r in live if abort[r] != layer]
+                    live_arr = pkv.pkv_cache_array([caches[r] for r in live])
+                    t_sum = sum(lens[r] + 1 for r in live)
                 if len(live) == n:
                     q, k, v, o = q_all[layer], k_all[layer], v_all[layer], out
                 else:
                     idx = torch.tensor(live, device="cuda")
                     q, k, v = q_all[layer][idx], k_all[layer][idx], v_all[layer][idx]
                     o = out[:len(live)]
-                t_sum = sum(lens[r] + 1 for r in live)
                 kv_bytes += t_sum * H * 2 * D * elt
-                pkv.pkv_append_and_attend_batched([caches[r] for r in live], layer, q, k, v, o,
-                                                  stream=stream)
+                pkv.pkv_append_and_attend_batched(live_arr, layer, q, k, v, o, stream=sh)
+            pkv.pkv_commit_token_batched(live_arr)
             for r in live:
-                pkv.pkv_commit_token(caches[r])
                 lens[r] += 1
             if timed:
                 step_kv_bytes.append(kv_bytes)
@@ -220,7 +250,7 @@ def main():
             "launches_timed": int(prof.attention_launches),
             "merge_launches": int(prof.merge_launches),
             "merge_avg_us": round(prof.merge_ms / max(1, prof.merge_launches) * 1e3, 2),
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
         },
     }
     if not args.no_cpu_baseline:

@@ -89,8 +89,9 @@ typedef struct pkv_pool_desc {
   int32_t max_context;    /* largest context of any cache of this pool        */
   int32_t max_caches;     /* live caches at once (device page-table rows); 0 = 256 */
   int32_t kv_dtype;       /* pkv_dtype                                        */
-  int32_t split_blocks;   /* split-K chunk in 16-row blocks; 0 = automatic,
-                             -1 = never split                                  */
+  int32_t split_blocks;   /* split-K chunk in 16-row blocks (a request of B
+                             blocks splits into ceil(B / split_blocks) even
+                             chunks); 0 = automatic, -1 = never split          */
   int32_t flags;          /* PKV_POOL_* bits; 0 by default                     */
   void* k_storage;
   void* v_storage;
@@ -127,8 +128,9 @@ typedef struct pkv_profile {
 /* Tunables of a pool (pkv_pool_set_option). */
 typedef enum pkv_option {
   PKV_OPT_SPLIT_BLOCKS = 1, /* as pkv_pool_desc.split_blocks                   */
-  PKV_OPT_MERGE_MODE = 2,   /* 0: separate merge kernel; 2: last-arriving
-                               chunk merges inside the attention kernel        */
+  PKV_OPT_MERGE_MODE = 2,   /* 2 (default): the last-arriving chunk merges
+                               inside the attention kernel; 0: a separate
+                               merge kernel after it                            */
   PKV_OPT_PROFILING = 3     /* 1: record kernel timing events; 0: stop         */
 } pkv_option;
 
@@ -226,6 +228,16 @@ pkv_status pkv_commit_token(pkv_cache* cache);
 /* Drops the pending token: length unchanged, a page leased by its begin
  * returned.  Errors: BAD_STATE (nothing pending). */
 pkv_status pkv_abort_token(pkv_cache* cache);
+
+/* begin_token on n caches of one pool, all or none: on any error no cache
+ * changes.  positions (may be null) receives the n reserved positions.
+ * Errors: as pkv_begin_token (the first failing cache is named in the
+ * message); OUT_OF_PAGES when the n begins together need more pages than are
+ * free; INVALID_ARGUMENT for a repeated cache or mixed pools. */
+pkv_status pkv_begin_token_batched(pkv_cache* const* caches, int32_t n, int32_t* positions);
+
+/* commit_token on n caches, all or none.  Errors: as pkv_commit_token. */
+pkv_status pkv_commit_token_batched(pkv_cache* const* caches, int32_t n);
 
 /* The same layer step for n pending caches of one pool in one launch:
  * q, k, v are [n,H,d_h] (pool dtype), out is [n,H,d_h] float32, row i

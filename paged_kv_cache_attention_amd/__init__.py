@@ -118,6 +118,8 @@ SIGNATURES = {
     "pkv_commit_token": (_I32, [_P]),
     "pkv_abort_token": (_I32, [_P]),
     "pkv_append_and_attend_batched": (_I32, [ctypes.POINTER(_P), _I32, _I32, _P, _P, _P, _P, _P]),
+    "pkv_begin_token_batched": (_I32, [ctypes.POINTER(_P), _I32, _PI32]),
+    "pkv_commit_token_batched": (_I32, [ctypes.POINTER(_P), _I32]),
     "pkv_plan_create": (_I32, [_P, ctypes.POINTER(_P)]),
     "pkv_plan_destroy": (_I32, [_P]),
     "pkv_plan_build": (_I32, [_P, _I32, _PI32, _I32, _P]),
@@ -305,9 +307,32 @@ def pkv_abort_token(cache: int) -> None:
     _check(_lib.pkv_abort_token(cache), "pkv_abort_token")
 
 
+def _cache_array(caches):
+    if isinstance(caches, ctypes.Array):
+        return caches, len(caches)
+    return (ctypes.c_void_p * max(1, len(caches)))(*caches), len(caches)
+
+
+def pkv_cache_array(caches):
+    """A reusable C array of cache handles for the batched calls."""
+    return _cache_array(caches)[0]
+
+
+def pkv_begin_token_batched(caches) -> list:
+    arr, n = _cache_array(caches)
+    pos = (ctypes.c_int32 * max(1, n))()
+    _check(_lib.pkv_begin_token_batched(arr, n, pos), "pkv_begin_token_batched")
+    return list(pos[:n])
+
+
+def pkv_commit_token_batched(caches) -> None:
+    arr, n = _cache_array(caches)
+    _check(_lib.pkv_commit_token_batched(arr, n), "pkv_commit_token_batched")
+
+
 def pkv_append_and_attend_batched(caches, layer: int, q, k, v, out, stream=None) -> None:
-    arr = (ctypes.c_void_p * max(1, len(caches)))(*caches)
-    _check(_lib.pkv_append_and_attend_batched(arr, len(caches), layer, _ptr(q), _ptr(k), _ptr(v),
+    arr, n = _cache_array(caches)
+    _check(_lib.pkv_append_and_attend_batched(arr, n, layer, _ptr(q), _ptr(k), _ptr(v),
                                               _ptr(out), _stream(stream)),
            "pkv_append_and_attend_batched")
 

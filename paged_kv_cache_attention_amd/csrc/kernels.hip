@@ -98,48 +98,68 @@ __device__ inline uint4 select4(bool c, const uint4& a, const uint4& b) {
   return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
 }
 
-// Ends one (chunk, head).  A request with one chunk writes its context; a
-// split request writes a partial (m, l, acc).  In kMergeLastArriver mode the
-// chunk that arrives last at the (request, head) counter then merges all
-// partials (merge_partials) and returns the counter to zero for the next
-// launch; in kMergeSeparate mode merge_kernel does that afterwards.
-// Called once per chunk by one whole wave.  Lane-held column e is
-// col0 + e * CSTRIDE, present when own_cols and below the head width.
-template <int NCOL, int CSTRIDE>
-__device__ inline void merge_partials(const AttnArgs& a, int req, const ReqEntry& rq, int h,
-                                      bool own_cols, int col0) {
-  // Second pass: o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, in split
-  // order, so the result does not depend on which chunk finished last.
-  const int D = a.head_width;
-  const int H = a.num_heads;
-  if (!own_cols) return;
-  const int64_t stride = (int64_t)H * (D + 2);
-  const float* base = a.partials + ((int64_t)rq.partial_base * H + h) * (D + 2);
-  float mx = -FLT_MAX;
-  for (int s = 0; s < rq.nsplit; ++s) mx = fmaxf(mx, base[s * stride]);
-  float lsum = 0.f;
-  float o[NCOL];
-#pragma unroll
-  for (int e = 0; e < NCOL; ++e) o[e] = 0.f;
-  for (int s = 0; s < rq.nsplit; ++s) {
-    const float* ps = base + s * stride;
-    const float wgt = fast_exp2(ps[0] - mx);
-    lsum = fmaf(ps[1], wgt, lsum);
-#pragma unroll
-    for (int e = 0; e < NCOL; ++e)
-      if (col0 + e * CSTRIDE < D) o[e] = fmaf(ps[2 + col0 + e * CSTRIDE], wgt, o[e]);
-  }
-  const float inv = 1.0f / lsum;
-  float* out = a.out + ((int64_t)req * H + h) * D + col0;
-#pragma unroll
-  for (int e = 0; e < NCOL; ++e)
-    if (col0 + e * CSTRIDE < D) out[e * CSTRIDE] = o[e] * inv;
+template <bool COHERENT>
+__device__ inline float load_part(const float* p) {
+  if constexpr (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
 }
 
-__device__ inline void store_agent(float* p, float v) {
+__device__ inline void store_part(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Second pass of split-K for one (request, head), by one whole wave:
+// o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
+// Lanes first reduce M and the denominator over the splits in parallel, then
+// each lane sums its columns (lane, lane + 64, ...) over the splits in a fixed
+// order, keeping four partial loads in flight.  The result does not depend on
+// which chunk finished last.  COHERENT reads use agent-scope atomic loads
+// (partials written by other workgroups inside the same kernel).
+template <bool COHERENT>
+__device__ void merge_wave(const AttnArgs& a, int req, const ReqEntry& rq, int h, int lane) {
+  const int D = a.head_width;
+  const int H = a.num_heads;
+  const int ns = rq.nsplit;
+  const int64_t stride = (int64_t)H * (D + 2);
+  const float* base = a.partials + ((int64_t)rq.partial_base * H + h) * (D + 2);
+  float mx = -FLT_MAX;
+  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, load_part<COHERENT>(base + s * stride));
+  mx = wave_max(mx);
+  float lsum = 0.f;
+  for (int s = lane; s < ns; s += 64)
+    lsum += load_part<COHERENT>(base + s * stride + 1) *
+            fast_exp2(load_part<COHERENT>(base + s * stride) - mx);
+  lsum = wave_sum(lsum);
+  const float inv = 1.0f / lsum;
+  float* out = a.out + ((int64_t)req * H + h) * D;
+  for (int d = lane; d < D; d += 64) {
+    const float* col = base + 2 + d;
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + 4 <= ns; s += 4) {
+      float mv[4], av[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        mv[j] = load_part<COHERENT>(base + (s + j) * stride);
+        av[j] = load_part<COHERENT>(col + (s + j) * stride);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = fmaf(av[j], fast_exp2(mv[j] - mx), o[j]);
+    }
+    for (; s < ns; ++s)
+      o[0] = fmaf(load_part<COHERENT>(col + s * stride),
+                  fast_exp2(load_part<COHERENT>(base + s * stride) - mx), o[0]);
+    out[d] = ((o[0] + o[1]) + (o[2] + o[3])) * inv;
+  }
+}
+
+// Ends one (chunk, head), called once per chunk by one whole wave.  A request
+// with one chunk writes its context; a split request writes a partial
+// (m, l, acc).  In kMergeLastArriver mode the chunk that arrives last at the
+// (request, head) counter then merges all partials and returns the counter to
+// zero for the next launch; in kMergeSeparate mode merge_kernel does that
+// afterwards.  Lane-held column e is col0 + e * CSTRIDE, present when own_cols
+// and below the head width.
 template <int NCOL, int CSTRIDE>
 __device__ inline void finish_chunk(const AttnArgs& a, const WorkItem& it, const ReqEntry& rq,
                                     int h, int lane, bool own_cols, int col0, float m, float l,
@@ -168,13 +188,14 @@ __device__ inline void finish_chunk(const AttnArgs& a, const WorkItem& it, const
   }
   // Last-arriver merge.  Agent-scope stores write through to the
   // device-coherent level; waiting for every outstanding memory operation
-  // orders them before the counter increment that publishes them.
+  // orders them before the counter increment that publishes them.  The last
+  // arriver reads with agent-scope loads, which are served from that level.
 #pragma unroll
   for (int e = 0; e < NCOL; ++e)
-    if (has(e)) store_agent(part + 2 + col0 + e * CSTRIDE, acc[e]);
+    if (has(e)) store_part(part + 2 + col0 + e * CSTRIDE, acc[e]);
   if (lane == 0) {
-    store_agent(part, m);
-    store_agent(part + 1, l);
+    store_part(part, m);
+    store_part(part + 1, l);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0);
@@ -183,9 +204,8 @@ __device__ inline void finish_chunk(const AttnArgs& a, const WorkItem& it, const
   if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   prev = __shfl(prev, 0);
   if (prev != rq.nsplit - 1) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (lane == 0) (void)__hip_atomic_exchange(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  merge_partials<NCOL, CSTRIDE>(a, it.req, rq, h, own_cols, col0);
+  merge_wave<true>(a, it.req, rq, h, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -476,7 +496,7 @@ __global__ __launch_bounds__(64) void attend_generic_kernel(AttnArgs a) {
 __global__ __launch_bounds__(64) void merge_kernel(AttnArgs a) {
   const int req = a.merge_reqs[blockIdx.x];
   const ReqEntry rq = a.reqs[req];
-  merge_partials<16, 64>(a, req, rq, blockIdx.y, true, threadIdx.x);
+  merge_wave<false>(a, req, rq, blockIdx.y, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------

@@ -71,8 +71,8 @@ enum class KernelPath { kFast, kGeneric };
 //             merges.  Partials are stored with agent-scope atomic stores,
 //             which write through to the device-coherent level; the writer
 //             waits for them to complete before its relaxed counter
-//             increment, and the last arriver runs an agent-scope acquire
-//             fence before reading.
+//             increment, and the last arriver reads them with agent-scope
+//             atomic loads.  No L2 write-back or invalidate is needed.
 enum MergeMode : int32_t { kMergeSeparate = 0, kMergeLastArriver = 2 };
 
 // Launchers (kernels.hip).  Each returns the hipError_t of the launch.

@@ -134,7 +134,7 @@ struct pkv_pool {
   pkv_plan txn_plan;   // transactional steps
   pkv_plan call_plan;  // one-call batched forms
   pkv_counters counters{};
-  int32_t merge_mode = pkv::kMergeSeparate;
+  int32_t merge_mode = pkv::kMergeLastArriver;
   bool profiling = false;
   struct Timed {
     hipEvent_t start, end;
@@ -206,14 +206,18 @@ pkv_status flush_patches(pkv_pool* p, hipStream_t stream) {
   return PKV_OK;
 }
 
+// Split-K chunk size in 16-row blocks.  The goal is about kTargetChunks
+// (chunk, head) workgroups per launch -- four resident rounds of 256 CUs x 4
+// workgroups -- so that a batch with few (request, head) pairs still fills
+// the GPU and one long context does not serialise on one workgroup, while a
+// batch that already has that many pairs is not split at all.
 int32_t choose_split_blocks(const pkv_pool* p, int64_t total_blocks) {
   if (p->desc.split_blocks > 0) return p->desc.split_blocks;
   if (p->desc.split_blocks < 0) return std::numeric_limits<int32_t>::max();
-  // Aim for enough (chunk, head) workgroups to fill 256 CUs several times,
-  // with chunks of 8..64 blocks (128..1024 rows).
-  const int64_t work = total_blocks * p->desc.num_heads;
+  constexpr int64_t kTargetChunks = 4096;
+  const int64_t work = total_blocks * p->desc.num_heads;  // (block, head) units
   int64_t c = 8;
-  while (c < 64 && work / (c * 2) >= 4096) c *= 2;
+  while (c < 512 && c * kTargetChunks < work) c *= 2;
   return static_cast<int32_t>(c);
 }
 
@@ -271,10 +275,13 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
     const int32_t nsplit = (int32_t)(((int64_t)blocks + chunk - 1) / chunk);
     reqs[r] = ReqEntry{rows[r], lens[r], nsplit, nsplit > 1 ? slots : -1};
     if (nsplit > 1) slots += nsplit;
+    // Even chunks: the first (blocks % nsplit) chunks take one block more.
+    const int32_t base = blocks / nsplit, extra = blocks % nsplit;
+    int32_t b0 = 0;
     for (int32_t s = 0; s < nsplit; ++s) {
-      const int32_t b0 = (int32_t)((int64_t)s * chunk);
-      const int32_t b1 = (int32_t)std::min<int64_t>((int64_t)(s + 1) * chunk, blocks);
+      const int32_t b1 = b0 + base + (s < extra ? 1 : 0);
       items.push_back(WorkItem{r, b0, b1, s});
+      b0 = b1;
     }
     rows_attended += (uint64_t)lens[r];
   }
@@ -784,6 +791,60 @@ pkv_status pkv_begin_token(pkv_cache* c, int32_t* position) {
   std::fill(c->appended.begin(), c->appended.end(), 0);
   c->appended_count = 0;
   if (position) *position = c->pending_pos;
+  return ok();
+}
+
+static pkv_status check_batch(pkv_cache* const* caches, int32_t n) {
+  if (!caches || n < 1) return fail(PKV_ERR_INVALID_ARGUMENT, "need at least one cache");
+  for (int32_t i = 0; i < n; ++i) {
+    if (!caches[i]) return fail(PKV_ERR_INVALID_ARGUMENT, "caches[%d] is null", i);
+    if (caches[i]->pool != caches[0]->pool)
+      return fail(PKV_ERR_INVALID_ARGUMENT, "caches[%d] belongs to another pool", i);
+  }
+  if (n > 1) {
+    std::vector<const pkv_cache*> sorted(caches, caches + n);
+    std::sort(sorted.begin(), sorted.end());
+    if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
+      return fail(PKV_ERR_INVALID_ARGUMENT, "a cache appears twice in the batch");
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_begin_token_batched(pkv_cache* const* caches, int32_t n, int32_t* positions) {
+  pkv_status st = check_batch(caches, n);
+  if (st != PKV_OK) return st;
+  pkv_pool* p = caches[0]->pool;
+  int64_t pages = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_cache* c = caches[i];
+    if (c->pending) return fail(PKV_ERR_BAD_STATE, "caches[%d]: a token is already pending", i);
+    if (c->len >= c->max_context)
+      return fail(PKV_ERR_CAPACITY_EXHAUSTED, "caches[%d] is at its capacity %d", i, c->max_context);
+    pages += c->len % p->desc.page_size == 0;
+  }
+  if (pages > (int64_t)p->free_stack.size())
+    return fail(PKV_ERR_OUT_OF_PAGES, "%lld pages needed, %zu free", (long long)pages,
+                p->free_stack.size());
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t pos = 0;
+    pkv_begin_token(caches[i], &pos);  // cannot fail after the checks above
+    if (positions) positions[i] = pos;
+  }
+  return ok();
+}
+
+pkv_status pkv_commit_token_batched(pkv_cache* const* caches, int32_t n) {
+  pkv_status st = check_batch(caches, n);
+  if (st != PKV_OK) return st;
+  const int32_t L = caches[0]->pool->desc.num_layers;
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_cache* c = caches[i];
+    if (!c->pending) return fail(PKV_ERR_BAD_STATE, "caches[%d]: no pending token", i);
+    if (c->appended_count != L)
+      return fail(PKV_ERR_BAD_STATE, "caches[%d]: only %d of %d layers appended", i,
+                  c->appended_count, L);
+  }
+  for (int32_t i = 0; i < n; ++i) pkv_commit_token(caches[i]);
   return ok();
 }
 

@@ -36,6 +36,7 @@ def test_every_declared_function_is_exported_and_bound():
 
 def make_pool(layers=2, heads=2, width=2, page=16, pages=8, ctx=64, caches=8, seed=1,
               dtype=0, split=0):
+    # host-only: the allocator and transaction run without device memory
     d = pkv.pkv_pool_desc_init()
     d.num_layers, d.num_heads, d.head_width = layers, heads, width
     d.page_size, d.num_pages, d.max_context = page, pages, ctx
@@ -246,6 +247,23 @@ def test_split_plan_chunking():
     pkv.pkv_pool_destroy(p)
 
 
+def test_automatic_split_targets_4096_chunks():
+    # 2 heads.  One 1000-block request: 2000 (block, head) units, far below
+    # 4096 chunks of 8 blocks -> 8-block chunks (125 of them).
+    p = make_pool(pages=4200, ctx=16 * 1024, heads=2)
+    plan = pkv.pkv_plan_create(p)
+    pkv.pkv_plan_build(plan, [16 * 1000], 1024, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 125
+    # 64 requests of 512 blocks: 65536 units -> 16-block chunks, 32 per request
+    pkv.pkv_plan_build(plan, [16 * 512] * 64, 1024, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 64 * 32
+    # 4096 requests of 128 blocks x 2 heads: 1M units -> 256-block chunks: no split
+    pkv.pkv_plan_build(plan, [16 * 128] * 4096, 1024, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 4096
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(p)
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_state_machine_matches_oracle_model(seed):
     rnd = random.Random(seed)
@@ -280,4 +298,33 @@ def test_state_machine_matches_oracle_model(seed):
     for c, _ in caches:
         pkv.pkv_cache_destroy(c)
     assert pkv.pkv_pool_get_counters(p).pages_free == pages
+    pkv.pkv_pool_destroy(p)
+
+
+def test_batched_begin_and_commit_all_or_nothing():
+    p = make_pool(layers=2, page=4, pages=3, ctx=16)
+    cs = [pkv.pkv_cache_create(p, 16) for _ in range(3)]
+    assert pkv.pkv_begin_token_batched(cs) == [0, 0, 0]          # three pages leased
+    for layer in range(2):
+        pkv.pkv_append_and_attend_batched(cs, layer, FAKE, FAKE, FAKE, FAKE, stream=0)
+    pkv.pkv_commit_token_batched(cs)
+    assert [pkv.pkv_cache_size(c) for c in cs] == [1, 1, 1]
+    pkv.pkv_cache_grow(cs[0], 3)                                   # cs[0] at a page boundary
+    free = pkv.pkv_pool_get_counters(p).pages_free
+    assert free == 0
+    # cs[0] needs a page, none free: the whole batch is rejected, nothing begins
+    assert status_of(pkv.pkv_begin_token_batched, cs) == Status.OUT_OF_PAGES
+    assert status_of(pkv.pkv_commit_token_batched, cs[1:]) == Status.BAD_STATE
+    assert status_of(pkv.pkv_begin_token_batched, [cs[1], cs[1]]) == Status.INVALID_ARGUMENT
+    assert pkv.pkv_begin_token_batched(cs[1:]) == [1, 1]
+    pkv.pkv_append_and_attend_batched(cs[1:], 0, FAKE, FAKE, FAKE, FAKE, stream=0)
+    pkv.pkv_append_and_attend(cs[1], 1, FAKE, FAKE, FAKE, FAKE, stream=0)
+    # cs[2] misses layer 1: no cache commits
+    assert status_of(pkv.pkv_commit_token_batched, cs[1:]) == Status.BAD_STATE
+    assert [pkv.pkv_cache_size(c) for c in cs] == [4, 1, 1]
+    pkv.pkv_append_and_attend(cs[2], 1, FAKE, FAKE, FAKE, FAKE, stream=0)
+    pkv.pkv_commit_token_batched(cs[1:])
+    assert [pkv.pkv_cache_size(c) for c in cs] == [4, 2, 2]
+    for c in cs:
+        pkv.pkv_cache_destroy(c)
     pkv.pkv_pool_destroy(p)

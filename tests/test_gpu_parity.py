@@ -369,6 +369,38 @@ def test_batch32_fp32_l12_full_step(merge):
     pkv.pkv_pool_destroy(pool)
 
 
+def test_last_arriver_merge_is_bitwise_separate_merge():
+    """Both merge modes run the same second pass in the same split order, so
+    their contexts agree bit for bit; repeated launches in last-arriver mode
+    (every 16-row block its own chunk: up to 64 arrivals per counter) must
+    never read a stale partial."""
+    w = W.batch32_fp32()
+    kp, vp = device_pool(w, layers=[0])
+    q = rows_to_device(w.q(0), "f32")
+    pt = _pt_device(w)
+    outs = {}
+    for merge in MERGES:
+        pool = _pool(w, kp, vp, split=1, merge=merge)
+        plan = pkv.pkv_plan_create(pool)
+        pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
+        assert pkv.pkv_plan_num_chunks(plan) == int(W.pages_needed(w.lengths, 16).sum())
+        got = []
+        for _ in range(25 if merge == pkv.PKV_MERGE_LAST_ARRIVER else 1):
+            out = torch.full((w.n, w.heads, w.head_width), float("nan"), device="cuda")
+            pkv.pkv_plan_decode_attention(plan, 0, q, pt, out)
+            got.append(out)
+        torch.cuda.synchronize()
+        outs[merge] = got
+        pkv.pkv_plan_destroy(plan)
+        pkv.pkv_pool_destroy(pool)
+    ref = outs[pkv.PKV_MERGE_SEPARATE][0]
+    for o in outs[pkv.PKV_MERGE_LAST_ARRIVER]:
+        assert torch.equal(o, ref)
+    qh = w.q(0)
+    for r in _sampled(w.n):
+        assert max_err(ref[r], _oracle_decode(w, 0, r, qh)) <= TOL["f32"]
+
+
 @pytest.mark.parametrize("maker", [W.batch256_bf16, W.skewed64_bf16])
 @pytest.mark.parametrize("merge", MERGES)
 def test_bf16_single_layer_full(maker, merge):
