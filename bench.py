@@ -10,10 +10,11 @@ then commit_token on every request.  Lengths grow by one per committed step;
 bytes are counted per step from the actual lengths.
 
 Prints one JSON line.  ``value`` is K/V GB/s over the timed steps (wall clock
-between device synchronisations); ``roofline`` reports the attention kernel
-alone: the library records HIP events on the launch stream immediately around
-every attention kernel of the timed steps (PKV_OPT_PROFILING) and sums its
-algorithmic bytes.
+between device synchronisations, nothing but the steps on the stream).
+``roofline`` reports the attention kernel alone, from a second timed pass of
+the same number of steps in which the library records HIP events on the
+launch stream immediately around every attention kernel (PKV_OPT_PROFILING)
+and sums each launch's algorithmic bytes.
 
 Other workloads (--workload): batch256_bf16, skewed64_bf16 (single-layer
 batched decode over existing rows) and fullstep128_bf16_l32 (32 layers, 128
@@ -61,11 +62,15 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="batch32_fp32_l12")
     ap.add_argument("--split-blocks", type=int, default=0)
+    ap.add_argument("--waves", type=int, default=0,
+                    help="waves per workgroup of the fast path (4, 8; 0 = per plan)")
     ap.add_argument("--merge-mode", type=int, default=2,
                     help="2: last-arriving chunk merges (default), 0: separate merge kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's timed CPU work")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="time the steps without per-kernel HIP events (no roofline)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one kernel that reads and writes 1 GiB (HBM counter "
                          "calibration)")
@@ -94,8 +99,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     maker = W.WORKLOADS[args.workload]
-    w = maker(extra_steps=args.steps + args.warmup + 2) if args.workload.startswith("fullstep") \
-        else maker()
+    grow = 2 * args.steps + args.warmup + 2   # committed tokens per request over both passes
+    w = maker(extra_steps=grow) if args.workload.startswith("fullstep") else maker()
     transactional = w.appends
     dt = sgpu.torch_dtype(w.dtype)
     H, D, L, n = w.heads, w.head_width, w.layers, w.n
@@ -126,7 +131,7 @@ def main():
         sgpu.fill_normal(v_all[layer], w.v_key(layer), w.dtype)
     out = torch.empty((n, H, D), dtype=torch.float32, device="cuda")
 
-    max_context = int(w.lengths.max()) + args.steps + args.warmup + 32
+    max_context = int(w.lengths.max()) + grow + 32
     d = pkv.pkv_pool_desc_init()
     d.num_layers, d.num_heads, d.head_width = L, H, D
     d.page_size, d.num_pages, d.max_context = w.page_size, w.num_pages, max_context
@@ -137,6 +142,7 @@ def main():
     d.free_list_seed = w.seed
     pool = pkv.pkv_pool_create(d)
     pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_MERGE_MODE, args.merge_mode)
+    pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_WAVES, args.waves)
 
     step_kv_bytes = []
 
@@ -191,20 +197,30 @@ def main():
 
     for _ in range(args.warmup):
         step(False)
+    # Pass 1: the timed steps, nothing else on the stream -> value.
     torch.cuda.synchronize()
-    pkv.pkv_pool_get_profile(pool, reset=True)
-    pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_PROFILING, 1)   # events around each kernel
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_PROFILING, 0)
-    prof = pkv.pkv_pool_get_profile(pool, reset=True)
-    avg_kern_s = prof.attention_ms / max(1, prof.attention_launches) / 1e3
-    bytes_per_launch = prof.algorithmic_bytes / max(1, prof.attention_launches)
-    achieved = bytes_per_launch / avg_kern_s / 1e9
     kv_total = float(sum(step_kv_bytes))
+    # Pass 2: the same number of steps with the library's HIP events around
+    # every attention kernel -> the kernel's average duration (the event
+    # packets lengthen a step, so they are kept out of pass 1).
+    prof = None
+    if not args.no_kernel_events:
+        pkv.pkv_pool_get_profile(pool, reset=True)
+        pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_PROFILING, 1)
+        for _ in range(args.steps):
+            step(False)
+        torch.cuda.synchronize()
+        pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_PROFILING, 0)
+        prof = pkv.pkv_pool_get_profile(pool, reset=True)
+    launches = prof.attention_launches if prof else 0
+    avg_kern_s = prof.attention_ms / max(1, launches) / 1e3 if prof else 0.0
+    bytes_per_launch = prof.algorithmic_bytes / max(1, launches) if prof else 0.0
+    achieved = bytes_per_launch / avg_kern_s / 1e9 if avg_kern_s > 0 else 0.0
     value = kv_total / elapsed / 1e9
     chunks = None
     if not transactional:
@@ -234,6 +250,7 @@ def main():
             "kv_bytes_per_step": int(kv_total / args.steps),
             "split_blocks": args.split_blocks,
             "merge_mode": args.merge_mode,
+            "waves_option": args.waves,
             "plan_chunks": chunks,
             "parallelism": "single GPU",
         },
@@ -247,9 +264,10 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "avg_launch_us": round(avg_kern_s * 1e6, 2),
             "bytes_per_launch": int(bytes_per_launch),
-            "launches_timed": int(prof.attention_launches),
-            "merge_launches": int(prof.merge_launches),
-            "merge_avg_us": round(prof.merge_ms / max(1, prof.merge_launches) * 1e3, 2),
+            "launches_timed": int(launches),
+            "merge_launches": int(prof.merge_launches) if prof else 0,
+            "merge_avg_us": round(prof.merge_ms / max(1, prof.merge_launches) * 1e3, 2)
+            if prof else 0.0,
             "traffic": measured_traffic(w.name),
         },
     }

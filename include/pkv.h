@@ -131,7 +131,9 @@ typedef enum pkv_option {
   PKV_OPT_MERGE_MODE = 2,   /* 2 (default): the last-arriving chunk merges
                                inside the attention kernel; 0: a separate
                                merge kernel after it                            */
-  PKV_OPT_PROFILING = 3     /* 1: record kernel timing events; 0: stop         */
+  PKV_OPT_PROFILING = 3,    /* 1: record kernel timing events; 0: stop         */
+  PKV_OPT_WAVES = 4         /* waves per workgroup of the fast path: 4, 8, or
+                               0 (default) to choose per plan                   */
 } pkv_option;
 
 /* Library version "major.minor.patch"; static string. */

@@ -17,6 +17,7 @@
 // split-K chunks combine by rescaling to the larger maximum.
 #include <cfloat>
 #include <cstdint>
+#include <type_traits>
 
 #include <hip/hip_runtime.h>
 
@@ -92,6 +93,32 @@ __device__ inline float wave_max(float x) {
 __device__ inline float wave_sum(float x) {
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
   return x;
+}
+
+// Read-only view of a page-table row for wave-uniform lookups.  Page tables
+// are never written while an attention kernel runs (patches are applied by an
+// earlier kernel on the stream), so uniform reads may go through the scalar
+// data cache: they then wait on the scalar counter, not on the vector-memory
+// counter that tracks K/V loads in flight.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
+__device__ inline const_i32_ptr as_const(const int32_t* p) {
+  return (const_i32_ptr)(p);
+}
+
+// Raw buffer access to one 16-row block: the descriptor (scalar registers)
+// holds the block's base address and a 4 KiB range; each load adds a 32-bit
+// lane offset.  Offsets past the range would read as zero instead of faulting.
+// Word 3 selects 32-bit data format for untyped loads on gfx9-family parts.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const char* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, bytes, kBufferWord3);
+}
+
+__device__ inline uint4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 __device__ inline uint4 select4(bool c, const uint4& a, const uint4& b) {
@@ -210,14 +237,14 @@ __device__ inline void finish_chunk(const AttnArgs& a, const WorkItem& it, const
 
 // ---------------------------------------------------------------------------
 // Fast path: rows of exactly 256 bytes (bf16 d_h=128, f32 d_h=64), pages a
-// multiple of 16 rows.  Workgroup = 4 waves on one (chunk, head).  A wave
-// takes every 4th 16-row block of the chunk; a block is one contiguous 4 KiB
+// multiple of 16 rows.  Workgroup = WAVES (4 or 8) waves on one (chunk,
+// head).  A wave takes every WAVES-th 16-row block of the chunk; a block is one contiguous 4 KiB
 // slab of K and one of V.  Lane (g, c): row i*4+g of each of the 4 loads, 16
 // bytes at column c, so one load instruction reads 1 KiB contiguous and the
 // 16 lanes of a DPP row hold one K/V row.  Each 16-lane group keeps its own
 // online-softmax state over its rows; groups merge in-wave, waves in LDS.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void attend_fast_kernel(AttnArgs a) {
+template <typename T, int D, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
   using KV = KVTraits<T>;
   constexpr int EPL = KV::kPerVec;
   constexpr int LPR = D / EPL;
@@ -225,18 +252,20 @@ __global__ __launch_bounds__(256) void attend_fast_kernel(AttnArgs a) {
   constexpr int RPI = 64 / LPR;            // rows per load instruction
   constexpr int NI = kBlockRows / RPI;     // load instructions per block
   constexpr int ROW_BYTES = D * (int)sizeof(T);
-  constexpr int WAVES = 4;
 
   const WorkItem it = a.items[blockIdx.x];
-  const ReqEntry rq = a.reqs[it.req];
+  const ReqEntry rq = it.rq;
   const int h = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // Wave-uniform: block indices, page-table reads and branches stay scalar, so
+  // the page lookups go through the scalar cache and never wait on the
+  // vector-memory counter that tracks the K/V loads in flight.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane / LPR;
   const int c = lane % LPR;
   const int t = rq.seq_len;
   const int S = a.page_size;
-  const int32_t* pt = a.page_table + (int64_t)rq.pt_row * a.pt_stride;
+  const const_i32_ptr pt = as_const(a.page_table + (int64_t)rq.pt_row * a.pt_stride);
   const int64_t qrow_bytes = (((int64_t)it.req * a.num_heads + h) * D) * (int64_t)sizeof(T);
   const int64_t head_off = (int64_t)h * a.head_bytes;
   const int last_blk = (t - 1) / kBlockRows;
@@ -264,17 +293,26 @@ __global__ __launch_bounds__(256) void attend_fast_kernel(AttnArgs a) {
     }
   }
 
-  auto load_block = [&](int b, uint4* kk, uint4* vv) {
+  // Physical page of a wave-uniform block index (clamped into the request's
+  // blocks so a look-ahead read past the end stays inside the table).
+  auto page_of = [&](int b) -> int32_t {
+    b = min(b, last_blk);
+    return pt[(b * kBlockRows) / S];
+  };
+  // Lane byte offsets inside a 16-row block: the block base is wave-uniform
+  // (scalar registers) and each load adds one unsigned 32-bit lane offset.
+  uint32_t lane_off[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) lane_off[i] = (uint32_t)((i * RPI + g) * ROW_BYTES + c * 16);
+  auto load_block = [&](int b, int32_t page, uint4* kk, uint4* vv) {
     const int row0 = b * kBlockRows;
-    const int64_t base = (int64_t)pt[row0 / S] * a.page_bytes + head_off +
-                         (int64_t)(row0 % S) * ROW_BYTES;
-    const char* kb = a.k_layer + base;
-    const char* vb = a.v_layer + base;
+    const int64_t base = (int64_t)page * a.page_bytes + head_off + (int64_t)(row0 % S) * ROW_BYTES;
+    const auto rk = block_rsrc(a.k_layer + base, kBlockRows * ROW_BYTES);
+    const auto rv = block_rsrc(a.v_layer + base, kBlockRows * ROW_BYTES);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int off = (i * RPI + g) * ROW_BYTES + c * 16;
-      kk[i] = *reinterpret_cast<const uint4*>(kb + off);
-      vv[i] = *reinterpret_cast<const uint4*>(vb + off);
+      kk[i] = load_b128(rk, lane_off[i]);
+      vv[i] = load_b128(rv, lane_off[i]);
     }
   };
 
@@ -283,11 +321,14 @@ __global__ __launch_bounds__(256) void attend_fast_kernel(AttnArgs a) {
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
 
-  auto step = [&](int b, uint4* kk, uint4* vv, bool edge) {
+  // EDGE is a compile-time tag: the masked variant exists only as its own
+  // code path, entered by a scalar branch for the request's last block.
+  auto step = [&](int b, uint4* kk, uint4* vv, auto edge_tag) {
+    constexpr bool edge = decltype(edge_tag)::value;
     bool valid[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) valid[i] = true;
-    if (edge) {
+    if constexpr (edge) {
       // The request's last block: rows >= t are masked (their bytes may be
       // anything), and with a fused append row t-1 comes from k_new/v_new.
 #pragma unroll
@@ -308,7 +349,9 @@ __global__ __launch_bounds__(256) void attend_fast_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) d = fmaf(qf[e], kf[e], d);
       s[i] = row16_sum(d);
-      if (edge && !valid[i]) s[i] = -INFINITY;
+      if constexpr (edge) {
+        if (!valid[i]) s[i] = -INFINITY;
+      }
     }
     float mb = s[0];
 #pragma unroll
@@ -335,18 +378,40 @@ __global__ __launch_bounds__(256) void attend_fast_kernel(AttnArgs a) {
     m = mn;
   };
 
+  // Software pipeline over this wave's blocks b, b+4, ..., wave_last: the
+  // K/V loads of the next block are issued before the current block is
+  // computed, and the page ID of the block after that is read one step
+  // ahead.  Look-ahead indices are clamped to wave_last instead of being
+  // guarded by a branch, so every path keeps the same loads in flight and the
+  // wait counts stay exact; the one redundant reload at the end of a wave
+  // hits in L2.  Only a wave's final block can be the request's last block
+  // (the masked "edge" step).
   {
-    uint4 k0[NI], v0[NI], k1[NI], v1[NI];
     const int end = it.blk_end;
-    int b = it.blk_begin + wave;
-    if (b < end) load_block(b, k0, v0);
-    for (; b < end; b += 2 * WAVES) {
-      const int b1 = b + WAVES;
-      if (b1 < end) load_block(b1, k1, v1);
-      step(b, k0, v0, b == last_blk);
-      if (b1 >= end) break;
-      if (b1 + WAVES < end) load_block(b1 + WAVES, k0, v0);
-      step(b1, k1, v1, b1 == last_blk);
+    const int first = it.blk_begin + wave;
+    if (first < end) {
+      const int wave_last = first + ((end - 1 - first) / WAVES) * WAVES;
+      uint4 ka[NI], va[NI], kb[NI], vb[NI];
+      load_block(first, page_of(first), ka, va);
+      int32_t p_next = page_of(min(first + WAVES, wave_last));
+      for (int b = first;; b += 2 * WAVES) {
+        const int b1 = min(b + WAVES, wave_last);
+        load_block(b1, p_next, kb, vb);
+        p_next = page_of(min(b + 2 * WAVES, wave_last));
+        if (b == last_blk)
+          step(b, ka, va, std::true_type{});
+        else
+          step(b, ka, va, std::false_type{});
+        if (b + WAVES > wave_last) break;
+        const int b2 = min(b + 2 * WAVES, wave_last);
+        load_block(b2, p_next, ka, va);
+        p_next = page_of(min(b + 3 * WAVES, wave_last));
+        if (b1 == last_blk)
+          step(b1, kb, vb, std::true_type{});
+        else
+          step(b1, kb, vb, std::false_type{});
+        if (b + 2 * WAVES > wave_last) break;
+      }
     }
   }
 
@@ -416,7 +481,7 @@ __global__ __launch_bounds__(64) void attend_generic_kernel(AttnArgs a) {
   float* ps = smem + D;     // [64]
 
   const WorkItem it = a.items[blockIdx.x];
-  const ReqEntry rq = a.reqs[it.req];
+  const ReqEntry rq = it.rq;
   const int h = blockIdx.y;
   const int lane = threadIdx.x;
   const int t = rq.seq_len;
@@ -530,8 +595,12 @@ __global__ __launch_bounds__(256) void patch_kernel(int32_t* arena, PatchBatch b
 
 template <typename T, int D>
 hipError_t launch_fast(const AttnArgs& a, int num_items, hipStream_t stream) {
-  hipLaunchKernelGGL((attend_fast_kernel<T, D>), dim3(num_items, a.num_heads), dim3(256), 0,
-                     stream, a);
+  if (a.waves == 8)
+    hipLaunchKernelGGL((attend_fast_kernel<T, D, 8>), dim3(num_items, a.num_heads), dim3(512), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((attend_fast_kernel<T, D, 4>), dim3(num_items, a.num_heads), dim3(256), 0,
+                       stream, a);
   return hipGetLastError();
 }
 

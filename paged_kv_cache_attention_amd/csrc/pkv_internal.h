@@ -22,12 +22,15 @@ struct ReqEntry {
   int32_t partial_base;
 };
 
-// One split-K chunk: blocks [blk_begin, blk_end) of request req, split index split.
+// One split-K chunk: blocks [blk_begin, blk_end) of request req, split index
+// split, with a copy of the request's entry so a workgroup starts from one
+// 32-byte scalar load.
 struct WorkItem {
   int32_t req;
   int32_t blk_begin;
   int32_t blk_end;
   int32_t split;
+  ReqEntry rq;
 };
 
 struct AttnArgs {
@@ -49,6 +52,7 @@ struct AttnArgs {
   int32_t head_width;
   int32_t fuse_append;    // 1: write k_new/v_new at row t-1 and attend with them
   int32_t merge_mode;     // MergeMode
+  int32_t waves;          // waves per workgroup of the fast path (4 or 8)
   int64_t page_bytes;     // H * S * D * elt
   int64_t head_bytes;     // S * D * elt
   float scale_log2e;      // log2(e) / sqrt(D)

@@ -85,6 +85,7 @@ struct pkv_plan {
   int32_t num_items = 0;
   int32_t total_splits = 0;
   int32_t num_split_reqs = 0;
+  int32_t waves = 4;
   bool any_split = false;
   uint64_t rows_attended = 0;  // sum of t_r
   std::vector<ReqEntry> reqs;
@@ -135,6 +136,7 @@ struct pkv_pool {
   pkv_plan call_plan;  // one-call batched forms
   pkv_counters counters{};
   int32_t merge_mode = pkv::kMergeLastArriver;
+  int32_t waves_option = 0;
   bool profiling = false;
   struct Timed {
     hipEvent_t start, end;
@@ -206,19 +208,30 @@ pkv_status flush_patches(pkv_pool* p, hipStream_t stream) {
   return PKV_OK;
 }
 
-// Split-K chunk size in 16-row blocks.  The goal is about kTargetChunks
-// (chunk, head) workgroups per launch -- four resident rounds of 256 CUs x 4
-// workgroups -- so that a batch with few (request, head) pairs still fills
-// the GPU and one long context does not serialise on one workgroup, while a
-// batch that already has that many pairs is not split at all.
-int32_t choose_split_blocks(const pkv_pool* p, int64_t total_blocks) {
-  if (p->desc.split_blocks > 0) return p->desc.split_blocks;
-  if (p->desc.split_blocks < 0) return std::numeric_limits<int32_t>::max();
+// Workgroup shape and split-K chunk size (in 16-row blocks) of a plan.
+//
+// Workgroups have four waves unless PKV_OPT_WAVES asks for eight (measured
+// on MI355X: eight-wave workgroups were not faster on any workload here).
+// Requests split into chunks sized for about kTargetChunks (chunk, head)
+// workgroups -- four resident rounds of 256 CUs x 4 workgroups -- so a batch
+// with few (request, head) pairs still fills the GPU and one long context
+// does not serialise on one workgroup; a batch that already has that many
+// pairs is not split.
+struct SplitChoice {
+  int32_t chunk;
+  int32_t waves;
+};
+
+SplitChoice choose_split(const pkv_pool* p, int64_t total_blocks) {
+  const int64_t H = p->desc.num_heads;
+  const int32_t waves = p->waves_option ? p->waves_option : 4;
+  if (p->desc.split_blocks > 0) return {p->desc.split_blocks, waves};
+  if (p->desc.split_blocks < 0) return {std::numeric_limits<int32_t>::max(), waves};
   constexpr int64_t kTargetChunks = 4096;
-  const int64_t work = total_blocks * p->desc.num_heads;  // (block, head) units
+  const int64_t work = total_blocks * H;  // (block, head) units
   int64_t c = 8;
   while (c < 512 && c * kTargetChunks < work) c *= 2;
-  return static_cast<int32_t>(c);
+  return {(int32_t)c, waves};
 }
 
 void plan_release(pkv_plan* pl) {
@@ -263,7 +276,8 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
   pkv_status st = ensure_device(p);
   if (st != PKV_OK) return st;
 
-  const int32_t chunk = choose_split_blocks(p, total_blocks);
+  const SplitChoice choice = choose_split(p, total_blocks);
+  const int32_t chunk = choice.chunk;
   const bool upload = !p->host_only;
   std::vector<ReqEntry> reqs(n);
   std::vector<WorkItem> items;
@@ -280,7 +294,7 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
     int32_t b0 = 0;
     for (int32_t s = 0; s < nsplit; ++s) {
       const int32_t b1 = b0 + base + (s < extra ? 1 : 0);
-      items.push_back(WorkItem{r, b0, b1, s});
+      items.push_back(WorkItem{r, b0, b1, s, reqs[r]});
       b0 = b1;
     }
     rows_attended += (uint64_t)lens[r];
@@ -370,6 +384,7 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
   pl->num_items = (int32_t)pl->items.size();
   pl->total_splits = slots;
   pl->num_split_reqs = (int32_t)merge_list.size();
+  pl->waves = choice.waves;
   pl->any_split = slots > 0;
   pl->rows_attended = rows_attended;
   pl->built = true;
@@ -395,6 +410,7 @@ AttnArgs make_args(const pkv_plan* pl, int32_t layer, const int32_t* page_table,
   a.merge_reqs = reinterpret_cast<const int32_t*>(pl->d_meta + pl->reqs.size() * sizeof(ReqEntry) +
                                                   pl->items.size() * sizeof(WorkItem));
   a.merge_mode = p->merge_mode;
+  a.waves = pl->waves;
   a.num_heads = p->desc.num_heads;
   a.page_size = p->desc.page_size;
   a.head_width = p->desc.head_width;
@@ -417,7 +433,11 @@ hipEvent_t take_event(pkv_pool* p) {
     p->spare.pop_back();
     return e;
   }
+  // Timing events without the system-scope cache write-back/invalidate, so
+  // recording them costs little next to the kernels they bracket.
   hipEvent_t e = nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) == hipSuccess) return e;
+  (void)hipGetLastError();
   if (hipEventCreate(&e) != hipSuccess) return nullptr;
   return e;
 }
@@ -637,6 +657,13 @@ pkv_status pkv_pool_set_option(pkv_pool* p, int32_t option, int64_t value) {
       if (value != pkv::kMergeSeparate && value != pkv::kMergeLastArriver)
         return fail(PKV_ERR_INVALID_ARGUMENT, "merge mode %lld", (long long)value);
       p->merge_mode = (int32_t)value;
+      return ok();
+    case PKV_OPT_WAVES:
+      if (value != 0 && value != 4 && value != 8)
+        return fail(PKV_ERR_INVALID_ARGUMENT, "waves %lld", (long long)value);
+      p->waves_option = (int32_t)value;
+      p->txn_plan.key.clear();
+      p->call_plan.key.clear();
       return ok();
     case PKV_OPT_PROFILING:
       if (value != 0 && value != 1) return fail(PKV_ERR_INVALID_ARGUMENT, "profiling %lld", (long long)value);
