@@ -137,46 +137,62 @@ __device__ inline void store_part(float* p, float v) {
 
 // Second pass of split-K for one (request, head), by one whole wave:
 // o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
-// Lanes first reduce M and the denominator over the splits in parallel, then
-// each lane sums its columns (lane, lane + 64, ...) over the splits in a fixed
-// order, keeping four partial loads in flight.  The result does not depend on
+// Splits go 64 at a time, lane j holding split g0 + j: the lanes load their
+// (m, l) pair while every lane also issues the loads of its columns for all
+// splits of the group, so a group costs one memory round trip.  Weights reach
+// the column sums through wave shuffles; a running maximum rescales across
+// groups.  The order of every sum is fixed, so the result does not depend on
 // which chunk finished last.  COHERENT reads use agent-scope atomic loads
 // (partials written by other workgroups inside the same kernel).
 template <bool COHERENT>
 __device__ void merge_wave(const AttnArgs& a, int req, const ReqEntry& rq, int h, int lane) {
+  constexpr int MAXC = 16;  // columns per lane: head_width <= 1024
+  constexpr int UNROLL = 8;
   const int D = a.head_width;
   const int H = a.num_heads;
   const int ns = rq.nsplit;
+  const int ncol = (D + 63) / 64;
   const int64_t stride = (int64_t)H * (D + 2);
   const float* base = a.partials + ((int64_t)rq.partial_base * H + h) * (D + 2);
-  float mx = -FLT_MAX;
-  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, load_part<COHERENT>(base + s * stride));
-  mx = wave_max(mx);
-  float lsum = 0.f;
-  for (int s = lane; s < ns; s += 64)
-    lsum += load_part<COHERENT>(base + s * stride + 1) *
-            fast_exp2(load_part<COHERENT>(base + s * stride) - mx);
-  lsum = wave_sum(lsum);
-  const float inv = 1.0f / lsum;
-  float* out = a.out + ((int64_t)req * H + h) * D;
-  for (int d = lane; d < D; d += 64) {
-    const float* col = base + 2 + d;
-    float o[4] = {0.f, 0.f, 0.f, 0.f};
-    int s = 0;
-    for (; s + 4 <= ns; s += 4) {
-      float mv[4], av[4];
+  float M = -FLT_MAX, L = 0.f;
+  float o[MAXC];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        mv[j] = load_part<COHERENT>(base + (s + j) * stride);
-        av[j] = load_part<COHERENT>(col + (s + j) * stride);
+  for (int v = 0; v < MAXC; ++v) o[v] = 0.f;
+  for (int g0 = 0; g0 < ns; g0 += 64) {
+    const int gn = min(64, ns - g0);
+    const bool mine = lane < gn;
+    const float* ps = base + (int64_t)(g0 + (mine ? lane : 0)) * stride;
+    const float m_s = mine ? load_part<COHERENT>(ps) : -FLT_MAX;
+    const float l_s = mine ? load_part<COHERENT>(ps + 1) : 0.f;
+    const float gm = wave_max(m_s);
+    const float newM = fmaxf(M, gm);
+    const float scale = fast_exp2(M - newM);
+    M = newM;
+    const float w = mine ? fast_exp2(m_s - M) : 0.f;
+    L = fmaf(L, scale, wave_sum(l_s * w));
+#pragma unroll
+    for (int v = 0; v < MAXC; ++v) {
+      if (v >= ncol) break;
+      const int d = lane + 64 * v;
+      const float* col = base + (int64_t)g0 * stride + 2 + (d < D ? d : 0);
+      float x = o[v] * scale;
+      for (int s = 0; s < gn; s += UNROLL) {
+        float av[UNROLL];
+#pragma unroll
+        for (int j = 0; j < UNROLL; ++j)
+          av[j] = (s + j < gn) ? load_part<COHERENT>(col + (int64_t)(s + j) * stride) : 0.f;
+#pragma unroll
+        for (int j = 0; j < UNROLL; ++j) x = fmaf(av[j], __shfl(w, s + j), x);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = fmaf(av[j], fast_exp2(mv[j] - mx), o[j]);
+      o[v] = x;
     }
-    for (; s < ns; ++s)
-      o[0] = fmaf(load_part<COHERENT>(col + s * stride),
-                  fast_exp2(load_part<COHERENT>(base + s * stride) - mx), o[0]);
-    out[d] = ((o[0] + o[1]) + (o[2] + o[3])) * inv;
+  }
+  const float inv = 1.0f / L;
+  float* out = a.out + ((int64_t)req * H + h) * D;
+#pragma unroll
+  for (int v = 0; v < MAXC; ++v) {
+    const int d = lane + 64 * v;
+    if (v < ncol && d < D) out[d] = o[v] * inv;
   }
 }
 
