@@ -37,22 +37,26 @@ HBM_PEAK_GBS = 8000.0
 # kernel source they were taken from (sha256 prefix of csrc/kernels.hip).
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
-    "batch32_fp32_l12": {"kernels_sha256_16": "00cbe2a2e504533e",
-                         "fetch_kib": 44375.5, "write_kib": 2004.4},
+    "batch32_fp32_l12": {"kernels_sha256_16": "ff5f18c9fa6b6ceb",
+                         "fetch_kib": 44691.9, "write_kib": 2008.4,
+                         "algorithmic_bytes": 88971264},
 }
 
 
 def measured_traffic(workload: str):
+    """(HBM bytes per attention launch, algorithmic bytes of the same
+    launches) from the PMC runs, or (None, None) if the kernel changed."""
     import hashlib
     m = MEASURED_TRAFFIC.get(workload)
     if m is None:
-        return None
+        return None, None
     src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_attention_amd",
                        "csrc", "kernels.hip")
     with open(src, "rb") as f:
         if hashlib.sha256(f.read()).hexdigest()[:16] != m["kernels_sha256_16"]:
-            return None
-    return int((m["fetch_kib"] * FETCH_SCALE + m["write_kib"] * WRITE_SCALE) * 1024)
+            return None, None
+    return (int((m["fetch_kib"] * FETCH_SCALE + m["write_kib"] * WRITE_SCALE) * 1024),
+            m["algorithmic_bytes"])
 
 
 def parse():
@@ -226,6 +230,7 @@ def main():
     if not transactional:
         chunks = pkv.pkv_plan_num_chunks(plan)
 
+    traffic, traffic_alg = measured_traffic(w.name)
     result = {
         "metric": "paged decode attention KV GB/s (% of HBM peak) + decode-attention steps/sec",
         "value": round(value, 2),
@@ -268,7 +273,8 @@ def main():
             "merge_launches": int(prof.merge_launches) if prof else 0,
             "merge_avg_us": round(prof.merge_ms / max(1, prof.merge_launches) * 1e3, 2)
             if prof else 0.0,
-            "traffic": measured_traffic(w.name),
+            "traffic": traffic,
+            "traffic_run_algorithmic_bytes": traffic_alg,
         },
     }
     if not args.no_cpu_baseline:
