@@ -182,6 +182,30 @@ def test_batched_decode_small(dtype, D, S, split, merge):
     pkv.pkv_pool_destroy(pool)
 
 
+@pytest.mark.parametrize("dtype,D,S", [c for c in SMALL_CASES if (c[0], c[1]) in
+                                        (("f32", 64), ("bf16", 128)) and c[2] % 16 == 0])
+@pytest.mark.parametrize("split,merge", [(0, 2), (2, 2), (2, 0), (-1, 2)])
+def test_eight_wave_workgroups(dtype, D, S, split, merge):
+    w = _small(f"w8_{dtype}_{D}_{S}", dtype, D, S, LENGTHS, seed=29)
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp, split=split, merge=merge)
+    pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_WAVES, 8)
+    plan = pkv.pkv_plan_create(pool)
+    pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
+    pt = _pt_device(w)
+    layer = 1
+    qh, kh, vh = w.q(layer), w.k_new(layer), w.v_new(layer)
+    q, k, v = (rows_to_device(x, dtype) for x in (qh, kh, vh))
+    out = torch.empty((w.n, w.heads, D), device="cuda")
+    pkv.pkv_plan_append_and_attend(plan, layer, pt, q, k, v, out)
+    torch.cuda.synchronize()
+    for r in range(w.n):
+        ref = _oracle_decode(w, layer, r, qh, appended=(kh, vh))
+        assert max_err(out[r], ref) <= TOL[dtype], (r, int(w.lengths[r]))
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(pool)
+
+
 @pytest.mark.parametrize("dtype,D,S", SMALL_CASES)
 @pytest.mark.parametrize("merge", MERGES)
 def test_append_and_attend_small(dtype, D, S, merge):
