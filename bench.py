@@ -17,8 +17,9 @@ launch stream immediately around every attention kernel (PKV_OPT_PROFILING)
 and sums each launch's algorithmic bytes.
 
 Other workloads (--workload): batch256_bf16, skewed64_bf16 (single-layer
-batched decode over existing rows) and fullstep128_bf16_l32 (32 layers, 128
-requests, bf16, 1% seeded aborts).
+batched decode over existing rows), fullstep128_bf16_l32 (32 layers, 128
+requests, bf16, 1% seeded aborts) and tiny (the latency-bound fixture:
+token-at-a-time steps of one request, reported in steps/s and us/step).
 """
 from __future__ import annotations
 
@@ -102,6 +103,8 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
 
+    if args.workload == "tiny":
+        return tiny_latency(args)
     maker = W.WORKLOADS[args.workload]
     grow = 2 * args.steps + args.warmup + 2   # committed tokens per request over both passes
     w = maker(extra_steps=grow) if args.workload.startswith("fullstep") else maker()
@@ -280,6 +283,65 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def tiny_latency(args):
+    """Tiny fixture: 1 request, 2 layers, H=2, d_h=2, 16-token pages, 8 pages,
+    float32, context 4: token-at-a-time steps (begin, append_and_attend per
+    layer, commit), reset after the fourth.  Latency-bound: reports us/step."""
+    import torch
+
+    import paged_kv_cache_attention_amd as pkv
+    from synth import gpu as sgpu
+    from synth import workloads as W
+
+    g = W.tiny_geometry()
+    L, H, D, C = g["layers"], g["heads"], g["head_width"], g["max_len"]
+    kp = torch.zeros((L, g["num_pages"], H, g["page_size"], D), device="cuda")
+    vp = torch.zeros_like(kp)
+    d = pkv.pkv_pool_desc_init()
+    d.num_layers, d.num_heads, d.head_width = L, H, D
+    d.page_size, d.num_pages, d.max_context = g["page_size"], g["num_pages"], C
+    d.k_storage, d.v_storage, d.free_list_seed = kp.data_ptr(), vp.data_ptr(), g["seed"]
+    pool = pkv.pkv_pool_create(d)
+    cache = pkv.pkv_cache_create(pool, C)
+    rows = [[tuple(sgpu.to_device(x, "f32", "cuda") for x in W.tiny_rows(g["seed"], l, p, H, D))
+             for l in range(L)] for p in range(C)]
+    out = torch.empty((H, D), device="cuda")
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        pos = i % C
+        if pos == 0 and pkv.pkv_cache_size(cache) == C:
+            pkv.pkv_cache_reset(cache)
+        pkv.pkv_begin_token(cache)
+        for layer in range(L):
+            q, k, v = rows[pos][layer]
+            pkv.pkv_append_and_attend(cache, layer, q, k, v, out, stream=sh)
+        pkv.pkv_commit_token(cache)
+
+    for i in range(args.warmup * C):
+        step(i)
+    torch.cuda.synchronize()
+    n = args.steps * C
+    t0 = time.perf_counter()
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    kv = sum(t for t in range(1, C + 1)) * args.steps * L * H * 2 * D * 4
+    print(json.dumps({
+        "metric": "paged decode attention KV GB/s (% of HBM peak) + decode-attention steps/sec",
+        "value": round(n / el, 1), "unit": "steps/s", "n_gpus": 1, "steps": n,
+        "warmup": args.warmup * C, "ms_per_step": round(el / n * 1e3, 4),
+        "us_per_step": round(el / n * 1e6, 2), "kv_bytes_per_step_mean": kv // n,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "tiny", "requests": 1, "layers": L, "heads": H, "head_width": D,
+                   "page_size": g["page_size"], "pool_pages": g["num_pages"], "context": C,
+                   "parallelism": "single GPU"}}), flush=True)
+    pkv.pkv_cache_destroy(cache)
+    pkv.pkv_pool_destroy(pool)
 
 
 def cpu_baseline(w, budget_s: float) -> dict:

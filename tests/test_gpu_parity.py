@@ -425,6 +425,45 @@ def test_last_arriver_merge_is_bitwise_separate_merge():
         assert max_err(ref[r], _oracle_decode(w, 0, r, qh)) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("merge", MERGES)
+def test_plan_decode_replays_from_a_hip_graph(merge):
+    """A multi-layer decode on a prebuilt plan, captured once in a HIP graph
+    and replayed: every replay (with eager work and synchronisation between
+    replays) equals the eager launch bit for bit.  The split-merge counters
+    return to zero by themselves, so no memset enters the graph."""
+    w = _small("graph", "bf16", 128, 16, [5, 300, 1500, 2600], heads=4, layers=3)
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp, split=8, merge=merge)
+    plan = pkv.pkv_plan_create(pool)
+    pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
+    assert pkv.pkv_plan_num_chunks(plan) > w.n
+    pt = _pt_device(w)
+    qs = [rows_to_device(w.q(layer), "bf16") for layer in range(w.layers)]
+    eager = [torch.empty((w.n, w.heads, 128), device="cuda") for _ in range(w.layers)]
+    for layer in range(w.layers):
+        pkv.pkv_plan_decode_attention(plan, layer, qs[layer], pt, eager[layer])
+    torch.cuda.synchronize()
+    outs = [torch.full_like(e, float("nan")) for e in eager]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for layer in range(w.layers):
+            pkv.pkv_plan_decode_attention(plan, layer, qs[layer], pt, outs[layer])
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"replay {rep}"
+        _ = (torch.randn(1 << 20, device="cuda") * 2).sum().item()   # eager work between replays
+    qh = w.q(2)
+    for r in range(w.n):
+        assert max_err(eager[2][r], _oracle_decode(w, 2, r, qh)) <= TOL["bf16"]
+    del graph
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(pool)
+
+
 @pytest.mark.parametrize("maker", [W.batch256_bf16, W.skewed64_bf16])
 @pytest.mark.parametrize("merge", MERGES)
 def test_bf16_single_layer_full(maker, merge):
