@@ -17,7 +17,8 @@ launch stream immediately around every attention kernel (PKV_OPT_PROFILING)
 and sums each launch's algorithmic bytes.
 
 Other workloads (--workload): batch256_bf16, skewed64_bf16 (single-layer
-batched decode over existing rows), fullstep128_bf16_l32 (32 layers, 128
+batched decode over existing rows), batch256_gqa8_bf16 (the same batch with
+32 query heads sharing 8 K/V heads), fullstep128_bf16_l32 (32 layers, 128
 requests, bf16, 1% seeded aborts) and tiny (the latency-bound fixture:
 token-at-a-time steps of one request, reported in steps/s and us/step).
 """
@@ -111,6 +112,7 @@ def main():
     transactional = w.appends
     dt = sgpu.torch_dtype(w.dtype)
     H, D, L, n = w.heads, w.head_width, w.layers, w.n
+    Hkv = w.hkv
     elt = w.elt
 
     if args.calibrate_copy:
@@ -122,16 +124,15 @@ def main():
         del src, dst
 
     # ---- pool and inputs, filled on the device by the seeded generator ----
-    shape = (L, w.num_pages, H, w.page_size, D)
+    shape = (L, w.num_pages, Hkv, w.page_size, D)
     kp = torch.empty(shape, dtype=dt, device="cuda")
     vp = torch.empty(shape, dtype=dt, device="cuda")
     for layer in range(L):
         sgpu.fill_normal(kp[layer], w.kpool_key(layer), w.dtype)
         sgpu.fill_normal(vp[layer], w.vpool_key(layer), w.dtype)
-    rows = (L, n, H, D)
-    q_all = torch.empty(rows, dtype=dt, device="cuda")
-    k_all = torch.empty(rows, dtype=dt, device="cuda")
-    v_all = torch.empty(rows, dtype=dt, device="cuda")
+    q_all = torch.empty((L, n, H, D), dtype=dt, device="cuda")
+    k_all = torch.empty((L, n, Hkv, D), dtype=dt, device="cuda")
+    v_all = torch.empty((L, n, Hkv, D), dtype=dt, device="cuda")
     for layer in range(L):
         sgpu.fill_normal(q_all[layer], w.q_key(layer), w.dtype)
         sgpu.fill_normal(k_all[layer], w.k_key(layer), w.dtype)
@@ -147,6 +148,7 @@ def main():
     d.split_blocks = args.split_blocks
     d.k_storage, d.v_storage = kp.data_ptr(), vp.data_ptr()
     d.free_list_seed = w.seed
+    d.num_kv_heads = Hkv
     pool = pkv.pkv_pool_create(d)
     pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_MERGE_MODE, args.merge_mode)
     pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_WAVES, args.waves)
@@ -184,7 +186,7 @@ def main():
                     idx = torch.tensor(live, device="cuda")
                     q, k, v = q_all[layer][idx], k_all[layer][idx], v_all[layer][idx]
                     o = out[:len(live)]
-                kv_bytes += t_sum * H * 2 * D * elt
+                kv_bytes += t_sum * Hkv * 2 * D * elt
                 pkv.pkv_append_and_attend_batched(live_arr, layer, q, k, v, o, stream=sh)
             pkv.pkv_commit_token_batched(live_arr)
             for r in live:
@@ -195,7 +197,7 @@ def main():
         plan = pkv.pkv_plan_create(pool)
         pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride, stream=stream)
         pt = torch.from_numpy(w.page_tables.copy()).to("cuda")
-        kv_once = int(w.lengths.sum()) * H * 2 * D * elt
+        kv_once = int(w.lengths.sum()) * Hkv * 2 * D * elt
 
         def step(timed: bool):
             pkv.pkv_plan_decode_attention(plan, 0, q_all[0], pt, out, stream=stream)
@@ -251,9 +253,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name,
-            "requests": n, "layers": L, "heads": H, "head_width": D,
+            "requests": n, "layers": L, "heads": H, "kv_heads": Hkv, "head_width": D,
             "page_size": w.page_size, "pool_pages": w.num_pages,
-            "mean_attended_len": round(kv_total / args.steps / L / (H * 2 * D * elt) /
+            "mean_attended_len": round(kv_total / args.steps / L / (Hkv * 2 * D * elt) /
                                        max(1, n), 1),
             "kv_bytes_per_step": int(kv_total / args.steps),
             "split_blocks": args.split_blocks,
@@ -384,8 +386,9 @@ def cpu_baseline(w, budget_s: float) -> dict:
                 oracle.append_and_attend(q[r], kn[r], vn[r], pages_k, pages_v, pt, t - 1,
                                          w.page_size)
             else:
-                oracle.paged_decode_attention(q[r], pages_k, pages_v, pt, t, w.page_size)
-            done_bytes += t * w.heads * 2 * w.head_width * w.elt
+                oracle.paged_decode_attention(q[r], pages_k, pages_v, pt, t, w.page_size,
+                                              num_kv_heads=w.hkv)
+            done_bytes += t * w.hkv * 2 * w.head_width * w.elt
             done += 1
             if time.perf_counter() - t0 > budget_s:
                 break

@@ -77,9 +77,14 @@ typedef struct pkv_plan pkv_plan;
 
 /* Pool geometry and storage.
  * k_storage and v_storage are caller-owned device buffers, each holding
- * num_layers * num_pages * num_heads * page_size * head_width elements of
- * kv_dtype, laid out [layer][physical_page][head][page_offset][head_width]
- * and 16-byte aligned.  They must stay alive until pkv_pool_destroy. */
+ * num_layers * num_pages * H_kv * page_size * head_width elements of
+ * kv_dtype, laid out [layer][physical_page][kv_head][page_offset][head_width]
+ * and 16-byte aligned.  They must stay alive until pkv_pool_destroy.
+ * Queries and contexts have num_heads heads; K/V rows (the k and v of an
+ * append, the pool pages) have H_kv heads.  The pages describe H_kv ==
+ * num_heads; with fewer K/V heads ("Rollout Serving, Caching, and Batching",
+ * key-value cache section, which allows them for grouped- and multi-query
+ * models) each K/V head serves num_heads / H_kv consecutive query heads. */
 typedef struct pkv_pool_desc {
   int32_t num_layers;     /* L >= 1                                           */
   int32_t num_heads;      /* H >= 1                                           */
@@ -93,6 +98,11 @@ typedef struct pkv_pool_desc {
                              blocks splits into ceil(B / split_blocks) even
                              chunks); 0 = automatic, -1 = never split          */
   int32_t flags;          /* PKV_POOL_* bits; 0 by default                     */
+  int32_t num_kv_heads;   /* K/V heads H_kv; 0 = num_heads.  num_heads must be
+                             a multiple: query head h reads K/V head
+                             h / (num_heads / H_kv) (grouped-query attention;
+                             1 K/V head = multi-query)                        */
+  int32_t reserved;       /* 0                                                 */
   void* k_storage;
   void* v_storage;
   uint64_t free_list_seed; /* seeds the shuffle of the initial free list      */
@@ -215,9 +225,9 @@ pkv_status pkv_cache_grow(pkv_cache* cache, int32_t n_tokens);
  * Errors: BAD_STATE (already pending), CAPACITY_EXHAUSTED, OUT_OF_PAGES. */
 pkv_status pkv_begin_token(pkv_cache* cache, int32_t* position);
 
-/* One layer of the pending token: writes k and v ([1,H,1,d_h], pool dtype,
- * device) into the pool at the pending position, then attends with q over
- * the length+1 rows, writing out ([1,H,1,d_h] float32, device).
+/* One layer of the pending token: writes k and v ([1,H_kv,1,d_h], pool
+ * dtype, device) into the pool at the pending position, then attends with q
+ * ([1,H,1,d_h]) over the length+1 rows, writing out ([1,H,1,d_h] float32).
  * Errors: BAD_STATE (no pending token, layer already appended),
  * INVALID_ARGUMENT (layer out of range, null pointer), DEVICE. */
 pkv_status pkv_append_and_attend(pkv_cache* cache, int32_t layer, const void* q,
@@ -242,9 +252,9 @@ pkv_status pkv_begin_token_batched(pkv_cache* const* caches, int32_t n, int32_t*
 pkv_status pkv_commit_token_batched(pkv_cache* const* caches, int32_t n);
 
 /* The same layer step for n pending caches of one pool in one launch:
- * q, k, v are [n,H,d_h] (pool dtype), out is [n,H,d_h] float32, row i
- * belonging to caches[i].  All caches are validated before any work is
- * enqueued.  Errors: as pkv_append_and_attend, per cache; INVALID_ARGUMENT
+ * q is [n,H,d_h], k and v are [n,H_kv,d_h] (pool dtype), out is [n,H,d_h]
+ * float32, row i belonging to caches[i].  All caches are validated before
+ * any work is enqueued.  Errors: as pkv_append_and_attend, per cache; INVALID_ARGUMENT
  * for a repeated cache or caches of different pools. */
 pkv_status pkv_append_and_attend_batched(pkv_cache* const* caches, int32_t n, int32_t layer,
                                          const void* q, const void* k, const void* v,
@@ -274,8 +284,8 @@ int32_t pkv_plan_num_chunks(const pkv_plan* plan);
 pkv_status pkv_plan_decode_attention(pkv_plan* plan, int32_t layer, const void* q,
                                      const int32_t* page_table, float* out, void* stream);
 
-/* Batched append: writes k[r], v[r] ([n,H,d_h], pool dtype) into row t_r-1
- * of each request's pages (a byte copy). */
+/* Batched append: writes k[r], v[r] ([n,H_kv,d_h], pool dtype) into row
+ * t_r-1 of each request's pages (a byte copy). */
 pkv_status pkv_plan_kv_append(pkv_plan* plan, int32_t layer, const int32_t* page_table,
                               const void* k, const void* v, void* stream);
 

@@ -10,7 +10,8 @@ Modules:
 
 * ``oracle.attention`` — gather through a page table, softmax(q K^T / sqrt(d_h)) V,
   append-then-attend with a candidate row, the newest row of full causal
-  attention, split partials and their log-sum-exp merge.
+  attention, split partials and their log-sum-exp merge, K/V heads shared by
+  groups of query heads.
 * ``oracle.counters`` — attention-score-cell counts and K/V byte accounting.
 * ``oracle.transaction`` — the visible-state model of begin / append / commit /
   abort / reset on a request cache backed by a page pool.
@@ -23,13 +24,14 @@ function has at least one pin); the pages' fixture logits are outside this
 path (they need model weights the pages do not give).
 """
 from .attention import (append_and_attend, attend, causal_attention, gather_prefix,
-                        kv_to_f64, merge_partials, paged_decode_attention, split_partials)
+                        kv_head_of, kv_to_f64, merge_partials, paged_decode_attention,
+                        split_partials)
 from .counters import (cached_score_cells, complete_prefix_score_cells, kv_cache_bytes,
                        qkv_projection_rows)
 from .transaction import CacheModel, PoolModel, Status
 
 __all__ = [
-    "append_and_attend", "attend", "causal_attention", "gather_prefix", "kv_to_f64",
+    "append_and_attend", "attend", "causal_attention", "gather_prefix", "kv_head_of", "kv_to_f64",
     "merge_partials", "paged_decode_attention", "split_partials",
     "cached_score_cells", "complete_prefix_score_cells", "kv_cache_bytes",
     "qkv_projection_rows", "CacheModel", "PoolModel", "Status",

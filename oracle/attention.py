@@ -18,6 +18,11 @@ Sources, by page and section:
   complete-prefix call rebuilds the whole causal score grid; the cached call
   forms only the newest query's row.
 
+* mbrenndoerfer "Rollout Serving, Caching, and Batching", key-value cache
+  section: grouped-query or multi-query attention keeps fewer K/V heads than
+  query heads.  Reading where the page is silent: query head h of H reads K/V
+  head h // (H / H_kv) (consecutive groups); H_kv = H is the pages' case.
+
 Floating point: everything is float64.  bfloat16 inputs arrive as uint16 bit
 patterns and widen exactly (bits << 16 is the float32 with the same value).
 """
@@ -75,16 +80,27 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
     return probs @ V
 
 
-def paged_decode_attention(q, k_pages, v_pages, page_table, t: int, page_size: int):
+def kv_head_of(h: int, num_heads: int, num_kv_heads: int) -> int:
+    """K/V head read by query head h: consecutive groups of H / H_kv."""
+    if num_heads % num_kv_heads:
+        raise ValueError("query heads must be a multiple of K/V heads")
+    return h // (num_heads // num_kv_heads)
+
+
+def paged_decode_attention(q, k_pages, v_pages, page_table, t: int, page_size: int,
+                           num_kv_heads: int | None = None):
     """Context [H, D] of one request whose attended prefix has ``t`` rows.
 
-    q: [H, D]; ``k_pages`` / ``v_pages`` index physical pages of one layer.
+    q: [H, D]; ``k_pages`` / ``v_pages`` index physical pages of one layer,
+    each [H_kv, S, D] (H_kv defaults to H).
     """
     H = q.shape[0]
+    Hkv = H if num_kv_heads is None else num_kv_heads
     out = np.empty((H, q.shape[1]), dtype=np.float64)
     for h in range(H):
-        K = gather_prefix(k_pages, page_table, t, page_size, h)
-        V = gather_prefix(v_pages, page_table, t, page_size, h)
+        kvh = kv_head_of(h, H, Hkv)
+        K = gather_prefix(k_pages, page_table, t, page_size, kvh)
+        V = gather_prefix(v_pages, page_table, t, page_size, kvh)
         out[h] = attend(q[h], K, V)
     return out
 
@@ -95,17 +111,20 @@ def append_and_attend(q, k_new, v_new, k_pages, v_pages, page_table, length: int
 
     The retained rows 0..length-1 come from the pages; the candidate row (k_new,
     v_new) sits at position ``length``; the query attends to all length+1 rows.
-    q, k_new, v_new: [H, D].  Returns the context [H, D] in float64.
+    q: [H, D]; k_new, v_new: [H_kv, D] (H_kv = H unless K/V heads are shared).
+    Returns the context [H, D] in float64.
     """
     H = q.shape[0]
+    Hkv = k_new.shape[0]
     out = np.empty((H, q.shape[1]), dtype=np.float64)
     for h in range(H):
-        K = kv_to_f64(gather_prefix(k_pages, page_table, length, page_size, h)) if length else \
+        kvh = kv_head_of(h, H, Hkv)
+        K = kv_to_f64(gather_prefix(k_pages, page_table, length, page_size, kvh)) if length else \
             np.zeros((0, q.shape[1]))
-        V = kv_to_f64(gather_prefix(v_pages, page_table, length, page_size, h)) if length else \
+        V = kv_to_f64(gather_prefix(v_pages, page_table, length, page_size, kvh)) if length else \
             np.zeros((0, q.shape[1]))
-        K = np.concatenate([K.reshape(-1, q.shape[1]), kv_to_f64(k_new[h])[None, :]], axis=0)
-        V = np.concatenate([V.reshape(-1, q.shape[1]), kv_to_f64(v_new[h])[None, :]], axis=0)
+        K = np.concatenate([K.reshape(-1, q.shape[1]), kv_to_f64(k_new[kvh])[None, :]], axis=0)
+        V = np.concatenate([V.reshape(-1, q.shape[1]), kv_to_f64(v_new[kvh])[None, :]], axis=0)
         out[h] = attend(q[h], K, V)
     return out
 

@@ -54,6 +54,8 @@ class pkv_pool_desc(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("split_blocks", ctypes.c_int32),
         ("flags", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
         ("k_storage", ctypes.c_void_p),
         ("v_storage", ctypes.c_void_p),
         ("free_list_seed", ctypes.c_uint64),

@@ -143,10 +143,10 @@ __device__ inline void store_part(float* p, float v) {
 // the column sums through wave shuffles; a running maximum rescales across
 // groups.  The order of every sum is fixed, so the result does not depend on
 // which chunk finished last.  COHERENT reads use agent-scope atomic loads
-// (partials written by other workgroups inside the same kernel).
-template <bool COHERENT>
+// (partials written by other workgroups inside the same kernel).  MAXC bounds
+// the columns per lane: head_width <= 64 * MAXC.
+template <int MAXC, bool COHERENT>
 __device__ void merge_wave(const AttnArgs& a, int req, const ReqEntry& rq, int h, int lane) {
-  constexpr int MAXC = 16;  // columns per lane: head_width <= 1024
   constexpr int UNROLL = 8;
   const int D = a.head_width;
   const int H = a.num_heads;
@@ -172,19 +172,20 @@ __device__ void merge_wave(const AttnArgs& a, int req, const ReqEntry& rq, int h
     L = fmaf(L, scale, wave_sum(l_s * w));
 #pragma unroll
     for (int v = 0; v < MAXC; ++v) {
-      if (v >= ncol) break;
-      const int d = lane + 64 * v;
-      const float* col = base + (int64_t)g0 * stride + 2 + (d < D ? d : 0);
-      float x = o[v] * scale;
-      for (int s = 0; s < gn; s += UNROLL) {
-        float av[UNROLL];
+      if (v < ncol) {
+        const int d = lane + 64 * v;
+        const float* col = base + (int64_t)g0 * stride + 2 + (d < D ? d : 0);
+        float x = o[v] * scale;
+        for (int s = 0; s < gn; s += UNROLL) {
+          float av[UNROLL];
 #pragma unroll
-        for (int j = 0; j < UNROLL; ++j)
-          av[j] = (s + j < gn) ? load_part<COHERENT>(col + (int64_t)(s + j) * stride) : 0.f;
+          for (int j = 0; j < UNROLL; ++j)
+            av[j] = (s + j < gn) ? load_part<COHERENT>(col + (int64_t)(s + j) * stride) : 0.f;
 #pragma unroll
-        for (int j = 0; j < UNROLL; ++j) x = fmaf(av[j], __shfl(w, s + j), x);
+          for (int j = 0; j < UNROLL; ++j) x = fmaf(av[j], __shfl(w, s + j), x);
+        }
+        o[v] = x;
       }
-      o[v] = x;
     }
   }
   const float inv = 1.0f / L;
@@ -202,8 +203,9 @@ __device__ void merge_wave(const AttnArgs& a, int req, const ReqEntry& rq, int h
 // (request, head) counter then merges all partials and returns the counter to
 // zero for the next launch; in kMergeSeparate mode merge_kernel does that
 // afterwards.  Lane-held column e is col0 + e * CSTRIDE, present when own_cols
-// and below the head width.
-template <int NCOL, int CSTRIDE>
+// and below the head width; the merge holds MCOLS columns per lane
+// (head_width <= 64 * MCOLS).
+template <int NCOL, int CSTRIDE, int MCOLS>
 __device__ inline void finish_chunk(const AttnArgs& a, const WorkItem& it, const ReqEntry& rq,
                                     int h, int lane, bool own_cols, int col0, float m, float l,
                                     const float* acc) {
@@ -248,18 +250,22 @@ __device__ inline void finish_chunk(const AttnArgs& a, const WorkItem& it, const
   prev = __shfl(prev, 0);
   if (prev != rq.nsplit - 1) return;
   if (lane == 0) (void)__hip_atomic_exchange(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  merge_wave<true>(a, it.req, rq, h, lane);
+  merge_wave<MCOLS, true>(a, it.req, rq, h, lane);
 }
 
 // ---------------------------------------------------------------------------
 // Fast path: rows of exactly 256 bytes (bf16 d_h=128, f32 d_h=64), pages a
-// multiple of 16 rows.  Workgroup = WAVES (4 or 8) waves on one (chunk,
-// head).  A wave takes every WAVES-th 16-row block of the chunk; a block is one contiguous 4 KiB
-// slab of K and one of V.  Lane (g, c): row i*4+g of each of the 4 loads, 16
-// bytes at column c, so one load instruction reads 1 KiB contiguous and the
-// 16 lanes of a DPP row hold one K/V row.  Each 16-lane group keeps its own
-// online-softmax state over its rows; groups merge in-wave, waves in LDS.
-template <typename T, int D, int WAVES>
+// multiple of 16 rows.  A workgroup of WAVES waves serves one (chunk, K/V
+// head) and the G query heads that share that K/V head: its waves form
+// WAVES/WPG head groups of HPW query heads each, and the WPG waves of a group
+// interleave the chunk's 16-row blocks, so each head group loads every K/V
+// byte of the chunk once for its HPW query heads (with one head group, once
+// for all G).  Multi-head attention is G = 1 (HPW = 1, WPG = WAVES).  A block is one contiguous 4 KiB slab of K and one of V.
+// Lane (g, c): row i*4+g of each of the 4 loads, 16 bytes at column c, so one
+// load instruction reads 1 KiB contiguous and the 16 lanes of a DPP row hold
+// one K/V row.  Each 16-lane group keeps its own online-softmax state per
+// query head; groups merge in-wave, the waves of a head group in LDS.
+template <typename T, int D, int WAVES, int HPW, int WPG>
 __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
   using KV = KVTraits<T>;
   constexpr int EPL = KV::kPerVec;
@@ -268,38 +274,47 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
   constexpr int RPI = 64 / LPR;            // rows per load instruction
   constexpr int NI = kBlockRows / RPI;     // load instructions per block
   constexpr int ROW_BYTES = D * (int)sizeof(T);
+  constexpr int NG = WAVES / WPG;          // head groups per workgroup
+  static_assert(NG * WPG == WAVES, "waves must split evenly into head groups");
+  constexpr int G = NG * HPW;              // query heads per K/V head
 
   const WorkItem it = a.items[blockIdx.x];
   const ReqEntry rq = it.rq;
-  const int h = blockIdx.y;
+  const int kvh = blockIdx.y;
   const int lane = threadIdx.x & 63;
   // Wave-uniform: block indices, page-table reads and branches stay scalar, so
   // the page lookups go through the scalar cache and never wait on the
   // vector-memory counter that tracks the K/V loads in flight.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hg = wave / WPG;               // head group of this wave
+  const int sub = wave % WPG;              // its place among the group's waves
+  const int qh0 = kvh * G + hg * HPW;      // first query head of this wave
   const int g = lane / LPR;
   const int c = lane % LPR;
   const int t = rq.seq_len;
   const int S = a.page_size;
   const const_i32_ptr pt = as_const(a.page_table + (int64_t)rq.pt_row * a.pt_stride);
-  const int64_t qrow_bytes = (((int64_t)it.req * a.num_heads + h) * D) * (int64_t)sizeof(T);
-  const int64_t head_off = (int64_t)h * a.head_bytes;
+  const int64_t kvrow_bytes =
+      (((int64_t)it.req * a.num_kv_heads + kvh) * D) * (int64_t)sizeof(T);
+  const int64_t head_off = (int64_t)kvh * a.head_bytes;
   const int last_blk = (t - 1) / kBlockRows;
   const bool fused = a.fuse_append != 0 && it.blk_end > last_blk;
 
-  float qf[EPL];
-  {
+  float qf[HPW][EPL];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    const int64_t qrow_bytes = (((int64_t)it.req * a.num_heads + qh0 + j) * D) * (int64_t)sizeof(T);
     const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + qrow_bytes +
                                                     c * 16);
-    KV::unpack(u, qf);
+    KV::unpack(u, qf[j]);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qf[e] *= a.scale_log2e;
+    for (int e = 0; e < EPL; ++e) qf[j][e] *= a.scale_log2e;
   }
 
   uint4 knew = make_uint4(0, 0, 0, 0), vnew = make_uint4(0, 0, 0, 0);
   if (fused) {
-    knew = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + qrow_bytes + c * 16);
-    vnew = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + qrow_bytes + c * 16);
+    knew = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + kvrow_bytes + c * 16);
+    vnew = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + kvrow_bytes + c * 16);
     if (wave == 0 && g == 0) {
       const int pos = t - 1;
       const int64_t slot = (int64_t)pt[pos / S] * a.page_bytes + head_off +
@@ -332,10 +347,15 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
     }
   };
 
-  float m = -FLT_MAX, l = 0.f;
-  float acc[EPL];
+  float m[HPW], l[HPW];
+  float acc[HPW][EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int j = 0; j < HPW; ++j) {
+    m[j] = -FLT_MAX;
+    l[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
+  }
 
   // EDGE is a compile-time tag: the masked variant exists only as its own
   // code path, entered by a scalar branch for the request's last block.
@@ -356,46 +376,55 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
         vv[i] = select4(valid[i], select4(is_new, vnew, vv[i]), make_uint4(0, 0, 0, 0));
       }
     }
-    float s[NI];
+    float s[HPW][NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float kf[EPL];
       KV::unpack(kk[i], kf);
-      float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) d = fmaf(qf[e], kf[e], d);
-      s[i] = row16_sum(d);
-      if constexpr (edge) {
-        if (!valid[i]) s[i] = -INFINITY;
+      for (int j = 0; j < HPW; ++j) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) d = fmaf(qf[j][e], kf[e], d);
+        s[j][i] = row16_sum(d);
+        if constexpr (edge) {
+          if (!valid[i]) s[j][i] = -INFINITY;
+        }
       }
     }
-    float mb = s[0];
+    float p[HPW][NI];
 #pragma unroll
-    for (int i = 1; i < NI; ++i) mb = fmaxf(mb, s[i]);
-    const float mn = fmaxf(m, mb);
-    const float alpha = fast_exp2(m - mn);
-    float p[NI];
-    float ps = 0.f;
+    for (int j = 0; j < HPW; ++j) {
+      float mb = s[j][0];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      p[i] = fast_exp2(s[i] - mn);
-      ps += p[i];
+      for (int i = 1; i < NI; ++i) mb = fmaxf(mb, s[j][i]);
+      const float mn = fmaxf(m[j], mb);
+      const float alpha = fast_exp2(m[j] - mn);
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        p[j][i] = fast_exp2(s[j][i] - mn);
+        ps += p[j][i];
+      }
+      l[j] = fmaf(l[j], alpha, ps);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[j][e] *= alpha;
+      m[j] = mn;
     }
-    l = fmaf(l, alpha, ps);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float vf[EPL];
       KV::unpack(vv[i], vf);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p[i], vf[e], acc[e]);
+      for (int j = 0; j < HPW; ++j) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(p[j][i], vf[e], acc[j][e]);
+      }
     }
-    m = mn;
   };
 
-  // Software pipeline over this wave's blocks b, b+4, ..., wave_last: the
-  // K/V loads of the next block are issued before the current block is
+  // Software pipeline over this wave's blocks first, first+WPG, ..., wave_last:
+  // the K/V loads of the next block are issued before the current block is
   // computed, and the page ID of the block after that is read one step
   // ahead.  Look-ahead indices are clamped to wave_last instead of being
   // guarded by a branch, so every path keeps the same loads in flight and the
@@ -404,87 +433,99 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
   // (the masked "edge" step).
   {
     const int end = it.blk_end;
-    const int first = it.blk_begin + wave;
+    const int first = it.blk_begin + sub;
     if (first < end) {
-      const int wave_last = first + ((end - 1 - first) / WAVES) * WAVES;
+      const int wave_last = first + ((end - 1 - first) / WPG) * WPG;
       uint4 ka[NI], va[NI], kb[NI], vb[NI];
       load_block(first, page_of(first), ka, va);
-      int32_t p_next = page_of(min(first + WAVES, wave_last));
-      for (int b = first;; b += 2 * WAVES) {
-        const int b1 = min(b + WAVES, wave_last);
+      int32_t p_next = page_of(min(first + WPG, wave_last));
+      for (int b = first;; b += 2 * WPG) {
+        const int b1 = min(b + WPG, wave_last);
         load_block(b1, p_next, kb, vb);
-        p_next = page_of(min(b + 2 * WAVES, wave_last));
+        p_next = page_of(min(b + 2 * WPG, wave_last));
         if (b == last_blk)
           step(b, ka, va, std::true_type{});
         else
           step(b, ka, va, std::false_type{});
-        if (b + WAVES > wave_last) break;
-        const int b2 = min(b + 2 * WAVES, wave_last);
+        if (b + WPG > wave_last) break;
+        const int b2 = min(b + 2 * WPG, wave_last);
         load_block(b2, p_next, ka, va);
-        p_next = page_of(min(b + 3 * WAVES, wave_last));
+        p_next = page_of(min(b + 3 * WPG, wave_last));
         if (b1 == last_blk)
           step(b1, kb, vb, std::true_type{});
         else
           step(b1, kb, vb, std::false_type{});
-        if (b + 2 * WAVES > wave_last) break;
+        if (b + 2 * WPG > wave_last) break;
       }
     }
   }
 
   // Merge the four 16-lane groups of the wave (lanes differing in bits 4, 5).
 #pragma unroll
-  for (int off = 16; off <= 32; off <<= 1) {
-    const float mo = __shfl_xor(m, off);
-    const float lo = __shfl_xor(l, off);
-    const float mx = fmaxf(m, mo);
-    const float wa = fast_exp2(m - mx), wb = fast_exp2(mo - mx);
-    l = l * wa + lo * wb;
+  for (int j = 0; j < HPW; ++j) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float ao = __shfl_xor(acc[e], off);
-      acc[e] = acc[e] * wa + ao * wb;
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float mo = __shfl_xor(m[j], off);
+      const float lo = __shfl_xor(l[j], off);
+      const float mx = fmaxf(m[j], mo);
+      const float wa = fast_exp2(m[j] - mx), wb = fast_exp2(mo - mx);
+      l[j] = l[j] * wa + lo * wb;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float ao = __shfl_xor(acc[j][e], off);
+        acc[j][e] = acc[j][e] * wa + ao * wb;
+      }
+      m[j] = mx;
     }
-    m = mx;
   }
 
-  // Merge the waves through LDS.
-  __shared__ float s_m[WAVES], s_l[WAVES];
-  __shared__ float s_acc[WAVES][D];
+  // Merge the waves of each head group through LDS; the group's first wave
+  // finishes its HPW query heads.
+  __shared__ float s_m[WAVES][HPW], s_l[WAVES][HPW];
+  __shared__ float s_acc[WAVES][HPW][D];
   if (lane < LPR) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) s_acc[wave][c * EPL + e] = acc[e];
-    if (lane == 0) {
-      s_m[wave] = m;
-      s_l[wave] = l;
+    for (int j = 0; j < HPW; ++j) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[wave][j][c * EPL + e] = acc[j][e];
+      if (lane == 0) {
+        s_m[wave][j] = m[j];
+        s_l[wave][j] = l[j];
+      }
     }
   }
   __syncthreads();
-  if (wave == 0) {
-    float mx = s_m[0];
+  if (sub == 0) {
+    const int w0 = hg * WPG;
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) mx = fmaxf(mx, s_m[w]);
-    float wt[WAVES];
-    float lsum = 0.f;
+    for (int j = 0; j < HPW; ++j) {
+      float mx = s_m[w0][j];
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
-      wt[w] = fast_exp2(s_m[w] - mx);
-      lsum = fmaf(s_l[w], wt[w], lsum);
+      for (int w = 1; w < WPG; ++w) mx = fmaxf(mx, s_m[w0 + w][j]);
+      float wt[WPG];
+      float lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < WPG; ++w) {
+        wt[w] = fast_exp2(s_m[w0 + w][j] - mx);
+        lsum = fmaf(s_l[w0 + w][j], wt[w], lsum);
+      }
+      float o[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float x = 0.f;
+#pragma unroll
+        for (int w = 0; w < WPG; ++w) x = fmaf(s_acc[w0 + w][j][c * EPL + e], wt[w], x);
+        o[e] = x;
+      }
+      finish_chunk<EPL, 1, D / 64>(a, it, rq, qh0 + j, lane, lane < LPR, c * EPL, mx, lsum, o);
     }
-    float o[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float x = 0.f;
-#pragma unroll
-      for (int w = 0; w < WAVES; ++w) x = fmaf(s_acc[w][c * EPL + e], wt[w], x);
-      o[e] = x;
-    }
-    finish_chunk<EPL, 1>(a, it, rq, h, lane, lane < LPR, c * EPL, mx, lsum, o);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Generic path: any head width up to 1024, any page size.  One wave per
-// (chunk, head).  Tiles of 64 rows: lane j scores row j of the tile, the wave
+// Generic path: any head width up to 1024, any page size, any query-head
+// group size.  One wave per (chunk, query head), reading its group's K/V
+// head.  Tiles of 64 rows: lane j scores row j of the tile, the wave
 // reduces max and sum, then lanes sweep head-width columns accumulating the
 // weighted value rows.
 template <typename T>
@@ -498,25 +539,29 @@ __global__ __launch_bounds__(64) void attend_generic_kernel(AttnArgs a) {
 
   const WorkItem it = a.items[blockIdx.x];
   const ReqEntry rq = it.rq;
-  const int h = blockIdx.y;
+  const int h = blockIdx.y;                                  // query head
+  const int group = a.num_heads / a.num_kv_heads;
+  const int kvh = h / group;                                 // its K/V head
   const int lane = threadIdx.x;
   const int t = rq.seq_len;
   const int S = a.page_size;
   const int32_t* pt = a.page_table + (int64_t)rq.pt_row * a.pt_stride;
   const int64_t qrow = ((int64_t)it.req * a.num_heads + h) * D;
-  const int64_t head_off = (int64_t)h * a.head_bytes;
+  const int64_t kvrow = ((int64_t)it.req * a.num_kv_heads + kvh) * D;
+  const int64_t head_off = (int64_t)kvh * a.head_bytes;
   const int64_t row_bytes = (int64_t)D * sizeof(T);
   const int row_begin = it.blk_begin * kBlockRows;
   const int row_end = min(it.blk_end * kBlockRows, t);
   const bool fused = a.fuse_append != 0 && row_end == t;
 
   for (int d = lane; d < D; d += 64) qs[d] = KV::load1(a.q, qrow + d) * a.scale_log2e;
-  if (fused) {
+  if (fused && h % group == 0) {
+    // One query head of the group writes the new K/V row.
     const int pos = t - 1;
     const int64_t slot = (int64_t)pt[pos / S] * a.page_bytes + head_off + (int64_t)(pos % S) * row_bytes;
     for (int d = lane; d < D; d += 64) {
-      reinterpret_cast<T*>(a.k_layer + slot)[d] = static_cast<const T*>(a.k_new)[qrow + d];
-      reinterpret_cast<T*>(a.v_layer + slot)[d] = static_cast<const T*>(a.v_new)[qrow + d];
+      reinterpret_cast<T*>(a.k_layer + slot)[d] = static_cast<const T*>(a.k_new)[kvrow + d];
+      reinterpret_cast<T*>(a.v_layer + slot)[d] = static_cast<const T*>(a.v_new)[kvrow + d];
     }
   }
   __syncthreads();
@@ -536,7 +581,7 @@ __global__ __launch_bounds__(64) void attend_generic_kernel(AttnArgs a) {
     float s = -INFINITY;
     if (valid) {
       const bool is_new = fused && row == t - 1;
-      const void* kp = is_new ? static_cast<const void*>(static_cast<const T*>(a.k_new) + qrow)
+      const void* kp = is_new ? static_cast<const void*>(static_cast<const T*>(a.k_new) + kvrow)
                               : row_ptr(a.k_layer, row);
       float dot = 0.f;
       for (int d = 0; d < D; ++d) dot = fmaf(qs[d], KV::load1(kp, d), dot);
@@ -555,7 +600,7 @@ __global__ __launch_bounds__(64) void attend_generic_kernel(AttnArgs a) {
     for (int j = 0; j < nrows; ++j) {
       const int rj = row0 + j;
       const void* vp = (fused && rj == t - 1)
-                           ? static_cast<const void*>(static_cast<const T*>(a.v_new) + qrow)
+                           ? static_cast<const void*>(static_cast<const T*>(a.v_new) + kvrow)
                            : row_ptr(a.v_layer, rj);
       const float pj = ps[j];
 #pragma unroll
@@ -568,7 +613,7 @@ __global__ __launch_bounds__(64) void attend_generic_kernel(AttnArgs a) {
   }
 
   // This lane holds columns lane, lane + 64, ...
-  finish_chunk<MAXV, 64>(a, it, rq, h, lane, true, lane, m, l, acc);
+  finish_chunk<MAXV, 64, MAXV>(a, it, rq, h, lane, true, lane, m, l, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -577,11 +622,11 @@ __global__ __launch_bounds__(64) void attend_generic_kernel(AttnArgs a) {
 __global__ __launch_bounds__(64) void merge_kernel(AttnArgs a) {
   const int req = a.merge_reqs[blockIdx.x];
   const ReqEntry rq = a.reqs[req];
-  merge_wave<false>(a, req, rq, blockIdx.y, threadIdx.x);
+  merge_wave<16, false>(a, req, rq, blockIdx.y, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
-// Append: row t-1 of request r, head h <- k[r][h][:], v[r][h][:] (bit copy).
+// Append: row t-1 of request r, K/V head h <- k[r][h][:], v[r][h][:] (bit copy).
 template <typename W>
 __global__ __launch_bounds__(64) void kv_append_kernel(AttnArgs a) {
   const int r = blockIdx.x;
@@ -593,7 +638,7 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AttnArgs a) {
   const int32_t* pt = a.page_table + (int64_t)rq.pt_row * a.pt_stride;
   const int64_t dst = (int64_t)pt[pos / S] * a.page_bytes + (int64_t)h * a.head_bytes +
                       (int64_t)(pos % S) * D * (int64_t)sizeof(W);
-  const int64_t src = ((int64_t)r * a.num_heads + h) * D;
+  const int64_t src = ((int64_t)r * a.num_kv_heads + h) * D;
   W* kd = reinterpret_cast<W*>(a.k_layer + dst);
   W* vd = reinterpret_cast<W*>(a.v_layer + dst);
   const W* ks = static_cast<const W*>(a.k_new) + src;
@@ -609,15 +654,34 @@ __global__ __launch_bounds__(256) void patch_kernel(int32_t* arena, PatchBatch b
   if (i < b.count) arena[b.offset[i]] = b.value[i];
 }
 
+template <typename T, int D, int WAVES, int HPW, int WPG>
+hipError_t launch_fast_shape(const AttnArgs& a, int num_items, hipStream_t stream) {
+  hipLaunchKernelGGL((attend_fast_kernel<T, D, WAVES, HPW, WPG>), dim3(num_items, a.num_kv_heads),
+                     dim3(64 * WAVES), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Workgroup shape by query heads per K/V head (1, 2, 4, 8, 16).  Up to four
+// heads per wave, every wave of the workgroup carries the whole group, so each
+// K/V block is loaded once and serves all of its query heads; the waves split
+// the chunk's blocks.  Groups of 8 and 16 split over 2 and 4 head groups of
+// four (each block loaded by 2 or 4 waves): more heads per wave would exceed
+// the register file.
 template <typename T, int D>
 hipError_t launch_fast(const AttnArgs& a, int num_items, hipStream_t stream) {
-  if (a.waves == 8)
-    hipLaunchKernelGGL((attend_fast_kernel<T, D, 8>), dim3(num_items, a.num_heads), dim3(512), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL((attend_fast_kernel<T, D, 4>), dim3(num_items, a.num_heads), dim3(256), 0,
-                       stream, a);
-  return hipGetLastError();
+  switch (a.num_heads / a.num_kv_heads) {
+    case 1:
+      return a.waves == 8 ? launch_fast_shape<T, D, 8, 1, 8>(a, num_items, stream)
+                          : launch_fast_shape<T, D, 4, 1, 4>(a, num_items, stream);
+    case 2:
+      return launch_fast_shape<T, D, 4, 2, 4>(a, num_items, stream);
+    case 4:
+      return launch_fast_shape<T, D, 4, 4, 4>(a, num_items, stream);
+    case 8:
+      return launch_fast_shape<T, D, 4, 4, 2>(a, num_items, stream);
+    default:
+      return launch_fast_shape<T, D, 4, 4, 1>(a, num_items, stream);
+  }
 }
 
 template <typename T>
@@ -630,8 +694,9 @@ hipError_t launch_generic(const AttnArgs& a, int num_items, hipStream_t stream) 
 
 }  // namespace
 
-bool fast_path_supported(int dtype, int head_width, int page_size) {
+bool fast_path_supported(int dtype, int head_width, int page_size, int group) {
   if (page_size % kBlockRows != 0) return false;
+  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return false;
   if (dtype == kDtypeF32) return head_width == 64;
   if (dtype == kDtypeBF16) return head_width == 128;
   return false;
@@ -639,7 +704,8 @@ bool fast_path_supported(int dtype, int head_width, int page_size) {
 
 hipError_t launch_attention(const AttnArgs& a, int dtype, int num_items, hipStream_t stream,
                             KernelPath* path_out) {
-  const bool fast = fast_path_supported(dtype, a.head_width, a.page_size);
+  const bool fast = fast_path_supported(dtype, a.head_width, a.page_size,
+                                        a.num_heads / a.num_kv_heads);
   if (path_out) *path_out = fast ? KernelPath::kFast : KernelPath::kGeneric;
   if (fast)
     return dtype == kDtypeF32 ? launch_fast<float, 64>(a, num_items, stream)
@@ -655,10 +721,10 @@ hipError_t launch_merge(const AttnArgs& a, int num_split_reqs, hipStream_t strea
 
 hipError_t launch_kv_append(const AttnArgs& a, int dtype, int num_reqs, hipStream_t stream) {
   if (dtype == kDtypeF32) {
-    hipLaunchKernelGGL(kv_append_kernel<uint32_t>, dim3(num_reqs, a.num_heads), dim3(64), 0,
+    hipLaunchKernelGGL(kv_append_kernel<uint32_t>, dim3(num_reqs, a.num_kv_heads), dim3(64), 0,
                        stream, a);
   } else {
-    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, dim3(num_reqs, a.num_heads), dim3(64), 0,
+    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, dim3(num_reqs, a.num_kv_heads), dim3(64), 0,
                        stream, a);
   }
   return hipGetLastError();

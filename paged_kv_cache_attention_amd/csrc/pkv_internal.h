@@ -35,7 +35,7 @@ struct WorkItem {
 
 struct AttnArgs {
   const void* q;          // [n][H][D] pool dtype
-  const void* k_new;      // [n][H][D] rows to append at t-1 (fused append), or null
+  const void* k_new;      // [n][H_kv][D] rows to append at t-1 (fused append), or null
   const void* v_new;
   float* out;             // [n][H][D]
   char* k_layer;          // K pool of this layer: [P][H][S][D]
@@ -47,13 +47,14 @@ struct AttnArgs {
   float* partials;        // [slots][H][D + 2]: (m, l, acc[D]); m in log2 units
   int32_t* merge_count;   // [n][H] arrival counters of split requests (self-resetting)
   const int32_t* merge_reqs;  // requests with nsplit > 1 (separate merge kernel)
-  int32_t num_heads;
+  int32_t num_heads;      // query heads H
+  int32_t num_kv_heads;   // K/V heads; H is a multiple of it
   int32_t page_size;
   int32_t head_width;
   int32_t fuse_append;    // 1: write k_new/v_new at row t-1 and attend with them
   int32_t merge_mode;     // MergeMode
   int32_t waves;          // waves per workgroup of the fast path (4 or 8)
-  int64_t page_bytes;     // H * S * D * elt
+  int64_t page_bytes;     // H_kv * S * D * elt
   int64_t head_bytes;     // S * D * elt
   float scale_log2e;      // log2(e) / sqrt(D)
 };
@@ -85,6 +86,6 @@ hipError_t launch_attention(const AttnArgs& a, int dtype, int num_items, hipStre
 hipError_t launch_merge(const AttnArgs& a, int num_split_reqs, hipStream_t stream);
 hipError_t launch_kv_append(const AttnArgs& a, int dtype, int num_reqs, hipStream_t stream);
 hipError_t launch_patches(int32_t* arena, const PatchBatch& b, hipStream_t stream);
-bool fast_path_supported(int dtype, int head_width, int page_size);
+bool fast_path_supported(int dtype, int head_width, int page_size, int group);
 
 }  // namespace pkv

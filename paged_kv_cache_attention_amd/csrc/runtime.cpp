@@ -223,7 +223,13 @@ struct SplitChoice {
 };
 
 SplitChoice choose_split(const pkv_pool* p, int64_t total_blocks) {
-  const int64_t H = p->desc.num_heads;
+  // Workgroups per chunk: one per K/V head on the fast path, one per query
+  // head on the generic path.
+  const int64_t H = pkv::fast_path_supported(p->desc.kv_dtype, p->desc.head_width,
+                                             p->desc.page_size,
+                                             p->desc.num_heads / p->desc.num_kv_heads)
+                        ? p->desc.num_kv_heads
+                        : p->desc.num_heads;
   const int32_t waves = p->waves_option ? p->waves_option : 4;
   if (p->desc.split_blocks > 0) return {p->desc.split_blocks, waves};
   if (p->desc.split_blocks < 0) return {std::numeric_limits<int32_t>::max(), waves};
@@ -412,6 +418,7 @@ AttnArgs make_args(const pkv_plan* pl, int32_t layer, const int32_t* page_table,
   a.merge_mode = p->merge_mode;
   a.waves = pl->waves;
   a.num_heads = p->desc.num_heads;
+  a.num_kv_heads = p->desc.num_kv_heads;
   a.page_size = p->desc.page_size;
   a.head_width = p->desc.head_width;
   a.fuse_append = fuse ? 1 : 0;
@@ -446,18 +453,19 @@ hipEvent_t take_event(pkv_pool* p) {
 // rows (read from the inputs and written to the pool) and the context.
 uint64_t launch_bytes(const pkv_plan* pl, bool fuse) {
   const pkv_pool* p = pl->pool;
-  const uint64_t row = (uint64_t)p->desc.num_heads * p->desc.head_width;  // per request
+  const uint64_t qrow = (uint64_t)p->desc.num_heads * p->desc.head_width;      // per request
+  const uint64_t kvrow = (uint64_t)p->desc.num_kv_heads * p->desc.head_width;  // per request
   const uint64_t kv_rows = pl->rows_attended - (fuse ? (uint64_t)pl->n : 0);
-  uint64_t b = kv_rows * row * 2 * p->elt;          // K and V rows from the pool
-  b += (uint64_t)pl->n * row * (p->elt + 4);        // q in, context out
-  if (fuse) b += (uint64_t)pl->n * row * 2 * p->elt * 2;  // new K/V rows in and out
+  uint64_t b = kv_rows * kvrow * 2 * p->elt;         // K and V rows from the pool
+  b += (uint64_t)pl->n * qrow * (p->elt + 4);        // q in, context out
+  if (fuse) b += (uint64_t)pl->n * kvrow * 2 * p->elt * 2;  // new K/V rows in and out
   return b;
 }
 
 pkv_status run_attention(pkv_plan* pl, int32_t layer, const int32_t* page_table, const void* q,
                          const void* k, const void* v, float* out, bool fuse, hipStream_t stream) {
   pkv_pool* p = pl->pool;
-  p->counters.kv_bytes_read += pl->rows_attended * (uint64_t)p->desc.num_heads * 2ull *
+  p->counters.kv_bytes_read += pl->rows_attended * (uint64_t)p->desc.num_kv_heads * 2ull *
                                (uint64_t)p->desc.head_width * p->elt;
   if (p->host_only) return PKV_OK;
   AttnArgs a = make_args(pl, layer, page_table, q, k, v, out, fuse);
@@ -560,8 +568,13 @@ pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out) {
   if (!desc || !out) return fail(PKV_ERR_INVALID_ARGUMENT, "null desc or out");
   pkv_pool_desc d = *desc;
   if (d.num_layers < 1 || d.num_heads < 1 || d.head_width < 1 || d.page_size < 1 ||
-      d.max_context < 1 || d.num_pages < 0 || d.max_caches < 0)
+      d.max_context < 1 || d.num_pages < 0 || d.max_caches < 0 || d.num_kv_heads < 0)
     return fail(PKV_ERR_INVALID_ARGUMENT, "sizes must be positive");
+  if (d.num_kv_heads == 0) d.num_kv_heads = d.num_heads;
+  if (d.num_heads % d.num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "num_heads %d is not a multiple of num_kv_heads %d",
+                d.num_heads, d.num_kv_heads);
+  if (d.reserved != 0) return fail(PKV_ERR_INVALID_ARGUMENT, "reserved field must be 0");
   if (d.head_width > 1024) return fail(PKV_ERR_INVALID_ARGUMENT, "head_width %d > 1024", d.head_width);
   if (d.kv_dtype != PKV_DTYPE_F32 && d.kv_dtype != PKV_DTYPE_BF16)
     return fail(PKV_ERR_INVALID_ARGUMENT, "unknown kv_dtype %d", d.kv_dtype);
@@ -576,7 +589,7 @@ pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out) {
     return fail(PKV_ERR_INVALID_ARGUMENT, "max_caches * pages per context overflows");
   const size_t elt = elt_bytes(d.kv_dtype);
   const double layer_bytes =
-      (double)d.num_pages * d.num_heads * d.page_size * d.head_width * (double)elt;
+      (double)d.num_pages * d.num_kv_heads * d.page_size * d.head_width * (double)elt;
   if (layer_bytes * d.num_layers > 9.0e18)
     return fail(PKV_ERR_INVALID_ARGUMENT, "pool larger than 2^63 bytes");
   pkv_pool* p = new (std::nothrow) pkv_pool();
@@ -586,7 +599,7 @@ pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out) {
     p->host_only = (d.flags & PKV_POOL_HOST_ONLY) != 0;
     p->elt = elt;
     p->head_bytes = (int64_t)d.page_size * d.head_width * (int64_t)elt;
-    p->page_bytes = p->head_bytes * d.num_heads;
+    p->page_bytes = p->head_bytes * d.num_kv_heads;
     p->layer_bytes = p->page_bytes * d.num_pages;
     p->arena_stride = (int32_t)pages_per_cache;
     p->free_stack.resize(d.num_pages);

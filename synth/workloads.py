@@ -40,8 +40,13 @@ class Workload:
     page_tables: np.ndarray = field(default=None)  # int32 [n, pt_stride], -1 = unused
     abort_rate: float = 0.0
     description: str = ""
+    kv_heads: int = 0            # K/V heads per layer; 0 = one per query head
 
     # ---- geometry -------------------------------------------------------
+    @property
+    def hkv(self) -> int:
+        return self.kv_heads or self.heads
+
     @property
     def elt(self) -> int:
         return ELT_BYTES[self.dtype]
@@ -52,12 +57,16 @@ class Workload:
 
     @property
     def layer_elems(self) -> int:
-        """Elements of one layer's K (or V) pool: P*H*S*D."""
-        return self.num_pages * self.heads * self.page_size * self.head_width
+        """Elements of one layer's K (or V) pool: P*H_kv*S*D."""
+        return self.num_pages * self.hkv * self.page_size * self.head_width
 
     @property
     def row_elems(self) -> int:
         return self.n * self.heads * self.head_width
+
+    @property
+    def kv_row_elems(self) -> int:
+        return self.n * self.hkv * self.head_width
 
     # ---- streams --------------------------------------------------------
     def kpool_key(self, layer: int) -> int:
@@ -81,24 +90,26 @@ class Workload:
             self.n, self.heads, self.head_width)
 
     def k_new(self, layer: int, step: int = 0) -> np.ndarray:
-        return normals(self.k_key(layer, step), 0, self.row_elems, self.dtype).reshape(
-            self.n, self.heads, self.head_width)
+        """New key rows ``[n, H_kv, D]``."""
+        return normals(self.k_key(layer, step), 0, self.kv_row_elems, self.dtype).reshape(
+            self.n, self.hkv, self.head_width)
 
     def v_new(self, layer: int, step: int = 0) -> np.ndarray:
-        return normals(self.v_key(layer, step), 0, self.row_elems, self.dtype).reshape(
-            self.n, self.heads, self.head_width)
+        return normals(self.v_key(layer, step), 0, self.kv_row_elems, self.dtype).reshape(
+            self.n, self.hkv, self.head_width)
 
     def pool_page(self, which: str, layer: int, page: int) -> np.ndarray:
-        """Generator content of one physical page ``[H, S, D]`` of one layer."""
-        per_page = self.heads * self.page_size * self.head_width
+        """Generator content of one physical page ``[H_kv, S, D]`` of one layer."""
+        per_page = self.hkv * self.page_size * self.head_width
         key = self.kpool_key(layer) if which == "k" else self.vpool_key(layer)
         vals = normals(key, page * per_page, per_page, self.dtype)
-        return vals.reshape(self.heads, self.page_size, self.head_width)
+        return vals.reshape(self.hkv, self.page_size, self.head_width)
 
     # ---- accounting -----------------------------------------------------
     def kv_bytes_per_layer(self) -> int:
-        """Algorithmic K/V bytes one layer's attention must read: sum_r t_r*H*2*D*elt."""
-        return int(self.lengths.sum()) * self.heads * 2 * self.head_width * self.elt
+        """Algorithmic K/V bytes one layer's attention must read:
+        sum_r t_r*H_kv*2*D*elt (a K/V head shared by a group is read once)."""
+        return int(self.lengths.sum()) * self.hkv * 2 * self.head_width * self.elt
 
     def kv_bytes(self) -> int:
         return self.kv_bytes_per_layer() * self.layers
@@ -209,9 +220,22 @@ def fullstep128_bf16(extra_steps: int = 64) -> Workload:
     return w
 
 
+def batch256_gqa8_bf16() -> Workload:
+    """The 256-request bf16 batch with grouped K/V heads: H=32 query heads
+    sharing H_kv=8 K/V heads (groups of 4), D=128, 16-token pages, lengths
+    U[512,4096] from the same stream as the multi-head batch."""
+    seed = 3
+    lengths = uniform_ints(stream_key(seed, TAG_LENGTHS), 256, 512, 4096)
+    P = int(pages_needed(lengths, 16).sum()) + 256
+    w = Workload("batch256_gqa8_bf16", seed, 256, 1, 32, 128, 16, P, "bf16", lengths,
+                 appends=False, description=batch256_gqa8_bf16.__doc__, kv_heads=8)
+    return _finish(w)
+
+
 WORKLOADS = {
     "batch32_fp32_l12": batch32_fp32,
     "batch256_bf16": batch256_bf16,
+    "batch256_gqa8_bf16": batch256_gqa8_bf16,
     "skewed64_bf16": skewed64_bf16,
     "fullstep128_bf16_l32": fullstep128_bf16,
 }

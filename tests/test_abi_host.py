@@ -70,7 +70,9 @@ def test_desc_defaults():
 @pytest.mark.parametrize("field,value", [("num_layers", 0), ("num_heads", -1), ("head_width", 0),
                                          ("head_width", 1025), ("page_size", 0),
                                          ("max_context", 0), ("kv_dtype", 7), ("flags", 2),
-                                         ("k_storage", None), ("v_storage", FAKE + 4)])
+                                         ("k_storage", None), ("v_storage", FAKE + 4),
+                                         ("num_kv_heads", -1), ("num_kv_heads", 2),
+                                         ("reserved", 1)])
 def test_pool_create_rejects(field, value):
     d = pkv.pkv_pool_desc_init()
     d.num_layers, d.num_heads, d.head_width, d.max_context = 1, 1, 8, 64
@@ -80,6 +82,24 @@ def test_pool_create_rejects(field, value):
     with pytest.raises(pkv.PkvError) as e:
         pkv.pkv_pool_create(d)
     assert e.value.status == pkv.PKV_ERR_INVALID_ARGUMENT
+
+
+def test_grouped_kv_heads_desc():
+    d = pkv.pkv_pool_desc_init()
+    d.num_layers, d.num_heads, d.head_width, d.max_context = 1, 6, 8, 64
+    d.flags = pkv.PKV_POOL_HOST_ONLY
+    d.k_storage = d.v_storage = FAKE
+    p = pkv.pkv_pool_create(d)
+    assert pkv.pkv_pool_get_desc(p).num_kv_heads == 6   # 0 means one per query head
+    pkv.pkv_pool_destroy(p)
+    for hkv, ok in ((1, True), (2, True), (3, True), (4, False), (5, False), (6, True), (12, False)):
+        d.num_kv_heads = hkv
+        if ok:
+            p = pkv.pkv_pool_create(d)
+            assert pkv.pkv_pool_get_desc(p).num_kv_heads == hkv
+            pkv.pkv_pool_destroy(p)
+        else:
+            assert status_of(pkv.pkv_pool_create, d) == Status.INVALID_ARGUMENT
 
 
 def test_free_list_is_seeded_permutation_and_raw_lease():

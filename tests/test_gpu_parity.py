@@ -29,16 +29,17 @@ def _pool(w, kp, vp, split=0, seed=0, max_caches=0, max_context=None, merge=0):
     d.split_blocks = split
     d.k_storage, d.v_storage = kp.data_ptr(), vp.data_ptr()
     d.free_list_seed = seed
+    d.num_kv_heads = w.kv_heads
     pool = pkv.pkv_pool_create(d)
     pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_MERGE_MODE, merge)
     return pool
 
 
-def _small(name, dtype, D, S, lengths, heads=3, layers=2, seed=17, extra_pages=5):
+def _small(name, dtype, D, S, lengths, heads=3, layers=2, seed=17, extra_pages=5, kv_heads=0):
     lengths = np.asarray(lengths, dtype=np.int64)
     P = int(W.pages_needed(lengths, S).sum()) + extra_pages
     w = W.Workload(name, seed, len(lengths), layers, heads, D, S, P, dtype, lengths,
-                   appends=True)
+                   appends=True, kv_heads=kv_heads)
     return W._finish(w)
 
 
@@ -49,7 +50,8 @@ def _oracle_decode(w, layer, r, q_host, appended=None):
     t = int(w.lengths[r])
     pt = w.page_tables[r]
     if appended is None:
-        return oracle.paged_decode_attention(q_host[r], kp, vp, pt, t, w.page_size)
+        return oracle.paged_decode_attention(q_host[r], kp, vp, pt, t, w.page_size,
+                                             num_kv_heads=w.hkv)
     k_new, v_new = appended
     return oracle.append_and_attend(q_host[r], k_new[r], v_new[r], kp, vp, pt, t - 1, w.page_size)
 
@@ -240,6 +242,122 @@ def test_append_and_attend_small(dtype, D, S, merge):
     pkv.pkv_plan_destroy(plan)
     pkv.pkv_pool_destroy(pool)
     pkv.pkv_pool_destroy(pool2)
+
+
+# ------------------------------------------------- grouped K/V heads --
+GQA_CASES = [
+    # dtype, D, S, H, H_kv: the fast kernel for groups of 2, 4, 8 and 16 ...
+    ("bf16", 128, 16, 8, 4), ("bf16", 128, 16, 8, 2), ("bf16", 128, 32, 16, 2),
+    ("bf16", 128, 16, 16, 1), ("f32", 64, 16, 4, 2), ("f32", 64, 16, 8, 1),
+    ("f32", 64, 16, 16, 2),
+    # ... and the generic kernel: a group of 3, a narrow head, a ragged page
+    ("f32", 64, 16, 6, 2), ("f32", 40, 16, 4, 1), ("bf16", 128, 7, 8, 2),
+]
+
+
+@pytest.mark.parametrize("dtype,D,S,H,Hkv", GQA_CASES)
+@pytest.mark.parametrize("split,merge", [(0, 2), (2, 0), (2, 2), (-1, 2)])
+def test_grouped_kv_heads(dtype, D, S, H, Hkv, split, merge):
+    w = _small(f"gqa_{dtype}_{D}_{S}_{H}_{Hkv}", dtype, D, S, LENGTHS, heads=H, kv_heads=Hkv,
+               seed=31)
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp, split=split, merge=merge)
+    plan = pkv.pkv_plan_create(pool)
+    pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
+    pt = _pt_device(w)
+    # layer 0: attention over the generator's rows
+    qh = w.q(0)
+    out = torch.empty((w.n, H, D), device="cuda")
+    pkv.pkv_plan_decode_attention(plan, 0, rows_to_device(qh, dtype), pt, out)
+    torch.cuda.synchronize()
+    for r in range(w.n):
+        assert max_err(out[r], _oracle_decode(w, 0, r, qh)) <= TOL[dtype], (r, int(w.lengths[r]))
+    # layer 1: fused append of the shared K/V rows, then attention
+    layer = 1
+    qh, kh, vh = w.q(layer), w.k_new(layer), w.v_new(layer)
+    assert kh.shape == (w.n, Hkv, D)
+    q, k, v = (rows_to_device(x, dtype) for x in (qh, kh, vh))
+    out = torch.empty((w.n, H, D), device="cuda")
+    pkv.pkv_plan_append_and_attend(plan, layer, pt, q, k, v, out)
+    torch.cuda.synchronize()
+    for r in range(w.n):
+        t = int(w.lengths[r])
+        page, slot = w.page_tables[r][(t - 1) // S], (t - 1) % S
+        assert np.array_equal(to_bits(kp[layer, page, :, slot, :], dtype), kh[r])
+        assert np.array_equal(to_bits(vp[layer, page, :, slot, :], dtype), vh[r])
+        ref = _oracle_decode(w, layer, r, qh, appended=(kh, vh))
+        assert max_err(out[r], ref) <= TOL[dtype], (r, t)
+    # the unfused pair gives bit-identical contexts and pages
+    kp2, vp2 = device_pool(w, layers=[layer])
+    pool2 = _pool(w, kp2, vp2, split=split, merge=merge)
+    pkv.pkv_kv_append(pool2, layer, pt, w.pt_stride, (w.lengths - 1).tolist(), k, v)
+    out2 = torch.empty_like(out)
+    pkv.pkv_decode_attention(pool2, layer, q, pt, w.pt_stride, w.lengths.tolist(), out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    assert torch.equal(kp[layer], kp2[layer]) and torch.equal(vp[layer], vp2[layer])
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(pool)
+    pkv.pkv_pool_destroy(pool2)
+
+
+@pytest.mark.parametrize("dtype,D,H,Hkv", [("bf16", 128, 8, 2), ("f32", 64, 4, 1),
+                                           ("f32", 40, 6, 3)])
+def test_grouped_kv_heads_transactional(dtype, D, H, Hkv):
+    """begin / batched append_and_attend / abort / commit on caches whose
+    pages hold H_kv heads; the aborted request retries with new rows."""
+    lengths = np.array([1, 16, 17, 250, 600], dtype=np.int64)
+    w = _small(f"gqa_txn_{dtype}", dtype, D, 16, lengths, heads=H, kv_heads=Hkv, layers=3,
+               seed=37, extra_pages=20)
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp, seed=9, max_caches=w.n, max_context=1024, merge=2)
+    caches = [pkv.pkv_cache_create(pool, 1024) for _ in range(w.n)]
+    prefix = w.lengths - 1
+    for c, n in zip(caches, prefix.tolist()):
+        pkv.pkv_cache_grow(c, n)
+    for c in caches:
+        pkv.pkv_begin_token(c)
+    tables = [pkv.pkv_cache_page_table(c) for c in caches]
+    aborted, abort_layer = 3, 1
+    live = list(range(w.n))
+    outs = {}
+    for layer in range(w.layers):
+        if layer == abort_layer:
+            pkv.pkv_abort_token(caches[aborted])
+            live.remove(aborted)
+        qa, ka, va = w.q(layer), w.k_new(layer), w.v_new(layer)
+        q, k, v = (rows_to_device(x[live], dtype) for x in (qa, ka, va))
+        out = torch.empty((len(live), H, D), device="cuda")
+        pkv.pkv_append_and_attend_batched([caches[r] for r in live], layer, q, k, v, out)
+        outs[layer] = (list(live), out)
+    torch.cuda.synchronize()
+    for r in live:
+        pkv.pkv_commit_token(caches[r])
+    for layer, (lv, out) in outs.items():
+        qa, ka, va = w.q(layer), w.k_new(layer), w.v_new(layer)
+        kpg, vpg = HostPages(w, "k", layer), HostPages(w, "v", layer)
+        for i, r in enumerate(lv):
+            ref = oracle.append_and_attend(qa[r], ka[r], va[r], kpg, vpg, tables[r],
+                                           int(prefix[r]), 16)
+            assert max_err(out[i], ref) <= TOL[dtype], (layer, r)
+    assert pkv.pkv_cache_size(caches[aborted]) == prefix[aborted]
+    # retry the aborted request with the next step's rows
+    assert pkv.pkv_begin_token(caches[aborted]) == prefix[aborted]
+    for layer in range(w.layers):
+        qa, ka, va = w.q(layer, 1), w.k_new(layer, 1), w.v_new(layer, 1)
+        q, k, v = (rows_to_device(x[[aborted]], dtype) for x in (qa, ka, va))
+        out = torch.empty((1, H, D), device="cuda")
+        pkv.pkv_append_and_attend_batched([caches[aborted]], layer, q, k, v, out)
+        torch.cuda.synchronize()
+        ref = oracle.append_and_attend(qa[aborted], ka[aborted], va[aborted],
+                                       HostPages(w, "k", layer), HostPages(w, "v", layer),
+                                       pkv.pkv_cache_page_table(caches[aborted]),
+                                       int(prefix[aborted]), 16)
+        assert max_err(out[0], ref) <= TOL[dtype], layer
+    pkv.pkv_commit_token(caches[aborted])
+    for c in caches:
+        pkv.pkv_cache_destroy(c)
+    pkv.pkv_pool_destroy(pool)
 
 
 @pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128), ("f32", 24)])
@@ -464,7 +582,7 @@ def test_plan_decode_replays_from_a_hip_graph(merge):
     pkv.pkv_pool_destroy(pool)
 
 
-@pytest.mark.parametrize("maker", [W.batch256_bf16, W.skewed64_bf16])
+@pytest.mark.parametrize("maker", [W.batch256_bf16, W.skewed64_bf16, W.batch256_gqa8_bf16])
 @pytest.mark.parametrize("merge", MERGES)
 def test_bf16_single_layer_full(maker, merge):
     w = maker()

@@ -241,3 +241,34 @@ def test_transaction_model_abort_and_rejections():
         assert c.commit() == Status.OK
     assert pool.leased == 2 and c.begin() == Status.OUT_OF_PAGES and c.length == 8
     assert c.reset() == Status.OK and pool.leased == 0 and c.length == 0
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 1), (8, 2), (8, 4), (6, 6)])
+def test_grouped_kv_heads_match_library_gqa(H, Hkv):
+    # torch's SDPA with enable_gqa (not used by the oracle) shares K/V head
+    # h // (H / Hkv) among consecutive query heads.
+    D, t, S = 16, 45, 16
+    npg = -(-t // S)
+    q = RNG.standard_normal((H, D))
+    K = RNG.standard_normal((Hkv, t, D))
+    V = RNG.standard_normal((Hkv, t, D))
+    pt = RNG.permutation(npg + 3)[:npg]
+    kp, vp = _scatter(K, S, pt, npg + 3), _scatter(V, S, pt, npg + 3)
+    got = oracle.paged_decode_attention(q, kp, vp, pt, t, S, num_kv_heads=Hkv)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, :, None, :], torch.from_numpy(K)[None], torch.from_numpy(V)[None],
+        enable_gqa=True)[0, :, 0, :].numpy()
+    assert np.max(np.abs(got - ref)) < 1e-12
+    # the same result as multi-head attention over K/V heads repeated per group
+    rep = np.repeat(np.arange(Hkv), H // Hkv)
+    full = oracle.paged_decode_attention(q, _scatter(K[rep], S, pt, npg + 3),
+                                         _scatter(V[rep], S, pt, npg + 3), pt, t, S)
+    assert np.array_equal(got, full)
+    # append-then-attend with shared new rows equals writing them then attending
+    kn, vn = RNG.standard_normal((Hkv, D)), RNG.standard_normal((Hkv, D))
+    got_a = oracle.append_and_attend(q, kn, vn, kp, vp, pt, t - 1, S)
+    kp2, vp2 = kp.copy(), vp.copy()
+    kp2[pt[(t - 1) // S], :, (t - 1) % S, :] = kn
+    vp2[pt[(t - 1) // S], :, (t - 1) % S, :] = vn
+    assert np.array_equal(got_a, oracle.paged_decode_attention(q, kp2, vp2, pt, t, S,
+                                                               num_kv_heads=Hkv))
