@@ -225,20 +225,35 @@ pkv_status pkv_cache_grow(pkv_cache* cache, int32_t n_tokens);
  * Errors: BAD_STATE (already pending), CAPACITY_EXHAUSTED, OUT_OF_PAGES. */
 pkv_status pkv_begin_token(pkv_cache* cache, int32_t* position);
 
-/* One layer of the pending token: writes k and v ([1,H_kv,1,d_h], pool
- * dtype, device) into the pool at the pending position, then attends with q
- * ([1,H,1,d_h]) over the length+1 rows, writing out ([1,H,1,d_h] float32).
+/* Reserves a chunk of count >= 1 positions length..length+count-1 as one
+ * transaction (a batched prefill chunk) and leases the pages they need;
+ * pkv_begin_token is count = 1.  The layer calls then take count rows, and
+ * row i of the chunk attends causally to rows 0..length+i -- what count
+ * token-at-a-time steps compute.  Commit makes all count positions visible;
+ * abort drops all of them and returns the pages this begin leased.
+ * ("Incremental Serving", Paged KV-cache layout: a later batched prefill
+ * writes the same paged cache that decode attention reads.)
+ * *position receives length.  Errors: INVALID_ARGUMENT (count < 1),
+ * BAD_STATE (already pending), CAPACITY_EXHAUSTED (length + count over the
+ * capacity), OUT_OF_PAGES. */
+pkv_status pkv_begin_tokens(pkv_cache* cache, int32_t count, int32_t* position);
+
+/* One layer of the pending token (or chunk of count tokens): writes k and v
+ * ([count,H_kv,d_h], pool dtype, device) into the pool at the pending
+ * positions, then attends with q ([count,H,d_h]), row i over rows
+ * 0..length+i, writing out ([count,H,d_h] float32).  For one token these are
+ * the [1,H,1,d_h] tensors of "Incremental Serving", Request flow.
  * Errors: BAD_STATE (no pending token, layer already appended),
  * INVALID_ARGUMENT (layer out of range, null pointer), DEVICE. */
 pkv_status pkv_append_and_attend(pkv_cache* cache, int32_t layer, const void* q,
                                  const void* k, const void* v, float* out, void* stream);
 
-/* Makes the pending position visible.  Errors: BAD_STATE (nothing pending,
- * or some layer not appended; the caller may then abort). */
+/* Makes the pending position(s) visible.  Errors: BAD_STATE (nothing
+ * pending, or some layer not appended; the caller may then abort). */
 pkv_status pkv_commit_token(pkv_cache* cache);
 
-/* Drops the pending token: length unchanged, a page leased by its begin
- * returned.  Errors: BAD_STATE (nothing pending). */
+/* Drops the pending token or chunk: length unchanged, the pages leased by
+ * its begin returned.  Errors: BAD_STATE (nothing pending). */
 pkv_status pkv_abort_token(pkv_cache* cache);
 
 /* begin_token on n caches of one pool, all or none: on any error no cache
@@ -248,13 +263,20 @@ pkv_status pkv_abort_token(pkv_cache* cache);
  * free; INVALID_ARGUMENT for a repeated cache or mixed pools. */
 pkv_status pkv_begin_token_batched(pkv_cache* const* caches, int32_t n, int32_t* positions);
 
+/* begin_tokens on n caches, counts[i] positions for caches[i] (counts may be
+ * null: one each), all or none.  Errors: as pkv_begin_tokens, and
+ * OUT_OF_PAGES when the begins together need more pages than are free. */
+pkv_status pkv_begin_tokens_batched(pkv_cache* const* caches, int32_t n, const int32_t* counts,
+                                    int32_t* positions);
+
 /* commit_token on n caches, all or none.  Errors: as pkv_commit_token. */
 pkv_status pkv_commit_token_batched(pkv_cache* const* caches, int32_t n);
 
-/* The same layer step for n pending caches of one pool in one launch:
- * q is [n,H,d_h], k and v are [n,H_kv,d_h] (pool dtype), out is [n,H,d_h]
- * float32, row i belonging to caches[i].  All caches are validated before
- * any work is enqueued.  Errors: as pkv_append_and_attend, per cache; INVALID_ARGUMENT
+/* The same layer step for n pending caches of one pool in one launch set:
+ * q is [T,H,d_h], k and v are [T,H_kv,d_h] (pool dtype), out is [T,H,d_h]
+ * float32, where T sums the caches' pending counts (T = n for single
+ * tokens) and the rows of caches[i] follow those of caches[0..i).  All
+ * caches are validated before any work is enqueued.  Errors: as pkv_append_and_attend, per cache; INVALID_ARGUMENT
  * for a repeated cache or caches of different pools. */
 pkv_status pkv_append_and_attend_batched(pkv_cache* const* caches, int32_t n, int32_t layer,
                                          const void* q, const void* k, const void* v,
@@ -299,6 +321,21 @@ pkv_status pkv_plan_append_and_attend(pkv_plan* plan, int32_t layer,
 pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, int32_t n, const void* q,
                                 const int32_t* page_table, int32_t pt_stride,
                                 const int32_t* seq_lens, float* out, void* stream);
+
+/* Batched prefill on caller page tables: request r appends counts[r] >= 1
+ * rows at positions starts[r]..starts[r]+counts[r]-1 (starts[r] >= 0, the
+ * last position below pt_stride * page_size), then each of them attends
+ * causally, row i over rows 0..starts[r]+i (the pages' token-at-a-time
+ * result, computed for the whole chunk; "Incremental Serving", Paged
+ * KV-cache layout names this batched prefill).  Rows are packed request
+ * after request: q [T,H,d_h], k and v [T,H_kv,d_h] (pool dtype), out
+ * [T,H,d_h] float32, T = sum of counts; starts and counts are host arrays.
+ * Rows 0..starts[r]-1 must already be in the pages.  Errors:
+ * INVALID_ARGUMENT (a range outside the table, a null pointer). */
+pkv_status pkv_prefill_attention(pkv_pool* pool, int32_t layer, int32_t n,
+                                 const int32_t* page_table, int32_t pt_stride,
+                                 const int32_t* starts, const int32_t* counts, const void* q,
+                                 const void* k, const void* v, float* out, void* stream);
 
 /* positions: host array of n row indices; row positions[r] of request r is
  * written, so positions[r] < pt_stride * page_size. */

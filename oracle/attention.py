@@ -129,6 +129,33 @@ def append_and_attend(q, k_new, v_new, k_pages, v_pages, page_table, length: int
     return out
 
 
+def prefill_attention(q, k_new, v_new, k_pages, v_pages, page_table, start: int,
+                      page_size: int):
+    """A chunk of n new rows at positions start..start+n-1, each attending
+    causally: row i sees the retained rows 0..start-1 (from the pages) and the
+    chunk's rows 0..i.
+
+    The pages process a prompt one token at a time and name a batched prefill
+    that writes the same paged cache as future work ("Incremental Serving",
+    Paged KV-cache layout); reading: a chunk computes exactly what n
+    token-at-a-time steps would, i.e. row i is the newest-query result at
+    attended length start+i+1.  q: [n, H, D]; k_new, v_new: [n, H_kv, D].
+    Returns the contexts [n, H, D] in float64.
+    """
+    n, H, D = q.shape
+    Hkv = k_new.shape[1]
+    out = np.empty((n, H, D), dtype=np.float64)
+    for h in range(H):
+        kvh = kv_head_of(h, H, Hkv)
+        Kp = kv_to_f64(gather_prefix(k_pages, page_table, start, page_size, kvh)).reshape(-1, D)
+        Vp = kv_to_f64(gather_prefix(v_pages, page_table, start, page_size, kvh)).reshape(-1, D)
+        K = np.concatenate([Kp, kv_to_f64(k_new[:, kvh, :])], axis=0)
+        V = np.concatenate([Vp, kv_to_f64(v_new[:, kvh, :])], axis=0)
+        for i in range(n):
+            out[i, h] = attend(q[i, h], K[:start + i + 1], V[:start + i + 1])
+    return out
+
+
 def causal_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
     """Full causal attention over t rows: row i attends to rows 0..i.
 

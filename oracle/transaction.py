@@ -13,8 +13,10 @@ Sources, by page and section:
   together": every block prepares before any cache commits, so commit requires
   all layers; rejected operations leave the committed state unchanged.
 
-Readings where the pages are silent: abort also returns a page that this
-token's begin leased (so pool and page table equal their state before begin);
+Readings where the pages are silent: abort also returns the pages that this
+transaction's begin leased (so pool and page table equal their state before
+begin); a begin may reserve a chunk of n positions (batched prefill, which the
+pages name as future work), and then commit and abort act on all n at once;
 reset while a token is pending is rejected; destroy always succeeds and
 returns every page, the pending one included; a call with an invalid argument
 is rejected as such before the state is consulted.
@@ -51,28 +53,29 @@ class CacheModel:
         self.capacity = capacity
         self.page_size = page_size
         self.length = 0
-        self.pending = None          # (position, leased_new_page, set of appended layers)
+        self.pending = None          # (position, new pages leased, appended layers, count)
         self.retained_lengths = []   # attended length of every committed token
         self.appends = 0
 
     @property
     def pages_held(self) -> int:
         n = -(-self.length // self.page_size)
-        if self.pending is not None and self.pending[1]:
-            n += 1
+        if self.pending is not None:
+            n += self.pending[1]
         return n
 
-    def begin(self) -> Status:
+    def begin(self, count: int = 1) -> Status:
+        if count < 1:
+            return Status.INVALID_ARGUMENT
         if self.pending is not None:
             return Status.BAD_STATE
-        if self.length >= self.capacity:
+        if self.length + count > self.capacity:
             return Status.CAPACITY_EXHAUSTED
-        needs_page = self.length % self.page_size == 0
-        if needs_page:
-            if self.pool.free == 0:
-                return Status.OUT_OF_PAGES
-            self.pool.leased += 1
-        self.pending = (self.length, needs_page, set())
+        new_pages = -(-(self.length + count) // self.page_size) - (-(-self.length // self.page_size))
+        if new_pages > self.pool.free:
+            return Status.OUT_OF_PAGES
+        self.pool.leased += new_pages
+        self.pending = (self.length, new_pages, set(), count)
         return Status.OK
 
     def append(self, layer: int) -> Status:
@@ -88,17 +91,17 @@ class CacheModel:
     def commit(self) -> Status:
         if self.pending is None or len(self.pending[2]) != self.layers:
             return Status.BAD_STATE
-        self.length += 1
-        self.retained_lengths.append(self.length)
-        self.appends += self.layers
+        for _ in range(self.pending[3]):
+            self.length += 1
+            self.retained_lengths.append(self.length)
+            self.appends += self.layers
         self.pending = None
         return Status.OK
 
     def abort(self) -> Status:
         if self.pending is None:
             return Status.BAD_STATE
-        if self.pending[1]:
-            self.pool.leased -= 1
+        self.pool.leased -= self.pending[1]
         self.pending = None
         return Status.OK
 

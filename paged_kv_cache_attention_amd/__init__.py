@@ -122,6 +122,9 @@ SIGNATURES = {
     "pkv_abort_token": (_I32, [_P]),
     "pkv_append_and_attend_batched": (_I32, [ctypes.POINTER(_P), _I32, _I32, _P, _P, _P, _P, _P]),
     "pkv_begin_token_batched": (_I32, [ctypes.POINTER(_P), _I32, _PI32]),
+    "pkv_begin_tokens": (_I32, [_P, _I32, _PI32]),
+    "pkv_begin_tokens_batched": (_I32, [ctypes.POINTER(_P), _I32, _PI32, _PI32]),
+    "pkv_prefill_attention": (_I32, [_P, _I32, _I32, _P, _I32, _PI32, _PI32, _P, _P, _P, _P, _P]),
     "pkv_commit_token_batched": (_I32, [ctypes.POINTER(_P), _I32]),
     "pkv_plan_create": (_I32, [_P, ctypes.POINTER(_P)]),
     "pkv_plan_destroy": (_I32, [_P]),
@@ -297,6 +300,12 @@ def pkv_begin_token(cache: int) -> int:
     return pos.value
 
 
+def pkv_begin_tokens(cache: int, count: int) -> int:
+    pos = ctypes.c_int32()
+    _check(_lib.pkv_begin_tokens(cache, count, ctypes.byref(pos)), "pkv_begin_tokens")
+    return pos.value
+
+
 def pkv_append_and_attend(cache: int, layer: int, q, k, v, out, stream=None) -> None:
     _check(_lib.pkv_append_and_attend(cache, layer, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                       _stream(stream)), "pkv_append_and_attend")
@@ -325,6 +334,14 @@ def pkv_begin_token_batched(caches) -> list:
     arr, n = _cache_array(caches)
     pos = (ctypes.c_int32 * max(1, n))()
     _check(_lib.pkv_begin_token_batched(arr, n, pos), "pkv_begin_token_batched")
+    return list(pos[:n])
+
+
+def pkv_begin_tokens_batched(caches, counts=None) -> list:
+    arr, n = _cache_array(caches)
+    pos = (ctypes.c_int32 * max(1, n))()
+    cnt = None if counts is None else (ctypes.c_int32 * max(1, n))(*counts)
+    _check(_lib.pkv_begin_tokens_batched(arr, n, cnt, pos), "pkv_begin_tokens_batched")
     return list(pos[:n])
 
 
@@ -391,6 +408,18 @@ def pkv_kv_append(pool: int, layer: int, page_table, pt_stride: int, positions, 
     arr = _i32_array(positions)
     _check(_lib.pkv_kv_append(pool, layer, len(positions), _ptr(page_table), pt_stride, arr,
                               _ptr(k), _ptr(v), _stream(stream)), "pkv_kv_append")
+
+
+def pkv_prefill_attention(pool: int, layer: int, page_table, pt_stride: int, starts, counts, q,
+                          k, v, out, stream=None) -> None:
+    n = len(starts)
+    if len(counts) != n:
+        raise ValueError("starts and counts differ in length")
+    st = (ctypes.c_int32 * max(1, n))(*starts)
+    ct = (ctypes.c_int32 * max(1, n))(*counts)
+    _check(_lib.pkv_prefill_attention(pool, layer, n, _ptr(page_table), pt_stride, st, ct, _ptr(q),
+                                      _ptr(k), _ptr(v), _ptr(out), _stream(stream)),
+           "pkv_prefill_attention")
 
 
 __all__ = [n for n in list(globals()) if n.startswith("pkv_")] + [

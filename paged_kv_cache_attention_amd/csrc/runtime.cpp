@@ -110,8 +110,9 @@ struct pkv_cache {
   int32_t len = 0;
   std::vector<int32_t> pages;
   bool pending = false;
-  int32_t pending_pos = 0;
-  bool pending_new_page = false;
+  int32_t pending_pos = 0;        // first reserved position
+  int32_t pending_count = 0;      // positions reserved by this begin
+  int32_t pending_new_pages = 0;  // pages leased by this begin
   std::vector<uint8_t> appended;
   int32_t appended_count = 0;
 };
@@ -132,8 +133,9 @@ struct pkv_pool {
   int device = -1;
   int32_t* d_arena = nullptr;
   std::vector<std::pair<int32_t, int32_t>> patches;  // (arena offset, page)
-  pkv_plan txn_plan;   // transactional steps
-  pkv_plan call_plan;  // one-call batched forms
+  pkv_plan txn_plan;      // transactional steps
+  pkv_plan call_plan;     // one-call batched forms
+  pkv_plan prefill_plan;  // chunks of several rows per request
   pkv_counters counters{};
   int32_t merge_mode = pkv::kMergeLastArriver;
   int32_t waves_option = 0;
@@ -504,6 +506,44 @@ pkv_status check_layer(const pkv_pool* p, int32_t layer) {
   return PKV_OK;
 }
 
+// A chunk of counts[r] new rows per request r at positions starts[r]...,
+// packed request after request in q, k, v and out: every row is written to
+// the pool, then each attends causally (row i of request r over rows
+// 0..starts[r]+i).  Each new row is run as its own decode query of attended
+// length starts[r]+i+1 on the request's page-table row, after all rows of
+// the chunk are written (a fused append would race with the rows of the
+// same chunk that other workgroups read).
+pkv_status run_prefill(pkv_pool* p, int32_t n, const int32_t* rows, const int32_t* starts,
+                       const int32_t* counts, int32_t pt_stride, int32_t layer,
+                       const int32_t* page_table, const void* q, const void* k, const void* v,
+                       float* out, hipStream_t stream) {
+  const int64_t max_len = (int64_t)pt_stride * p->desc.page_size;
+  int64_t total = 0;
+  for (int32_t r = 0; r < n; ++r) {
+    if (counts[r] < 1 || starts[r] < 0 || (int64_t)starts[r] + counts[r] > max_len)
+      return fail(PKV_ERR_INVALID_ARGUMENT, "request %d: rows [%d, %d + %d) outside [0, %lld)", r,
+                  starts[r], starts[r], counts[r], (long long)max_len);
+    total += counts[r];
+  }
+  if (total > std::numeric_limits<int32_t>::max() / 2)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%lld rows in one prefill call", (long long)total);
+  std::vector<int32_t> vrows((size_t)total), vlens((size_t)total);
+  size_t j = 0;
+  for (int32_t r = 0; r < n; ++r)
+    for (int32_t i = 0; i < counts[r]; ++i, ++j) {
+      vrows[j] = rows[r];
+      vlens[j] = starts[r] + i + 1;
+    }
+  pkv_plan* pl = &p->prefill_plan;
+  pkv_status st = plan_build(pl, (int32_t)total, vrows.data(), vlens.data(), pt_stride, stream);
+  if (st != PKV_OK) return st;
+  if (!p->host_only) {
+    AttnArgs a = make_args(pl, layer, page_table, q, k, v, out, false);
+    PKV_HIP_TRY(pkv::launch_kv_append(a, p->desc.kv_dtype, (int32_t)total, stream));
+  }
+  return run_attention(pl, layer, page_table, q, nullptr, nullptr, out, false, stream);
+}
+
 // Shared body of the single and batched transactional layer step.
 pkv_status txn_step(pkv_cache* const* caches, int32_t n, int32_t layer, const void* q,
                     const void* k, const void* v, float* out, void* stream) {
@@ -516,7 +556,8 @@ pkv_status txn_step(pkv_cache* const* caches, int32_t n, int32_t layer, const vo
   if ((st = check_ptr(q, "q")) != PKV_OK || (st = check_ptr(k, "k")) != PKV_OK ||
       (st = check_ptr(v, "v")) != PKV_OK || (st = check_ptr(out, "out")) != PKV_OK)
     return st;
-  std::vector<int32_t> rows(n), lens(n);
+  std::vector<int32_t> rows(n), lens(n), starts(n), counts(n);
+  bool chunked = false;
   for (int32_t i = 0; i < n; ++i) {
     const pkv_cache* c = caches[i];
     if (c->pool != p) return fail(PKV_ERR_INVALID_ARGUMENT, "caches[%d] belongs to another pool", i);
@@ -525,6 +566,9 @@ pkv_status txn_step(pkv_cache* const* caches, int32_t n, int32_t layer, const vo
       return fail(PKV_ERR_BAD_STATE, "caches[%d] already appended layer %d", i, layer);
     rows[i] = c->slot;
     lens[i] = c->pending_pos + 1;
+    starts[i] = c->pending_pos;
+    counts[i] = c->pending_count;
+    chunked |= c->pending_count > 1;
   }
   if (n > 1) {
     std::vector<int32_t> sorted(rows);
@@ -535,10 +579,17 @@ pkv_status txn_step(pkv_cache* const* caches, int32_t n, int32_t layer, const vo
   if ((st = ensure_device(p)) != PKV_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = flush_patches(p, s)) != PKV_OK) return st;
-  if ((st = plan_build(&p->txn_plan, n, rows.data(), lens.data(), p->arena_stride, s)) != PKV_OK)
-    return st;
-  if ((st = run_attention(&p->txn_plan, layer, p->d_arena, q, k, v, out, true, s)) != PKV_OK)
-    return st;
+  if (chunked) {
+    st = run_prefill(p, n, rows.data(), starts.data(), counts.data(), p->arena_stride, layer,
+                     p->d_arena, q, k, v, out, s);
+    if (st != PKV_OK) return st;
+  } else {
+    if ((st = plan_build(&p->txn_plan, n, rows.data(), lens.data(), p->arena_stride, s)) !=
+        PKV_OK)
+      return st;
+    if ((st = run_attention(&p->txn_plan, layer, p->d_arena, q, k, v, out, true, s)) != PKV_OK)
+      return st;
+  }
   for (int32_t i = 0; i < n; ++i) {
     caches[i]->appended[layer] = 1;
     caches[i]->appended_count += 1;
@@ -617,6 +668,8 @@ pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out) {
     p->txn_plan.internal = true;
     p->call_plan.pool = p;
     p->call_plan.internal = true;
+    p->prefill_plan.pool = p;
+    p->prefill_plan.internal = true;
   } catch (const std::bad_alloc&) {
     delete p;
     return fail(PKV_ERR_ALLOC, "pool metadata");
@@ -632,6 +685,7 @@ pkv_status pkv_pool_destroy(pkv_pool* p) {
                 p->live_caches, p->live_plans, p->raw_leased);
   plan_release(&p->txn_plan);
   plan_release(&p->call_plan);
+  plan_release(&p->prefill_plan);
   for (const auto& t : p->timed) {
     (void)hipEventSynchronize(t.end);
     p->spare.push_back(t.start);
@@ -760,7 +814,7 @@ static void cache_return_pages(pkv_cache* c) {
 pkv_status pkv_cache_destroy(pkv_cache* c) {
   if (!c) return fail(PKV_ERR_INVALID_ARGUMENT, "null cache");
   pkv_pool* p = c->pool;
-  if (c->pending) p->counters.aborted_tokens += 1;
+  if (c->pending) p->counters.aborted_tokens += (uint64_t)c->pending_count;
   cache_return_pages(c);
   p->free_slots.push_back(c->slot);
   p->live_caches -= 1;
@@ -812,26 +866,55 @@ pkv_status pkv_cache_grow(pkv_cache* c, int32_t n_tokens) {
   return ok();
 }
 
-pkv_status pkv_begin_token(pkv_cache* c, int32_t* position) {
-  if (!c) return fail(PKV_ERR_INVALID_ARGUMENT, "null cache");
-  if (c->pending) return fail(PKV_ERR_BAD_STATE, "a token is already pending");
-  if (c->len >= c->max_context)
-    return fail(PKV_ERR_CAPACITY_EXHAUSTED, "cache is at its capacity %d", c->max_context);
+// Pages a begin of `count` positions must lease for cache c.
+static int32_t pages_for(const pkv_cache* c, int32_t count) {
+  const int32_t S = c->pool->desc.page_size;
+  return (int32_t)(((int64_t)c->len + count + S - 1) / S - ((int64_t)c->len + S - 1) / S);
+}
+
+static pkv_status check_begin(const pkv_cache* c, int32_t count, int32_t i) {
+  if (count < 1) return fail(PKV_ERR_INVALID_ARGUMENT, "caches[%d]: count %d < 1", i, count);
+  if (c->pending) return fail(PKV_ERR_BAD_STATE, "caches[%d]: a token is already pending", i);
+  if ((int64_t)c->len + count > c->max_context)
+    return fail(PKV_ERR_CAPACITY_EXHAUSTED, "caches[%d]: length %d + %d exceeds capacity %d", i,
+                c->len, count, c->max_context);
+  return PKV_OK;
+}
+
+// Reserves positions len..len+count-1; the caller has checked the state and
+// that enough pages are free.
+static int32_t begin_unchecked(pkv_cache* c, int32_t count) {
   pkv_pool* p = c->pool;
-  const bool new_page = c->len % p->desc.page_size == 0;
-  if (new_page && p->free_stack.empty()) return fail(PKV_ERR_OUT_OF_PAGES, "no free page");
-  if (new_page) {
+  const int32_t need = pages_for(c, count);
+  for (int32_t i = 0; i < need; ++i) {
     const int32_t page = lease_page(p, kCache);
     record_patch(c, (int32_t)c->pages.size(), page);
     c->pages.push_back(page);
   }
   c->pending = true;
   c->pending_pos = c->len;
-  c->pending_new_page = new_page;
+  c->pending_count = count;
+  c->pending_new_pages = need;
   std::fill(c->appended.begin(), c->appended.end(), 0);
   c->appended_count = 0;
-  if (position) *position = c->pending_pos;
+  return c->pending_pos;
+}
+
+pkv_status pkv_begin_tokens(pkv_cache* c, int32_t count, int32_t* position) {
+  if (!c) return fail(PKV_ERR_INVALID_ARGUMENT, "null cache");
+  pkv_status st = check_begin(c, count, 0);
+  if (st != PKV_OK) return st;
+  const int32_t need = pages_for(c, count);
+  if (need > (int32_t)c->pool->free_stack.size())
+    return fail(PKV_ERR_OUT_OF_PAGES, "%d pages needed, %zu free", need,
+                c->pool->free_stack.size());
+  const int32_t pos = begin_unchecked(c, count);
+  if (position) *position = pos;
   return ok();
+}
+
+pkv_status pkv_begin_token(pkv_cache* c, int32_t* position) {
+  return pkv_begin_tokens(c, 1, position);
 }
 
 static pkv_status check_batch(pkv_cache* const* caches, int32_t n) {
@@ -850,27 +933,29 @@ static pkv_status check_batch(pkv_cache* const* caches, int32_t n) {
   return PKV_OK;
 }
 
-pkv_status pkv_begin_token_batched(pkv_cache* const* caches, int32_t n, int32_t* positions) {
+pkv_status pkv_begin_tokens_batched(pkv_cache* const* caches, int32_t n, const int32_t* counts,
+                                    int32_t* positions) {
   pkv_status st = check_batch(caches, n);
   if (st != PKV_OK) return st;
   pkv_pool* p = caches[0]->pool;
   int64_t pages = 0;
   for (int32_t i = 0; i < n; ++i) {
-    const pkv_cache* c = caches[i];
-    if (c->pending) return fail(PKV_ERR_BAD_STATE, "caches[%d]: a token is already pending", i);
-    if (c->len >= c->max_context)
-      return fail(PKV_ERR_CAPACITY_EXHAUSTED, "caches[%d] is at its capacity %d", i, c->max_context);
-    pages += c->len % p->desc.page_size == 0;
+    const int32_t count = counts ? counts[i] : 1;
+    if ((st = check_begin(caches[i], count, i)) != PKV_OK) return st;
+    pages += pages_for(caches[i], count);
   }
   if (pages > (int64_t)p->free_stack.size())
     return fail(PKV_ERR_OUT_OF_PAGES, "%lld pages needed, %zu free", (long long)pages,
                 p->free_stack.size());
   for (int32_t i = 0; i < n; ++i) {
-    int32_t pos = 0;
-    pkv_begin_token(caches[i], &pos);  // cannot fail after the checks above
+    const int32_t pos = begin_unchecked(caches[i], counts ? counts[i] : 1);
     if (positions) positions[i] = pos;
   }
   return ok();
+}
+
+pkv_status pkv_begin_token_batched(pkv_cache* const* caches, int32_t n, int32_t* positions) {
+  return pkv_begin_tokens_batched(caches, n, nullptr, positions);
 }
 
 pkv_status pkv_commit_token_batched(pkv_cache* const* caches, int32_t n) {
@@ -907,23 +992,25 @@ pkv_status pkv_commit_token(pkv_cache* c) {
   if (c->appended_count != p->desc.num_layers)
     return fail(PKV_ERR_BAD_STATE, "only %d of %d layers appended", c->appended_count,
                 p->desc.num_layers);
-  c->len = c->pending_pos + 1;
+  const uint64_t lanes = (uint64_t)p->desc.num_layers * p->desc.num_heads;
+  for (int32_t i = 0; i < c->pending_count; ++i)
+    p->counters.score_cells += lanes * (uint64_t)(c->pending_pos + i + 1);
+  c->len = c->pending_pos + c->pending_count;
   c->pending = false;
-  p->counters.committed_tokens += 1;
-  p->counters.cache_appends += (uint64_t)p->desc.num_layers;
-  p->counters.score_cells += (uint64_t)p->desc.num_layers * p->desc.num_heads * (uint64_t)c->len;
+  p->counters.committed_tokens += (uint64_t)c->pending_count;
+  p->counters.cache_appends += (uint64_t)p->desc.num_layers * c->pending_count;
   return ok();
 }
 
 pkv_status pkv_abort_token(pkv_cache* c) {
   if (!c) return fail(PKV_ERR_INVALID_ARGUMENT, "null cache");
   if (!c->pending) return fail(PKV_ERR_BAD_STATE, "no pending token");
-  if (c->pending_new_page) {
+  for (int32_t i = 0; i < c->pending_new_pages; ++i) {
     release_page(c->pool, c->pages.back());
     c->pages.pop_back();
   }
   c->pending = false;
-  c->pool->counters.aborted_tokens += 1;
+  c->pool->counters.aborted_tokens += (uint64_t)c->pending_count;
   return ok();
 }
 
@@ -1017,6 +1104,25 @@ pkv_status pkv_decode_attention(pkv_pool* p, int32_t layer, int32_t n, const voi
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = plan_build(&p->call_plan, n, rows.data(), seq_lens, pt_stride, s)) != PKV_OK) return st;
   st = run_attention(&p->call_plan, layer, page_table, q, nullptr, nullptr, out, false, s);
+  return st == PKV_OK ? ok() : st;
+}
+
+pkv_status pkv_prefill_attention(pkv_pool* p, int32_t layer, int32_t n,
+                                 const int32_t* page_table, int32_t pt_stride,
+                                 const int32_t* starts, const int32_t* counts, const void* q,
+                                 const void* k, const void* v, float* out, void* stream) {
+  if (!p || !starts || !counts || n < 1 || pt_stride < 1)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "null pool/starts/counts or non-positive n/pt_stride");
+  pkv_status st = check_layer(p, layer);
+  if (st != PKV_OK) return st;
+  if (!page_table) return fail(PKV_ERR_INVALID_ARGUMENT, "page_table is null");
+  if ((st = check_ptr(q, "q")) != PKV_OK || (st = check_ptr(k, "k")) != PKV_OK ||
+      (st = check_ptr(v, "v")) != PKV_OK || (st = check_ptr(out, "out")) != PKV_OK)
+    return st;
+  std::vector<int32_t> rows(n);
+  for (int32_t r = 0; r < n; ++r) rows[r] = r;
+  st = run_prefill(p, n, rows.data(), starts, counts, pt_stride, layer, page_table, q, k, v, out,
+                   static_cast<hipStream_t>(stream));
   return st == PKV_OK ? ok() : st;
 }
 

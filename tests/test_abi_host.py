@@ -292,12 +292,15 @@ def test_state_machine_matches_oracle_model(seed):
     pool_model = oracle.PoolModel(pages)
     caches = [(pkv.pkv_cache_create(p, ctx), oracle.CacheModel(pool_model, layers, ctx, page))
               for _ in range(3)]
-    ops = ["begin", "append", "commit", "abort", "reset"]
+    ops = ["begin", "begin_chunk", "append", "commit", "abort", "reset"]
     for _ in range(600):
         c, m = rnd.choice(caches)
-        op = rnd.choices(ops, weights=[4, 6, 3, 1, 0.3])[0]
+        op = rnd.choices(ops, weights=[4, 2, 6, 3, 1, 0.3])[0]
         if op == "begin":
             got, want = status_of(pkv.pkv_begin_token, c), m.begin()
+        elif op == "begin_chunk":
+            count = rnd.randrange(-1, 9)
+            got, want = status_of(pkv.pkv_begin_tokens, c, count), m.begin(count)
         elif op == "append":
             layer = rnd.randrange(layers + 1)
             got = status_of(pkv.pkv_append_and_attend, c, layer, FAKE, FAKE, FAKE, FAKE, 0)
@@ -312,6 +315,11 @@ def test_state_machine_matches_oracle_model(seed):
         assert pkv.pkv_cache_size(c) == m.length
         assert len(pkv.pkv_cache_page_table(c)) == m.pages_held
         assert pkv.pkv_pool_get_counters(p).pages_free == pool_model.free
+    cnt = pkv.pkv_pool_get_counters(p)
+    models = [m for _, m in caches]
+    assert cnt.committed_tokens == sum(len(m.retained_lengths) for m in models)
+    assert cnt.cache_appends == sum(m.appends for m in models)
+    assert cnt.score_cells == layers * 2 * sum(sum(m.retained_lengths) for m in models)
     tables = [pkv.pkv_cache_page_table(c) for c, _ in caches]
     flat = [x for t in tables for x in t]
     assert len(flat) == len(set(flat)) and all(0 <= x < pages for x in flat)
@@ -347,4 +355,46 @@ def test_batched_begin_and_commit_all_or_nothing():
     assert [pkv.pkv_cache_size(c) for c in cs] == [4, 2, 2]
     for c in cs:
         pkv.pkv_cache_destroy(c)
+    pkv.pkv_pool_destroy(p)
+
+
+def test_chunk_begin_all_or_nothing_and_abort_returns_pages():
+    p = make_pool(layers=2, page=4, pages=6, ctx=24)
+    a, b = pkv.pkv_cache_create(p, 24), pkv.pkv_cache_create(p, 24)
+    assert pkv.pkv_begin_tokens(a, 9) == 0                         # 3 pages
+    assert len(pkv.pkv_cache_page_table(a)) == 3
+    assert status_of(pkv.pkv_begin_tokens, b, 13) == Status.OUT_OF_PAGES   # needs 4, 3 free
+    assert status_of(pkv.pkv_begin_tokens, b, 25) == Status.CAPACITY_EXHAUSTED
+    assert status_of(pkv.pkv_begin_tokens, b, 0) == Status.INVALID_ARGUMENT
+    assert pkv.pkv_cache_page_table(b) == [] and pkv.pkv_pool_get_counters(p).pages_free == 3
+    pkv.pkv_abort_token(a)
+    assert pkv.pkv_cache_page_table(a) == [] and pkv.pkv_pool_get_counters(p).pages_free == 6
+    # batched: the pair needs 3 + 4 pages of 6 -> nothing begins
+    assert status_of(pkv.pkv_begin_tokens_batched, [a, b], [9, 13]) == Status.OUT_OF_PAGES
+    assert pkv.pkv_begin_tokens_batched([a, b], [9, 3]) == [0, 0]
+    for layer in range(2):
+        pkv.pkv_append_and_attend_batched([a, b], layer, FAKE, FAKE, FAKE, FAKE, stream=0)
+    pkv.pkv_commit_token_batched([a, b])
+    assert (pkv.pkv_cache_size(a), pkv.pkv_cache_size(b)) == (9, 3)
+    cnt = pkv.pkv_pool_get_counters(p)
+    assert cnt.committed_tokens == 12 and cnt.cache_appends == 24
+    assert cnt.score_cells == 2 * 2 * (sum(range(1, 10)) + sum(range(1, 4)))
+    # a single token after a chunk continues at the committed length
+    assert pkv.pkv_begin_token(b) == 3
+    pkv.pkv_abort_token(b)
+    for c in (a, b):
+        pkv.pkv_cache_destroy(c)
+    pkv.pkv_pool_destroy(p)
+
+
+def test_prefill_call_validates_ranges_host_only():
+    p = make_pool(layers=1, page=4, pages=8, ctx=16)
+    pt = FAKE
+    pkv.pkv_prefill_attention(p, 0, pt, 4, [0, 3], [16, 13], FAKE, FAKE, FAKE, FAKE, stream=0)
+    for starts, counts in (([0], [17]), ([15], [2]), ([-1], [2]), ([0], [0]), ([2], [-3])):
+        assert status_of(pkv.pkv_prefill_attention, p, 0, pt, 4, starts, counts, FAKE, FAKE,
+                         FAKE, FAKE, 0) == Status.INVALID_ARGUMENT, (starts, counts)
+    assert status_of(pkv.pkv_prefill_attention, p, 1, pt, 4, [0], [1], FAKE, FAKE, FAKE, FAKE,
+                     0) == Status.INVALID_ARGUMENT   # layer out of range
+    assert pkv.pkv_pool_get_counters(p).kv_bytes_read > 0
     pkv.pkv_pool_destroy(p)

@@ -360,6 +360,137 @@ def test_grouped_kv_heads_transactional(dtype, D, H, Hkv):
     pkv.pkv_pool_destroy(pool)
 
 
+# ------------------------------------------------------- batched prefill --
+def _chunk_rows(w, layer, total, step=0):
+    """q [T,H,D], k and v [T,H_kv,D] for T new rows, from the generator."""
+    out = []
+    for tag, heads in ((synth.TAG_Q, w.heads), (synth.TAG_K, w.hkv), (synth.TAG_V, w.hkv)):
+        key = synth.stream_key(w.seed, tag, layer, 1000 + step)
+        out.append(synth.normals(key, 0, total * heads * w.head_width, w.dtype).reshape(
+            total, heads, w.head_width))
+    return tuple(out)
+
+
+def _check_prefill(w, layer, starts, counts, qh, kh, vh, out, kp, vp, tables=None):
+    S = w.page_size
+    kpg, vpg = HostPages(w, "k", layer), HostPages(w, "v", layer)
+    off = 0
+    for r, (st, n) in enumerate(zip(starts, counts)):
+        pt = w.page_tables[r] if tables is None else tables[r]
+        sl = slice(off, off + n)
+        for i in (0, n // 2, n - 1):
+            pos = st + i
+            page, slot = pt[pos // S], pos % S
+            assert np.array_equal(to_bits(kp[layer, page, :, slot, :], w.dtype), kh[off + i])
+            assert np.array_equal(to_bits(vp[layer, page, :, slot, :], w.dtype), vh[off + i])
+        ref = oracle.prefill_attention(qh[sl], kh[sl], vh[sl], kpg, vpg, pt, st, S)
+        err = np.max(np.abs(out[sl].cpu().numpy().astype(np.float64) - ref))
+        assert err <= TOL[w.dtype], (r, st, n, err)
+        off += n
+
+
+PREFILL_CASES = [
+    # dtype, D, S, H, H_kv
+    ("bf16", 128, 16, 4, 4), ("f32", 64, 16, 3, 3), ("bf16", 128, 16, 8, 2),
+    ("f32", 40, 16, 2, 1), ("bf16", 128, 7, 2, 2),
+]
+PREFILL_CHUNKS = [(0, 1), (0, 37), (5, 20), (16, 16), (100, 70), (1000, 33), (0, 300)]
+
+
+@pytest.mark.parametrize("dtype,D,S,H,Hkv", PREFILL_CASES)
+@pytest.mark.parametrize("merge", MERGES)
+def test_prefill_attention_small(dtype, D, S, H, Hkv, merge):
+    starts = [a for a, _ in PREFILL_CHUNKS]
+    counts = [b for _, b in PREFILL_CHUNKS]
+    w = _small(f"prefill_{dtype}_{D}_{S}_{H}_{Hkv}", dtype, D, S,
+               [a + b for a, b in PREFILL_CHUNKS], heads=H, kv_heads=Hkv, layers=2, seed=41)
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp, merge=merge)
+    layer = 1
+    qh, kh, vh = _chunk_rows(w, layer, sum(counts))
+    q, k, v = (rows_to_device(x, dtype) for x in (qh, kh, vh))
+    out = torch.full((sum(counts), H, D), float("nan"), device="cuda")
+    pkv.pkv_prefill_attention(pool, layer, _pt_device(w), w.pt_stride, starts, counts, q, k, v,
+                              out)
+    torch.cuda.synchronize()
+    _check_prefill(w, layer, starts, counts, qh, kh, vh, out, kp, vp)
+    pkv.pkv_pool_destroy(pool)
+
+
+def test_prefill_rejects_ranges_outside_the_table():
+    w = _small("prefill_rej", "f32", 64, 16, [40], heads=1, layers=1)
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp)
+    q = torch.zeros((64, 1, 64), device="cuda")
+    pt = _pt_device(w)
+    for starts, counts in (([0], [0]), ([-1], [4]), ([w.pt_stride * 16 - 3], [4]), ([0], [1, 2])):
+        with pytest.raises((pkv.PkvError, ValueError)):
+            pkv.pkv_prefill_attention(pool, 0, pt, w.pt_stride, starts, counts, q, q, q, q)
+    pkv.pkv_pool_destroy(pool)
+
+
+@pytest.mark.parametrize("dtype,D,H,Hkv", [("bf16", 128, 4, 2), ("f32", 64, 2, 2)])
+def test_prefill_transactional_chunks(dtype, D, H, Hkv):
+    """begin_tokens chunks on several caches (one of them a single token),
+    batched append_and_attend per layer, commit; an aborted chunk returns its
+    pages and its retry matches the oracle; a decode step then reads the
+    committed chunk."""
+    chunks = [37, 1, 16, 130]
+    prefix = np.array([0, 20, 16, 3], dtype=np.int64)
+    w = _small(f"prefill_txn_{dtype}", dtype, D, 16, prefix + np.array(chunks) + 2, heads=H,
+               kv_heads=Hkv, layers=2, seed=43, extra_pages=30)
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp, seed=5, max_caches=8, max_context=1024, merge=2)
+    caches = [pkv.pkv_cache_create(pool, 1024) for _ in chunks]
+    for c, n in zip(caches, prefix.tolist()):
+        pkv.pkv_cache_grow(c, n)
+    free0 = pkv.pkv_pool_get_counters(pool).pages_free
+    assert pkv.pkv_begin_tokens_batched(caches, chunks) == prefix.tolist()
+    # abort cache 3's chunk before any layer, then begin it again
+    pkv.pkv_abort_token(caches[3])
+    assert len(pkv.pkv_cache_page_table(caches[3])) == 1
+    assert pkv.pkv_begin_tokens(caches[3], chunks[3]) == prefix[3]
+    tables = [pkv.pkv_cache_page_table(c) for c in caches]
+    T = sum(chunks)
+    outs = []
+    for layer in range(w.layers):
+        qh, kh, vh = _chunk_rows(w, layer, T)
+        q, k, v = (rows_to_device(x, dtype) for x in (qh, kh, vh))
+        out = torch.empty((T, H, D), device="cuda")
+        pkv.pkv_append_and_attend_batched(caches, layer, q, k, v, out)
+        outs.append((qh, kh, vh, out))
+    torch.cuda.synchronize()
+    pkv.pkv_commit_token_batched(caches)
+    assert [pkv.pkv_cache_size(c) for c in caches] == (prefix + np.array(chunks)).tolist()
+    held = sum(-(-(int(a) + b) // 16) for a, b in zip(prefix, chunks))
+    assert pkv.pkv_pool_get_counters(pool).pages_free == w.num_pages - held
+    for layer, (qh, kh, vh, out) in enumerate(outs):
+        _check_prefill(w, layer, prefix.tolist(), chunks, qh, kh, vh, out, kp, vp, tables)
+    # one decode token on every cache reads the committed chunk
+    layer = 1
+    qh, kh, vh = _chunk_rows(w, layer, len(chunks), step=1)
+    q, k, v = (rows_to_device(x, dtype) for x in (qh, kh, vh))
+    pkv.pkv_begin_token_batched(caches)
+    out = torch.empty((len(chunks), H, D), device="cuda")
+    pkv.pkv_append_and_attend_batched(caches, layer, q, k, v, out)
+    torch.cuda.synchronize()
+    prev_q, prev_k, prev_v, _ = outs[layer]
+    off = 0
+    for r, c in enumerate(caches):
+        sl = slice(off, off + chunks[r])
+        # rows: generator prefix, the committed chunk, then the new token
+        ref = oracle.prefill_attention(
+            np.concatenate([prev_q[sl], qh[r:r + 1]]), np.concatenate([prev_k[sl], kh[r:r + 1]]),
+            np.concatenate([prev_v[sl], vh[r:r + 1]]), HostPages(w, "k", layer),
+            HostPages(w, "v", layer), pkv.pkv_cache_page_table(c), int(prefix[r]), 16)[-1]
+        assert max_err(out[r], ref) <= TOL[dtype], r
+        off += chunks[r]
+    for c in caches:
+        pkv.pkv_abort_token(c)
+        pkv.pkv_cache_destroy(c)
+    pkv.pkv_pool_destroy(pool)
+
+
 @pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128), ("f32", 24)])
 @pytest.mark.parametrize("merge", MERGES)
 def test_page_table_permutation_is_bit_identical(dtype, D, merge):

@@ -272,3 +272,60 @@ def test_grouped_kv_heads_match_library_gqa(H, Hkv):
     vp2[pt[(t - 1) // S], :, (t - 1) % S, :] = vn
     assert np.array_equal(got_a, oracle.paged_decode_attention(q, kp2, vp2, pt, t, S,
                                                                num_kv_heads=Hkv))
+
+
+@pytest.mark.parametrize("start,n,H,Hkv,S", [(0, 1, 2, 2, 16), (0, 37, 2, 2, 16), (5, 20, 4, 2, 4),
+                                            (33, 17, 3, 1, 16), (16, 16, 2, 2, 16)])
+def test_prefill_matches_library_masked_attention(start, n, H, Hkv, S):
+    # torch's float64 SDPA over the whole sequence with an explicit mask that
+    # lets row start+i see rows 0..start+i; the chunk's rows are the last n.
+    D, t = 16, start + n
+    K = RNG.standard_normal((Hkv, t, D))
+    V = RNG.standard_normal((Hkv, t, D))
+    q = RNG.standard_normal((n, H, D))
+    npg = -(-t // S) + 2
+    pt = RNG.permutation(npg + 4)[:npg]
+    kp = _scatter(K[:, :start], S, pt, npg + 4) if start else np.zeros((npg + 4, Hkv, S, D))
+    vp = _scatter(V[:, :start], S, pt, npg + 4) if start else np.zeros((npg + 4, Hkv, S, D))
+    got = oracle.prefill_attention(q, K[:, start:].transpose(1, 0, 2), V[:, start:].transpose(1, 0, 2),
+                                   kp, vp, pt, start, S)
+    allowed = torch.from_numpy(np.arange(t)[None, :] <= (start + np.arange(n))[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.transpose(1, 0, 2))[None], torch.from_numpy(K)[None],
+        torch.from_numpy(V)[None], attn_mask=allowed, enable_gqa=True)[0].numpy()
+    assert np.max(np.abs(got - ref.transpose(1, 0, 2))) < 1e-12
+    if start == 0 and H == Hkv:
+        # no prefix: the complete-prefix computation of every row
+        for h in range(H):
+            assert np.max(np.abs(got[:, h] - oracle.causal_attention(q[:, h], K[h], V[h]))) < 1e-12
+
+
+def test_prefill_of_one_row_is_append_and_attend():
+    H, D, S, P, start = 2, 8, 4, 9, 10
+    kp = RNG.standard_normal((P, H, S, D))
+    vp = RNG.standard_normal((P, H, S, D))
+    pt = np.array([3, 7, 1])
+    q, kn, vn = (RNG.standard_normal((1, H, D)) for _ in range(3))
+    got = oracle.prefill_attention(q, kn, vn, kp, vp, pt, start, S)
+    assert np.array_equal(got[0], oracle.append_and_attend(q[0], kn[0], vn[0], kp, vp, pt, start, S))
+
+
+def test_chunk_transaction_equals_token_steps():
+    # A committed chunk of n positions leaves the same visible state as n
+    # committed single-token transactions (the reading of a chunked begin).
+    for n in (1, 3, 4, 5, 9):
+        chunk_pool, step_pool = oracle.PoolModel(10), oracle.PoolModel(10)
+        chunk = oracle.CacheModel(chunk_pool, 2, 40, 4)
+        steps = oracle.CacheModel(step_pool, 2, 40, 4)
+        for m, counts in ((chunk, [2, n]), (steps, [1] * (2 + n))):
+            for c in counts:
+                assert m.begin(c) == Status.OK
+                for layer in range(2):
+                    assert m.append(layer) == Status.OK
+                assert m.commit() == Status.OK
+        assert chunk.length == steps.length == 2 + n
+        assert chunk.retained_lengths == steps.retained_lengths
+        assert chunk.appends == steps.appends and chunk_pool.free == step_pool.free
+    m = oracle.CacheModel(oracle.PoolModel(2), 1, 40, 4)
+    assert m.begin(9) == Status.OUT_OF_PAGES and m.begin(41) == Status.CAPACITY_EXHAUSTED
+    assert m.begin(0) == Status.INVALID_ARGUMENT and m.pages_held == 0
