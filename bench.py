@@ -19,7 +19,8 @@ and sums each launch's algorithmic bytes.
 Other workloads (--workload): batch256_bf16, skewed64_bf16 (single-layer
 batched decode over existing rows), batch256_gqa8_bf16 (the same batch with
 32 query heads sharing 8 K/V heads), fullstep128_bf16_l32 (32 layers, 128
-requests, bf16, 1% seeded aborts) and tiny (the latency-bound fixture:
+requests, bf16, 1% seeded aborts), prefill32_bf16 (batched prefill chunks,
+reported in TFLOP/s against the bf16 matrix-core peak) and tiny (the latency-bound fixture:
 token-at-a-time steps of one request, reported in steps/s and us/step).
 """
 from __future__ import annotations
@@ -106,6 +107,8 @@ def main():
 
     if args.workload == "tiny":
         return tiny_latency(args)
+    if args.workload.startswith("prefill"):
+        return prefill_bench(args, W.WORKLOADS[args.workload]())
     maker = W.WORKLOADS[args.workload]
     grow = 2 * args.steps + args.warmup + 2   # committed tokens per request over both passes
     w = maker(extra_steps=grow) if args.workload.startswith("fullstep") else maker()
@@ -285,6 +288,153 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_bench(args, w):
+    """Batched prefill of one layer: every request's chunk is appended and
+    attends causally over its prefix and itself, in one pkv_prefill_attention
+    call (append launch + matrix-core attention launch).  Reported in TFLOP/s
+    of the score and value products (4 d_h per new row, head and attended
+    row); the roofline is the attention kernel against bf16 dense MFMA."""
+    import torch
+
+    import paged_kv_cache_attention_amd as pkv
+    from synth import gpu as sgpu
+
+    dt = sgpu.torch_dtype(w.dtype)
+    H, Hkv, D = w.heads, w.hkv, w.head_width
+    T = int(w.chunks.sum())
+    shape = (1, w.num_pages, Hkv, w.page_size, D)
+    kp = torch.empty(shape, dtype=dt, device="cuda")
+    vp = torch.empty(shape, dtype=dt, device="cuda")
+    sgpu.fill_normal(kp[0], w.kpool_key(0), w.dtype)
+    sgpu.fill_normal(vp[0], w.vpool_key(0), w.dtype)
+    q = torch.empty((T, H, D), dtype=dt, device="cuda")
+    k = torch.empty((T, Hkv, D), dtype=dt, device="cuda")
+    v = torch.empty((T, Hkv, D), dtype=dt, device="cuda")
+    from synth import TAG_K, TAG_Q, TAG_V, stream_key
+    for t, tag in ((q, TAG_Q), (k, TAG_K), (v, TAG_V)):
+        sgpu.fill_normal(t, stream_key(w.seed, tag, 0, 1000), w.dtype)
+    out = torch.empty((T, H, D), dtype=torch.float32, device="cuda")
+    d = pkv.pkv_pool_desc_init()
+    d.num_layers, d.num_heads, d.head_width, d.num_kv_heads = 1, H, D, Hkv
+    d.page_size, d.num_pages = w.page_size, w.num_pages
+    d.max_context = w.pt_stride * w.page_size
+    d.kv_dtype = pkv.PKV_DTYPE_F32 if w.dtype == "f32" else pkv.PKV_DTYPE_BF16
+    d.k_storage, d.v_storage = kp.data_ptr(), vp.data_ptr()
+    d.free_list_seed = w.seed
+    pool = pkv.pkv_pool_create(d)
+    pt = torch.from_numpy(w.page_tables.copy()).to("cuda")
+    starts, counts = w.starts.tolist(), w.chunks.tolist()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pkv.pkv_prefill_attention(pool, 0, pt, w.pt_stride, starts, counts, q, k, v, out,
+                                  stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    flops = w.prefill_flops()
+    value = flops * args.steps / elapsed / 1e12
+    prof = None
+    if not args.no_kernel_events:
+        pkv.pkv_pool_get_profile(pool, reset=True)
+        pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_PROFILING, 1)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_PROFILING, 0)
+        prof = pkv.pkv_pool_get_profile(pool, reset=True)
+    launches = prof.prefill_launches if prof else 0
+    avg_s = prof.prefill_ms / max(1, launches) / 1e3 if prof else 0.0
+    achieved = (prof.prefill_flops / max(1, launches)) / avg_s / 1e12 if avg_s > 0 else 0.0
+    result = {
+        "metric": "batched prefill attention TFLOP/s (score and value products)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "requests": w.n, "layers": 1, "heads": H, "kv_heads": Hkv,
+            "head_width": D, "page_size": w.page_size, "pool_pages": w.num_pages,
+            "new_rows": T, "mean_prefix": round(float(w.starts.mean()), 1),
+            "flops_per_step": flops, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "prefill_mfma_kernel",
+            "achieved": round(achieved, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "avg_launch_us": round(avg_s * 1e6, 2),
+            "flops_per_launch": int(prof.prefill_flops / max(1, launches)) if prof else 0,
+            "launches_timed": int(launches),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = prefill_cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    pkv.pkv_pool_destroy(pool)
+
+
+def prefill_cpu_baseline(w, budget_s: float) -> dict:
+    """The oracle's prefill, one thread, over whole requests' chunks in order
+    (shortest first) until the time budget is spent."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    qa, ka, va = w.chunk_rows(0)
+    offs = np.concatenate([[0], np.cumsum(w.chunks)])
+    order = np.argsort(w.chunks, kind="stable")
+    pk, pv = {}, {}
+    limiter = threadpool_limits(limits=1) if threadpool_limits else None
+    done_flops, done = 0, 0
+    t0 = time.perf_counter()
+    try:
+        for r in order.tolist():
+            st, n = int(w.starts[r]), int(w.chunks[r])
+            pt = w.page_tables[r]
+            for p in pt[: -(-st // w.page_size)].tolist():
+                if p not in pk:
+                    pk[p] = w.pool_page("k", 0, p)
+                    pv[p] = w.pool_page("v", 0, p)
+            sl = slice(int(offs[r]), int(offs[r + 1]))
+            oracle.prefill_attention(qa[sl], ka[sl], va[sl], pk, pv, pt, st, w.page_size)
+            done_flops += (n * st + n * (n + 1) // 2) * w.heads * 4 * w.head_width
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
+    el = time.perf_counter() - t0
+    return {"value": round(done_flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"layer 0 of {w.name}: {done} of {w.n} requests (shortest chunks first), "
+                      f"all {w.heads} heads, {done_flops} flops in {el:.2f} s (float64, one thread, "
+                      f"page generation included)"}
 
 
 def tiny_latency(args):

@@ -124,15 +124,21 @@ typedef struct pkv_counters {
 
 /* Kernel timing of one pool, collected while PKV_OPT_PROFILING is on: HIP
  * events recorded on the launch stream immediately before and after each
- * attention kernel (and each separate merge kernel).  algorithmic_bytes sums
- * what the attention launches must move: the K/V rows read from the pool,
- * q, the appended rows (read and written) and the float32 context. */
+ * decode attention kernel (and each separate merge kernel), and each
+ * matrix-core prefill attention kernel.  algorithmic_bytes sums what the
+ * decode launches must move: the K/V rows read from the pool, q, the
+ * appended rows (read and written) and the float32 context.  prefill_flops
+ * sums the prefill launches' score and value products, 4 * d_h per (query
+ * row, query head, attended row). */
 typedef struct pkv_profile {
   uint64_t attention_launches;
   double attention_ms;
   uint64_t merge_launches;
   double merge_ms;
   uint64_t algorithmic_bytes;
+  uint64_t prefill_launches;
+  double prefill_ms;
+  uint64_t prefill_flops;
 } pkv_profile;
 
 /* Tunables of a pool (pkv_pool_set_option). */

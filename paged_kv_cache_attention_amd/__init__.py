@@ -81,6 +81,9 @@ class pkv_profile(ctypes.Structure):
         ("merge_launches", ctypes.c_uint64),
         ("merge_ms", ctypes.c_double),
         ("algorithmic_bytes", ctypes.c_uint64),
+        ("prefill_launches", ctypes.c_uint64),
+        ("prefill_ms", ctypes.c_double),
+        ("prefill_flops", ctypes.c_uint64),
     ]
 
 

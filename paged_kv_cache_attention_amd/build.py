@@ -30,7 +30,7 @@ def _run(cmd):
 
 
 def build_libpkv() -> str:
-    srcs = [os.path.join(HERE, "csrc", "kernels.hip"), os.path.join(HERE, "csrc", "runtime.cpp")]
+    srcs = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "prefill.hip", "runtime.cpp")]
     tmp = LIBPKV + ".tmp"
     _run([HIPCC, *COMMON, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp])
     os.replace(tmp, LIBPKV)

@@ -26,9 +26,6 @@
 namespace pkv {
 namespace {
 
-constexpr int kDtypeF32 = 0;
-constexpr int kDtypeBF16 = 1;
-
 struct bf16_t {
   uint16_t bits;
 };

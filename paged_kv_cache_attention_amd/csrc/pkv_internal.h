@@ -11,6 +11,10 @@ namespace pkv {
 // head is one contiguous 16 x d_h slab when page_size is a multiple of 16.
 constexpr int kBlockRows = 16;
 
+// K/V element types (the values of pkv_dtype).
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBF16 = 1;
+
 // One request of a plan.  pt_row selects the request's row of the page-table
 // array the launch receives; seq_len is the attended length t (newest row
 // included).  nsplit > 1 means the request's chunks write partials starting at
@@ -59,6 +63,35 @@ struct AttnArgs {
   float scale_log2e;      // log2(e) / sqrt(D)
 };
 
+// One prefill work tile: up to 64 consecutive rows of one request's chunk.
+struct PrefillTile {
+  int32_t pt_row;   // page-table row of the request
+  int32_t start;    // position of the chunk's first row
+  int32_t off;      // packed index of the chunk's first row in q, k, v and out
+  int32_t i0;       // first chunk row of the tile
+  int32_t nq;       // rows in the tile, 1..64
+  int32_t key_end;  // the tile reads rows 0..key_end-1 (start + i0 + nq)
+};
+
+struct PrefillArgs {
+  const void* q;          // [T][H][D] pool dtype, packed request after request
+  const void* k_new;      // [T][H_kv][D] rows to write at start + i
+  const void* v_new;
+  float* out;             // [T][H][D]
+  char* k_layer;          // K pool of this layer
+  char* v_layer;
+  const int32_t* page_table;
+  int64_t pt_stride;
+  const PrefillTile* tiles;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t page_size;
+  int32_t pad;
+  int64_t page_bytes;
+  int64_t head_bytes;
+  float scale_log2e;
+};
+
 struct PatchBatch {
   static constexpr int kMax = 248;
   int32_t count;
@@ -87,5 +120,12 @@ hipError_t launch_merge(const AttnArgs& a, int num_split_reqs, hipStream_t strea
 hipError_t launch_kv_append(const AttnArgs& a, int dtype, int num_reqs, hipStream_t stream);
 hipError_t launch_patches(int32_t* arena, const PatchBatch& b, hipStream_t stream);
 bool fast_path_supported(int dtype, int head_width, int page_size, int group);
+
+// Prefill on matrix cores (bf16, head width 128, pages of a multiple of 16
+// rows): append the chunk's rows, then causal attention over each tile.
+bool prefill_fast_supported(int dtype, int head_width, int page_size);
+hipError_t launch_prefill_append(const PrefillArgs& a, int num_tiles, hipStream_t stream);
+hipError_t launch_prefill_attention(const PrefillArgs& a, int num_tiles, hipStream_t stream);
+constexpr int kPrefillTileRows = 64;
 
 }  // namespace pkv

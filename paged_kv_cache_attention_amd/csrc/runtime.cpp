@@ -30,6 +30,8 @@
 
 using pkv::AttnArgs;
 using pkv::PatchBatch;
+using pkv::PrefillArgs;
+using pkv::PrefillTile;
 using pkv::ReqEntry;
 using pkv::WorkItem;
 
@@ -140,9 +142,10 @@ struct pkv_pool {
   int32_t merge_mode = pkv::kMergeLastArriver;
   int32_t waves_option = 0;
   bool profiling = false;
+  enum TimedKind { kTimedAttention, kTimedMerge, kTimedPrefill };
   struct Timed {
     hipEvent_t start, end;
-    bool merge;
+    TimedKind kind;
   };
   std::vector<Timed> timed;         // recorded, not yet summed
   std::vector<hipEvent_t> spare;    // reusable events
@@ -261,6 +264,54 @@ void plan_release(pkv_plan* pl) {
   pl->built = false;
 }
 
+struct MetaPart {
+  const void* data;
+  size_t bytes;
+};
+
+// Copies the parts, back to back, into the plan's device metadata buffer on
+// the stream, through pinned host staging.  The staging buffer is reused only
+// after the previous upload's copy has completed (an event on the stream);
+// growing the device buffer waits for the device to finish with the old one.
+pkv_status upload_meta(pkv_plan* pl, const MetaPart* parts, int nparts, hipStream_t stream) {
+  size_t bytes = 0;
+  for (int i = 0; i < nparts; ++i) bytes += parts[i].bytes;
+  if (pl->ev_pending) {
+    PKV_HIP_TRY(hipEventSynchronize(pl->ev));
+    pl->ev_pending = false;
+  }
+  if (!pl->ev) PKV_HIP_TRY(hipEventCreateWithFlags(&pl->ev, hipEventDisableTiming));
+  if (bytes > pl->d_meta_cap) {
+    const size_t cap = std::max(bytes, pl->d_meta_cap * 2);
+    void* d = nullptr;
+    if (hipMalloc(&d, cap) != hipSuccess) return fail(PKV_ERR_ALLOC, "plan buffer %zu bytes", cap);
+    if (pl->d_meta) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(pl->d_meta);
+    }
+    pl->d_meta = static_cast<char*>(d);
+    pl->d_meta_cap = cap;
+  }
+  if (bytes > pl->h_stage_cap) {
+    const size_t cap = std::max(bytes, pl->h_stage_cap * 2);
+    void* h = nullptr;
+    if (hipHostMalloc(&h, cap, hipHostMallocDefault) != hipSuccess)
+      return fail(PKV_ERR_ALLOC, "pinned staging %zu bytes", cap);
+    if (pl->h_stage) (void)hipHostFree(pl->h_stage);
+    pl->h_stage = static_cast<char*>(h);
+    pl->h_stage_cap = cap;
+  }
+  size_t off = 0;
+  for (int i = 0; i < nparts; ++i) {
+    if (parts[i].bytes) std::memcpy(pl->h_stage + off, parts[i].data, parts[i].bytes);
+    off += parts[i].bytes;
+  }
+  PKV_HIP_TRY(hipMemcpyAsync(pl->d_meta, pl->h_stage, bytes, hipMemcpyHostToDevice, stream));
+  PKV_HIP_TRY(hipEventRecord(pl->ev, stream));
+  pl->ev_pending = true;
+  return PKV_OK;
+}
+
 // Builds the split plan for n requests (rows[r] selects the page-table row,
 // lens[r] the attended length) and uploads it on the stream.
 pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_t* lens,
@@ -315,34 +366,7 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
     return (a.blk_end - a.blk_begin) > (b.blk_end - b.blk_begin);
   });
 
-  const size_t meta_bytes = reqs.size() * sizeof(ReqEntry) + items.size() * sizeof(WorkItem) +
-                            merge_list.size() * sizeof(int32_t);
   if (upload) {
-  if (pl->ev_pending) {
-    PKV_HIP_TRY(hipEventSynchronize(pl->ev));
-    pl->ev_pending = false;
-  }
-  if (!pl->ev) PKV_HIP_TRY(hipEventCreateWithFlags(&pl->ev, hipEventDisableTiming));
-  if (meta_bytes > pl->d_meta_cap) {
-    const size_t cap = std::max(meta_bytes, pl->d_meta_cap * 2);
-    void* d = nullptr;
-    if (hipMalloc(&d, cap) != hipSuccess) return fail(PKV_ERR_ALLOC, "plan buffer %zu bytes", cap);
-    if (pl->d_meta) {
-      (void)hipDeviceSynchronize();
-      (void)hipFree(pl->d_meta);
-    }
-    pl->d_meta = static_cast<char*>(d);
-    pl->d_meta_cap = cap;
-  }
-  if (meta_bytes > pl->h_stage_cap) {
-    const size_t cap = std::max(meta_bytes, pl->h_stage_cap * 2);
-    void* h = nullptr;
-    if (hipHostMalloc(&h, cap, hipHostMallocDefault) != hipSuccess)
-      return fail(PKV_ERR_ALLOC, "pinned staging %zu bytes", cap);
-    if (pl->h_stage) (void)hipHostFree(pl->h_stage);
-    pl->h_stage = static_cast<char*>(h);
-    pl->h_stage_cap = cap;
-  }
   const size_t part_floats = (size_t)slots * p->desc.num_heads * (p->desc.head_width + 2);
   if (part_floats > pl->partials_cap) {
     const size_t cap = std::max(part_floats, pl->partials_cap * 2);
@@ -373,15 +397,10 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
     pl->d_counters = static_cast<int32_t*>(d);
     pl->counters_cap = cap;
   }
-  std::memcpy(pl->h_stage, reqs.data(), reqs.size() * sizeof(ReqEntry));
-  std::memcpy(pl->h_stage + reqs.size() * sizeof(ReqEntry), items.data(),
-              items.size() * sizeof(WorkItem));
-  if (!merge_list.empty())
-    std::memcpy(pl->h_stage + reqs.size() * sizeof(ReqEntry) + items.size() * sizeof(WorkItem),
-                merge_list.data(), merge_list.size() * sizeof(int32_t));
-  PKV_HIP_TRY(hipMemcpyAsync(pl->d_meta, pl->h_stage, meta_bytes, hipMemcpyHostToDevice, stream));
-  PKV_HIP_TRY(hipEventRecord(pl->ev, stream));
-  pl->ev_pending = true;
+  const MetaPart parts[3] = {{reqs.data(), reqs.size() * sizeof(ReqEntry)},
+                             {items.data(), items.size() * sizeof(WorkItem)},
+                             {merge_list.data(), merge_list.size() * sizeof(int32_t)}};
+  if ((st = upload_meta(pl, parts, 3, stream)) != PKV_OK) return st;
   }  // upload
 
   pl->reqs = std::move(reqs);
@@ -481,7 +500,7 @@ pkv_status run_attention(pkv_plan* pl, int32_t layer, const int32_t* page_table,
   PKV_HIP_TRY(pkv::launch_attention(a, p->desc.kv_dtype, pl->num_items, stream, nullptr));
   if (p->profiling) {
     PKV_HIP_TRY(hipEventRecord(e1, stream));
-    p->timed.push_back({e0, e1, false});
+    p->timed.push_back({e0, e1, pkv_pool::kTimedAttention});
     p->profile.algorithmic_bytes += launch_bytes(pl, fuse);
   }
   if (pl->any_split && p->merge_mode == pkv::kMergeSeparate) {
@@ -494,7 +513,7 @@ pkv_status run_attention(pkv_plan* pl, int32_t layer, const int32_t* page_table,
     PKV_HIP_TRY(pkv::launch_merge(a, pl->num_split_reqs, stream));
     if (p->profiling) {
       PKV_HIP_TRY(hipEventRecord(e1, stream));
-      p->timed.push_back({e0, e1, true});
+      p->timed.push_back({e0, e1, pkv_pool::kTimedMerge});
     }
   }
   return PKV_OK;
@@ -503,6 +522,81 @@ pkv_status run_attention(pkv_plan* pl, int32_t layer, const int32_t* page_table,
 pkv_status check_layer(const pkv_pool* p, int32_t layer) {
   if (layer < 0 || layer >= p->desc.num_layers)
     return fail(PKV_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", layer, p->desc.num_layers);
+  return PKV_OK;
+}
+
+// Matrix-core prefill: the chunks cut into tiles of up to 64 rows, longest
+// visible prefix first; one append launch writes every new row, then one
+// attention launch covers all (tile, query head) pairs.  The tile list is
+// uploaded once and reused by later layers of the same chunks.
+pkv_status run_prefill_tiles(pkv_pool* p, int32_t n, const int32_t* rows, const int32_t* starts,
+                             const int32_t* counts, int32_t pt_stride, int32_t layer,
+                             const int32_t* page_table, const void* q, const void* k,
+                             const void* v, float* out, uint64_t score_rows,
+                             hipStream_t stream) {
+  pkv_plan* pl = &p->prefill_plan;
+  std::vector<int64_t> key(3 * (size_t)n + 2);
+  key[0] = -1;  // never equal to a decode-plan key (those start with pt_stride)
+  key[1] = pt_stride;
+  for (int32_t r = 0; r < n; ++r) {
+    key[2 + 3 * r] = rows[r];
+    key[3 + 3 * r] = starts[r];
+    key[4 + 3 * r] = counts[r];
+  }
+  if (!(pl->built && key == pl->key)) {
+    std::vector<PrefillTile> tiles;
+    int32_t off = 0;
+    for (int32_t r = 0; r < n; ++r) {
+      for (int32_t i0 = 0; i0 < counts[r]; i0 += pkv::kPrefillTileRows) {
+        const int32_t nq = std::min(pkv::kPrefillTileRows, counts[r] - i0);
+        tiles.push_back(PrefillTile{rows[r], starts[r], off, i0, nq, starts[r] + i0 + nq});
+      }
+      off += counts[r];
+    }
+    std::stable_sort(tiles.begin(), tiles.end(), [](const PrefillTile& x, const PrefillTile& y) {
+      return x.key_end > y.key_end;
+    });
+    pkv_status st = ensure_device(p);
+    if (st != PKV_OK) return st;
+    const MetaPart part{tiles.data(), tiles.size() * sizeof(PrefillTile)};
+    if ((st = upload_meta(pl, &part, 1, stream)) != PKV_OK) return st;
+    pl->key = std::move(key);
+    pl->built = true;
+    pl->num_items = (int32_t)tiles.size();
+    pl->reqs.clear();
+    pl->items.clear();
+  }
+  PrefillArgs a{};
+  a.q = q;
+  a.k_new = k;
+  a.v_new = v;
+  a.out = out;
+  a.k_layer = static_cast<char*>(p->desc.k_storage) + (int64_t)layer * p->layer_bytes;
+  a.v_layer = static_cast<char*>(p->desc.v_storage) + (int64_t)layer * p->layer_bytes;
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.tiles = reinterpret_cast<const PrefillTile*>(pl->d_meta);
+  a.num_heads = p->desc.num_heads;
+  a.num_kv_heads = p->desc.num_kv_heads;
+  a.page_size = p->desc.page_size;
+  a.page_bytes = p->page_bytes;
+  a.head_bytes = p->head_bytes;
+  a.scale_log2e = (float)(1.4426950408889634 / std::sqrt((double)p->desc.head_width));
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (p->profiling) {
+    e0 = take_event(p);
+    e1 = take_event(p);
+    if (!e0 || !e1) return fail(PKV_ERR_DEVICE, "hipEventCreate failed");
+  }
+  PKV_HIP_TRY(pkv::launch_prefill_append(a, pl->num_items, stream));
+  if (p->profiling) PKV_HIP_TRY(hipEventRecord(e0, stream));
+  PKV_HIP_TRY(pkv::launch_prefill_attention(a, pl->num_items, stream));
+  if (p->profiling) {
+    PKV_HIP_TRY(hipEventRecord(e1, stream));
+    p->timed.push_back({e0, e1, pkv_pool::kTimedPrefill});
+    p->profile.prefill_flops +=
+        score_rows * (uint64_t)p->desc.num_heads * 4ull * (uint64_t)p->desc.head_width;
+  }
   return PKV_OK;
 }
 
@@ -527,6 +621,15 @@ pkv_status run_prefill(pkv_pool* p, int32_t n, const int32_t* rows, const int32_
   }
   if (total > std::numeric_limits<int32_t>::max() / 2)
     return fail(PKV_ERR_INVALID_ARGUMENT, "%lld rows in one prefill call", (long long)total);
+  const int64_t D = p->desc.head_width;
+  uint64_t score_rows = 0;  // sum over new rows of their attended lengths
+  for (int32_t r = 0; r < n; ++r)
+    score_rows += (uint64_t)counts[r] * starts[r] + (uint64_t)counts[r] * (counts[r] + 1) / 2;
+  p->counters.kv_bytes_read += score_rows * (uint64_t)p->desc.num_kv_heads * 2ull * D * p->elt;
+  if (!p->host_only &&
+      pkv::prefill_fast_supported(p->desc.kv_dtype, p->desc.head_width, p->desc.page_size))
+    return run_prefill_tiles(p, n, rows, starts, counts, pt_stride, layer, page_table, q, k, v,
+                             out, score_rows, stream);
   std::vector<int32_t> vrows((size_t)total), vlens((size_t)total);
   size_t j = 0;
   for (int32_t r = 0; r < n; ++r)
@@ -541,7 +644,11 @@ pkv_status run_prefill(pkv_pool* p, int32_t n, const int32_t* rows, const int32_
     AttnArgs a = make_args(pl, layer, page_table, q, k, v, out, false);
     PKV_HIP_TRY(pkv::launch_kv_append(a, p->desc.kv_dtype, (int32_t)total, stream));
   }
-  return run_attention(pl, layer, page_table, q, nullptr, nullptr, out, false, stream);
+  // run_attention counts the decode-form K/V reads; this call counted its own
+  const uint64_t before = p->counters.kv_bytes_read;
+  st = run_attention(pl, layer, page_table, q, nullptr, nullptr, out, false, stream);
+  p->counters.kv_bytes_read = before;
+  return st;
 }
 
 // Shared body of the single and batched transactional layer step.
@@ -747,9 +854,12 @@ pkv_status pkv_pool_get_profile(pkv_pool* p, pkv_profile* out, int32_t reset) {
     PKV_HIP_TRY(hipEventSynchronize(t.end));
     float ms = 0.f;
     PKV_HIP_TRY(hipEventElapsedTime(&ms, t.start, t.end));
-    if (t.merge) {
+    if (t.kind == pkv_pool::kTimedMerge) {
       p->profile.merge_launches += 1;
       p->profile.merge_ms += ms;
+    } else if (t.kind == pkv_pool::kTimedPrefill) {
+      p->profile.prefill_launches += 1;
+      p->profile.prefill_ms += ms;
     } else {
       p->profile.attention_launches += 1;
       p->profile.attention_ms += ms;

@@ -41,6 +41,7 @@ class Workload:
     abort_rate: float = 0.0
     description: str = ""
     kv_heads: int = 0            # K/V heads per layer; 0 = one per query head
+    chunks: np.ndarray = field(default=None)  # prefill: new rows per request (ending at t)
 
     # ---- geometry -------------------------------------------------------
     @property
@@ -97,6 +98,29 @@ class Workload:
     def v_new(self, layer: int, step: int = 0) -> np.ndarray:
         return normals(self.v_key(layer, step), 0, self.kv_row_elems, self.dtype).reshape(
             self.n, self.hkv, self.head_width)
+
+    def chunk_rows(self, layer: int, step: int = 0):
+        """Prefill rows of every request's chunk, packed request after request:
+        q [T, H, D], k and v [T, H_kv, D] with T = sum of chunks."""
+        total = int(np.sum(self.chunks))
+        out = []
+        for tag, heads in ((TAG_Q, self.heads), (TAG_K, self.hkv), (TAG_V, self.hkv)):
+            key = stream_key(self.seed, tag, layer, 1000 + step)
+            out.append(normals(key, 0, total * heads * self.head_width, self.dtype).reshape(
+                total, heads, self.head_width))
+        return tuple(out)
+
+    @property
+    def starts(self) -> np.ndarray:
+        """Prefill: position of each chunk's first row (the retained prefix)."""
+        return self.lengths - self.chunks
+
+    def prefill_flops(self) -> int:
+        """Score and value products of one prefill layer: 4 d_h per (new row,
+        query head, attended row)."""
+        c, st = self.chunks.astype(np.int64), self.starts.astype(np.int64)
+        rows = int(np.sum(c * st + c * (c + 1) // 2))
+        return rows * self.heads * 4 * self.head_width
 
     def pool_page(self, which: str, layer: int, page: int) -> np.ndarray:
         """Generator content of one physical page ``[H_kv, S, D]`` of one layer."""
@@ -232,10 +256,25 @@ def batch256_gqa8_bf16() -> Workload:
     return _finish(w)
 
 
+def prefill32_bf16() -> Workload:
+    """Batched prefill: 32 requests, one layer, H=32, D=128, 16-token pages,
+    bf16; each request appends a chunk of U[256, 2048] new rows after a
+    retained prefix of U[0, 2048] rows, every new row attending causally."""
+    seed = 6
+    prefix = uniform_ints(stream_key(seed, TAG_LENGTHS, 0), 32, 0, 2048)
+    chunks = uniform_ints(stream_key(seed, TAG_LENGTHS, 1), 32, 256, 2048)
+    lengths = prefix + chunks
+    P = int(pages_needed(lengths, 16).sum()) + 32
+    w = Workload("prefill32_bf16", seed, 32, 1, 32, 128, 16, P, "bf16", lengths,
+                 appends=True, description=prefill32_bf16.__doc__, chunks=chunks)
+    return _finish(w)
+
+
 WORKLOADS = {
     "batch32_fp32_l12": batch32_fp32,
     "batch256_bf16": batch256_bf16,
     "batch256_gqa8_bf16": batch256_gqa8_bf16,
+    "prefill32_bf16": prefill32_bf16,
     "skewed64_bf16": skewed64_bf16,
     "fullstep128_bf16_l32": fullstep128_bf16,
 }

@@ -362,7 +362,8 @@ def test_grouped_kv_heads_transactional(dtype, D, H, Hkv):
 
 # ------------------------------------------------------- batched prefill --
 def _chunk_rows(w, layer, total, step=0):
-    """q [T,H,D], k and v [T,H_kv,D] for T new rows, from the generator."""
+    """q [T,H,D], k and v [T,H_kv,D] for T new rows, from the generator
+    (the stream keys of Workload.chunk_rows)."""
     out = []
     for tag, heads in ((synth.TAG_Q, w.heads), (synth.TAG_K, w.hkv), (synth.TAG_V, w.hkv)):
         key = synth.stream_key(w.seed, tag, layer, 1000 + step)
@@ -488,6 +489,56 @@ def test_prefill_transactional_chunks(dtype, D, H, Hkv):
     for c in caches:
         pkv.pkv_abort_token(c)
         pkv.pkv_cache_destroy(c)
+    pkv.pkv_pool_destroy(pool)
+
+
+def test_prefill32_bf16_full_sampled():
+    """The full prefill workload (32 chunks of 256-2048 rows over prefixes of
+    0-2048, H=32, d_h=128, bf16) in the bench's call; sampled (row, head)
+    contexts against the oracle, sampled page writes bit-exact."""
+    from synth import gpu as sgpu
+    w = W.prefill32_bf16()
+    H, Hkv, D, S = w.heads, w.hkv, w.head_width, w.page_size
+    T = int(w.chunks.sum())
+    kp, vp = device_pool(w)
+    keys = [synth.stream_key(w.seed, tag, 0, 1000) for tag in (synth.TAG_Q, synth.TAG_K,
+                                                                   synth.TAG_V)]
+    q = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((T, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((T, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    for t, key in zip((q, k, v), keys):
+        sgpu.fill_normal(t, key, "bf16")
+    pool = _pool(w, kp, vp)
+    out = torch.full((T, H, D), float("nan"), device="cuda")
+    pkv.pkv_prefill_attention(pool, 0, _pt_device(w), w.pt_stride, w.starts.tolist(),
+                              w.chunks.tolist(), q, k, v, out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    offs = np.concatenate([[0], np.cumsum(w.chunks)])
+    kpg, vpg = HostPages(w, "k", 0), HostPages(w, "v", 0)
+
+    def rows(key, first, n, heads, head):
+        idx = (((first + np.arange(n, dtype=np.uint64))[:, None] * np.uint64(heads) +
+                np.uint64(head)) * np.uint64(D) + np.arange(D, dtype=np.uint64)).ravel()
+        return synth.normals_at(key, idx, "bf16").reshape(n, D)
+
+    picks = {int(np.argmax(w.chunks)), int(np.argmin(w.chunks)), int(np.argmax(w.starts))}
+    for r in sorted(picks):
+        st, n = int(w.starts[r]), int(w.chunks[r])
+        for i in (0, n // 2, n - 1):
+            j = int(offs[r]) + i
+            pos = st + i
+            page, slot = w.page_tables[r][pos // S], pos % S
+            assert np.array_equal(to_bits(kp[0, page, :, slot, :], "bf16"),
+                                  np.stack([rows(keys[1], j, 1, Hkv, h)[0] for h in range(Hkv)]))
+            for h in (0, 13, H - 1):
+                K = np.concatenate([oracle.kv_to_f64(oracle.gather_prefix(kpg, w.page_tables[r], st, S, h)).reshape(-1, D),
+                                    oracle.kv_to_f64(rows(keys[1], int(offs[r]), i + 1, Hkv, h))])
+                V = np.concatenate([oracle.kv_to_f64(oracle.gather_prefix(vpg, w.page_tables[r], st, S, h)).reshape(-1, D),
+                                    oracle.kv_to_f64(rows(keys[2], int(offs[r]), i + 1, Hkv, h))])
+                ref = oracle.attend(rows(keys[0], j, 1, H, h)[0], K, V)
+                err = float(np.max(np.abs(out[j, h].cpu().numpy().astype(np.float64) - ref)))
+                assert err <= TOL["bf16"], (r, i, h, err)
     pkv.pkv_pool_destroy(pool)
 
 
