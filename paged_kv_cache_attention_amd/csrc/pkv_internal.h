@@ -63,13 +63,14 @@ struct AttnArgs {
   float scale_log2e;      // log2(e) / sqrt(D)
 };
 
-// One prefill work tile: up to 64 consecutive rows of one request's chunk.
+// One prefill work tile: up to kPrefillTileRows consecutive rows of one
+// request's chunk.
 struct PrefillTile {
   int32_t pt_row;   // page-table row of the request
   int32_t start;    // position of the chunk's first row
   int32_t off;      // packed index of the chunk's first row in q, k, v and out
   int32_t i0;       // first chunk row of the tile
-  int32_t nq;       // rows in the tile, 1..64
+  int32_t nq;       // rows in the tile, 1..kPrefillTileRows
   int32_t key_end;  // the tile reads rows 0..key_end-1 (start + i0 + nq)
 };
 
@@ -122,10 +123,11 @@ hipError_t launch_patches(int32_t* arena, const PatchBatch& b, hipStream_t strea
 bool fast_path_supported(int dtype, int head_width, int page_size, int group);
 
 // Prefill on matrix cores (bf16, head width 128, pages of a multiple of 16
-// rows): append the chunk's rows, then causal attention over each tile.
+// rows): an append launch writes the chunk's rows, then an attention launch
+// runs the causal attention of every (tile, query head).
 bool prefill_fast_supported(int dtype, int head_width, int page_size);
 hipError_t launch_prefill_append(const PrefillArgs& a, int num_tiles, hipStream_t stream);
 hipError_t launch_prefill_attention(const PrefillArgs& a, int num_tiles, hipStream_t stream);
-constexpr int kPrefillTileRows = 64;
+constexpr int kPrefillTileRows = 128;
 
 }  // namespace pkv

@@ -9,7 +9,7 @@
 // incremental mixture: scores q.k/sqrt(d_h), stable softmax, weighted values).
 //
 // Unlike decode, a chunk has many query rows per key row, so the score and
-// value products are dense contractions: 64 query rows share every K/V block
+// value products are dense contractions: 128 query rows share every K/V block
 // staged in LDS, and both products run on MFMA (bf16 in, float32 accumulate).
 #include <hip/hip_runtime.h>
 
@@ -25,7 +25,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;            // head width of this kernel (256-byte bf16 rows)
 constexpr int kRowBytes = kD * 2;
-static_assert(kPrefillTileRows == 64, "four waves of 16 query rows");
+static_assert(kPrefillTileRows == 128, "four waves of 32 query rows");
 constexpr int kBlockKeys = 64;     // keys per LDS block
 constexpr int kKStride = kD + 8;   // bf16 per K row in LDS (272 B: rows 4 banks apart)
 constexpr int kVStride = kBlockKeys + 4;  // bf16 per transposed V row in LDS (136 B)
@@ -46,23 +46,33 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Workgroup: 4 waves on one tile (request, 64 consecutive chunk rows) and one
-// query head.  Every 64-key block of the rows the tile can see (0 .. the
-// tile's last position) is staged in LDS -- K as rows, V transposed -- and
-// each wave scores its 16 query rows against it.
+// Transposed V in LDS: sV[dim][key] with the 4-key groups of each row
+// XOR-swizzled by the row's 32-dim band, so the 64 lanes that store one dim
+// each (16 dims apart across lanes, 34 banks per row) hit 64 distinct banks;
+// readers apply the same swizzle (uniform across a 16-dim tile).
+__device__ inline int vt_index(int dim, int key) {
+  return dim * kVStride + (((key >> 2) ^ (((dim >> 5) & 3) << 2)) << 2) + (key & 3);
+}
+
+// Workgroup: 4 waves on one tile (request, up to 128 consecutive chunk rows)
+// and one query head; each wave owns 32 query rows as two sets of 16.  Every
+// 64-key block of the rows the tile can see (0 .. the tile's last position)
+// is staged in LDS -- K as rows, V transposed -- while the next block's K/V
+// are already being fetched into registers.
 //
 // Scores are formed transposed, S^T = K Q^T (A operand: 16 keys x 32 dims of
 // K from LDS; B operand: Q held in registers), so lane l holds, for query
-// l%16, the scores of keys 4(l/16)..4(l/16)+3 of each 16-key tile.  Those are
-// exactly the A-operand elements of the value product O = P V when the 32
-// keys of an MFMA step are taken in the order {tile 2c: 4g..4g+3, tile 2c+1:
-// 4g..4g+3} for lane group g -- so probabilities never move between lanes;
-// the transposed V in LDS is read in the same key order.  Online softmax per
-// query in log2 units; the running maximum and sum are reduced across the
-// four lane groups with shuffles.  The context accumulates in the MFMA
+// l%16 of a set, the scores of keys 4(l/16)..4(l/16)+3 of each 16-key tile.
+// Those are exactly the A-operand elements of the value product O = P V when
+// the 32 keys of an MFMA step are taken in the order {tile 2c: 4g..4g+3,
+// tile 2c+1: 4g..4g+3} for lane group g -- so probabilities never move
+// between lanes; the transposed V is read in the same key order.  Each K or V
+// fragment read from LDS feeds the MFMAs of both query sets.  Online softmax
+// per query in log2 units; the running maximum and sum are reduced across
+// the four lane groups with shuffles.  The context accumulates in the MFMA
 // output layout (lane l: rows 4(l/16)..+3, column l%16 of each 16-column
 // tile), whose per-row scale factors come from the owning lanes by shuffle.
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[kBlockKeys * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t sV[kD * kVStride];
 
@@ -77,74 +87,92 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
   const int S = a.page_size;
   const int32_t* pt = a.page_table + (int64_t)tile.pt_row * a.pt_stride;
   const int64_t head_off = (int64_t)kvh * a.head_bytes;
+  const int pos0 = tile.start + tile.i0;  // position of the tile's first row
 
-  // This lane's query row (rows past the tile's count attend like its last
-  // row; their results are not stored).
-  const int wrow0 = 16 * wave;                       // first tile row of the wave
-  const int my_row = min(wrow0 + ql, tile.nq - 1);   // tile row of this lane's query
-  const int my_pos = tile.start + tile.i0 + my_row;  // its absolute position
-  const int wave_first_pos = tile.start + tile.i0 + min(wrow0, tile.nq - 1);
-  const int wave_last_pos = tile.start + tile.i0 + min(wrow0 + 15, tile.nq - 1);
-  const bool wave_active = wrow0 < tile.nq;
-
-  bf16x8_t qf[4];
-  {
-    const int64_t qrow = (int64_t)(tile.off + tile.i0 + my_row) * a.num_heads + h;
+  // This lane's two query rows (rows past the tile's count attend like its
+  // last row; their results are not stored).
+  const int wrow0 = 32 * wave;
+  int my_pos[2];
+  bf16x8_t qf[2][4];
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const int row = min(wrow0 + 16 * qs + ql, tile.nq - 1);
+    my_pos[qs] = pos0 + row;
+    const int64_t qrow = (int64_t)(tile.off + tile.i0 + row) * a.num_heads + h;
     const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
                                                       qrow * kRowBytes);
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) qf[dc] = as_bf16x8(src[4 * dc + g]);
+    for (int dc = 0; dc < 4; ++dc) qf[qs][dc] = as_bf16x8(src[4 * dc + g]);
   }
+  const int wave_first_pos = pos0 + min(wrow0, tile.nq - 1);
+  const int wave_last_pos = pos0 + min(wrow0 + 31, tile.nq - 1);
+  const bool wave_active = wrow0 < tile.nq;
 
-  float m = -INFINITY, l = 0.f;
-  f32x4_t acc[8];
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  f32x4_t acc[2][8];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[qs][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Global -> register fetch of one block (keys clamped to the last row the
+  // tile may read, so no lookup goes past the request's pages).  K chunk
+  // c = tid + 256 i is key c/16, bytes 16 (c%16) of its row; V chunk i of a
+  // thread is key 2 vpair + i/2, bytes 32 vdg + 16 (i%2).
+  const int vpair = tid >> 3;
+  const int vdg = tid & 7;
+  auto k_src = [&](int key0, int i) -> const uint4* {
+    const int c = tid + 256 * i;
+    const int key = min(key0 + (c >> 4), tile.key_end - 1);
+    return reinterpret_cast<const uint4*>(a.k_layer + (int64_t)pt[key / S] * a.page_bytes +
+                                          head_off + (int64_t)(key % S) * kRowBytes +
+                                          (c & 15) * 16);
+  };
+  auto v_src = [&](int key0, int i) -> const uint4* {
+    const int key = min(key0 + 2 * vpair + (i >> 1), tile.key_end - 1);
+    return reinterpret_cast<const uint4*>(a.v_layer + (int64_t)pt[key / S] * a.page_bytes +
+                                          head_off + (int64_t)(key % S) * kRowBytes +
+                                          vdg * 32 + (i & 1) * 16);
+  };
+  uint4 k0 = *k_src(0, 0), k1 = *k_src(0, 1), k2 = *k_src(0, 2), k3 = *k_src(0, 3);
+  uint4 v0 = *v_src(0, 0), v1 = *v_src(0, 1), v2 = *v_src(0, 2), v3 = *v_src(0, 3);
 
   const int nblocks = (tile.key_end + kBlockKeys - 1) / kBlockKeys;
   for (int kb = 0; kb < nblocks; ++kb) {
     const int key0 = kb * kBlockKeys;
-    // ---- stage K and V of keys key0 .. key0+63 (clamped to the last row the
-    // tile may read, so no lookup goes past the request's pages) ----
-    // K chunk c = tid + 256 i is key c/16, bytes 16 (c%16) of its row
-    auto load_k = [&](int i) -> uint4 {
-      const int c = tid + 256 * i;
-      const int key = min(key0 + (c >> 4), tile.key_end - 1);
-      const int64_t src = (int64_t)pt[key / S] * a.page_bytes + head_off +
-                          (int64_t)(key % S) * kRowBytes + (c & 15) * 16;
-      return *reinterpret_cast<const uint4*>(a.k_layer + src);
-    };
-    const uint4 k0 = load_k(0), k1 = load_k(1), k2 = load_k(2), k3 = load_k(3);
-    uint4 vreg[4];
-    const int vpair = tid >> 3;              // keys 2*vpair, 2*vpair+1
-    const int vdg = tid & 7;                 // dims 16*vdg .. 16*vdg+15
+    __syncthreads();  // every wave is done with the previous block in LDS
+    {
+      auto store_k = [&](int i, const uint4& u) {
+        const int c = tid + 256 * i;
+        *reinterpret_cast<uint4*>(&sK[(c >> 4) * kKStride + (c & 15) * 8]) = u;
+      };
+      store_k(0, k0);
+      store_k(1, k1);
+      store_k(2, k2);
+      store_k(3, k3);
+      // V transposed; one 32-bit store per dim holds the key pair (v0, v1:
+      // key 2 vpair, dims 16 vdg + 0..15; v2, v3: key 2 vpair + 1).
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = min(key0 + 2 * vpair + (i >> 1), tile.key_end - 1);
-      const int64_t src = (int64_t)pt[key / S] * a.page_bytes + head_off +
-                          (int64_t)(key % S) * kRowBytes + vdg * 32 + (i & 1) * 16;
-      vreg[i] = *reinterpret_cast<const uint4*>(a.v_layer + src);
-    }
-    __syncthreads();  // the previous block's reads of LDS are done
-    auto store_k = [&](int i, const uint4& u) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<uint4*>(&sK[(c >> 4) * kKStride + (c & 15) * 8]) = u;
-    };
-    store_k(0, k0);
-    store_k(1, k1);
-    store_k(2, k2);
-    store_k(3, k3);
-    // V transposed: sV[dim][key]; one 32-bit store per dim holds the key
-    // pair (vreg[0..1]: key 2p, dims +0..15; vreg[2..3]: key 2p+1).
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t w0 = word_of(vreg[e >> 3], (e & 7) >> 1);
-      const uint32_t w1 = word_of(vreg[2 + (e >> 3)], (e & 7) >> 1);
-      const uint32_t pair = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
-                                    : ((w0 & 0xffffu) | (w1 << 16));
-      *reinterpret_cast<uint32_t*>(&sV[(16 * vdg + e) * kVStride + 2 * vpair]) = pair;
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t w0 = word_of(e < 8 ? v0 : v1, (e & 7) >> 1);
+        const uint32_t w1 = word_of(e < 8 ? v2 : v3, (e & 7) >> 1);
+        const uint32_t pair = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
+                                      : ((w0 & 0xffffu) | (w1 << 16));
+        *reinterpret_cast<uint32_t*>(&sV[vt_index(16 * vdg + e, 2 * vpair)]) = pair;
+      }
     }
     __syncthreads();
+    if (kb + 1 < nblocks) {  // the next block's loads fly during this block's math
+      const int next = key0 + kBlockKeys;
+      k0 = *k_src(next, 0);
+      k1 = *k_src(next, 1);
+      k2 = *k_src(next, 2);
+      k3 = *k_src(next, 3);
+      v0 = *v_src(next, 0);
+      v1 = *v_src(next, 1);
+      v2 = *v_src(next, 2);
+      v3 = *v_src(next, 3);
+    }
 
     // A wave whose queries all precede every key of the block has nothing
     // to add from it (causal), and an empty wave has nothing at all.  Block 0
@@ -153,109 +181,131 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     // (scale 1, weights 0).
     if (!wave_active || wave_last_pos < key0) continue;
 
-    // ---- scores S^T = K Q^T: s[kt][j] = q(ql) . k(key0 + 16 kt + 4 g + j) ----
-    float s[4][4];
+    // ---- scores S^T = K Q^T: s[qs][kt][j] = q . k(key0 + 16 kt + 4 g + j) ----
+    float s[2][4][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      f32x4_t c4 = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dc = 0; dc < 4; ++dc) {
-        const bf16x8_t kf =
-            as_bf16x8(*reinterpret_cast<const uint4*>(&sK[(16 * kt + ql) * kKStride + 32 * dc + 8 * g]));
-        c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[dc], c4, 0, 0, 0);
+        const bf16x8_t kf = as_bf16x8(
+            *reinterpret_cast<const uint4*>(&sK[(16 * kt + ql) * kKStride + 32 * dc + 8 * g]));
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][dc], c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][dc], c1, 0, 0, 0);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s[kt][j] = c4[j] * a.scale_log2e;
+      for (int j = 0; j < 4; ++j) {  // raw q.k; the log2 scale joins in the exponent
+        s[0][kt][j] = c0[j];
+        s[1][kt][j] = c1[j];
+      }
     }
     // causal mask where the block reaches past this wave's first position
     if (key0 + kBlockKeys - 1 > wave_first_pos) {
 #pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (key0 + 16 * kt + 4 * g + j > my_pos[qs]) s[qs][kt][j] = -INFINITY;
+    }
+    float alpha[2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      float mb = s[qs][0][0];
+#pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (key0 + 16 * kt + 4 * g + j > my_pos) s[kt][j] = -INFINITY;
+        for (int j = 0; j < 4; ++j) mb = fmaxf(mb, s[qs][kt][j]);
+      mb = fmaxf(mb, __shfl_xor(mb, 16));
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      // m is kept in scaled log2 units; the scale is positive, so the maximum
+      // of the raw products scales to the maximum of the scores
+      const float mn = fmaxf(m[qs], mb * a.scale_log2e);
+      alpha[qs] = __builtin_amdgcn_exp2f(m[qs] - mn);
+      float ps = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s[qs][kt][j] = __builtin_amdgcn_exp2f(fmaf(s[qs][kt][j], a.scale_log2e, -mn));
+          ps += s[qs][kt][j];
+        }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      l[qs] = fmaf(l[qs], alpha[qs], ps);
+      m[qs] = mn;
     }
-    float mb = s[0][0];
+    // rescale the context rows 4g+j of each set by their queries' factors,
+    // unless no running maximum of the wave moved (every factor is 1)
+    if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mb = fmaxf(mb, s[kt][j]);
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const float mn = fmaxf(m, mb);
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    float ps = 0.f;
+        for (int j = 0; j < 4; ++j) {
+          const float aj = __shfl(alpha[qs], 4 * g + j);
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s[kt][j] = __builtin_amdgcn_exp2f(s[kt][j] - mn);
-        ps += s[kt][j];
-      }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    l = fmaf(l, alpha, ps);
-    m = mn;
-    // rescale the context rows 4g+j by their queries' factors
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float aj = __shfl(alpha, 4 * g + j);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) acc[dt][j] *= aj;
+          for (int dt = 0; dt < 8; ++dt) acc[qs][dt][j] *= aj;
+        }
     }
     // ---- O += P V over two 32-key steps ----
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      uint4 pu;
-      pu.x = pack_bf16x2(s[2 * kc][0], s[2 * kc][1]);
-      pu.y = pack_bf16x2(s[2 * kc][2], s[2 * kc][3]);
-      pu.z = pack_bf16x2(s[2 * kc + 1][0], s[2 * kc + 1][1]);
-      pu.w = pack_bf16x2(s[2 * kc + 1][2], s[2 * kc + 1][3]);
-      const bf16x8_t pf = as_bf16x8(pu);
+      bf16x8_t pf[2];
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        uint4 pu;
+        pu.x = pack_bf16x2(s[qs][2 * kc][0], s[qs][2 * kc][1]);
+        pu.y = pack_bf16x2(s[qs][2 * kc][2], s[qs][2 * kc][3]);
+        pu.z = pack_bf16x2(s[qs][2 * kc + 1][0], s[qs][2 * kc + 1][1]);
+        pu.w = pack_bf16x2(s[qs][2 * kc + 1][2], s[qs][2 * kc + 1][3]);
+        pf[qs] = as_bf16x8(pu);
+      }
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const uint16_t* row = &sV[(16 * dt + ql) * kVStride + 32 * kc + 4 * g];
-        uint4 vu;
-        const uint2 lo = *reinterpret_cast<const uint2*>(row);
-        const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
-        vu.x = lo.x;
-        vu.y = lo.y;
-        vu.z = hi.x;
-        vu.w = hi.y;
-        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, as_bf16x8(vu), acc[dt], 0, 0, 0);
+        const int dim = 16 * dt + ql;
+        const uint2 lo = *reinterpret_cast<const uint2*>(&sV[vt_index(dim, 32 * kc + 4 * g)]);
+        const uint2 hi =
+            *reinterpret_cast<const uint2*>(&sV[vt_index(dim, 32 * kc + 16 + 4 * g)]);
+        const bf16x8_t vf = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
+        acc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[0], vf, acc[0][dt], 0, 0, 0);
+        acc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[1], vf, acc[1][dt], 0, 0, 0);
       }
     }
   }
 
   if (!wave_active) return;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = wrow0 + 4 * g + j;
-    const float inv = 1.0f / __shfl(l, 4 * g + j);
-    if (row < tile.nq) {
-      float* o = a.out + ((int64_t)(tile.off + tile.i0 + row) * a.num_heads + h) * kD;
+  for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[16 * dt + ql] = acc[dt][j] * inv;
+    for (int j = 0; j < 4; ++j) {
+      const int row = wrow0 + 16 * qs + 4 * g + j;
+      const float inv = 1.0f / __shfl(l[qs], 4 * g + j);
+      if (row < tile.nq) {
+        float* o = a.out + ((int64_t)(tile.off + tile.i0 + row) * a.num_heads + h) * kD;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[16 * dt + ql] = acc[qs][dt][j] * inv;
+      }
     }
-  }
 }
 
 // Writes the chunk's new K/V rows into their slots: one workgroup per (tile,
-// K/V head), 16 bytes per lane.
-template <int ROW_BYTES>
+// K/V head), 16 bytes per lane.  It runs before the attention launch, which
+// reads the chunk's keys back from the pages (4 KiB contiguous per 16 keys
+// of a head, where the packed inputs put consecutive keys H_kv rows apart).
 __global__ __launch_bounds__(256) void prefill_append_kernel(PrefillArgs a) {
   const PrefillTile tile = a.tiles[blockIdx.x];
   const int kvh = blockIdx.y;
   const int S = a.page_size;
   const int32_t* pt = a.page_table + (int64_t)tile.pt_row * a.pt_stride;
-  constexpr int kChunks = ROW_BYTES / 16;
+  constexpr int kChunks = kRowBytes / 16;
   for (int c = threadIdx.x; c < tile.nq * kChunks; c += 256) {
     const int i = tile.i0 + c / kChunks;
     const int col = (c % kChunks) * 16;
     const int pos = tile.start + i;
     const int64_t dst = (int64_t)pt[pos / S] * a.page_bytes + (int64_t)kvh * a.head_bytes +
-                        (int64_t)(pos % S) * ROW_BYTES + col;
-    const int64_t src = ((int64_t)(tile.off + i) * a.num_kv_heads + kvh) * ROW_BYTES + col;
+                        (int64_t)(pos % S) * kRowBytes + col;
+    const int64_t src = ((int64_t)(tile.off + i) * a.num_kv_heads + kvh) * kRowBytes + col;
     *reinterpret_cast<uint4*>(a.k_layer + dst) =
         *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + src);
     *reinterpret_cast<uint4*>(a.v_layer + dst) =
@@ -270,8 +320,8 @@ bool prefill_fast_supported(int dtype, int head_width, int page_size) {
 }
 
 hipError_t launch_prefill_append(const PrefillArgs& a, int num_tiles, hipStream_t stream) {
-  hipLaunchKernelGGL(prefill_append_kernel<kRowBytes>, dim3(num_tiles, a.num_kv_heads), dim3(256),
-                     0, stream, a);
+  hipLaunchKernelGGL(prefill_append_kernel, dim3(num_tiles, a.num_kv_heads), dim3(256), 0, stream,
+                     a);
   return hipGetLastError();
 }
 

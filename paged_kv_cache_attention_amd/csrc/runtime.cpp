@@ -525,10 +525,10 @@ pkv_status check_layer(const pkv_pool* p, int32_t layer) {
   return PKV_OK;
 }
 
-// Matrix-core prefill: the chunks cut into tiles of up to 64 rows, longest
-// visible prefix first; one append launch writes every new row, then one
-// attention launch covers all (tile, query head) pairs.  The tile list is
-// uploaded once and reused by later layers of the same chunks.
+// Matrix-core prefill: the chunks cut into tiles of up to kPrefillTileRows
+// rows, longest visible prefix first; an append launch writes every new row,
+// then one attention launch covers all (tile, query head) pairs.  The tile
+// list is uploaded once and reused by later layers of the same chunks.
 pkv_status run_prefill_tiles(pkv_pool* p, int32_t n, const int32_t* rows, const int32_t* starts,
                              const int32_t* counts, int32_t pt_stride, int32_t layer,
                              const int32_t* page_table, const void* q, const void* k,
