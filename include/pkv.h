@@ -120,6 +120,9 @@ typedef struct pkv_counters {
   uint64_t kv_bytes_read;     /* algorithmic K/V bytes read by attention launches */
   int32_t pages_free;
   int32_t pages_leased;
+  uint64_t cow_copies;        /* shared pages copied before a write            */
+  int32_t pages_shared;       /* pages held by more than one holder now        */
+  int32_t reserved;
 } pkv_counters;
 
 /* Kernel timing of one pool, collected while PKV_OPT_PROFILING is on: HIP
@@ -221,9 +224,29 @@ pkv_status pkv_cache_page_table(const pkv_cache* cache, int32_t* out, int32_t ca
                                 int32_t* n_out);
 
 /* Extends the committed length by n_tokens rows whose K/V bytes the caller
- * writes itself (a bulk prefill writer), leasing the pages they need.
+ * writes itself (a bulk prefill writer), leasing the pages they need.  When
+ * the last page is shared and partly filled, its private copy is made on the
+ * null stream and completed before the call returns.
  * Errors: BAD_STATE (token pending), CAPACITY_EXHAUSTED, OUT_OF_PAGES. */
 pkv_status pkv_cache_grow(pkv_cache* cache, int32_t n_tokens);
+
+/* A new cache that shares the first n_tokens rows of src (0 <= n_tokens <=
+ * its committed length): it holds references to src's first
+ * ceil(n_tokens / page_size) pages instead of copies, and its length is
+ * n_tokens.  Full shared pages are never written again (writes go only to
+ * positions >= length); the first write into a shared, partly filled page
+ * -- by either cache -- first gives the writer a private copy of that page
+ * (every layer's K and V), queued on the stream of the writer's next layer
+ * call (or completed before pkv_cache_grow returns), and abort undoes it.
+ * A page returns to the free list when its last holder lets it go.
+ * ("Incremental Serving", Current scope: paged storage alone does not share
+ * pages between matching prompts or manage prefixes by copy-on-write; this
+ * is that mechanism, with the choice of which prefix to share left to the
+ * caller.)  Errors: BAD_STATE (src has a pending token, or no cache slot is
+ * free), INVALID_ARGUMENT (n_tokens out of range, max_context below
+ * n_tokens or above the pool's). */
+pkv_status pkv_cache_fork(const pkv_cache* src, int32_t n_tokens, int32_t max_context,
+                          pkv_cache** out);
 
 /* --------------------------------------------------- token transaction -- */
 

@@ -71,6 +71,9 @@ class pkv_counters(ctypes.Structure):
         ("kv_bytes_read", ctypes.c_uint64),
         ("pages_free", ctypes.c_int32),
         ("pages_leased", ctypes.c_int32),
+        ("cow_copies", ctypes.c_uint64),
+        ("pages_shared", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -118,6 +121,7 @@ SIGNATURES = {
     "pkv_cache_capacity": (_I32, [_P]),
     "pkv_cache_block_size": (_I32, [_P]),
     "pkv_cache_page_table": (_I32, [_P, _PI32, _I32, _PI32]),
+    "pkv_cache_fork": (_I32, [_P, _I32, _I32, ctypes.POINTER(_P)]),
     "pkv_cache_grow": (_I32, [_P, _I32]),
     "pkv_begin_token": (_I32, [_P, _PI32]),
     "pkv_append_and_attend": (_I32, [_P, _I32, _P, _P, _P, _P, _P]),
@@ -290,6 +294,12 @@ def pkv_cache_page_table(cache: int) -> list:
     n = ctypes.c_int32()
     _check(_lib.pkv_cache_page_table(cache, buf, cap, ctypes.byref(n)), "pkv_cache_page_table")
     return list(buf[:n.value])
+
+
+def pkv_cache_fork(src: int, n_tokens: int, max_context: int) -> int:
+    h = ctypes.c_void_p()
+    _check(_lib.pkv_cache_fork(src, n_tokens, max_context, ctypes.byref(h)), "pkv_cache_fork")
+    return h.value
 
 
 def pkv_cache_grow(cache: int, n_tokens: int) -> None:

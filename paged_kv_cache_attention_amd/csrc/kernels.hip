@@ -646,6 +646,23 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AttnArgs a) {
   }
 }
 
+// One workgroup per (copy, layer, K or V): the page's bytes of that layer.
+// Pages of a multiple of 16 bytes move 16 bytes per lane, others 2.
+__global__ __launch_bounds__(256) void page_copy_kernel(char* k_storage, char* v_storage,
+                                                        int64_t layer_bytes, int64_t page_bytes,
+                                                        CopyBatch b) {
+  char* base = (blockIdx.z == 0 ? k_storage : v_storage) + (int64_t)blockIdx.y * layer_bytes;
+  const char* src = base + (int64_t)b.src[blockIdx.x] * page_bytes;
+  char* dst = base + (int64_t)b.dst[blockIdx.x] * page_bytes;
+  if (page_bytes % 16 == 0) {
+    for (int64_t i = threadIdx.x; i < page_bytes / 16; i += 256)
+      reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(src)[i];
+  } else {
+    for (int64_t i = threadIdx.x; i < page_bytes / 2; i += 256)
+      reinterpret_cast<uint16_t*>(dst)[i] = reinterpret_cast<const uint16_t*>(src)[i];
+  }
+}
+
 __global__ __launch_bounds__(256) void patch_kernel(int32_t* arena, PatchBatch b) {
   const int i = threadIdx.x;
   if (i < b.count) arena[b.offset[i]] = b.value[i];
@@ -724,6 +741,14 @@ hipError_t launch_kv_append(const AttnArgs& a, int dtype, int num_reqs, hipStrea
     hipLaunchKernelGGL(kv_append_kernel<uint16_t>, dim3(num_reqs, a.num_kv_heads), dim3(64), 0,
                        stream, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_page_copies(char* k_storage, char* v_storage, int64_t layer_bytes,
+                              int64_t page_bytes, int32_t num_layers, const CopyBatch& b,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(page_copy_kernel, dim3(b.count, num_layers, 2), dim3(256), 0, stream,
+                     k_storage, v_storage, layer_bytes, page_bytes, b);
   return hipGetLastError();
 }
 

@@ -101,6 +101,16 @@ struct PatchBatch {
   int32_t value[kMax];
 };
 
+// Copy-on-write page copies carried in kernel arguments: every layer's K and
+// V of page src[i] are copied to page dst[i].
+struct CopyBatch {
+  static constexpr int kMax = 120;
+  int32_t count;
+  int32_t pad;
+  int32_t src[kMax];
+  int32_t dst[kMax];
+};
+
 enum class KernelPath { kFast, kGeneric };
 
 // How split requests are merged.
@@ -120,6 +130,9 @@ hipError_t launch_attention(const AttnArgs& a, int dtype, int num_items, hipStre
 hipError_t launch_merge(const AttnArgs& a, int num_split_reqs, hipStream_t stream);
 hipError_t launch_kv_append(const AttnArgs& a, int dtype, int num_reqs, hipStream_t stream);
 hipError_t launch_patches(int32_t* arena, const PatchBatch& b, hipStream_t stream);
+hipError_t launch_page_copies(char* k_storage, char* v_storage, int64_t layer_bytes,
+                              int64_t page_bytes, int32_t num_layers, const CopyBatch& b,
+                              hipStream_t stream);
 bool fast_path_supported(int dtype, int head_width, int page_size, int group);
 
 // Prefill on matrix cores (bf16, head width 128, pages of a multiple of 16

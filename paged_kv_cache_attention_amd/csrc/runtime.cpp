@@ -21,6 +21,7 @@
 #include <limits>
 #include <new>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include <hip/hip_runtime.h>
@@ -115,6 +116,8 @@ struct pkv_cache {
   int32_t pending_pos = 0;        // first reserved position
   int32_t pending_count = 0;      // positions reserved by this begin
   int32_t pending_new_pages = 0;  // pages leased by this begin
+  int32_t cow_logical = -1;       // logical page this begin copied on write, or -1
+  int32_t cow_old = -1;           // the shared page that copy replaced
   std::vector<uint8_t> appended;
   int32_t appended_count = 0;
 };
@@ -125,6 +128,12 @@ struct pkv_pool {
   int64_t head_bytes = 0, page_bytes = 0, layer_bytes = 0;
   std::vector<int32_t> free_stack;  // lease pops from the back
   std::vector<uint8_t> owner;
+  std::vector<int32_t> refs;  // holders per page: caches, a raw lease, and a pending
+                              // transaction's hold on the shared page it copied
+  struct PageCopy {
+    int32_t src, dst;
+  };
+  std::vector<PageCopy> copies;  // copy-on-write copies not yet enqueued
   int32_t raw_leased = 0;
   int32_t live_caches = 0;
   int32_t live_plans = 0;
@@ -158,12 +167,23 @@ int32_t lease_page(pkv_pool* p, uint8_t who) {
   const int32_t page = p->free_stack.back();
   p->free_stack.pop_back();
   p->owner[page] = who;
+  p->refs[page] = 1;
   return page;
 }
 
+// Drops one holder of the page; the last one returns it to the free list.
+// A page that becomes free cancels any copy still queued into it (its
+// destination no longer belongs to anyone).
 void release_page(pkv_pool* p, int32_t page) {
+  if (--p->refs[page] > 0) return;
   p->owner[page] = kFree;
   p->free_stack.push_back(page);
+  for (size_t i = 0; i < p->copies.size();) {
+    if (p->copies[i].dst == page)
+      p->copies.erase(p->copies.begin() + (std::ptrdiff_t)i);
+    else
+      ++i;
+  }
 }
 
 void record_patch(pkv_cache* c, int32_t logical, int32_t page) {
@@ -194,10 +214,49 @@ pkv_status ensure_device(pkv_pool* p) {
   return PKV_OK;
 }
 
+// Enqueues the copy-on-write page copies.  A queued copy's source is held by
+// the pending transaction that made it (or by pkv_cache_grow until the copy
+// is complete), so it stays allocated until the copy has run.
+pkv_status flush_copies(pkv_pool* p, hipStream_t stream) {
+  if (p->copies.empty()) return PKV_OK;
+  if (!p->host_only) {
+    for (size_t i = 0; i < p->copies.size();) {
+      pkv::CopyBatch b{};
+      b.count = 0;
+      for (; i < p->copies.size() && b.count < pkv::CopyBatch::kMax; ++i, ++b.count) {
+        b.src[b.count] = p->copies[i].src;
+        b.dst[b.count] = p->copies[i].dst;
+      }
+      PKV_HIP_TRY(pkv::launch_page_copies(static_cast<char*>(p->desc.k_storage),
+                                          static_cast<char*>(p->desc.v_storage), p->layer_bytes,
+                                          p->page_bytes, p->desc.num_layers, b, stream));
+    }
+  }
+  p->copies.clear();
+  return PKV_OK;
+}
+
 pkv_status flush_patches(pkv_pool* p, hipStream_t stream) {
+  pkv_status st = flush_copies(p, stream);
+  if (st != PKV_OK) return st;
   if (p->host_only) {
     p->patches.clear();
     return PKV_OK;
+  }
+  // One patch per arena entry, the last one recorded: the patch kernel
+  // writes a batch's entries in parallel, so two values for one entry (a
+  // fork's shared page, then its copy on write) would race.
+  if (p->patches.size() > 1) {
+    std::unordered_map<int32_t, size_t> last;
+    last.reserve(p->patches.size());
+    for (size_t j = 0; j < p->patches.size(); ++j) last[p->patches[j].first] = j;
+    if (last.size() < p->patches.size()) {
+      std::vector<std::pair<int32_t, int32_t>> kept;
+      kept.reserve(last.size());
+      for (size_t j = 0; j < p->patches.size(); ++j)
+        if (last[p->patches[j].first] == j) kept.push_back(p->patches[j]);
+      p->patches.swap(kept);
+    }
   }
   size_t i = 0;
   while (i < p->patches.size()) {
@@ -769,6 +828,7 @@ pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out) {
     }
     std::reverse(p->free_stack.begin(), p->free_stack.end());  // first lease = first shuffled ID
     p->owner.assign(d.num_pages, kFree);
+    p->refs.assign(d.num_pages, 0);
     p->free_slots.resize(d.max_caches);
     for (int32_t i = 0; i < d.max_caches; ++i) p->free_slots[i] = d.max_caches - 1 - i;
     p->txn_plan.pool = p;
@@ -815,6 +875,8 @@ pkv_status pkv_pool_get_counters(const pkv_pool* p, pkv_counters* out) {
   *out = p->counters;
   out->pages_free = (int32_t)p->free_stack.size();
   out->pages_leased = p->desc.num_pages - out->pages_free;
+  out->pages_shared = 0;
+  for (int32_t r : p->refs) out->pages_shared += r > 1;
   return ok();
 }
 
@@ -925,6 +987,7 @@ pkv_status pkv_cache_destroy(pkv_cache* c) {
   if (!c) return fail(PKV_ERR_INVALID_ARGUMENT, "null cache");
   pkv_pool* p = c->pool;
   if (c->pending) p->counters.aborted_tokens += (uint64_t)c->pending_count;
+  if (c->pending && c->cow_logical >= 0) release_page(p, c->cow_old);
   cache_return_pages(c);
   p->free_slots.push_back(c->slot);
   p->live_caches -= 1;
@@ -955,6 +1018,9 @@ pkv_status pkv_cache_page_table(const pkv_cache* c, int32_t* out, int32_t cap, i
   return ok();
 }
 
+static bool needs_cow(const pkv_cache* c);
+static int32_t copy_on_write(pkv_cache* c);
+
 pkv_status pkv_cache_grow(pkv_cache* c, int32_t n_tokens) {
   if (!c) return fail(PKV_ERR_INVALID_ARGUMENT, "null cache");
   if (n_tokens < 0) return fail(PKV_ERR_INVALID_ARGUMENT, "negative n_tokens");
@@ -964,9 +1030,22 @@ pkv_status pkv_cache_grow(pkv_cache* c, int32_t n_tokens) {
                 n_tokens, c->max_context);
   pkv_pool* p = c->pool;
   const int32_t S = p->desc.page_size;
+  const bool cow = n_tokens > 0 && needs_cow(c);
   const int32_t need = (c->len + n_tokens + S - 1) / S - (int32_t)c->pages.size();
-  if (need > (int32_t)p->free_stack.size())
-    return fail(PKV_ERR_OUT_OF_PAGES, "need %d pages, %zu free", need, p->free_stack.size());
+  if (need + (cow ? 1 : 0) > (int32_t)p->free_stack.size())
+    return fail(PKV_ERR_OUT_OF_PAGES, "need %d pages, %zu free", need + (cow ? 1 : 0),
+                p->free_stack.size());
+  if (cow) {
+    // The caller writes the grown rows itself right after this call, so the
+    // private copy of the shared last page is complete when it returns.
+    pkv_status st = ensure_device(p);
+    if (st != PKV_OK) return st;
+    const int32_t old = c->pages[c->len / S];
+    copy_on_write(c);
+    if ((st = flush_copies(p, nullptr)) != PKV_OK) return st;
+    if (!p->host_only) PKV_HIP_TRY(hipStreamSynchronize(nullptr));
+    release_page(p, old);
+  }
   for (int32_t i = 0; i < need; ++i) {
     const int32_t page = lease_page(p, kCache);
     record_patch(c, (int32_t)c->pages.size(), page);
@@ -976,10 +1055,38 @@ pkv_status pkv_cache_grow(pkv_cache* c, int32_t n_tokens) {
   return ok();
 }
 
-// Pages a begin of `count` positions must lease for cache c.
+// Whether writing position len of cache c needs a private copy of its last
+// page first: the page is partly filled and shared with another holder.
+static bool needs_cow(const pkv_cache* c) {
+  if (c->len == 0) return false;
+  const int32_t S = c->pool->desc.page_size;
+  return c->len % S != 0 && c->pool->refs[c->pages[c->len / S]] > 1;
+}
+
+// Pages a begin of `count` positions must lease for cache c (a copy-on-write
+// page included).
 static int32_t pages_for(const pkv_cache* c, int32_t count) {
   const int32_t S = c->pool->desc.page_size;
-  return (int32_t)(((int64_t)c->len + count + S - 1) / S - ((int64_t)c->len + S - 1) / S);
+  return (int32_t)(((int64_t)c->len + count + S - 1) / S - ((int64_t)c->len + S - 1) / S) +
+         (needs_cow(c) ? 1 : 0);
+}
+
+// Replaces the shared, partly filled last page of c by a private copy (a new
+// page, its contents queued for copying).  The caller keeps the cache's
+// reference on the old page until the copy can no longer be undone or
+// cancelled (commit or abort of the transaction; grow after the copy ran).
+// Returns the logical page, or -1 when none is needed.
+static int32_t copy_on_write(pkv_cache* c) {
+  if (!needs_cow(c)) return -1;
+  pkv_pool* p = c->pool;
+  const int32_t lp = c->len / p->desc.page_size;
+  const int32_t old = c->pages[lp];
+  const int32_t page = lease_page(p, kCache);
+  p->copies.push_back({old, page});
+  c->pages[lp] = page;
+  record_patch(c, lp, page);
+  p->counters.cow_copies += 1;
+  return lp;
 }
 
 static pkv_status check_begin(const pkv_cache* c, int32_t count, int32_t i) {
@@ -995,7 +1102,10 @@ static pkv_status check_begin(const pkv_cache* c, int32_t count, int32_t i) {
 // that enough pages are free.
 static int32_t begin_unchecked(pkv_cache* c, int32_t count) {
   pkv_pool* p = c->pool;
-  const int32_t need = pages_for(c, count);
+  const bool cow = needs_cow(c);
+  const int32_t need = pages_for(c, count) - (cow ? 1 : 0);
+  c->cow_old = cow ? c->pages[c->len / p->desc.page_size] : -1;
+  c->cow_logical = copy_on_write(c);
   for (int32_t i = 0; i < need; ++i) {
     const int32_t page = lease_page(p, kCache);
     record_patch(c, (int32_t)c->pages.size(), page);
@@ -1008,6 +1118,31 @@ static int32_t begin_unchecked(pkv_cache* c, int32_t count) {
   std::fill(c->appended.begin(), c->appended.end(), 0);
   c->appended_count = 0;
   return c->pending_pos;
+}
+
+pkv_status pkv_cache_fork(const pkv_cache* src, int32_t n_tokens, int32_t max_context,
+                          pkv_cache** out) {
+  if (!src || !out) return fail(PKV_ERR_INVALID_ARGUMENT, "null argument");
+  if (src->pending) return fail(PKV_ERR_BAD_STATE, "fork of a cache with a pending token");
+  if (n_tokens < 0 || n_tokens > src->len)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "n_tokens %d outside [0, %d]", n_tokens, src->len);
+  if (max_context < n_tokens)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "max_context %d below n_tokens %d", max_context,
+                n_tokens);
+  pkv_pool* p = src->pool;
+  pkv_cache* c = nullptr;
+  pkv_status st = pkv_cache_create(p, max_context, &c);
+  if (st != PKV_OK) return st;
+  const int32_t np = (n_tokens + p->desc.page_size - 1) / p->desc.page_size;
+  for (int32_t i = 0; i < np; ++i) {
+    const int32_t page = src->pages[i];
+    p->refs[page] += 1;
+    record_patch(c, i, page);
+    c->pages.push_back(page);
+  }
+  c->len = n_tokens;
+  *out = c;
+  return ok();
 }
 
 pkv_status pkv_begin_tokens(pkv_cache* c, int32_t count, int32_t* position) {
@@ -1107,6 +1242,8 @@ pkv_status pkv_commit_token(pkv_cache* c) {
     p->counters.score_cells += lanes * (uint64_t)(c->pending_pos + i + 1);
   c->len = c->pending_pos + c->pending_count;
   c->pending = false;
+  if (c->cow_logical >= 0) release_page(p, c->cow_old);  // the copy is the cache's now
+  c->cow_logical = c->cow_old = -1;
   p->counters.committed_tokens += (uint64_t)c->pending_count;
   p->counters.cache_appends += (uint64_t)p->desc.num_layers * c->pending_count;
   return ok();
@@ -1115,9 +1252,19 @@ pkv_status pkv_commit_token(pkv_cache* c) {
 pkv_status pkv_abort_token(pkv_cache* c) {
   if (!c) return fail(PKV_ERR_INVALID_ARGUMENT, "null cache");
   if (!c->pending) return fail(PKV_ERR_BAD_STATE, "no pending token");
+  pkv_pool* p = c->pool;
   for (int32_t i = 0; i < c->pending_new_pages; ++i) {
-    release_page(c->pool, c->pages.back());
+    release_page(p, c->pages.back());
     c->pages.pop_back();
+  }
+  if (c->cow_logical >= 0) {
+    // back to the shared page (the transaction's hold on it becomes the
+    // cache's again); the private copy goes, cancelling its copy if queued
+    const int32_t copy = c->pages[c->cow_logical];
+    c->pages[c->cow_logical] = c->cow_old;
+    record_patch(c, c->cow_logical, c->cow_old);
+    release_page(p, copy);
+    c->cow_logical = c->cow_old = -1;
   }
   c->pending = false;
   c->pool->counters.aborted_tokens += (uint64_t)c->pending_count;

@@ -284,6 +284,118 @@ def test_automatic_split_targets_4096_chunks():
     pkv.pkv_pool_destroy(p)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_state_machine_with_forks_matches_oracle_model(seed):
+    """Random begin / chunk / append / commit / abort / reset / grow / fork /
+    destroy on caches that share pages; after every step the library and
+    the model agree on status, length, pages held, free and shared pages."""
+    rnd = random.Random(100 + seed)
+    layers, page, pages, ctx = 2, 4, 24, 28
+    p = make_pool(layers=layers, page=page, pages=pages, ctx=ctx, caches=8)
+    pool_model = oracle.PoolModel(pages)
+    caches = [(pkv.pkv_cache_create(p, ctx), oracle.CacheModel(pool_model, layers, ctx, page))
+              for _ in range(2)]
+    ops = ["begin", "begin_chunk", "append", "commit", "abort", "reset", "grow", "fork",
+           "destroy"]
+    for _ in range(800):
+        i = rnd.randrange(len(caches))
+        c, m = caches[i]
+        op = rnd.choices(ops, weights=[4, 2, 7, 4, 1, 0.3, 1, 1.2, 0.6])[0]
+        if op == "begin":
+            got, want = status_of(pkv.pkv_begin_token, c), m.begin()
+        elif op == "begin_chunk":
+            count = rnd.randrange(1, 7)
+            got, want = status_of(pkv.pkv_begin_tokens, c, count), m.begin(count)
+        elif op == "append":
+            layer = rnd.randrange(layers)
+            got = status_of(pkv.pkv_append_and_attend, c, layer, FAKE, FAKE, FAKE, FAKE, 0)
+            want = m.append(layer)
+        elif op == "commit":
+            got, want = status_of(pkv.pkv_commit_token, c), m.commit()
+        elif op == "abort":
+            got, want = status_of(pkv.pkv_abort_token, c), m.abort()
+        elif op == "reset":
+            got, want = status_of(pkv.pkv_cache_reset, c), m.reset()
+        elif op == "grow":
+            n = rnd.randrange(0, 6)
+            got, want = status_of(pkv.pkv_cache_grow, c, n), m.grow(n)
+        elif op == "fork":
+            if len(caches) >= 8:
+                continue
+            n = rnd.randrange(0, m.length + 2)
+            want, mm = m.fork(n, ctx)
+            try:
+                cc = pkv.pkv_cache_fork(c, n, ctx)
+                got = Status.OK
+                caches.append((cc, mm))
+            except pkv.PkvError as e:
+                got = Status(e.status)
+        else:
+            if len(caches) <= 1:
+                continue
+            got = status_of(pkv.pkv_cache_destroy, c)
+            want = m.destroy()
+            caches.pop(i)
+        assert got == want, (op, got, want)
+        for cc, mm in caches:
+            assert pkv.pkv_cache_size(cc) == mm.length
+            assert len(pkv.pkv_cache_page_table(cc)) == mm.pages_held
+        cnt = pkv.pkv_pool_get_counters(p)
+        assert cnt.pages_free == pool_model.free, op
+        assert cnt.pages_shared == pool_model.shared, op
+    # every cache's table holds distinct pages; shared pages appear in several
+    held = [x for cc, _ in caches for x in pkv.pkv_cache_page_table(cc)]
+    assert all(0 <= x < pages for x in held)
+    # leased pages are the held ones plus shared pages that a pending copy
+    # replaced and no cache holds (counted in the model's page identities)
+    held_model = {x for _, m in caches for x in m.pages}
+    pending_old = {m.pending[4][1] for _, m in caches if m.pending and m.pending[4]}
+    assert len(set(held)) + len(pending_old - held_model) == \
+        pages - pkv.pkv_pool_get_counters(p).pages_free
+    for cc, _ in caches:
+        status_of(pkv.pkv_abort_token, cc)       # drop a pending token, if any
+        pkv.pkv_cache_destroy(cc)
+    assert pkv.pkv_pool_get_counters(p).pages_free == pages
+    pkv.pkv_pool_destroy(p)
+
+
+def test_fork_rejections_and_copy_on_write_accounting():
+    p = make_pool(layers=2, page=4, pages=10, ctx=24)
+    a = pkv.pkv_cache_create(p, 24)
+    pkv.pkv_cache_grow(a, 10)                                       # 3 pages, last holds 2 rows
+    assert status_of(pkv.pkv_cache_fork, a, 11, 24) == Status.INVALID_ARGUMENT
+    assert status_of(pkv.pkv_cache_fork, a, 8, 7) == Status.INVALID_ARGUMENT
+    pkv.pkv_begin_token(a)
+    assert status_of(pkv.pkv_cache_fork, a, 4, 24) == Status.BAD_STATE
+    pkv.pkv_abort_token(a)
+    b = pkv.pkv_cache_fork(a, 9, 24)                                # shares all 3 pages
+    ta, tb = pkv.pkv_cache_page_table(a), pkv.pkv_cache_page_table(b)
+    assert tb == ta and pkv.pkv_cache_size(b) == 9
+    cnt = pkv.pkv_pool_get_counters(p)
+    assert cnt.pages_shared == 3 and cnt.pages_free == 7
+    # b writes position 9 inside the shared third page: private copy
+    assert pkv.pkv_begin_token(b) == 9
+    tb2 = pkv.pkv_cache_page_table(b)
+    assert tb2[:2] == ta[:2] and tb2[2] not in ta
+    cnt = pkv.pkv_pool_get_counters(p)
+    assert cnt.cow_copies == 1 and cnt.pages_free == 6
+    pkv.pkv_abort_token(b)                                          # undone
+    assert pkv.pkv_cache_page_table(b) == ta and pkv.pkv_pool_get_counters(p).pages_free == 7
+    # a writes position 10: a copies (b still holds the shared page)
+    pkv.pkv_begin_token(a)
+    for layer in range(2):
+        pkv.pkv_append_and_attend(a, layer, FAKE, FAKE, FAKE, FAKE, stream=0)
+    pkv.pkv_commit_token(a)
+    assert pkv.pkv_cache_page_table(a)[2] != ta[2] and pkv.pkv_cache_page_table(b)[2] == ta[2]
+    cnt = pkv.pkv_pool_get_counters(p)
+    assert cnt.pages_shared == 2 and cnt.pages_free == 6
+    pkv.pkv_cache_destroy(a)
+    assert pkv.pkv_pool_get_counters(p).pages_free == 7             # b keeps its 3 pages
+    pkv.pkv_cache_destroy(b)
+    assert pkv.pkv_pool_get_counters(p).pages_free == 10
+    pkv.pkv_pool_destroy(p)
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_state_machine_matches_oracle_model(seed):
     rnd = random.Random(seed)

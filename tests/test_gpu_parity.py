@@ -542,6 +542,90 @@ def test_prefill32_bf16_full_sampled():
     pkv.pkv_pool_destroy(pool)
 
 
+# --------------------------------------------- prefix sharing, copy on write --
+@pytest.mark.parametrize("dtype,D,H,Hkv", [("f32", 64, 2, 2), ("bf16", 128, 4, 2),
+                                           ("f32", 40, 3, 3)])
+def test_forked_caches_share_prefix_and_copy_on_write(dtype, D, H, Hkv):
+    """A holds 37 rows; B forks at 21 (inside a page), C at 32 (a page
+    boundary).  One token on each: B's write copies the shared page, C
+    leases a new one, A is untouched; every context matches the oracle over
+    the shared prefix plus the cache's own row.  Then an aborted copy whose
+    shared page lost its other holders, and a grow into a shared page."""
+    S, L = 16, 2
+    w = _small(f"fork_{dtype}_{D}", dtype, D, S, [40], heads=H, kv_heads=Hkv, layers=L,
+               seed=47, extra_pages=40)
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp, seed=3, max_caches=8, max_context=256, merge=2)
+    A = pkv.pkv_cache_create(pool, 256)
+    pkv.pkv_cache_grow(A, 37)
+    tA = pkv.pkv_cache_page_table(A)
+    B = pkv.pkv_cache_fork(A, 21, 256)
+    C = pkv.pkv_cache_fork(A, 32, 256)
+    assert pkv.pkv_cache_page_table(B) == tA[:2] and pkv.pkv_cache_page_table(C) == tA[:2]
+    kA_before = kp[:, tA[1]].clone()
+    caches, starts = [A, B, C], [37, 21, 32]
+    assert pkv.pkv_begin_token_batched(caches) == starts
+    tB, tC = pkv.pkv_cache_page_table(B), pkv.pkv_cache_page_table(C)
+    assert tB[0] == tA[0] and tB[1] not in tA                      # B copied page 1
+    assert tC[:2] == tA[:2] and tC[2] not in tA                    # C leased page 2
+    assert pkv.pkv_pool_get_counters(pool).cow_copies == 1
+    outs = []
+    for layer in range(L):
+        qh, kh, vh = _chunk_rows(w, layer, 3)
+        q, k, v = (rows_to_device(x, dtype) for x in (qh, kh, vh))
+        out = torch.empty((3, H, D), device="cuda")
+        pkv.pkv_append_and_attend_batched(caches, layer, q, k, v, out)
+        outs.append((qh, kh, vh, out))
+    torch.cuda.synchronize()
+    pkv.pkv_commit_token_batched(caches)
+    for layer, (qh, kh, vh, out) in enumerate(outs):
+        kpg, vpg = HostPages(w, "k", layer), HostPages(w, "v", layer)
+        for r, st in enumerate(starts):
+            ref = oracle.append_and_attend(qh[r], kh[r], vh[r], kpg, vpg, tA, st, S)
+            assert max_err(out[r], ref) <= TOL[dtype], (layer, r)
+        # B's copy: A's rows 16..20 bit-exact in every layer, then B's own row
+        assert torch.equal(kp[layer, tB[1], :, :5], kA_before[layer, :, :5])
+        assert np.array_equal(to_bits(kp[layer, tB[1], :, 5], dtype), kh[1])
+    assert torch.equal(kp[:, tA[1]], kA_before)                    # A's page untouched
+    # D forks at 21 and writes (its copy is enqueued at its first layer call);
+    # every other holder of the shared page then lets it go; D aborts back to
+    # that page, which its transaction kept alive, and retries.
+    Dc = pkv.pkv_cache_fork(A, 21, 256)
+    assert pkv.pkv_begin_token(Dc) == 21
+    qh, kh, vh = _chunk_rows(w, 0, 1, step=1)
+    out = torch.empty((1, H, D), device="cuda")
+    pkv.pkv_append_and_attend(Dc, 0, rows_to_device(qh, dtype), rows_to_device(kh, dtype),
+                              rows_to_device(vh, dtype), out)
+    torch.cuda.synchronize()
+    for c in (A, C):
+        pkv.pkv_cache_destroy(c)
+    pkv.pkv_abort_token(Dc)
+    assert pkv.pkv_cache_page_table(Dc) == tA[:2]
+    assert pkv.pkv_begin_token(Dc) == 21                           # sole holder: no copy
+    assert pkv.pkv_cache_page_table(Dc) == tA[:2]
+    for layer in range(L):
+        qh, kh, vh = _chunk_rows(w, layer, 1, step=2)
+        out = torch.empty((1, H, D), device="cuda")
+        pkv.pkv_append_and_attend(Dc, layer, rows_to_device(qh, dtype),
+                                  rows_to_device(kh, dtype), rows_to_device(vh, dtype), out)
+        torch.cuda.synchronize()
+        ref = oracle.append_and_attend(qh[0], kh[0], vh[0], HostPages(w, "k", layer),
+                                       HostPages(w, "v", layer), tA, 21, S)
+        assert max_err(out[0], ref) <= TOL[dtype], layer
+    pkv.pkv_commit_token(Dc)
+    # grow into a shared partly filled page: the copy is complete on return
+    E = pkv.pkv_cache_fork(Dc, 22, 256)
+    pkv.pkv_cache_grow(E, 3)
+    tE = pkv.pkv_cache_page_table(E)
+    assert tE[0] == tA[0] and tE[1] != tA[1]
+    assert torch.equal(kp[:, tE[1], :, :6], kp[:, tA[1], :, :6])
+    assert torch.equal(vp[:, tE[1], :, :6], vp[:, tA[1], :, :6])
+    for c in (B, Dc, E):
+        pkv.pkv_cache_destroy(c)
+    assert pkv.pkv_pool_get_counters(pool).pages_free == w.num_pages
+    pkv.pkv_pool_destroy(pool)
+
+
 @pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128), ("f32", 24)])
 @pytest.mark.parametrize("merge", MERGES)
 def test_page_table_permutation_is_bit_identical(dtype, D, merge):
