@@ -33,30 +33,37 @@ import time
 
 HBM_PEAK_GBS = 8000.0
 
-# Calibrated HBM traffic per attention launch from rocprofv3 PMC runs:
-# FETCH_SIZE and WRITE_SIZE in KiB per dispatch, scaled by what the same
-# counters read for one kernel that reads and writes exactly 1 GiB
-# (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000 on MI355X).  Valid only for the
-# kernel source they were taken from (sha256 prefix of csrc/kernels.hip).
+# Calibrated HBM traffic per launch of each workload's dominant kernel from
+# rocprofv3 PMC runs: FETCH_SIZE and WRITE_SIZE in KiB per dispatch, scaled
+# by what the same counters read for one kernel that reads and writes
+# exactly 1 GiB (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000 on MI355X).  Valid
+# only for the kernel source they were taken from (sha256 prefix of that
+# file under csrc/).
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
-    "batch32_fp32_l12": {"kernels_sha256_16": "ff5f18c9fa6b6ceb",
-                         "fetch_kib": 44691.9, "write_kib": 2008.4,
+    "batch32_fp32_l12": {"source": "kernels.hip", "sha256_16": "f021c5e38f8e1620",
+                         "fetch_kib": 44681.4, "write_kib": 2008.5,
                          "algorithmic_bytes": 88971264},
+    "batch256_bf16": {"source": "kernels.hip", "sha256_16": "f021c5e38f8e1620",
+                      "fetch_kib": 4761676.0, "write_kib": 4415.1,
+                      "algorithmic_bytes": 9718775808},
+    "prefill32_bf16": {"source": "prefill.hip", "sha256_16": "103892798313250f",
+                       "fetch_kib": 725500.4, "write_kib": 518320.1,
+                       "algorithmic_bytes": 1854562304},
 }
 
 
 def measured_traffic(workload: str):
-    """(HBM bytes per attention launch, algorithmic bytes of the same
-    launches) from the PMC runs, or (None, None) if the kernel changed."""
+    """(HBM bytes per launch, algorithmic bytes of the same launches) from
+    the PMC runs, or (None, None) if the kernel source changed since."""
     import hashlib
     m = MEASURED_TRAFFIC.get(workload)
     if m is None:
         return None, None
     src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_attention_amd",
-                       "csrc", "kernels.hip")
+                       "csrc", m["source"])
     with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest()[:16] != m["kernels_sha256_16"]:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != m["sha256_16"]:
             return None, None
     return (int((m["fetch_kib"] * FETCH_SCALE + m["write_kib"] * WRITE_SCALE) * 1024),
             m["algorithmic_bytes"])
@@ -105,6 +112,14 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
 
+    if args.calibrate_copy:
+        # one elementwise kernel that reads 1 GiB and writes 1 GiB
+        src = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     if args.workload == "tiny":
         return tiny_latency(args)
     if args.workload.startswith("prefill"):
@@ -117,14 +132,6 @@ def main():
     H, D, L, n = w.heads, w.head_width, w.layers, w.n
     Hkv = w.hkv
     elt = w.elt
-
-    if args.calibrate_copy:
-        # one elementwise kernel that reads 1 GiB and writes 1 GiB
-        src = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
 
     # ---- pool and inputs, filled on the device by the seeded generator ----
     shape = (L, w.num_pages, Hkv, w.page_size, D)
@@ -354,6 +361,7 @@ def prefill_bench(args, w):
         torch.cuda.synchronize()
         pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_PROFILING, 0)
         prof = pkv.pkv_pool_get_profile(pool, reset=True)
+    traffic, traffic_alg = measured_traffic(w.name)
     launches = prof.prefill_launches if prof else 0
     avg_s = prof.prefill_ms / max(1, launches) / 1e3 if prof else 0.0
     achieved = (prof.prefill_flops / max(1, launches)) / avg_s / 1e12 if avg_s > 0 else 0.0
@@ -386,7 +394,8 @@ def prefill_bench(args, w):
             "avg_launch_us": round(avg_s * 1e6, 2),
             "flops_per_launch": int(prof.prefill_flops / max(1, launches)) if prof else 0,
             "launches_timed": int(launches),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_run_algorithmic_bytes": traffic_alg,
         },
     }
     if not args.no_cpu_baseline:

@@ -84,10 +84,10 @@ struct PrefillArgs {
   const int32_t* page_table;
   int64_t pt_stride;
   const PrefillTile* tiles;
+  int32_t num_tiles;
   int32_t num_heads;
   int32_t num_kv_heads;
   int32_t page_size;
-  int32_t pad;
   int64_t page_bytes;
   int64_t head_bytes;
   float scale_log2e;

@@ -29,6 +29,7 @@ static_assert(kPrefillTileRows == 128, "four waves of 32 query rows");
 constexpr int kBlockKeys = 64;     // keys per LDS block
 constexpr int kKStride = kD + 8;   // bf16 per K row in LDS (272 B: rows 4 banks apart)
 constexpr int kVStride = kBlockKeys + 4;  // bf16 per transposed V row in LDS (136 B)
+constexpr int kXcds = 8;           // accelerator complex dies of an MI355X
 
 __device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
@@ -76,8 +77,16 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[kBlockKeys * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t sV[kD * kVStride];
 
-  const PrefillTile tile = a.tiles[blockIdx.x];
-  const int h = blockIdx.y;
+  // Work item (query head, tile): consecutive items share a request's K/V
+  // (the tile list is grouped by request).  Workgroups go to the eight XCDs
+  // round-robin, each with its own L2, so each XCD gets a contiguous range of
+  // items: tiles that re-read the same K/V rows then share one L2.
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int per = nwg / kXcds, rem = nwg % kXcds;
+  const int item = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  const int h = item / a.num_tiles;
+  const PrefillTile tile = a.tiles[item - h * a.num_tiles];
   const int kvh = h / (a.num_heads / a.num_kv_heads);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -326,7 +335,7 @@ hipError_t launch_prefill_append(const PrefillArgs& a, int num_tiles, hipStream_
 }
 
 hipError_t launch_prefill_attention(const PrefillArgs& a, int num_tiles, hipStream_t stream) {
-  hipLaunchKernelGGL(prefill_mfma_kernel, dim3(num_tiles, a.num_heads), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(prefill_mfma_kernel, dim3(num_tiles * a.num_heads), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

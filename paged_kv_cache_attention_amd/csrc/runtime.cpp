@@ -603,18 +603,27 @@ pkv_status run_prefill_tiles(pkv_pool* p, int32_t n, const int32_t* rows, const 
     key[4 + 3 * r] = counts[r];
   }
   if (!(pl->built && key == pl->key)) {
-    std::vector<PrefillTile> tiles;
+    // Tiles grouped by request (they re-read the request's K/V), requests
+    // with the longest visible prefix first, each request's longest tile
+    // first.
+    std::vector<int32_t> order(n), offs(n);
     int32_t off = 0;
     for (int32_t r = 0; r < n; ++r) {
-      for (int32_t i0 = 0; i0 < counts[r]; i0 += pkv::kPrefillTileRows) {
-        const int32_t nq = std::min(pkv::kPrefillTileRows, counts[r] - i0);
-        tiles.push_back(PrefillTile{rows[r], starts[r], off, i0, nq, starts[r] + i0 + nq});
-      }
+      order[r] = r;
+      offs[r] = off;
       off += counts[r];
     }
-    std::stable_sort(tiles.begin(), tiles.end(), [](const PrefillTile& x, const PrefillTile& y) {
-      return x.key_end > y.key_end;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+      return starts[x] + counts[x] > starts[y] + counts[y];
     });
+    std::vector<PrefillTile> tiles;
+    for (int32_t r : order) {
+      const int32_t last = (counts[r] - 1) / pkv::kPrefillTileRows * pkv::kPrefillTileRows;
+      for (int32_t i0 = last; i0 >= 0; i0 -= pkv::kPrefillTileRows) {
+        const int32_t nq = std::min(pkv::kPrefillTileRows, counts[r] - i0);
+        tiles.push_back(PrefillTile{rows[r], starts[r], offs[r], i0, nq, starts[r] + i0 + nq});
+      }
+    }
     pkv_status st = ensure_device(p);
     if (st != PKV_OK) return st;
     const MetaPart part{tiles.data(), tiles.size() * sizeof(PrefillTile)};
@@ -635,6 +644,7 @@ pkv_status run_prefill_tiles(pkv_pool* p, int32_t n, const int32_t* rows, const 
   a.page_table = page_table;
   a.pt_stride = pt_stride;
   a.tiles = reinterpret_cast<const PrefillTile*>(pl->d_meta);
+  a.num_tiles = pl->num_items;
   a.num_heads = p->desc.num_heads;
   a.num_kv_heads = p->desc.num_kv_heads;
   a.page_size = p->desc.page_size;
