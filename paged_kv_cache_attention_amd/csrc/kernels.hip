@@ -520,6 +520,317 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Grouped K/V heads on matrix cores: bf16, d_h = 128, pages of a multiple of
+// 16 rows, G = 4, 8 or 16 query heads per K/V head.  With G query heads
+// reading every K/V row, the score and value products of a 16-row block are
+// small dense contractions (G x 128 by 128 x 16, G x 16 by 16 x 128), so
+// they run on MFMA and the vector ALUs keep only the softmax.
+//
+// Workgroup = 4 waves on one (chunk, K/V head); wave w takes blocks w, w+4,
+// ... of the chunk, for all G heads (rows of the MFMA tiles; G < 16 pads with
+// repeats of the last head, whose results are dropped).  Per block:
+//   S^T = K Q^T on 16x16x32 MFMA: A = 16 keys x 32 dims of K, straight from
+//     memory (lane l: key l%16, dims 8(l/16)..+7 of a 32-dim slice); B = the
+//     G query rows held in registers.  Lane l gets, for head row l%16, the
+//     scores of keys 4(l/16)..4(l/16)+3.
+//   O^T += V^T P^T on 16x16x16 MFMA: B = P^T is exactly that score layout;
+//     A = 16 dims x 16 keys of V^T, staged transposed in the wave's own LDS
+//     region (a lane loads 4 keys x 8 dims and stores 8 dims x 4 keys).
+//     Lane l accumulates, for head row l%16, dims 16 dt + 4(l/16)..+3, so the
+//     online-softmax rescale never leaves the lane.
+// Waves run independently until the end, then combine through LDS; each wave
+// publishes a quarter of the G heads (finish_heads: the contexts, or split-K
+// partials and the last-arriver merge, all heads of a wave at once).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ inline uint32_t word_of(const uint4& u, int i) {
+  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+}
+
+// Ends one chunk for NH heads of a wave at once (lanes 0..15 hold columns
+// col0..col0+7 of each head's context).  Unsplit requests write contexts;
+// split ones store all NH partials, order them with one wait, publish them
+// with NH counter increments issued back to back, and merge each head whose
+// last partial this chunk was -- one memory round trip per step instead of
+// one per head.
+template <int NH>
+__device__ void finish_heads(const AttnArgs& a, const WorkItem& it, const ReqEntry& rq,
+                             const int* heads, int lane, int col0, const float* m,
+                             const float* l, const float (*o)[8]) {
+  const int D = a.head_width;
+  const int H = a.num_heads;
+  const bool own = lane < 16;
+  if (rq.nsplit == 1) {
+#pragma unroll
+    for (int k = 0; k < NH; ++k) {
+      const float inv = 1.0f / l[k];
+      float* out = a.out + ((int64_t)it.req * H + heads[k]) * D + col0;
+      if (own) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = o[k][e] * inv;
+      }
+    }
+    return;
+  }
+  const bool coherent = a.merge_mode != kMergeSeparate;
+#pragma unroll
+  for (int k = 0; k < NH; ++k) {
+    float* part = a.partials + ((int64_t)(rq.partial_base + it.split) * H + heads[k]) * (D + 2);
+    if (own) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (coherent)
+          store_part(part + 2 + col0 + e, o[k][e]);
+        else
+          part[2 + col0 + e] = o[k][e];
+      }
+    }
+    if (lane == 0) {
+      if (coherent) {
+        store_part(part, m[k]);
+        store_part(part + 1, l[k]);
+      } else {
+        part[0] = m[k];
+        part[1] = l[k];
+      }
+    }
+  }
+  if (!coherent) return;
+  // As in finish_chunk: agent-scope stores, then wait for every outstanding
+  // memory operation before the counter increments that publish them.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  int prev[NH];
+#pragma unroll
+  for (int k = 0; k < NH; ++k) {
+    prev[k] = 0;
+    if (lane == 0)
+      prev[k] = __hip_atomic_fetch_add(a.merge_count + (int64_t)it.req * H + heads[k], 1,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int k = 0; k < NH; ++k) {
+    if (__shfl(prev[k], 0) != rq.nsplit - 1) continue;
+    if (lane == 0)
+      (void)__hip_atomic_exchange(a.merge_count + (int64_t)it.req * H + heads[k], 0,
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    merge_wave<2, true>(a, it.req, rq, heads[k], lane);
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void attend_group_mfma_kernel(AttnArgs a) {
+  constexpr int D = 128;
+  constexpr int ROW_BYTES = D * 2;
+  constexpr int VT_STRIDE = 20;  // bf16 per V^T row (40 B: 16 rows of a read on distinct banks)
+  static_assert(G == 4 || G == 8 || G == 16, "groups of 4, 8 or 16 heads");
+  // Per wave: the final partial context [16 rows][D]; while blocks stream,
+  // its first 128 * VT_STRIDE bf16 hold the wave's V^T staging.
+  __shared__ __attribute__((aligned(16))) float s_acc[4][16][D];
+  __shared__ float s_m[4][16], s_l[4][16];
+
+  const WorkItem it = a.items[blockIdx.x];
+  const ReqEntry rq = it.rq;
+  const int kvh = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ql = lane & 15;
+  const int g = lane >> 4;
+  const int t = rq.seq_len;
+  const int S = a.page_size;
+  const const_i32_ptr pt = as_const(a.page_table + (int64_t)rq.pt_row * a.pt_stride);
+  const int64_t head_off = (int64_t)kvh * a.head_bytes;
+  const int last_blk = (t - 1) / kBlockRows;
+  const bool fused = a.fuse_append != 0 && it.blk_end > last_blk;
+  const int64_t kvrow = ((int64_t)it.req * a.num_kv_heads + kvh) * ROW_BYTES;
+  uint16_t* vt = reinterpret_cast<uint16_t*>(&s_acc[wave][0][0]);
+
+  bf16x8_t qf[4];
+  {
+    const int64_t qrow = ((int64_t)it.req * a.num_heads + kvh * G + min(ql, G - 1)) * ROW_BYTES;
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc)
+      qf[dc] = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + qrow +
+                                                    (4 * dc + g) * 16));
+  }
+  if (fused && wave == 0 && lane < 16) {
+    const int pos = t - 1;
+    const int64_t slot = (int64_t)pt[pos / S] * a.page_bytes + head_off +
+                         (int64_t)(pos % S) * ROW_BYTES + lane * 16;
+    *reinterpret_cast<uint4*>(a.k_layer + slot) =
+        *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + kvrow + lane * 16);
+    *reinterpret_cast<uint4*>(a.v_layer + slot) =
+        *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + kvrow + lane * 16);
+  }
+
+  // K: lane (key ql, dims 32 dc + 8 g); V: lane (keys 4 g + i, dims 8 ql..+7).
+  auto load_block = [&](int b, uint4* kk, uint4* vv) {
+    const int row0 = b * kBlockRows;
+    const int64_t base = (int64_t)pt[row0 / S] * a.page_bytes + head_off +
+                         (int64_t)(row0 % S) * ROW_BYTES;
+    const auto rk = block_rsrc(a.k_layer + base, kBlockRows * ROW_BYTES);
+    const auto rv = block_rsrc(a.v_layer + base, kBlockRows * ROW_BYTES);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kk[i] = load_b128(rk, (uint32_t)(ql * ROW_BYTES + (4 * i + g) * 16));
+      vv[i] = load_b128(rv, (uint32_t)((4 * g + i) * ROW_BYTES + ql * 16));
+    }
+  };
+
+  float m = -INFINITY, l = 0.f;
+  f32x4_t acc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](int b, uint4* kk, uint4* vv, auto edge_tag) {
+    constexpr bool edge = decltype(edge_tag)::value;
+    float valid_k[4];
+    if constexpr (edge) {
+      // The request's last block: keys >= t are masked and their V rows
+      // zeroed (stale bytes may be anything); with a fused append, key t-1
+      // comes from the inputs.
+      const int row0 = b * kBlockRows;
+      if (fused && row0 + ql == t - 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          kk[i] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + kvrow +
+                                                  (4 * i + g) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = row0 + 4 * g + i;
+        if (fused && key == t - 1)
+          vv[i] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + kvrow +
+                                                  ql * 16);
+        if (key >= t) vv[i] = make_uint4(0, 0, 0, 0);
+        valid_k[i] = key < t ? 0.f : -INFINITY;
+      }
+    }
+    // V^T into this wave's LDS: 8 dims x 4 keys per lane, one 8-byte store per dim
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1;
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+      uint2 x;
+      x.x = __builtin_amdgcn_perm(word_of(vv[1], w), word_of(vv[0], w), sel);
+      x.y = __builtin_amdgcn_perm(word_of(vv[3], w), word_of(vv[2], w), sel);
+      *reinterpret_cast<uint2*>(&vt[(8 * ql + e) * VT_STRIDE + 4 * g]) = x;
+    }
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[dc]), qf[dc], c,
+                                                   0, 0, 0);
+    float sc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sc[j] = c[j];
+      if constexpr (edge) sc[j] += valid_k[j];
+    }
+    float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const float mn = fmaxf(m, mb * a.scale_log2e);
+    const float alpha = fast_exp2(m - mn);
+    float p[4], ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = fast_exp2(fmaf(sc[j], a.scale_log2e, -mn));
+      ps += p[j];
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l = fmaf(l, alpha, ps);
+    m = mn;
+    if (alpha != 1.f) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
+    }
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    bf16x4_t pb4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pb4[j] = (__bf16)p[j];
+    const s16x4_t pb = __builtin_bit_cast(s16x4_t, pb4);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint2 v2 = *reinterpret_cast<const uint2*>(&vt[(16 * dt + ql) * VT_STRIDE + 4 * g]);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, v2), pb,
+                                                          acc[dt], 0, 0, 0);
+    }
+  };
+
+  {
+    const int end = it.blk_end;
+    const int first = it.blk_begin + wave;
+    if (first < end) {
+      const int wave_last = first + ((end - 1 - first) / 4) * 4;
+      uint4 ka[4], va[4], kb[4], vb[4];
+      load_block(first, ka, va);
+      for (int b = first;; b += 8) {
+        const int b1 = min(b + 4, wave_last);
+        load_block(b1, kb, vb);
+        if (b == last_blk)
+          step(b, ka, va, std::true_type{});
+        else
+          step(b, ka, va, std::false_type{});
+        if (b + 4 > wave_last) break;
+        const int b2 = min(b + 8, wave_last);
+        load_block(b2, ka, va);
+        if (b1 == last_blk)
+          step(b1, kb, vb, std::true_type{});
+        else
+          step(b1, kb, vb, std::false_type{});
+        if (b + 8 > wave_last) break;
+      }
+    }
+  }
+
+  // Combine the four waves through LDS (each wave's V^T staging is done: its
+  // LDS operations complete in order), then each wave publishes heads
+  // wave, wave + 4, ...
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s_acc[wave][ql][16 * dt + 4 * g + j] = acc[dt][j];
+  if (g == 0) {
+    s_m[wave][ql] = m;
+    s_l[wave][ql] = l;
+  }
+  __syncthreads();
+  constexpr int NH = G / 4;
+  const int c0 = (lane & 15) * 8;
+  int heads[NH];
+  float hm[NH], hl[NH], ho[NH][8];
+#pragma unroll
+  for (int k = 0; k < NH; ++k) {
+    const int r = wave + 4 * k;
+    heads[k] = kvh * G + r;
+    float mx = s_m[0][r];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) mx = fmaxf(mx, s_m[w][r]);
+    float wt[4], lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wt[w] = s_m[w][r] == -INFINITY ? 0.f : fast_exp2(s_m[w][r] - mx);
+      lsum = fmaf(s_l[w][r], wt[w], lsum);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) x = fmaf(s_acc[w][r][c0 + e], wt[w], x);
+      ho[k][e] = x;
+    }
+    hm[k] = mx;
+    hl[k] = lsum;
+  }
+  finish_heads<NH>(a, it, rq, heads, lane, c0, hm, hl, ho);
+}
+
+// ---------------------------------------------------------------------------
 // Generic path: any head width up to 1024, any page size, any query-head
 // group size.  One wave per (chunk, query head), reading its group's K/V
 // head.  Tiles of 64 rows: lane j scores row j of the tile, the wave
@@ -708,6 +1019,11 @@ hipError_t launch_generic(const AttnArgs& a, int num_items, hipStream_t stream) 
 
 }  // namespace
 
+bool group_mfma_supported(int dtype, int head_width, int page_size, int group) {
+  return dtype == kDtypeBF16 && head_width == 128 && page_size % kBlockRows == 0 &&
+         (group == 4 || group == 8 || group == 16);
+}
+
 bool fast_path_supported(int dtype, int head_width, int page_size, int group) {
   if (page_size % kBlockRows != 0) return false;
   if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return false;
@@ -718,8 +1034,26 @@ bool fast_path_supported(int dtype, int head_width, int page_size, int group) {
 
 hipError_t launch_attention(const AttnArgs& a, int dtype, int num_items, hipStream_t stream,
                             KernelPath* path_out) {
-  const bool fast = fast_path_supported(dtype, a.head_width, a.page_size,
-                                        a.num_heads / a.num_kv_heads);
+  const int group = a.num_heads / a.num_kv_heads;
+  if (group_mfma_supported(dtype, a.head_width, a.page_size, group)) {
+    if (path_out) *path_out = KernelPath::kFast;
+    switch (group) {
+      case 4:
+        hipLaunchKernelGGL(attend_group_mfma_kernel<4>, dim3(num_items, a.num_kv_heads), dim3(256),
+                           0, stream, a);
+        break;
+      case 8:
+        hipLaunchKernelGGL(attend_group_mfma_kernel<8>, dim3(num_items, a.num_kv_heads), dim3(256),
+                           0, stream, a);
+        break;
+      default:
+        hipLaunchKernelGGL(attend_group_mfma_kernel<16>, dim3(num_items, a.num_kv_heads),
+                           dim3(256), 0, stream, a);
+        break;
+    }
+    return hipGetLastError();
+  }
+  const bool fast = fast_path_supported(dtype, a.head_width, a.page_size, group);
   if (path_out) *path_out = fast ? KernelPath::kFast : KernelPath::kGeneric;
   if (fast)
     return dtype == kDtypeF32 ? launch_fast<float, 64>(a, num_items, stream)

@@ -276,8 +276,8 @@ pkv_status flush_patches(pkv_pool* p, hipStream_t stream) {
 //
 // Workgroups have four waves unless PKV_OPT_WAVES asks for eight (measured
 // on MI355X: eight-wave workgroups were not faster on any workload here).
-// Requests split into chunks sized for about kTargetChunks (chunk, head)
-// workgroups -- four resident rounds of 256 CUs x 4 workgroups -- so a batch
+// Requests split into chunks sized for about kTargetChunks (chunk, query
+// head) units -- four resident rounds of 256 CUs x 4 workgroups -- so a batch
 // with few (request, head) pairs still fills the GPU and one long context
 // does not serialise on one workgroup; a batch that already has that many
 // pairs is not split.
@@ -287,13 +287,11 @@ struct SplitChoice {
 };
 
 SplitChoice choose_split(const pkv_pool* p, int64_t total_blocks) {
-  // Workgroups per chunk: one per K/V head on the fast path, one per query
-  // head on the generic path.
-  const int64_t H = pkv::fast_path_supported(p->desc.kv_dtype, p->desc.head_width,
-                                             p->desc.page_size,
-                                             p->desc.num_heads / p->desc.num_kv_heads)
-                        ? p->desc.num_kv_heads
-                        : p->desc.num_heads;
+  // Work is counted in (block, query head) units: a workgroup serving a K/V
+  // head does the work of its whole group, so grouped heads split like the
+  // multi-head case (measured: splitting them further only adds partial
+  // publishes).
+  const int64_t H = p->desc.num_heads;
   const int32_t waves = p->waves_option ? p->waves_option : 4;
   if (p->desc.split_blocks > 0) return {p->desc.split_blocks, waves};
   if (p->desc.split_blocks < 0) return {std::numeric_limits<int32_t>::max(), waves};

@@ -284,6 +284,23 @@ def test_automatic_split_targets_4096_chunks():
     pkv.pkv_pool_destroy(p)
 
 
+def test_split_counts_query_heads_of_grouped_pools():
+    # 8 query heads sharing 2 K/V heads: 64 requests of 512 blocks are
+    # 262144 (block, query head) units -> 64-block chunks, 8 per request
+    # (counting K/V heads would give 65536 units and 16-block chunks).
+    d = pkv.pkv_pool_desc_init()
+    d.num_layers, d.num_heads, d.num_kv_heads, d.head_width = 1, 8, 2, 128
+    d.max_context, d.num_pages, d.kv_dtype = 16 * 1024, 8, pkv.PKV_DTYPE_BF16
+    d.flags = pkv.PKV_POOL_HOST_ONLY
+    d.k_storage = d.v_storage = FAKE
+    p = pkv.pkv_pool_create(d)
+    plan = pkv.pkv_plan_create(p)
+    pkv.pkv_plan_build(plan, [16 * 512] * 64, 1024, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 64 * 8
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(p)
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_state_machine_with_forks_matches_oracle_model(seed):
     """Random begin / chunk / append / commit / abort / reset / grow / fork /
