@@ -391,9 +391,10 @@ def _check_prefill(w, layer, starts, counts, qh, kh, vh, out, kp, vp, tables=Non
 
 
 PREFILL_CASES = [
-    # dtype, D, S, H, H_kv
-    ("bf16", 128, 16, 4, 4), ("f32", 64, 16, 3, 3), ("bf16", 128, 16, 8, 2),
-    ("f32", 40, 16, 2, 1), ("bf16", 128, 7, 2, 2),
+    # dtype, D, S, H, H_kv: matrix-core path (16- and 32-token pages) ...
+    ("bf16", 128, 16, 4, 4), ("bf16", 128, 16, 8, 2), ("bf16", 128, 32, 4, 1),
+    # ... and per-row decode kernels
+    ("f32", 64, 16, 3, 3), ("f32", 40, 16, 2, 1), ("bf16", 128, 7, 2, 2),
 ]
 PREFILL_CHUNKS = [(0, 1), (0, 37), (5, 20), (16, 16), (100, 70), (1000, 33), (0, 300)]
 
@@ -620,7 +621,24 @@ def test_forked_caches_share_prefix_and_copy_on_write(dtype, D, H, Hkv):
     assert tE[0] == tA[0] and tE[1] != tA[1]
     assert torch.equal(kp[:, tE[1], :, :6], kp[:, tA[1], :, :6])
     assert torch.equal(vp[:, tE[1], :, :6], vp[:, tA[1], :, :6])
-    for c in (B, Dc, E):
+    # a prefill chunk on a fork inside a shared page: the chunk's begin copies
+    # the page, the append writes the copy, and every row matches the oracle
+    F = pkv.pkv_cache_fork(Dc, 19, 256)
+    assert pkv.pkv_begin_tokens(F, 30) == 19
+    tF = pkv.pkv_cache_page_table(F)
+    assert tF[0] == tA[0] and tF[1] != tA[1]
+    for layer in range(L):
+        qh, kh, vh = _chunk_rows(w, layer, 30, step=3)
+        out = torch.empty((30, H, D), device="cuda")
+        pkv.pkv_append_and_attend(F, layer, rows_to_device(qh, dtype), rows_to_device(kh, dtype),
+                                  rows_to_device(vh, dtype), out)
+        torch.cuda.synchronize()
+        ref = oracle.prefill_attention(qh, kh, vh, HostPages(w, "k", layer),
+                                       HostPages(w, "v", layer), tA, 19, S)
+        assert np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref)) <= TOL[dtype], layer
+        assert torch.equal(kp[layer, tF[1], :, :3], kp[layer, tA[1], :, :3])
+    pkv.pkv_commit_token(F)
+    for c in (B, Dc, E, F):
         pkv.pkv_cache_destroy(c)
     assert pkv.pkv_pool_get_counters(pool).pages_free == w.num_pages
     pkv.pkv_pool_destroy(pool)
