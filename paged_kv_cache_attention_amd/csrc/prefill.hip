@@ -33,6 +33,19 @@ constexpr int kXcds = 8;           // accelerator complex dies of an MI355X
 
 __device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
+// Page-table reads that are uniform across a wave go through the scalar data
+// cache (the table is not written while this kernel runs).
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
+// Raw buffer access to one 4 KiB head-page: a scalar base in the descriptor,
+// a 32-bit lane offset per load (word 3: 32-bit data format for untyped
+// loads on gfx9-family parts).
+__device__ inline uint4 page_load(const char* page, uint32_t off) {
+  const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(page), 0, 16 * kRowBytes,
+                                                   0x00020000);
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 // 32-bit word i (a compile-time constant after unrolling) of a 16-byte value.
 __device__ inline uint32_t word_of(const uint4& u, int i) {
   return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
@@ -70,9 +83,14 @@ __device__ inline int vt_index(int dim, int key) {
 // between lanes; the transposed V is read in the same key order.  Each K or V
 // fragment read from LDS feeds the MFMAs of both query sets.  Online softmax
 // per query in log2 units; the running maximum and sum are reduced across
-// the four lane groups with shuffles.  The context accumulates in the MFMA
+// the four lane groups with shuffles, and the maximum moves lazily (only by
+// more than 2^8 in weight).  The context accumulates in the MFMA
 // output layout (lane l: rows 4(l/16)..+3, column l%16 of each 16-column
 // tile), whose per-row scale factors come from the owning lanes by shuffle.
+//
+// PAGE16: pages of exactly 16 rows, so a row's page and slot are a shift and
+// a mask instead of a division (the lookups run per lane for every load).
+template <bool PAGE16>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[kBlockKeys * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t sV[kD * kVStride];
@@ -130,21 +148,56 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   // thread is key 2 vpair + i/2, bytes 32 vdg + 16 (i%2).
   const int vpair = tid >> 3;
   const int vdg = tid & 7;
+  auto row_off = [&](int key) -> int64_t {
+    const int page = PAGE16 ? key >> 4 : key / S;
+    const int slot = PAGE16 ? key & 15 : key % S;
+    return (int64_t)pt[page] * a.page_bytes + head_off + (int64_t)slot * kRowBytes;
+  };
   auto k_src = [&](int key0, int i) -> const uint4* {
     const int c = tid + 256 * i;
     const int key = min(key0 + (c >> 4), tile.key_end - 1);
-    return reinterpret_cast<const uint4*>(a.k_layer + (int64_t)pt[key / S] * a.page_bytes +
-                                          head_off + (int64_t)(key % S) * kRowBytes +
-                                          (c & 15) * 16);
+    return reinterpret_cast<const uint4*>(a.k_layer + row_off(key) + (c & 15) * 16);
   };
   auto v_src = [&](int key0, int i) -> const uint4* {
     const int key = min(key0 + 2 * vpair + (i >> 1), tile.key_end - 1);
-    return reinterpret_cast<const uint4*>(a.v_layer + (int64_t)pt[key / S] * a.page_bytes +
-                                          head_off + (int64_t)(key % S) * kRowBytes +
-                                          vdg * 32 + (i & 1) * 16);
+    return reinterpret_cast<const uint4*>(a.v_layer + row_off(key) + vdg * 32 + (i & 1) * 16);
   };
-  uint4 k0 = *k_src(0, 0), k1 = *k_src(0, 1), k2 = *k_src(0, 2), k3 = *k_src(0, 3);
-  uint4 v0 = *v_src(0, 0), v1 = *v_src(0, 1), v2 = *v_src(0, 2), v3 = *v_src(0, 3);
+  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+  // A block's K/V.  With 16-row pages and all 64 keys visible, K load i is
+  // page key0/16 + i for the whole workgroup (thread t: bytes 16 t) and a
+  // wave's V rows all lie in page key0/16 + wave: four wave-uniform page
+  // reads and constant lane offsets.  Otherwise (other page sizes, or the
+  // tile's last, clamped block) every lane looks its row up.
+  auto fetch = [&](int key0) {
+    if (PAGE16 && key0 + kBlockKeys <= tile.key_end) {
+      const const_i32_ptr ptc = (const_i32_ptr)pt;
+      const int pg0 = key0 >> 4;
+      const char* kp0 = a.k_layer + (int64_t)ptc[pg0] * a.page_bytes + head_off;
+      const char* kp1 = a.k_layer + (int64_t)ptc[pg0 + 1] * a.page_bytes + head_off;
+      const char* kp2 = a.k_layer + (int64_t)ptc[pg0 + 2] * a.page_bytes + head_off;
+      const char* kp3 = a.k_layer + (int64_t)ptc[pg0 + 3] * a.page_bytes + head_off;
+      const char* vp = a.v_layer + (int64_t)ptc[pg0 + wave] * a.page_bytes + head_off;
+      k0 = page_load(kp0, tid * 16);
+      k1 = page_load(kp1, tid * 16);
+      k2 = page_load(kp2, tid * 16);
+      k3 = page_load(kp3, tid * 16);
+      const uint32_t vrow = (uint32_t)(2 * (vpair & 7)) * kRowBytes + vdg * 32;
+      v0 = page_load(vp, vrow);
+      v1 = page_load(vp, vrow + 16);
+      v2 = page_load(vp, vrow + kRowBytes);
+      v3 = page_load(vp, vrow + kRowBytes + 16);
+    } else {
+      k0 = *k_src(key0, 0);
+      k1 = *k_src(key0, 1);
+      k2 = *k_src(key0, 2);
+      k3 = *k_src(key0, 3);
+      v0 = *v_src(key0, 0);
+      v1 = *v_src(key0, 1);
+      v2 = *v_src(key0, 2);
+      v3 = *v_src(key0, 3);
+    }
+  };
+  fetch(0);
 
   const int nblocks = (tile.key_end + kBlockKeys - 1) / kBlockKeys;
   for (int kb = 0; kb < nblocks; ++kb) {
@@ -171,17 +224,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       }
     }
     __syncthreads();
-    if (kb + 1 < nblocks) {  // the next block's loads fly during this block's math
-      const int next = key0 + kBlockKeys;
-      k0 = *k_src(next, 0);
-      k1 = *k_src(next, 1);
-      k2 = *k_src(next, 2);
-      k3 = *k_src(next, 3);
-      v0 = *v_src(next, 0);
-      v1 = *v_src(next, 1);
-      v2 = *v_src(next, 2);
-      v3 = *v_src(next, 3);
-    }
+    if (kb + 1 < nblocks) fetch(key0 + kBlockKeys);  // flies during this block's math
 
     // A wave whose queries all precede every key of the block has nothing
     // to add from it (causal), and an empty wave has nothing at all.  Block 0
@@ -218,7 +261,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
           for (int j = 0; j < 4; ++j)
             if (key0 + 16 * kt + 4 * g + j > my_pos[qs]) s[qs][kt][j] = -INFINITY;
     }
-    float alpha[2];
+    // Block maxima in scaled log2 units (the scale is positive, so the
+    // maximum of the raw products scales to the maximum of the scores).
+    float cand[2];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       float mb = s[qs][0][0];
@@ -228,34 +273,42 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         for (int j = 0; j < 4; ++j) mb = fmaxf(mb, s[qs][kt][j]);
       mb = fmaxf(mb, __shfl_xor(mb, 16));
       mb = fmaxf(mb, __shfl_xor(mb, 32));
-      // m is kept in scaled log2 units; the scale is positive, so the maximum
-      // of the raw products scales to the maximum of the scores
-      const float mn = fmaxf(m[qs], mb * a.scale_log2e);
-      alpha[qs] = __builtin_amdgcn_exp2f(m[qs] - mn);
+      cand[qs] = mb * a.scale_log2e;
+    }
+    // Lazy rescale: the running maxima move (and the context and sums are
+    // rescaled) only when some query of the wave sees a block maximum more
+    // than kSlack above its own; otherwise the weights exp2(s - m) stay at
+    // most 2^kSlack, which float32 sums and bf16 weights carry exactly as
+    // well.  The first block always moves them from -inf.
+    constexpr float kSlack = 8.f;
+    if (__builtin_expect(__any(cand[0] > m[0] + kSlack || cand[1] > m[1] + kSlack), 0)) {
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const float mn = fmaxf(m[qs], cand[qs]);
+        const float alpha = __builtin_amdgcn_exp2f(m[qs] - mn);
+        l[qs] *= alpha;
+        m[qs] = mn;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float aj = __shfl(alpha, 4 * g + j);
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) acc[qs][dt][j] *= aj;
+        }
+      }
+    }
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
       float ps = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          s[qs][kt][j] = __builtin_amdgcn_exp2f(fmaf(s[qs][kt][j], a.scale_log2e, -mn));
+          s[qs][kt][j] = __builtin_amdgcn_exp2f(fmaf(s[qs][kt][j], a.scale_log2e, -m[qs]));
           ps += s[qs][kt][j];
         }
       ps += __shfl_xor(ps, 16);
       ps += __shfl_xor(ps, 32);
-      l[qs] = fmaf(l[qs], alpha[qs], ps);
-      m[qs] = mn;
-    }
-    // rescale the context rows 4g+j of each set by their queries' factors,
-    // unless no running maximum of the wave moved (every factor is 1)
-    if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float aj = __shfl(alpha[qs], 4 * g + j);
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) acc[qs][dt][j] *= aj;
-        }
+      l[qs] += ps;
     }
     // ---- O += P V over two 32-key steps ----
 #pragma unroll
@@ -335,7 +388,12 @@ hipError_t launch_prefill_append(const PrefillArgs& a, int num_tiles, hipStream_
 }
 
 hipError_t launch_prefill_attention(const PrefillArgs& a, int num_tiles, hipStream_t stream) {
-  hipLaunchKernelGGL(prefill_mfma_kernel, dim3(num_tiles * a.num_heads), dim3(256), 0, stream, a);
+  if (a.page_size == 16)
+    hipLaunchKernelGGL(prefill_mfma_kernel<true>, dim3(num_tiles * a.num_heads), dim3(256), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(prefill_mfma_kernel<false>, dim3(num_tiles * a.num_heads), dim3(256), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
