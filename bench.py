@@ -41,14 +41,14 @@ HBM_PEAK_GBS = 8000.0
 # file under csrc/).
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
-    "batch32_fp32_l12": {"source": "kernels.hip", "sha256_16": "f021c5e38f8e1620",
-                         "fetch_kib": 44681.4, "write_kib": 2008.5,
+    "batch32_fp32_l12": {"source": "kernels.hip", "sha256_16": "50247967e0981231",
+                         "fetch_kib": 44685.3, "write_kib": 2008.5,
                          "algorithmic_bytes": 88971264},
-    "batch256_bf16": {"source": "kernels.hip", "sha256_16": "f021c5e38f8e1620",
-                      "fetch_kib": 4761676.0, "write_kib": 4415.1,
+    "batch256_bf16": {"source": "kernels.hip", "sha256_16": "50247967e0981231",
+                      "fetch_kib": 4761669.8, "write_kib": 4420.4,
                       "algorithmic_bytes": 9718775808},
-    "prefill32_bf16": {"source": "prefill.hip", "sha256_16": "103892798313250f",
-                       "fetch_kib": 725500.4, "write_kib": 518320.1,
+    "prefill32_bf16": {"source": "prefill.hip", "sha256_16": "3eab7081b3b11055",
+                       "fetch_kib": 699401.5, "write_kib": 518320.2,
                        "algorithmic_bytes": 1854562304},
 }
 
