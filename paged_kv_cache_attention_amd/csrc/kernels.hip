@@ -275,7 +275,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
   static_assert(NG * WPG == WAVES, "waves must split evenly into head groups");
   constexpr int G = NG * HPW;              // query heads per K/V head
 
-  const WorkItem it = a.items[blockIdx.x];
+  const WorkItem it = plan_item(a);
   const ReqEntry rq = it.rq;
   const int kvh = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -631,7 +631,7 @@ __global__ __launch_bounds__(256) void attend_group_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float s_acc[4][16][D];
   __shared__ float s_m[4][16], s_l[4][16];
 
-  const WorkItem it = a.items[blockIdx.x];
+  const WorkItem it = plan_item(a);
   const ReqEntry rq = it.rq;
   const int kvh = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -845,7 +845,7 @@ __global__ __launch_bounds__(64) void attend_generic_kernel(AttnArgs a) {
   float* qs = smem;         // [D]
   float* ps = smem + D;     // [64]
 
-  const WorkItem it = a.items[blockIdx.x];
+  const WorkItem it = plan_item(a);
   const ReqEntry rq = it.rq;
   const int h = blockIdx.y;                                  // query head
   const int group = a.num_heads / a.num_kv_heads;
@@ -939,7 +939,7 @@ template <typename W>
 __global__ __launch_bounds__(64) void kv_append_kernel(AttnArgs a) {
   const int r = blockIdx.x;
   const int h = blockIdx.y;
-  const ReqEntry rq = a.reqs[r];
+  const ReqEntry rq = plan_req(a, r);
   const int pos = rq.seq_len - 1;
   const int S = a.page_size;
   const int D = a.head_width;

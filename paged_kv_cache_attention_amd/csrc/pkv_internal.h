@@ -37,6 +37,10 @@ struct WorkItem {
   ReqEntry rq;
 };
 
+// Plans of at most this many requests and work items, none split, are
+// passed inline in the kernel arguments.
+constexpr int kInlinePlan = 16;
+
 struct AttnArgs {
   const void* q;          // [n][H][D] pool dtype
   const void* k_new;      // [n][H_kv][D] rows to append at t-1 (fused append), or null
@@ -61,7 +65,31 @@ struct AttnArgs {
   int64_t page_bytes;     // H_kv * S * D * elt
   int64_t head_bytes;     // S * D * elt
   float scale_log2e;      // log2(e) / sqrt(D)
+  // Small plans without split requests travel in the arguments themselves
+  // (no upload before the launch): num_inline > 0 replaces reqs and items.
+  int32_t num_inline;
+  ReqEntry inline_reqs[kInlinePlan];
+  WorkItem inline_items[kInlinePlan];
 };
+
+// The work item of this workgroup and request entry r of the plan.  The item
+// is uniform across the workgroup; readfirstlane keeps its fields in scalar
+// registers whichever source it came from.
+__device__ inline WorkItem plan_item(const AttnArgs& a) {
+  WorkItem w = a.num_inline ? a.inline_items[blockIdx.x] : a.items[blockIdx.x];
+  w.req = __builtin_amdgcn_readfirstlane(w.req);
+  w.blk_begin = __builtin_amdgcn_readfirstlane(w.blk_begin);
+  w.blk_end = __builtin_amdgcn_readfirstlane(w.blk_end);
+  w.split = __builtin_amdgcn_readfirstlane(w.split);
+  w.rq.pt_row = __builtin_amdgcn_readfirstlane(w.rq.pt_row);
+  w.rq.seq_len = __builtin_amdgcn_readfirstlane(w.rq.seq_len);
+  w.rq.nsplit = __builtin_amdgcn_readfirstlane(w.rq.nsplit);
+  w.rq.partial_base = __builtin_amdgcn_readfirstlane(w.rq.partial_base);
+  return w;
+}
+__device__ inline ReqEntry plan_req(const AttnArgs& a, int r) {
+  return a.num_inline ? a.inline_reqs[r] : a.reqs[r];
+}
 
 // One prefill work tile: up to kPrefillTileRows consecutive rows of one
 // request's chunk.

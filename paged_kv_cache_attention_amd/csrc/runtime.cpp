@@ -90,6 +90,7 @@ struct pkv_plan {
   int32_t num_split_reqs = 0;
   int32_t waves = 4;
   bool any_split = false;
+  bool inline_plan = false;    // reqs/items go in the kernel arguments
   uint64_t rows_attended = 0;  // sum of t_r
   std::vector<ReqEntry> reqs;
   std::vector<WorkItem> items;
@@ -423,7 +424,10 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
     return (a.blk_end - a.blk_begin) > (b.blk_end - b.blk_begin);
   });
 
-  if (upload) {
+  // Small unsplit plans are passed inline in the kernel arguments.
+  const bool inline_plan = n <= pkv::kInlinePlan && (int64_t)items.size() <= pkv::kInlinePlan &&
+                           slots == 0;
+  if (upload && !inline_plan) {
   const size_t part_floats = (size_t)slots * p->desc.num_heads * (p->desc.head_width + 2);
   if (part_floats > pl->partials_cap) {
     const size_t cap = std::max(part_floats, pl->partials_cap * 2);
@@ -470,6 +474,7 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
   pl->num_split_reqs = (int32_t)merge_list.size();
   pl->waves = choice.waves;
   pl->any_split = slots > 0;
+  pl->inline_plan = inline_plan;
   pl->rows_attended = rows_attended;
   pl->built = true;
   return PKV_OK;
@@ -503,6 +508,12 @@ AttnArgs make_args(const pkv_plan* pl, int32_t layer, const int32_t* page_table,
   a.page_bytes = p->page_bytes;
   a.head_bytes = p->head_bytes;
   a.scale_log2e = (float)(1.4426950408889634 / std::sqrt((double)p->desc.head_width));
+  a.num_inline = 0;
+  if (pl->inline_plan) {
+    a.num_inline = (int32_t)pl->items.size();
+    std::memcpy(a.inline_reqs, pl->reqs.data(), pl->reqs.size() * sizeof(ReqEntry));
+    std::memcpy(a.inline_items, pl->items.data(), pl->items.size() * sizeof(WorkItem));
+  }
   return a;
 }
 
