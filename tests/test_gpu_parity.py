@@ -964,3 +964,65 @@ def test_fullstep128_bf16_l32_transactional():
     for c in caches:
         pkv.pkv_cache_destroy(c)
     pkv.pkv_pool_destroy(pool)
+
+
+# ------------------------------------------------------ randomized sweep --
+def _random_case(rng):
+    dtype = ["f32", "bf16"][rng.integers(2)]
+    D = int(rng.choice([64, 128, 40, 96] if dtype == "f32" else [128, 128, 64, 80]))
+    S = int(rng.choice([16, 16, 32, 8, 5]))
+    H = int(rng.choice([1, 2, 4, 6, 8, 16]))
+    divisors = [d for d in range(1, H + 1) if H % d == 0]
+    Hkv = int(rng.choice(divisors))
+    n = int(rng.integers(1, 7))
+    lengths = rng.integers(1, 700, size=n)
+    split = int(rng.choice([0, 0, -1, 1, 3]))
+    merge = int(rng.choice([0, 2]))
+    op = ["decode", "append", "prefill"][rng.integers(3)]
+    return dtype, D, S, H, Hkv, lengths, split, merge, op
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_randomized_configurations(case):
+    """Seeded random geometry, dtype, grouping, split and operation: every
+    context against the oracle, appended rows bit-exact."""
+    rng = np.random.default_rng(9000 + case)
+    dtype, D, S, H, Hkv, lengths, split, merge, op = _random_case(rng)
+    w = _small(f"rand{case}", dtype, D, S, lengths, heads=H, kv_heads=Hkv, layers=1,
+               seed=100 + case, extra_pages=8)
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp, split=split, merge=merge)
+    pt = _pt_device(w)
+    info = (case, dtype, D, S, H, Hkv, lengths.tolist(), split, merge, op)
+    if op == "prefill":
+        counts = [int(min(t, rng.integers(1, 200))) for t in w.lengths]
+        starts = [int(t) - c for t, c in zip(w.lengths, counts)]
+        qh, kh, vh = _chunk_rows(w, 0, sum(counts))
+        out = torch.empty((sum(counts), H, D), device="cuda")
+        pkv.pkv_prefill_attention(pool, 0, pt, w.pt_stride, starts, counts,
+                                  *(rows_to_device(x, dtype) for x in (qh, kh, vh)), out)
+        torch.cuda.synchronize()
+        _check_prefill(w, 0, starts, counts, qh, kh, vh, out, kp, vp)
+    else:
+        qh = w.q(0)
+        out = torch.empty((w.n, H, D), device="cuda")
+        plan = pkv.pkv_plan_create(pool)
+        pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
+        if op == "decode":
+            pkv.pkv_plan_decode_attention(plan, 0, rows_to_device(qh, dtype), pt, out)
+            torch.cuda.synchronize()
+            for r in range(w.n):
+                assert max_err(out[r], _oracle_decode(w, 0, r, qh)) <= TOL[dtype], (info, r)
+        else:
+            kh, vh = w.k_new(0), w.v_new(0)
+            pkv.pkv_plan_append_and_attend(plan, 0, pt, *(rows_to_device(x, dtype)
+                                                           for x in (qh, kh, vh)), out)
+            torch.cuda.synchronize()
+            for r in range(w.n):
+                t = int(w.lengths[r])
+                page, slot = w.page_tables[r][(t - 1) // S], (t - 1) % S
+                assert np.array_equal(to_bits(kp[0, page, :, slot, :], dtype), kh[r]), info
+                ref = _oracle_decode(w, 0, r, qh, appended=(kh, vh))
+                assert max_err(out[r], ref) <= TOL[dtype], (info, r)
+        pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(pool)
