@@ -541,6 +541,28 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
 // Waves run independently until the end, then combine through LDS; each wave
 // publishes a quarter of the G heads (finish_heads: the contexts, or split-K
 // partials and the last-arriver merge, all heads of a wave at once).
+// Reductions across the four 16-lane rows of a wave on the vector ALU
+// (gfx950 permlane swaps): with both operands x, permlane16_swap returns rows
+// (0,0,2,2) and (1,1,3,3), permlane32_swap the low half twice and the high
+// half twice; combining the two gives every lane the result over lanes
+// l, l^16 (then l^32), added in the same order in every lane.
+__device__ inline float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -731,8 +753,7 @@ __global__ __launch_bounds__(256) void attend_group_mfma_kernel(AttnArgs a) {
       if constexpr (edge) sc[j] += valid_k[j];
     }
     float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    mb = xor32_max(xor16_max(mb));
     const float mn = fmaxf(m, mb * a.scale_log2e);
     const float alpha = fast_exp2(m - mn);
     float p[4], ps = 0.f;
@@ -741,9 +762,7 @@ __global__ __launch_bounds__(256) void attend_group_mfma_kernel(AttnArgs a) {
       p[j] = fast_exp2(fmaf(sc[j], a.scale_log2e, -mn));
       ps += p[j];
     }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    l = fmaf(l, alpha, ps);
+    l = fmaf(l, alpha, xor32_sum(xor16_sum(ps)));
     m = mn;
     if (alpha != 1.f) {
 #pragma unroll

@@ -46,6 +46,28 @@ __device__ inline uint4 page_load(const char* page, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
+// Reductions across the four 16-lane rows of a wave on the vector ALU
+// (gfx950 permlane swaps): with both operands x, permlane16_swap returns rows
+// (0,0,2,2) and (1,1,3,3), permlane32_swap the low half twice and the high
+// half twice; combining the two gives every lane the result over lanes
+// l, l^16 (then l^32), added in the same order in every lane.
+__device__ inline float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // 32-bit word i (a compile-time constant after unrolling) of a 16-byte value.
 __device__ inline uint32_t word_of(const uint4& u, int i) {
   return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
@@ -271,9 +293,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) mb = fmaxf(mb, s[qs][kt][j]);
-      mb = fmaxf(mb, __shfl_xor(mb, 16));
-      mb = fmaxf(mb, __shfl_xor(mb, 32));
-      cand[qs] = mb * a.scale_log2e;
+      cand[qs] = xor32_max(xor16_max(mb)) * a.scale_log2e;
     }
     // Lazy rescale: the running maxima move (and the context and sums are
     // rescaled) only when some query of the wave sees a block maximum more
@@ -306,9 +326,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
           s[qs][kt][j] = __builtin_amdgcn_exp2f(fmaf(s[qs][kt][j], a.scale_log2e, -m[qs]));
           ps += s[qs][kt][j];
         }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
-      l[qs] += ps;
+      l[qs] += xor32_sum(xor16_sum(ps));
     }
     // ---- O += P V over two 32-key steps ----
 #pragma unroll
