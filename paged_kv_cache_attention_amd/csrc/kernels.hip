@@ -1,6 +1,8 @@
-// gfx950 kernels of libpkv: paged decode attention (fast and generic paths),
-// the log-sum-exp merge of split-K partials, the K/V row append and the
-// page-table patch.
+// gfx950 kernels of libpkv: paged decode attention (the vector-ALU fast and
+// generic paths, and the matrix-core path for grouped K/V heads), the
+// log-sum-exp merge of split-K partials, the K/V row append, copy-on-write
+// page copies and the page-table patch.  Prefill kernels live in
+// prefill.hip.
 //
 // What is computed (learn_llm ch.38 "cached generation", section "Prepare
 // every block, then commit every cache together"): for one request, layer and
@@ -10,7 +12,9 @@
 // table in pages laid out [physical_page, head, page_offset, head_width]
 // ("Incremental Serving", section "Paged KV-cache layout").
 //
-// Arithmetic: float32 throughout (bf16 K/V widen exactly).  Scores are kept in
+// Arithmetic: float32 throughout (bf16 K/V widen exactly; the grouped-head
+// matrix path multiplies bf16 operands exactly and rounds the softmax weights
+// to bf16 for the value product).  Scores are kept in
 // log2 units (q is pre-multiplied by log2(e)/sqrt(d_h)) so every exponential is
 // one v_exp_f32.  Softmax is online: each lane group keeps a running maximum m,
 // a running sum l of 2^(s-m) and an accumulator of 2^(s-m) v; groups, waves and

@@ -1,5 +1,7 @@
-// Host runtime and C ABI of libpkv: page pool and free list, request caches
-// and their per-token transaction, split-K plans, device page-table mirror.
+// Host runtime and C ABI of libpkv: page pool and free list with reference
+// counts, request caches (forks share pages, copy on write), their per-token
+// or per-chunk transaction, split-K plans and prefill tiles, device
+// page-table mirror.
 //
 // Sources (by page and section):
 //  - riftco-transformer "Incremental Serving", "Paged KV-cache layout": shared
@@ -13,6 +15,9 @@
 //  - learn_llm ch.38 "cached generation": every layer prepares before any
 //    commit; rejected operations leave committed state unchanged; reset keeps
 //    the allocation; work counters (appends, score values).
+//  - "Incremental Serving", "Current scope": page sharing between requests and
+//    copy-on-write prefixes, and a batched prefill, lie beyond paged storage
+//    alone; both are built here on the same pool.
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
