@@ -17,8 +17,8 @@ launch stream immediately around every attention kernel (PKV_OPT_PROFILING)
 and sums each launch's algorithmic bytes.
 
 Other workloads (--workload): batch256_bf16, skewed64_bf16 (single-layer
-batched decode over existing rows), batch256_gqa8_bf16 (the same batch with
-32 query heads sharing 8 K/V heads), fullstep128_bf16_l32 (32 layers, 128
+batched decode over existing rows), batch256_gqa8_bf16 and batch256_mqa_bf16
+(the same batch with 32 query heads sharing 8 K/V heads, or one), fullstep128_bf16_l32 (32 layers, 128
 requests, bf16, 1% seeded aborts), prefill32_bf16 (batched prefill chunks,
 reported in TFLOP/s against the bf16 matrix-core peak) and tiny (the latency-bound fixture:
 token-at-a-time steps of one request, reported in steps/s and us/step).
@@ -125,7 +125,7 @@ def main():
     if args.workload.startswith("prefill"):
         return prefill_bench(args, W.WORKLOADS[args.workload]())
     maker = W.WORKLOADS[args.workload]
-    grow = 2 * args.steps + args.warmup + 2   # committed tokens per request over both passes
+    grow = 3 * args.steps + args.warmup + 2   # committed tokens per request over three passes
     w = maker(extra_steps=grow) if args.workload.startswith("fullstep") else maker()
     transactional = w.appends
     dt = sgpu.torch_dtype(w.dtype)
@@ -236,6 +236,8 @@ def main():
         torch.cuda.synchronize()
         pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_PROFILING, 0)
         prof = pkv.pkv_pool_get_profile(pool, reset=True)
+    # Pass 3: one stream event between successive steps -> per-step spread.
+    spread = step_spread(lambda: step(False), args.steps)
     launches = prof.attention_launches if prof else 0
     avg_kern_s = prof.attention_ms / max(1, launches) / 1e3 if prof else 0.0
     bytes_per_launch = prof.algorithmic_bytes / max(1, launches) if prof else 0.0
@@ -255,6 +257,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(elapsed / args.steps * 1e3, 4),
         "steps_per_sec": round(args.steps / elapsed, 2),
+        "step_ms": spread,
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
@@ -276,8 +279,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("attend_fast_kernel<float,64>" if w.dtype == "f32" else
-                       "attend_fast_kernel<bf16,128>"),
+            "kernel": dominant_kernel(w),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -298,6 +300,39 @@ def main():
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def step_spread(step, steps: int) -> dict:
+    """Median, min and max step time (ms) from one stream event recorded
+    between successive steps; a separate pass, so the events do not touch the
+    timed whole-job figure."""
+    import statistics
+
+    import torch
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return {"median": round(statistics.median(ms), 4), "min": round(min(ms), 4),
+            "max": round(max(ms), 4), "steps": steps}
+
+
+def dominant_kernel(w) -> str:
+    """The attention kernel the library dispatches for a decode workload: the
+    matrix-core grouped kernel for bf16 d_h=128 when a multiple of 4 query
+    heads share a K/V head (16, 8 or 4 of them per workgroup), else the
+    vector fast path."""
+    group = w.heads // w.hkv
+    if w.dtype == "bf16" and w.head_width == 128 and w.page_size % 16 == 0 and group % 4 == 0:
+        share = next(s for s in (16, 8, 4) if group % s == 0)
+        return f"attend_group_mfma_kernel<{share}>"
+    return ("attend_fast_kernel<float,64>" if w.dtype == "f32" else
+            "attend_fast_kernel<bf16,128>")
 
 
 def prefill_bench(args, w):
@@ -361,6 +396,7 @@ def prefill_bench(args, w):
         torch.cuda.synchronize()
         pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_PROFILING, 0)
         prof = pkv.pkv_pool_get_profile(pool, reset=True)
+    spread = step_spread(step, args.steps)
     traffic, traffic_alg = measured_traffic(w.name)
     launches = prof.prefill_launches if prof else 0
     avg_s = prof.prefill_ms / max(1, launches) / 1e3 if prof else 0.0
@@ -373,6 +409,7 @@ def prefill_bench(args, w):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "step_ms": spread,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -490,12 +527,15 @@ def tiny_latency(args):
         step(i)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    it = iter(range(n, 2 * n))
+    spread = step_spread(lambda: step(next(it)), n)
     kv = sum(t for t in range(1, C + 1)) * args.steps * L * H * 2 * D * 4
     print(json.dumps({
         "metric": "paged decode attention KV GB/s (% of HBM peak) + decode-attention steps/sec",
         "value": round(n / el, 1), "unit": "steps/s", "n_gpus": 1, "steps": n,
         "warmup": args.warmup * C, "ms_per_step": round(el / n * 1e3, 4),
-        "us_per_step": round(el / n * 1e6, 2), "kv_bytes_per_step_mean": kv // n,
+        "us_per_step": round(el / n * 1e6, 2), "step_ms": spread,
+        "kv_bytes_per_step_mean": kv // n,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "tiny", "requests": 1, "layers": L, "heads": H, "head_width": D,

@@ -21,6 +21,7 @@
 // split-K chunks combine by rescaling to the larger maximum.
 #include <cfloat>
 #include <cstdint>
+#include <initializer_list>
 #include <type_traits>
 
 #include <hip/hip_runtime.h>
@@ -281,7 +282,12 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
 
   const WorkItem it = plan_item(a);
   const ReqEntry rq = it.rq;
-  const int kvh = blockIdx.y;
+  // Grid y: K/V head kvh, and which of its head_tiles consecutive shares of
+  // G query heads this workgroup serves (one share unless the group exceeds
+  // what one workgroup holds or has an odd factor).
+  const int tiles = a.head_tiles;
+  const int kvh = tiles == 1 ? (int)blockIdx.y : (int)blockIdx.y / tiles;
+  const int tile = (int)blockIdx.y - kvh * tiles;
   const int lane = threadIdx.x & 63;
   // Wave-uniform: block indices, page-table reads and branches stay scalar, so
   // the page lookups go through the scalar cache and never wait on the
@@ -289,7 +295,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hg = wave / WPG;               // head group of this wave
   const int sub = wave % WPG;              // its place among the group's waves
-  const int qh0 = kvh * G + hg * HPW;      // first query head of this wave
+  const int qh0 = (kvh * tiles + tile) * G + hg * HPW;  // first query head of this wave
   const int g = lane / LPR;
   const int c = lane % LPR;
   const int t = rq.seq_len;
@@ -316,7 +322,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
   if (fused) {
     knew = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + kvrow_bytes + c * 16);
     vnew = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + kvrow_bytes + c * 16);
-    if (wave == 0 && g == 0) {
+    if (wave == 0 && g == 0 && tile == 0) {
       const int pos = t - 1;
       const int64_t slot = (int64_t)pt[pos / S] * a.page_bytes + head_off +
                            (int64_t)(pos % S) * ROW_BYTES + c * 16;
@@ -659,7 +665,10 @@ __global__ __launch_bounds__(256) void attend_group_mfma_kernel(AttnArgs a) {
 
   const WorkItem it = plan_item(a);
   const ReqEntry rq = it.rq;
-  const int kvh = blockIdx.y;
+  const int tiles = a.head_tiles;  // shares of G query heads per K/V head, as in the fast kernel
+  const int kvh = tiles == 1 ? (int)blockIdx.y : (int)blockIdx.y / tiles;
+  const int tile = (int)blockIdx.y - kvh * tiles;
+  const int qbase = (kvh * tiles + tile) * G;  // first query head of this workgroup
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ql = lane & 15;
@@ -675,14 +684,14 @@ __global__ __launch_bounds__(256) void attend_group_mfma_kernel(AttnArgs a) {
 
   bf16x8_t qf[4];
   {
-    const int64_t qrow = ((int64_t)it.req * a.num_heads + kvh * G + min(ql, G - 1)) * ROW_BYTES;
+    const int64_t qrow = ((int64_t)it.req * a.num_heads + qbase + min(ql, G - 1)) * ROW_BYTES;
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc)
       qf[dc] = __builtin_bit_cast(
           bf16x8_t, *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + qrow +
                                                     (4 * dc + g) * 16));
   }
-  if (fused && wave == 0 && lane < 16) {
+  if (fused && wave == 0 && lane < 16 && tile == 0) {
     const int pos = t - 1;
     const int64_t slot = (int64_t)pt[pos / S] * a.page_bytes + head_off +
                          (int64_t)(pos % S) * ROW_BYTES + lane * 16;
@@ -830,7 +839,7 @@ __global__ __launch_bounds__(256) void attend_group_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int k = 0; k < NH; ++k) {
     const int r = wave + 4 * k;
-    heads[k] = kvh * G + r;
+    heads[k] = qbase + r;
     float mx = s_m[0][r];
 #pragma unroll
     for (int w = 1; w < 4; ++w) mx = fmaxf(mx, s_m[w][r]);
@@ -1004,20 +1013,21 @@ __global__ __launch_bounds__(256) void patch_kernel(int32_t* arena, PatchBatch b
 
 template <typename T, int D, int WAVES, int HPW, int WPG>
 hipError_t launch_fast_shape(const AttnArgs& a, int num_items, hipStream_t stream) {
-  hipLaunchKernelGGL((attend_fast_kernel<T, D, WAVES, HPW, WPG>), dim3(num_items, a.num_kv_heads),
-                     dim3(64 * WAVES), 0, stream, a);
+  hipLaunchKernelGGL((attend_fast_kernel<T, D, WAVES, HPW, WPG>),
+                     dim3(num_items, a.num_kv_heads * a.head_tiles), dim3(64 * WAVES), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
-// Workgroup shape by query heads per K/V head (1, 2, 4, 8, 16).  Up to four
-// heads per wave, every wave of the workgroup carries the whole group, so each
-// K/V block is loaded once and serves all of its query heads; the waves split
-// the chunk's blocks.  Groups of 8 and 16 split over 2 and 4 head groups of
-// four (each block loaded by 2 or 4 waves): more heads per wave would exceed
-// the register file.
+// Workgroup shape by query heads per workgroup (1, 2, 4, 8, 16).  Up to four
+// heads per wave, every wave of the workgroup carries the whole share, so
+// each K/V block is loaded once and serves all of its query heads; the waves
+// split the chunk's blocks.  Shares of 8 and 16 split over 2 and 4 head groups
+// of four (each block loaded by 2 or 4 waves): more heads per wave would
+// exceed the register file.
 template <typename T, int D>
-hipError_t launch_fast(const AttnArgs& a, int num_items, hipStream_t stream) {
-  switch (a.num_heads / a.num_kv_heads) {
+hipError_t launch_fast(const AttnArgs& a, int share, int num_items, hipStream_t stream) {
+  switch (share) {
     case 1:
       return a.waves == 8 ? launch_fast_shape<T, D, 8, 1, 8>(a, num_items, stream)
                           : launch_fast_shape<T, D, 4, 1, 4>(a, num_items, stream);
@@ -1042,45 +1052,59 @@ hipError_t launch_generic(const AttnArgs& a, int num_items, hipStream_t stream) 
 
 }  // namespace
 
+// Query heads per workgroup for a group of `group` query heads per K/V head:
+// the largest of `shares` (descending) that divides it.  A group above the
+// largest share, or with an odd factor, takes several workgroups per K/V
+// head; they read the same K/V blocks (the later reads mostly hit in cache).
+static int head_share(int group, std::initializer_list<int> shares) {
+  for (int s : shares)
+    if (group % s == 0) return s;
+  return 0;
+}
+
 bool group_mfma_supported(int dtype, int head_width, int page_size, int group) {
   return dtype == kDtypeBF16 && head_width == 128 && page_size % kBlockRows == 0 &&
-         (group == 4 || group == 8 || group == 16);
+         group % 4 == 0;
 }
 
 bool fast_path_supported(int dtype, int head_width, int page_size, int group) {
-  if (page_size % kBlockRows != 0) return false;
-  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return false;
+  if (page_size % kBlockRows != 0 || group < 1) return false;
   if (dtype == kDtypeF32) return head_width == 64;
   if (dtype == kDtypeBF16) return head_width == 128;
   return false;
 }
 
-hipError_t launch_attention(const AttnArgs& a, int dtype, int num_items, hipStream_t stream,
+hipError_t launch_attention(const AttnArgs& args, int dtype, int num_items, hipStream_t stream,
                             KernelPath* path_out) {
+  AttnArgs a = args;
   const int group = a.num_heads / a.num_kv_heads;
   if (group_mfma_supported(dtype, a.head_width, a.page_size, group)) {
     if (path_out) *path_out = KernelPath::kFast;
-    switch (group) {
+    const int share = head_share(group, {16, 8, 4});
+    a.head_tiles = group / share;
+    const dim3 grid(num_items, a.num_kv_heads * a.head_tiles);
+    switch (share) {
       case 4:
-        hipLaunchKernelGGL(attend_group_mfma_kernel<4>, dim3(num_items, a.num_kv_heads), dim3(256),
-                           0, stream, a);
+        hipLaunchKernelGGL(attend_group_mfma_kernel<4>, grid, dim3(256), 0, stream, a);
         break;
       case 8:
-        hipLaunchKernelGGL(attend_group_mfma_kernel<8>, dim3(num_items, a.num_kv_heads), dim3(256),
-                           0, stream, a);
+        hipLaunchKernelGGL(attend_group_mfma_kernel<8>, grid, dim3(256), 0, stream, a);
         break;
       default:
-        hipLaunchKernelGGL(attend_group_mfma_kernel<16>, dim3(num_items, a.num_kv_heads),
-                           dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(attend_group_mfma_kernel<16>, grid, dim3(256), 0, stream, a);
         break;
     }
     return hipGetLastError();
   }
   const bool fast = fast_path_supported(dtype, a.head_width, a.page_size, group);
   if (path_out) *path_out = fast ? KernelPath::kFast : KernelPath::kGeneric;
-  if (fast)
-    return dtype == kDtypeF32 ? launch_fast<float, 64>(a, num_items, stream)
-                              : launch_fast<bf16_t, 128>(a, num_items, stream);
+  if (fast) {
+    const int share = head_share(group, {16, 8, 4, 2, 1});
+    a.head_tiles = group / share;
+    return dtype == kDtypeF32 ? launch_fast<float, 64>(a, share, num_items, stream)
+                              : launch_fast<bf16_t, 128>(a, share, num_items, stream);
+  }
+  a.head_tiles = 1;
   return dtype == kDtypeF32 ? launch_generic<float>(a, num_items, stream)
                             : launch_generic<bf16_t>(a, num_items, stream);
 }

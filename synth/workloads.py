@@ -256,6 +256,18 @@ def batch256_gqa8_bf16() -> Workload:
     return _finish(w)
 
 
+def batch256_mqa_bf16() -> Workload:
+    """The 256-request bf16 batch with one K/V head under all H=32 query
+    heads (multi-query attention), D=128, 16-token pages, lengths U[512,4096]
+    from the same stream as the multi-head batch."""
+    seed = 3
+    lengths = uniform_ints(stream_key(seed, TAG_LENGTHS), 256, 512, 4096)
+    P = int(pages_needed(lengths, 16).sum()) + 256
+    w = Workload("batch256_mqa_bf16", seed, 256, 1, 32, 128, 16, P, "bf16", lengths,
+                 appends=False, description=batch256_mqa_bf16.__doc__, kv_heads=1)
+    return _finish(w)
+
+
 def prefill32_bf16() -> Workload:
     """Batched prefill: 32 requests, one layer, H=32, D=128, 16-token pages,
     bf16; each request appends a chunk of U[256, 2048] new rows after a
@@ -274,6 +286,7 @@ WORKLOADS = {
     "batch32_fp32_l12": batch32_fp32,
     "batch256_bf16": batch256_bf16,
     "batch256_gqa8_bf16": batch256_gqa8_bf16,
+    "batch256_mqa_bf16": batch256_mqa_bf16,
     "prefill32_bf16": prefill32_bf16,
     "skewed64_bf16": skewed64_bf16,
     "fullstep128_bf16_l32": fullstep128_bf16,

@@ -246,12 +246,17 @@ def test_append_and_attend_small(dtype, D, S, merge):
 
 # ------------------------------------------------- grouped K/V heads --
 GQA_CASES = [
-    # dtype, D, S, H, H_kv: the fast kernel for groups of 2, 4, 8 and 16 ...
+    # dtype, D, S, H, H_kv: the fast kernels, one workgroup per K/V head for
+    # groups of 2, 4, 8 and 16 ...
     ("bf16", 128, 16, 8, 4), ("bf16", 128, 16, 8, 2), ("bf16", 128, 32, 16, 2),
     ("bf16", 128, 16, 16, 1), ("f32", 64, 16, 4, 2), ("f32", 64, 16, 8, 1),
     ("f32", 64, 16, 16, 2),
-    # ... and the generic kernel: a group of 3, a narrow head, a ragged page
-    ("f32", 64, 16, 6, 2), ("f32", 40, 16, 4, 1), ("bf16", 128, 7, 8, 2),
+    # ... several per K/V head: one K/V head under 32 query heads (16 per
+    # workgroup), groups of 12 and 24 (4 and 8 per workgroup), 6 and 3 ...
+    ("bf16", 128, 16, 32, 1), ("bf16", 128, 16, 24, 2), ("bf16", 128, 16, 12, 1),
+    ("bf16", 128, 16, 6, 1), ("f32", 64, 16, 32, 1), ("f32", 64, 16, 6, 2),
+    # ... and the generic kernel: a narrow head, a ragged page
+    ("f32", 40, 16, 4, 1), ("bf16", 128, 7, 8, 2),
 ]
 
 
@@ -302,7 +307,8 @@ def test_grouped_kv_heads(dtype, D, S, H, Hkv, split, merge):
 
 
 @pytest.mark.parametrize("dtype,D,H,Hkv", [("bf16", 128, 8, 2), ("f32", 64, 4, 1),
-                                           ("f32", 40, 6, 3)])
+                                           ("f32", 40, 6, 3), ("bf16", 128, 32, 1),
+                                           ("f32", 64, 12, 2)])
 def test_grouped_kv_heads_transactional(dtype, D, H, Hkv):
     """begin / batched append_and_attend / abort / commit on caches whose
     pages hold H_kv heads; the aborted request retries with new rows."""
@@ -866,7 +872,8 @@ def test_plan_decode_replays_from_a_hip_graph(merge):
     pkv.pkv_pool_destroy(pool)
 
 
-@pytest.mark.parametrize("maker", [W.batch256_bf16, W.skewed64_bf16, W.batch256_gqa8_bf16])
+@pytest.mark.parametrize("maker", [W.batch256_bf16, W.skewed64_bf16, W.batch256_gqa8_bf16,
+                                   W.batch256_mqa_bf16])
 @pytest.mark.parametrize("merge", MERGES)
 def test_bf16_single_layer_full(maker, merge):
     w = maker()
