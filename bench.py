@@ -325,12 +325,12 @@ def step_spread(step, steps: int) -> dict:
 def dominant_kernel(w) -> str:
     """The attention kernel the library dispatches for a decode workload: the
     matrix-core grouped kernel for bf16 d_h=128 when a multiple of 4 query
-    heads share a K/V head (16, 8 or 4 of them per workgroup), else the
-    vector fast path."""
+    heads share a K/V head (16, 8 or 4 of them per workgroup; template
+    arguments: heads, waves per workgroup), else the vector fast path."""
     group = w.heads // w.hkv
     if w.dtype == "bf16" and w.head_width == 128 and w.page_size % 16 == 0 and group % 4 == 0:
         share = next(s for s in (16, 8, 4) if group % s == 0)
-        return f"attend_group_mfma_kernel<{share}>"
+        return f"attend_group_mfma_kernel<{share},{8 if share >= 8 else 4}>"
     return ("attend_fast_kernel<float,64>" if w.dtype == "f32" else
             "attend_fast_kernel<bf16,128>")
 

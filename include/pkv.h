@@ -151,8 +151,8 @@ typedef enum pkv_option {
                                inside the attention kernel; 0: a separate
                                merge kernel after it                            */
   PKV_OPT_PROFILING = 3,    /* 1: record kernel timing events; 0: stop         */
-  PKV_OPT_WAVES = 4         /* waves per workgroup of the fast path: 4, 8, or
-                               0 (default) to choose per plan                   */
+  PKV_OPT_WAVES = 4         /* waves per workgroup of the fast paths: 4, 8, or
+                               0 (default) to choose per kernel                 */
 } pkv_option;
 
 /* Library version "major.minor.patch"; static string. */

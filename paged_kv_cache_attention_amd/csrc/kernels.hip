@@ -652,16 +652,17 @@ __device__ void finish_heads(const AttnArgs& a, const WorkItem& it, const ReqEnt
   }
 }
 
-template <int G>
-__global__ __launch_bounds__(256) void attend_group_mfma_kernel(AttnArgs a) {
+template <int G, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void attend_group_mfma_kernel(AttnArgs a) {
   constexpr int D = 128;
   constexpr int ROW_BYTES = D * 2;
   constexpr int VT_STRIDE = 20;  // bf16 per V^T row (40 B: 16 rows of a read on distinct banks)
   static_assert(G == 4 || G == 8 || G == 16, "groups of 4, 8 or 16 heads");
+  static_assert((W == 4 || W == 8) && G % W == 0, "4 or 8 waves, each publishing G / W heads");
   // Per wave: the final partial context [16 rows][D]; while blocks stream,
   // its first 128 * VT_STRIDE bf16 hold the wave's V^T staging.
-  __shared__ __attribute__((aligned(16))) float s_acc[4][16][D];
-  __shared__ float s_m[4][16], s_l[4][16];
+  __shared__ __attribute__((aligned(16))) float s_acc[W][16][D];
+  __shared__ float s_m[W][16], s_l[W][16];
 
   const WorkItem it = plan_item(a);
   const ReqEntry rq = it.rq;
@@ -702,10 +703,9 @@ __global__ __launch_bounds__(256) void attend_group_mfma_kernel(AttnArgs a) {
   }
 
   // K: lane (key ql, dims 32 dc + 8 g); V: lane (keys 4 g + i, dims 8 ql..+7).
-  auto load_block = [&](int b, uint4* kk, uint4* vv) {
+  auto load_block = [&](int b, int32_t page, uint4* kk, uint4* vv) {
     const int row0 = b * kBlockRows;
-    const int64_t base = (int64_t)pt[row0 / S] * a.page_bytes + head_off +
-                         (int64_t)(row0 % S) * ROW_BYTES;
+    const int64_t base = (int64_t)page * a.page_bytes + head_off + (int64_t)(row0 % S) * ROW_BYTES;
     const auto rk = block_rsrc(a.k_layer + base, kBlockRows * ROW_BYTES);
     const auto rv = block_rsrc(a.v_layer + base, kBlockRows * ROW_BYTES);
 #pragma unroll
@@ -766,21 +766,30 @@ __global__ __launch_bounds__(256) void attend_group_mfma_kernel(AttnArgs a) {
       if constexpr (edge) sc[j] += valid_k[j];
     }
     float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mb = xor32_max(xor16_max(mb));
-    const float mn = fmaxf(m, mb * a.scale_log2e);
-    const float alpha = fast_exp2(m - mn);
-    float p[4], ps = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p[j] = fast_exp2(fmaf(sc[j], a.scale_log2e, -mn));
-      ps += p[j];
-    }
-    l = fmaf(l, alpha, xor32_sum(xor16_sum(ps)));
-    m = mn;
-    if (alpha != 1.f) {
+    const float cand = xor32_max(xor16_max(mb)) * a.scale_log2e;
+    // Lazy rescale: a head's running maximum moves (and its context and sum
+    // are rescaled) only when some head of the wave sees a block maximum more
+    // than kSlack above its own, so the weights exp2(s - m) stay below
+    // 2^kSlack, which float32 sums and bf16 weights carry as well as values
+    // below 1.  The branch is wave-uniform and rare after the first block
+    // (which always moves m from -inf); the context stays in the matrix
+    // accumulators in between.
+    constexpr float kSlack = 8.f;
+    if (__builtin_expect(__any(cand > m + kSlack), 0)) {
+      const float mn = fmaxf(m, cand);
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+      m = mn;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
     }
+    float p[4], ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = fast_exp2(fmaf(sc[j], a.scale_log2e, -m));
+      ps += p[j];
+    }
+    l += xor32_sum(xor16_sum(ps));
     typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
     bf16x4_t pb4;
 #pragma unroll
@@ -794,28 +803,56 @@ __global__ __launch_bounds__(256) void attend_group_mfma_kernel(AttnArgs a) {
     }
   };
 
+  // Blocks first, first+4, ..., wave_last of this wave (index j: block
+  // first + 4 j), the next block's loads always issued before the current one
+  // is computed.  Only the final block can be the request's last (masked)
+  // block, so it is peeled off the loop: the loop body is one unmasked step
+  // per buffer and the context stays in the same registers throughout.
+  // Page IDs come 64 blocks at a time in one vector load (lane i: block
+  // j0 + i) and are picked out with readlane, so issuing a block's loads
+  // never waits on a page-table round trip.
   {
     const int end = it.blk_end;
     const int first = it.blk_begin + wave;
     if (first < end) {
-      const int wave_last = first + ((end - 1 - first) / 4) * 4;
+      const int wave_last = first + ((end - 1 - first) / W) * W;
+      const int nj = (wave_last - first) / W + 1;
+      const bool edge = wave_last == last_blk;
+      int32_t pv = 0;
+      int j0 = 0;
+      auto fetch_pages = [&](int jf) {
+        const int bb = min(first + W * (jf + lane), wave_last);
+        pv = a.page_table[(int64_t)rq.pt_row * a.pt_stride + (bb * kBlockRows) / S];
+        j0 = jf;
+        // Complete the load here, so that no later use of pv (after this
+        // rare branch rejoins the loop) waits on the K/V loads in flight.
+        __builtin_amdgcn_s_waitcnt(0);
+      };
+      auto page_at = [&](int jj) -> int32_t { return __builtin_amdgcn_readlane(pv, jj - j0); };
+      auto blk = [&](int jj) { return first + W * jj; };
       uint4 ka[4], va[4], kb[4], vb[4];
-      load_block(first, ka, va);
-      for (int b = first;; b += 8) {
-        const int b1 = min(b + 4, wave_last);
-        load_block(b1, kb, vb);
-        if (b == last_blk)
-          step(b, ka, va, std::true_type{});
+      fetch_pages(0);
+      load_block(first, page_at(0), ka, va);
+      int jc = 0;
+      for (; jc + 2 < nj; jc += 2) {  // blocks jc and jc + 1 both precede the final one
+        if (jc + 2 - j0 > 63) fetch_pages(jc + 1);
+        load_block(blk(jc + 1), page_at(jc + 1), kb, vb);
+        step(blk(jc), ka, va, std::false_type{});
+        load_block(blk(jc + 2), page_at(jc + 2), ka, va);
+        step(blk(jc + 1), kb, vb, std::false_type{});
+      }
+      if (jc + 2 == nj) {
+        if (jc + 1 - j0 > 63) fetch_pages(jc + 1);
+        load_block(wave_last, page_at(jc + 1), kb, vb);
+        step(blk(jc), ka, va, std::false_type{});
+        if (edge)
+          step(wave_last, kb, vb, std::true_type{});
         else
-          step(b, ka, va, std::false_type{});
-        if (b + 4 > wave_last) break;
-        const int b2 = min(b + 8, wave_last);
-        load_block(b2, ka, va);
-        if (b1 == last_blk)
-          step(b1, kb, vb, std::true_type{});
-        else
-          step(b1, kb, vb, std::false_type{});
-        if (b + 8 > wave_last) break;
+          step(wave_last, kb, vb, std::false_type{});
+      } else if (edge) {
+        step(wave_last, ka, va, std::true_type{});
+      } else {
+        step(wave_last, ka, va, std::false_type{});
       }
     }
   }
@@ -832,20 +869,20 @@ __global__ __launch_bounds__(256) void attend_group_mfma_kernel(AttnArgs a) {
     s_l[wave][ql] = l;
   }
   __syncthreads();
-  constexpr int NH = G / 4;
+  constexpr int NH = G / W;
   const int c0 = (lane & 15) * 8;
   int heads[NH];
   float hm[NH], hl[NH], ho[NH][8];
 #pragma unroll
   for (int k = 0; k < NH; ++k) {
-    const int r = wave + 4 * k;
+    const int r = wave + W * k;
     heads[k] = qbase + r;
     float mx = s_m[0][r];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) mx = fmaxf(mx, s_m[w][r]);
-    float wt[4], lsum = 0.f;
+    for (int w = 1; w < W; ++w) mx = fmaxf(mx, s_m[w][r]);
+    float wt[W], lsum = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < W; ++w) {
       wt[w] = s_m[w][r] == -INFINITY ? 0.f : fast_exp2(s_m[w][r] - mx);
       lsum = fmaf(s_l[w][r], wt[w], lsum);
     }
@@ -853,7 +890,7 @@ __global__ __launch_bounds__(256) void attend_group_mfma_kernel(AttnArgs a) {
     for (int e = 0; e < 8; ++e) {
       float x = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) x = fmaf(s_acc[w][r][c0 + e], wt[w], x);
+      for (int w = 0; w < W; ++w) x = fmaf(s_acc[w][r][c0 + e], wt[w], x);
       ho[k][e] = x;
     }
     hm[k] = mx;
@@ -1085,13 +1122,19 @@ hipError_t launch_attention(const AttnArgs& args, int dtype, int num_items, hipS
     const dim3 grid(num_items, a.num_kv_heads * a.head_tiles);
     switch (share) {
       case 4:
-        hipLaunchKernelGGL(attend_group_mfma_kernel<4>, grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((attend_group_mfma_kernel<4, 4>), grid, dim3(256), 0, stream, a);
         break;
       case 8:
-        hipLaunchKernelGGL(attend_group_mfma_kernel<8>, grid, dim3(256), 0, stream, a);
+        if (a.waves != 4)
+          hipLaunchKernelGGL((attend_group_mfma_kernel<8, 8>), grid, dim3(512), 0, stream, a);
+        else
+          hipLaunchKernelGGL((attend_group_mfma_kernel<8, 4>), grid, dim3(256), 0, stream, a);
         break;
       default:
-        hipLaunchKernelGGL(attend_group_mfma_kernel<16>, grid, dim3(256), 0, stream, a);
+        if (a.waves != 4)
+          hipLaunchKernelGGL((attend_group_mfma_kernel<16, 8>), grid, dim3(512), 0, stream, a);
+        else
+          hipLaunchKernelGGL((attend_group_mfma_kernel<16, 4>), grid, dim3(256), 0, stream, a);
         break;
     }
     return hipGetLastError();

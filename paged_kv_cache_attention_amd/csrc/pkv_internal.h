@@ -61,7 +61,7 @@ struct AttnArgs {
   int32_t head_width;
   int32_t fuse_append;    // 1: write k_new/v_new at row t-1 and attend with them
   int32_t merge_mode;     // MergeMode
-  int32_t waves;          // waves per workgroup of the fast path (4 or 8)
+  int32_t waves;          // waves per workgroup of the fast paths (4 or 8; 0: per kernel)
   int32_t head_tiles;     // workgroups per K/V head along grid y, each serving
                           // an equal, consecutive share of its query heads
   int64_t page_bytes;     // H_kv * S * D * elt

@@ -93,7 +93,7 @@ struct pkv_plan {
   int32_t num_items = 0;
   int32_t total_splits = 0;
   int32_t num_split_reqs = 0;
-  int32_t waves = 4;
+  int32_t waves = 0;
   bool any_split = false;
   bool inline_plan = false;    // reqs/items go in the kernel arguments
   uint64_t rows_attended = 0;  // sum of t_r
@@ -280,8 +280,10 @@ pkv_status flush_patches(pkv_pool* p, hipStream_t stream) {
 
 // Workgroup shape and split-K chunk size (in 16-row blocks) of a plan.
 //
-// Workgroups have four waves unless PKV_OPT_WAVES asks for eight (measured
-// on MI355X: eight-wave workgroups were not faster on any workload here).
+// Waves per workgroup: PKV_OPT_WAVES, or 0 to let the launcher choose per
+// kernel (four for the vector kernels; eight for the matrix-core kernel when
+// a workgroup serves 8 or 16 query heads, whose requests then finish in half
+// the block steps per wave).
 // Requests split into chunks sized for about kTargetChunks (chunk, query
 // head) units -- four resident rounds of 256 CUs x 4 workgroups -- so a batch
 // with few (request, head) pairs still fills the GPU and one long context
@@ -298,7 +300,7 @@ SplitChoice choose_split(const pkv_pool* p, int64_t total_blocks) {
   // multi-head case (measured: splitting them further only adds partial
   // publishes).
   const int64_t H = p->desc.num_heads;
-  const int32_t waves = p->waves_option ? p->waves_option : 4;
+  const int32_t waves = p->waves_option;
   if (p->desc.split_blocks > 0) return {p->desc.split_blocks, waves};
   if (p->desc.split_blocks < 0) return {std::numeric_limits<int32_t>::max(), waves};
   constexpr int64_t kTargetChunks = 4096;

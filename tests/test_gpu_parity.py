@@ -306,6 +306,30 @@ def test_grouped_kv_heads(dtype, D, S, H, Hkv, split, merge):
     pkv.pkv_pool_destroy(pool2)
 
 
+@pytest.mark.parametrize("H,Hkv", [(16, 2), (16, 1), (32, 1), (24, 1), (8, 1)])
+@pytest.mark.parametrize("waves", [4, 8])
+@pytest.mark.parametrize("split", [0, 3])
+def test_grouped_workgroup_waves(H, Hkv, waves, split):
+    """The matrix-core grouped kernel with four and with eight waves per
+    workgroup (eight is the default when a workgroup serves 8 or 16 query
+    heads): every context against the oracle, unsplit and split."""
+    w = _small(f"gqa_waves_{H}_{Hkv}", "bf16", 128, 16, LENGTHS, heads=H, kv_heads=Hkv, seed=47,
+               layers=1)
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp, split=split, merge=2)
+    pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_WAVES, waves)
+    plan = pkv.pkv_plan_create(pool)
+    pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
+    qh = w.q(0)
+    out = torch.empty((w.n, H, 128), device="cuda")
+    pkv.pkv_plan_decode_attention(plan, 0, rows_to_device(qh, "bf16"), _pt_device(w), out)
+    torch.cuda.synchronize()
+    for r in range(w.n):
+        assert max_err(out[r], _oracle_decode(w, 0, r, qh)) <= TOL["bf16"], (r, int(w.lengths[r]))
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(pool)
+
+
 @pytest.mark.parametrize("dtype,D,H,Hkv", [("bf16", 128, 8, 2), ("f32", 64, 4, 1),
                                            ("f32", 40, 6, 3), ("bf16", 128, 32, 1),
                                            ("f32", 64, 12, 2)])
