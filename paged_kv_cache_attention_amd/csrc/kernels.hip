@@ -255,6 +255,25 @@ __device__ inline void finish_chunk(const AttnArgs& a, const WorkItem& it, const
   merge_wave<MCOLS, true>(a, it.req, rq, h, lane);
 }
 
+// Work item and head tile of a workgroup when the query heads of a K/V head
+// span `tiles` workgroups (grid x = items x tiles).  The tiles of one item
+// sit 8 workgroup IDs apart: workgroups are dealt to the 8 XCDs round-robin,
+// so they share an XCD, start together and read the same K/V blocks at about
+// the same time, and the later reads can hit that XCD's L2.  Bijective: each
+// group of up to 8 items takes 8 x tiles consecutive IDs.
+struct ItemTile {
+  int item, tile;
+};
+__device__ inline ItemTile item_tile(int tiles) {
+  const int id = blockIdx.x;
+  if (tiles == 1) return {id, 0};
+  const int n = gridDim.x / tiles;
+  const int span = 8 * tiles;
+  const int q = id / span, r = id - q * span;
+  const int m = min(8, n - 8 * q);
+  return {8 * q + r % m, r / m};
+}
+
 // ---------------------------------------------------------------------------
 // Fast path: rows of exactly 256 bytes (bf16 d_h=128, f32 d_h=64), pages a
 // multiple of 16 rows.  A workgroup of WAVES waves serves one (chunk, K/V
@@ -280,14 +299,15 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
   static_assert(NG * WPG == WAVES, "waves must split evenly into head groups");
   constexpr int G = NG * HPW;              // query heads per K/V head
 
-  const WorkItem it = plan_item(a);
-  const ReqEntry rq = it.rq;
-  // Grid y: K/V head kvh, and which of its head_tiles consecutive shares of
-  // G query heads this workgroup serves (one share unless the group exceeds
-  // what one workgroup holds or has an odd factor).
+  // Grid y: K/V head kvh; grid x: work item and which of head_tiles
+  // consecutive shares of G query heads this workgroup serves (one share
+  // unless the group exceeds what one workgroup holds or has an odd factor).
   const int tiles = a.head_tiles;
-  const int kvh = tiles == 1 ? (int)blockIdx.y : (int)blockIdx.y / tiles;
-  const int tile = (int)blockIdx.y - kvh * tiles;
+  const ItemTile itl = item_tile(tiles);
+  const WorkItem it = plan_item(a, itl.item);
+  const ReqEntry rq = it.rq;
+  const int kvh = blockIdx.y;
+  const int tile = itl.tile;
   const int lane = threadIdx.x & 63;
   // Wave-uniform: block indices, page-table reads and branches stay scalar, so
   // the page lookups go through the scalar cache and never wait on the
@@ -664,11 +684,12 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attend_group_mfma_kernel(AttnAr
   __shared__ __attribute__((aligned(16))) float s_acc[W][16][D];
   __shared__ float s_m[W][16], s_l[W][16];
 
-  const WorkItem it = plan_item(a);
-  const ReqEntry rq = it.rq;
   const int tiles = a.head_tiles;  // shares of G query heads per K/V head, as in the fast kernel
-  const int kvh = tiles == 1 ? (int)blockIdx.y : (int)blockIdx.y / tiles;
-  const int tile = (int)blockIdx.y - kvh * tiles;
+  const ItemTile itl = item_tile(tiles);
+  const WorkItem it = plan_item(a, itl.item);
+  const ReqEntry rq = it.rq;
+  const int kvh = blockIdx.y;
+  const int tile = itl.tile;
   const int qbase = (kvh * tiles + tile) * G;  // first query head of this workgroup
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1051,7 +1072,7 @@ __global__ __launch_bounds__(256) void patch_kernel(int32_t* arena, PatchBatch b
 template <typename T, int D, int WAVES, int HPW, int WPG>
 hipError_t launch_fast_shape(const AttnArgs& a, int num_items, hipStream_t stream) {
   hipLaunchKernelGGL((attend_fast_kernel<T, D, WAVES, HPW, WPG>),
-                     dim3(num_items, a.num_kv_heads * a.head_tiles), dim3(64 * WAVES), 0, stream,
+                     dim3(num_items * a.head_tiles, a.num_kv_heads), dim3(64 * WAVES), 0, stream,
                      a);
   return hipGetLastError();
 }
@@ -1119,7 +1140,7 @@ hipError_t launch_attention(const AttnArgs& args, int dtype, int num_items, hipS
     if (path_out) *path_out = KernelPath::kFast;
     const int share = head_share(group, {16, 8, 4});
     a.head_tiles = group / share;
-    const dim3 grid(num_items, a.num_kv_heads * a.head_tiles);
+    const dim3 grid(num_items * a.head_tiles, a.num_kv_heads);
     switch (share) {
       case 4:
         hipLaunchKernelGGL((attend_group_mfma_kernel<4, 4>), grid, dim3(256), 0, stream, a);

@@ -62,8 +62,8 @@ struct AttnArgs {
   int32_t fuse_append;    // 1: write k_new/v_new at row t-1 and attend with them
   int32_t merge_mode;     // MergeMode
   int32_t waves;          // waves per workgroup of the fast paths (4 or 8; 0: per kernel)
-  int32_t head_tiles;     // workgroups per K/V head along grid y, each serving
-                          // an equal, consecutive share of its query heads
+  int32_t head_tiles;     // workgroups per (item, K/V head), each serving an
+                          // equal, consecutive share of its query heads
   int64_t page_bytes;     // H_kv * S * D * elt
   int64_t head_bytes;     // S * D * elt
   float scale_log2e;      // log2(e) / sqrt(D)
@@ -77,8 +77,8 @@ struct AttnArgs {
 // The work item of this workgroup and request entry r of the plan.  The item
 // is uniform across the workgroup; readfirstlane keeps its fields in scalar
 // registers whichever source it came from.
-__device__ inline WorkItem plan_item(const AttnArgs& a) {
-  WorkItem w = a.num_inline ? a.inline_items[blockIdx.x] : a.items[blockIdx.x];
+__device__ inline WorkItem plan_item(const AttnArgs& a, int idx) {
+  WorkItem w = a.num_inline ? a.inline_items[idx] : a.items[idx];
   w.req = __builtin_amdgcn_readfirstlane(w.req);
   w.blk_begin = __builtin_amdgcn_readfirstlane(w.blk_begin);
   w.blk_end = __builtin_amdgcn_readfirstlane(w.blk_end);
@@ -89,6 +89,7 @@ __device__ inline WorkItem plan_item(const AttnArgs& a) {
   w.rq.partial_base = __builtin_amdgcn_readfirstlane(w.rq.partial_base);
   return w;
 }
+__device__ inline WorkItem plan_item(const AttnArgs& a) { return plan_item(a, blockIdx.x); }
 __device__ inline ReqEntry plan_req(const AttnArgs& a, int r) {
   return a.num_inline ? a.inline_reqs[r] : a.reqs[r];
 }
