@@ -27,8 +27,6 @@ constexpr int kD = 128;            // head width of this kernel (256-byte bf16 r
 constexpr int kRowBytes = kD * 2;
 static_assert(kPrefillTileRows == 128, "four waves of 32 query rows");
 constexpr int kBlockKeys = 64;     // keys per LDS block
-constexpr int kKStride = kD + 8;   // bf16 per K row in LDS (272 B: rows 4 banks apart)
-constexpr int kVStride = kBlockKeys + 4;  // bf16 per transposed V row in LDS (136 B)
 constexpr int kXcds = 8;           // accelerator complex dies of an MI355X
 
 __device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -82,19 +80,26 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Transposed V in LDS: sV[dim][key] with the 4-key groups of each row
-// XOR-swizzled by the row's 32-dim band, so the 64 lanes that store one dim
-// each (16 dims apart across lanes, 34 banks per row) hit 64 distinct banks;
-// readers apply the same swizzle (uniform across a 16-dim tile).
-__device__ inline int vt_index(int dim, int key) {
-  return dim * kVStride + (((key >> 2) ^ (((dim >> 5) & 3) << 2)) << 2) + (key & 3);
+// K and V blocks in LDS: 64 rows of 256 bytes each, row-major, with the
+// 16-byte chunks of row r stored XOR-swizzled by r mod 16.  Sixteen lanes
+// reading one chunk column of sixteen rows (the score operand), or four rows
+// of one 32-byte span each (the transposing value read), then hit distinct
+// banks.  Byte offset of chunk c of row r:
+__device__ inline int kv_byte(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ (row & 15)) << 4);
 }
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Workgroup: 4 waves on one tile (request, up to 128 consecutive chunk rows)
 // and one query head; each wave owns 32 query rows as two sets of 16.  Every
 // 64-key block of the rows the tile can see (0 .. the tile's last position)
-// is staged in LDS -- K as rows, V transposed -- while the next block's K/V
-// are already being fetched into registers.
+// goes to LDS by direct buffer-to-LDS loads (no registers, no stores), into
+// one of two buffers while the other one is computed on: one barrier per
+// block.  The request's last, partial block takes clamped loads through
+// registers instead, so no read passes its pages and every row is finite.
 //
 // Scores are formed transposed, S^T = K Q^T (A operand: 16 keys x 32 dims of
 // K from LDS; B operand: Q held in registers), so lane l holds, for query
@@ -102,20 +107,25 @@ __device__ inline int vt_index(int dim, int key) {
 // Those are exactly the A-operand elements of the value product O = P V when
 // the 32 keys of an MFMA step are taken in the order {tile 2c: 4g..4g+3,
 // tile 2c+1: 4g..4g+3} for lane group g -- so probabilities never move
-// between lanes; the transposed V is read in the same key order.  Each K or V
-// fragment read from LDS feeds the MFMAs of both query sets.  Online softmax
-// per query in log2 units; the running maximum and sum are reduced across
-// the four lane groups with shuffles, and the maximum moves lazily (only by
-// more than 2^8 in weight).  The context accumulates in the MFMA
-// output layout (lane l: rows 4(l/16)..+3, column l%16 of each 16-column
-// tile), whose per-row scale factors come from the owning lanes by shuffle.
+// between lanes.  The V operand (8 keys of one dim per lane, in that order)
+// comes from row-major V with two transposing LDS reads (ds_read_b64_tr_b16:
+// in each 16-lane group, lane j receives halfword j%4 of the 8 bytes that
+// lane 4k + j/4 addresses, k = 0..3; lane i addressing key base + i/4, dims
+// 16 dt + 4 (i%4)..+3 then hands lane j the dim 16 dt + j of keys base..+3).
+// Each K or V fragment read from LDS feeds the MFMAs of both query sets.
+// Online softmax per query in log2 units; the running maximum and sum are
+// reduced across the four lane groups with permlane swaps, and the maximum
+// moves lazily (only by more than 2^8 in weight).  The context accumulates in
+// the MFMA output layout (lane l: rows 4(l/16)..+3, column l%16 of each
+// 16-column tile), whose per-row scale factors come from the owning lanes by
+// shuffle.
 //
-// PAGE16: pages of exactly 16 rows, so a row's page and slot are a shift and
-// a mask instead of a division (the lookups run per lane for every load).
+// PAGE16: pages of exactly 16 rows (a row's page and slot are a shift and a
+// mask instead of a division).
 template <bool PAGE16>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kBlockKeys * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kD * kVStride];
+  // [buffer][0: K, 1: V][64 rows x 256 B], swizzled as kv_byte describes
+  __shared__ __attribute__((aligned(16))) char sKV[2][2][kBlockKeys * kRowBytes];
 
   // Work item (query head, tile): consecutive items share a request's K/V
   // (the tile list is grouped by request).  Workgroups go to the eight XCDs
@@ -164,89 +174,69 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[qs][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Global -> register fetch of one block (keys clamped to the last row the
-  // tile may read, so no lookup goes past the request's pages).  K chunk
-  // c = tid + 256 i is key c/16, bytes 16 (c%16) of its row; V chunk i of a
-  // thread is key 2 vpair + i/2, bytes 32 vdg + 16 (i%2).
-  const int vpair = tid >> 3;
-  const int vdg = tid & 7;
-  auto row_off = [&](int key) -> int64_t {
-    const int page = PAGE16 ? key >> 4 : key / S;
-    const int slot = PAGE16 ? key & 15 : key % S;
-    return (int64_t)pt[page] * a.page_bytes + head_off + (int64_t)slot * kRowBytes;
-  };
-  auto k_src = [&](int key0, int i) -> const uint4* {
-    const int c = tid + 256 * i;
-    const int key = min(key0 + (c >> 4), tile.key_end - 1);
-    return reinterpret_cast<const uint4*>(a.k_layer + row_off(key) + (c & 15) * 16);
-  };
-  auto v_src = [&](int key0, int i) -> const uint4* {
-    const int key = min(key0 + 2 * vpair + (i >> 1), tile.key_end - 1);
-    return reinterpret_cast<const uint4*>(a.v_layer + row_off(key) + vdg * 32 + (i & 1) * 16);
-  };
-  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
-  // A block's K/V.  With 16-row pages and all 64 keys visible, K load i is
-  // page key0/16 + i for the whole workgroup (thread t: bytes 16 t) and a
-  // wave's V rows all lie in page key0/16 + wave: four wave-uniform page
-  // reads and constant lane offsets.  Otherwise (other page sizes, or the
-  // tile's last, clamped block) every lane looks its row up.
-  auto fetch = [&](int key0) {
-    if (PAGE16 && key0 + kBlockKeys <= tile.key_end) {
-      const const_i32_ptr ptc = (const_i32_ptr)pt;
-      const int pg0 = key0 >> 4;
-      const char* kp0 = a.k_layer + (int64_t)ptc[pg0] * a.page_bytes + head_off;
-      const char* kp1 = a.k_layer + (int64_t)ptc[pg0 + 1] * a.page_bytes + head_off;
-      const char* kp2 = a.k_layer + (int64_t)ptc[pg0 + 2] * a.page_bytes + head_off;
-      const char* kp3 = a.k_layer + (int64_t)ptc[pg0 + 3] * a.page_bytes + head_off;
-      const char* vp = a.v_layer + (int64_t)ptc[pg0 + wave] * a.page_bytes + head_off;
-      k0 = page_load(kp0, tid * 16);
-      k1 = page_load(kp1, tid * 16);
-      k2 = page_load(kp2, tid * 16);
-      k3 = page_load(kp3, tid * 16);
-      const uint32_t vrow = (uint32_t)(2 * (vpair & 7)) * kRowBytes + vdg * 32;
-      v0 = page_load(vp, vrow);
-      v1 = page_load(vp, vrow + 16);
-      v2 = page_load(vp, vrow + kRowBytes);
-      v3 = page_load(vp, vrow + kRowBytes + 16);
+  // Staging of one 64-key block into buffer b.  Wave w, part i (0..3) covers
+  // block rows 16 i + 4 w .. +3, which lie in one page; lane L takes row
+  // 16 i + 4 w + L/16 and LDS chunk position L%16, i.e. global chunk
+  // (L%16) ^ (row & 15) of that row, and lands at LDS byte base + 16 L.
+  const int lrow = lane >> 4;   // row within the part
+  const int lpos = lane & 15;   // LDS chunk position
+  const const_i32_ptr ptc = (const_i32_ptr)pt;
+  auto stage = [&](int key0, int b) {
+    if (key0 + kBlockKeys <= tile.key_end) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r0 = 16 * i + 4 * wave;          // first block row of the part
+        const int key = key0 + r0;
+        const int page_idx = PAGE16 ? key >> 4 : key / S;
+        const int slot0 = PAGE16 ? key & 15 : key - page_idx * S;
+        const int64_t page = (int64_t)ptc[page_idx] * a.page_bytes + head_off;
+        const int r = r0 + lrow;
+        const int voff = (slot0 + lrow) * kRowBytes + ((lpos ^ (r & 15)) << 4);
+        const auto rk = __builtin_amdgcn_make_buffer_rsrc(a.k_layer + page, 0, S * kRowBytes,
+                                                          0x00020000);
+        const auto rv = __builtin_amdgcn_make_buffer_rsrc(a.v_layer + page, 0, S * kRowBytes,
+                                                          0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)&sKV[b][0][r0 * kRowBytes], 16,
+                                                 voff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&sKV[b][1][r0 * kRowBytes], 16,
+                                                 voff, 0, 0, 0);
+      }
     } else {
-      k0 = *k_src(key0, 0);
-      k1 = *k_src(key0, 1);
-      k2 = *k_src(key0, 2);
-      k3 = *k_src(key0, 3);
-      v0 = *v_src(key0, 0);
-      v1 = *v_src(key0, 1);
-      v2 = *v_src(key0, 2);
-      v3 = *v_src(key0, 3);
+      // Partial block: keys clamped to the last row the tile may read (the
+      // clamped rows are masked, and finite, so they add nothing).
+      uint4 kx[4], vx[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * i + 4 * wave + lrow;
+        const int key = min(key0 + r, tile.key_end - 1);
+        const int page_idx = PAGE16 ? key >> 4 : key / S;
+        const int slot = PAGE16 ? key & 15 : key - page_idx * S;
+        const int64_t off = (int64_t)pt[page_idx] * a.page_bytes + head_off +
+                            (int64_t)slot * kRowBytes + ((lpos ^ (r & 15)) << 4);
+        kx[i] = *reinterpret_cast<const uint4*>(a.k_layer + off);
+        vx[i] = *reinterpret_cast<const uint4*>(a.v_layer + off);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * i + 4 * wave + lrow;
+        *reinterpret_cast<uint4*>(&sKV[b][0][r * kRowBytes + lpos * 16]) = kx[i];
+        *reinterpret_cast<uint4*>(&sKV[b][1][r * kRowBytes + lpos * 16]) = vx[i];
+      }
     }
   };
-  fetch(0);
+  stage(0, 0);
 
   const int nblocks = (tile.key_end + kBlockKeys - 1) / kBlockKeys;
   for (int kb = 0; kb < nblocks; ++kb) {
     const int key0 = kb * kBlockKeys;
-    __syncthreads();  // every wave is done with the previous block in LDS
-    {
-      auto store_k = [&](int i, const uint4& u) {
-        const int c = tid + 256 * i;
-        *reinterpret_cast<uint4*>(&sK[(c >> 4) * kKStride + (c & 15) * 8]) = u;
-      };
-      store_k(0, k0);
-      store_k(1, k1);
-      store_k(2, k2);
-      store_k(3, k3);
-      // V transposed; one 32-bit store per dim holds the key pair (v0, v1:
-      // key 2 vpair, dims 16 vdg + 0..15; v2, v3: key 2 vpair + 1).
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t w0 = word_of(e < 8 ? v0 : v1, (e & 7) >> 1);
-        const uint32_t w1 = word_of(e < 8 ? v2 : v3, (e & 7) >> 1);
-        const uint32_t pair = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
-                                      : ((w0 & 0xffffu) | (w1 << 16));
-        *reinterpret_cast<uint32_t*>(&sV[vt_index(16 * vdg + e, 2 * vpair)]) = pair;
-      }
-    }
+    const int b = kb & 1;
+    // This wave's loads and stores into buffer b are complete; the barrier
+    // then makes every wave's visible and ends all reads of buffer b ^ 1.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kb + 1 < nblocks) fetch(key0 + kBlockKeys);  // flies during this block's math
+    if (kb + 1 < nblocks) stage(key0 + kBlockKeys, b ^ 1);  // flies during this block's math
+    const char* sK = sKV[b][0];
+    const char* sV = sKV[b][1];
 
     // A wave whose queries all precede every key of the block has nothing
     // to add from it (causal), and an empty wave has nothing at all.  Block 0
@@ -262,8 +252,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dc = 0; dc < 4; ++dc) {
-        const bf16x8_t kf = as_bf16x8(
-            *reinterpret_cast<const uint4*>(&sK[(16 * kt + ql) * kKStride + 32 * dc + 8 * g]));
+        const bf16x8_t kf =
+            as_bf16x8(*reinterpret_cast<const uint4*>(sK + kv_byte(16 * kt + ql, 4 * dc + g)));
         c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][dc], c0, 0, 0, 0);
         c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][dc], c1, 0, 0, 0);
       }
@@ -341,13 +331,19 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         pu.w = pack_bf16x2(s[qs][2 * kc + 1][2], s[qs][2 * kc + 1][3]);
         pf[qs] = as_bf16x8(pu);
       }
+      // transposing reads: lane (g, i) addresses key 32 kc + 4 g + i/4 (and
+      // + 16), dims 16 dt + 4 (i%4)..+3
+      const int vrow = 32 * kc + 4 * g + (ql >> 2);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const int dim = 16 * dt + ql;
-        const uint2 lo = *reinterpret_cast<const uint2*>(&sV[vt_index(dim, 32 * kc + 4 * g)]);
-        const uint2 hi =
-            *reinterpret_cast<const uint2*>(&sV[vt_index(dim, 32 * kc + 16 + 4 * g)]);
-        const bf16x8_t vf = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
+        const int chunk = 2 * dt + ((ql & 3) >> 1);
+        const int half = (ql & 1) * 8;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(sV + kv_byte(vrow, chunk) + half));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(sV + kv_byte(vrow + 16, chunk) + half));
+        const bf16x8_t vf = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[0], vf, acc[0][dt], 0, 0, 0);
         acc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[1], vf, acc[1][dt], 0, 0, 0);
       }
