@@ -41,20 +41,20 @@ HBM_PEAK_GBS = 8000.0
 # file under csrc/).
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
-    "batch32_fp32_l12": {"source": "kernels.hip", "sha256_16": "e34848d483ac3a1c",
-                         "fetch_kib": 44757.3, "write_kib": 2017.0,
+    "batch32_fp32_l12": {"source": "kernels.hip", "sha256_16": "c2afc447ff1e6120",
+                         "fetch_kib": 44774.7, "write_kib": 2017.0,
                          "algorithmic_bytes": 88971264},
-    "batch256_bf16": {"source": "kernels.hip", "sha256_16": "e34848d483ac3a1c",
-                      "fetch_kib": 4761782.2, "write_kib": 4341.3,
+    "batch256_bf16": {"source": "kernels.hip", "sha256_16": "c2afc447ff1e6120",
+                      "fetch_kib": 4761861.3, "write_kib": 4337.9,
                       "algorithmic_bytes": 9718775808},
-    "batch256_gqa8_bf16": {"source": "kernels.hip", "sha256_16": "e34848d483ac3a1c",
-                           "fetch_kib": 1193045.6, "write_kib": 4096.9,
+    "batch256_gqa8_bf16": {"source": "kernels.hip", "sha256_16": "c2afc447ff1e6120",
+                           "fetch_kib": 1192872.1, "write_kib": 4096.6,
                            "algorithmic_bytes": 2434412544},
-    "batch256_mqa_bf16": {"source": "kernels.hip", "sha256_16": "e34848d483ac3a1c",
-                          "fetch_kib": 298256.2, "write_kib": 4096.1,
+    "batch256_mqa_bf16": {"source": "kernels.hip", "sha256_16": "c2afc447ff1e6120",
+                          "fetch_kib": 152139.4, "write_kib": 4096.0,
                           "algorithmic_bytes": 309806592},
-    "prefill32_bf16": {"source": "prefill.hip", "sha256_16": "54cea5c7828b78eb",
-                       "fetch_kib": 700827.7, "write_kib": 518320.2,
+    "prefill32_bf16": {"source": "prefill.hip", "sha256_16": "abea1b0f35d52af6",
+                       "fetch_kib": 664078.7, "write_kib": 518320.0,
                        "algorithmic_bytes": 1854562304},
 }
 
