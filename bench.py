@@ -553,7 +553,8 @@ def tiny_latency(args):
 
 def cpu_baseline(w, budget_s: float) -> dict:
     """The oracle as it is, single-threaded, on a bounded sample of the same
-    workload: layer 0, requests in order until the time budget is spent.
+    workload: layer 0, requests in order, in repeated passes until the time
+    budget is spent (a pass over a small layer takes well under a second).
     Page generation is done before timing; only the oracle is timed."""
     import numpy as np
 
@@ -584,27 +585,35 @@ def cpu_baseline(w, budget_s: float) -> dict:
     limiter = threadpool_limits(limits=1) if threadpool_limits else None
     done_bytes = 0
     done = 0
+    passes = 0
+    out_of_time = False
     t0 = time.perf_counter()
     try:
-        for r, t, pt in prepared:
-            if w.appends:
-                oracle.append_and_attend(q[r], kn[r], vn[r], pages_k, pages_v, pt, t - 1,
-                                         w.page_size)
+        while not out_of_time:
+            for r, t, pt in prepared:
+                if w.appends:
+                    # re-appending the same row at the same slot is idempotent
+                    oracle.append_and_attend(q[r], kn[r], vn[r], pages_k, pages_v, pt, t - 1,
+                                             w.page_size)
+                else:
+                    oracle.paged_decode_attention(q[r], pages_k, pages_v, pt, t, w.page_size,
+                                                  num_kv_heads=w.hkv)
+                done_bytes += t * w.hkv * 2 * w.head_width * w.elt
+                done += 1
+                if time.perf_counter() - t0 > budget_s:
+                    out_of_time = True
+                    break
             else:
-                oracle.paged_decode_attention(q[r], pages_k, pages_v, pt, t, w.page_size,
-                                              num_kv_heads=w.hkv)
-            done_bytes += t * w.hkv * 2 * w.head_width * w.elt
-            done += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
+                passes += 1
     finally:
         if limiter is not None:
             limiter.restore_original_limits()
     el = time.perf_counter() - t0
     return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"layer 0 of {w.name}: {done} of {w.n} requests, all {w.heads} heads, "
-                      f"{done_bytes} K/V bytes in {el:.2f} s (float64, one thread)"}
+            "sample": f"layer 0 of {w.name}: {len(prepared)} of {w.n} requests, all {w.heads} "
+                      f"heads, {passes} full passes, {done} request calls, {done_bytes} K/V "
+                      f"bytes in {el:.2f} s (float64, one thread)"}
 
 
 if __name__ == "__main__":
