@@ -551,14 +551,16 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Grouped K/V heads on matrix cores: bf16, d_h = 128, pages of a multiple of
-// 16 rows, G = 4, 8 or 16 query heads per K/V head.  With G query heads
-// reading every K/V row, the score and value products of a 16-row block are
-// small dense contractions (G x 128 by 128 x 16, G x 16 by 16 x 128), so
-// they run on MFMA and the vector ALUs keep only the softmax.
+// 16 rows, G = 4, 8 or 16 query heads per workgroup (a share of a larger
+// group, see head_share).  With G query heads reading every K/V row, the
+// score and value products of a 16-row block are small dense contractions
+// (G x 128 by 128 x 16, G x 16 by 16 x 128), so they run on MFMA and the
+// vector ALUs keep only the softmax.
 //
-// Workgroup = 4 waves on one (chunk, K/V head); wave w takes blocks w, w+4,
-// ... of the chunk, for all G heads (rows of the MFMA tiles; G < 16 pads with
-// repeats of the last head, whose results are dropped).  Per block:
+// Workgroup = W waves (4, or 8 for G = 8 and 16) on one (chunk, K/V head);
+// wave w takes blocks w, w+W, ... of the chunk, for all G heads (rows of the
+// MFMA tiles; G < 16 pads with repeats of the last head, whose results are
+// dropped).  Per block:
 //   S^T = K Q^T on 16x16x32 MFMA: A = 16 keys x 32 dims of K, straight from
 //     memory (lane l: key l%16, dims 8(l/16)..+7 of a 32-dim slice); B = the
 //     G query rows held in registers.  Lane l gets, for head row l%16, the
@@ -569,7 +571,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
 //     Lane l accumulates, for head row l%16, dims 16 dt + 4(l/16)..+3, so the
 //     online-softmax rescale never leaves the lane.
 // Waves run independently until the end, then combine through LDS; each wave
-// publishes a quarter of the G heads (finish_heads: the contexts, or split-K
+// publishes G / W of the heads (finish_heads: the contexts, or split-K
 // partials and the last-arriver merge, all heads of a wave at once).
 // Reductions across the four 16-lane rows of a wave on the vector ALU
 // (gfx950 permlane swaps): with both operands x, permlane16_swap returns rows
