@@ -127,6 +127,89 @@ __device__ inline uint4 select4(bool c, const uint4& a, const uint4& b) {
   return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
 }
 
+// A lane's share of one K/V row on the fast path: VB bytes (8, 16 or 32) as
+// 32-bit words, so that 16 lanes hold a row of 128, 256 or 512 bytes.  Every
+// index below is a compile-time constant after unrolling (the words stay in
+// registers).
+template <int VB>
+struct RowVec {
+  static constexpr int kWords = VB / 4;
+  uint32_t w[kWords];
+
+  __device__ static inline RowVec zero() {
+    RowVec v;
+#pragma unroll
+    for (int k = 0; k < kWords; ++k) v.w[k] = 0;
+    return v;
+  }
+  __device__ static inline RowVec select(bool c, const RowVec& a, const RowVec& b) {
+    RowVec v;
+#pragma unroll
+    for (int k = 0; k < kWords; ++k) v.w[k] = c ? a.w[k] : b.w[k];
+    return v;
+  }
+  // Buffer load at a lane byte offset (16-byte pieces are adjacent).
+  __device__ static inline RowVec load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    RowVec v;
+    if constexpr (VB == 8) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+      v.w[0] = x[0];
+      v.w[1] = x[1];
+    } else {
+#pragma unroll
+      for (int h = 0; h < VB / 16; ++h) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16 * h), 0, 0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v.w[4 * h + k] = x[k];
+      }
+    }
+    return v;
+  }
+  __device__ static inline RowVec load(const char* p) {
+    RowVec v;
+    if constexpr (VB == 8) {
+      const uint2 x = *reinterpret_cast<const uint2*>(p);
+      v.w[0] = x.x;
+      v.w[1] = x.y;
+    } else {
+#pragma unroll
+      for (int h = 0; h < VB / 16; ++h) {
+        const uint4 x = *reinterpret_cast<const uint4*>(p + 16 * h);
+        v.w[4 * h] = x.x;
+        v.w[4 * h + 1] = x.y;
+        v.w[4 * h + 2] = x.z;
+        v.w[4 * h + 3] = x.w;
+      }
+    }
+    return v;
+  }
+  __device__ inline void store(char* p) const {
+    if constexpr (VB == 8) {
+      *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+    } else {
+#pragma unroll
+      for (int h = 0; h < VB / 16; ++h)
+        *reinterpret_cast<uint4*>(p + 16 * h) =
+            make_uint4(w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]);
+    }
+  }
+};
+
+// Elements of a RowVec as float (float32: one per word; bf16: two per word,
+// low half first).
+template <typename T, int VB>
+__device__ inline void unpack_row(const RowVec<VB>& v, float* f) {
+#pragma unroll
+  for (int k = 0; k < VB / 4; ++k) {
+    if constexpr (std::is_same<T, float>::value) {
+      f[k] = __uint_as_float(v.w[k]);
+    } else {
+      f[2 * k] = __uint_as_float(v.w[k] << 16);
+      f[2 * k + 1] = __uint_as_float(v.w[k] & 0xFFFF0000u);
+    }
+  }
+}
+
 template <bool COHERENT>
 __device__ inline float load_part(const float* p) {
   if constexpr (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -275,26 +358,27 @@ __device__ inline ItemTile item_tile(int tiles) {
 }
 
 // ---------------------------------------------------------------------------
-// Fast path: rows of exactly 256 bytes (bf16 d_h=128, f32 d_h=64), pages a
-// multiple of 16 rows.  A workgroup of WAVES waves serves one (chunk, K/V
+// Fast path: rows of 128, 256 or 512 bytes (bf16 d_h = 64, 128, 256; f32
+// d_h = 32, 64, 128), pages a multiple of 16 rows.  A workgroup of WAVES waves serves one (chunk, K/V
 // head) and the G query heads that share that K/V head: its waves form
 // WAVES/WPG head groups of HPW query heads each, and the WPG waves of a group
 // interleave the chunk's 16-row blocks, so each head group loads every K/V
 // byte of the chunk once for its HPW query heads (with one head group, once
 // for all G).  Multi-head attention is G = 1 (HPW = 1, WPG = WAVES).  A block is one contiguous 4 KiB slab of K and one of V.
-// Lane (g, c): row i*4+g of each of the 4 loads, 16 bytes at column c, so one
-// load instruction reads 1 KiB contiguous and the 16 lanes of a DPP row hold
-// one K/V row.  Each 16-lane group keeps its own online-softmax state per
+// Lane (g, c): row i*4+g of each of the 4 loads, VB = row bytes / 16 bytes at
+// column c, so one load instruction reads four whole rows and the 16 lanes of
+// a DPP row hold one K/V row (512-byte rows take two 16-byte loads per lane).  Each 16-lane group keeps its own online-softmax state per
 // query head; groups merge in-wave, the waves of a head group in LDS.
 template <typename T, int D, int WAVES, int HPW, int WPG>
 __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
-  using KV = KVTraits<T>;
-  constexpr int EPL = KV::kPerVec;
-  constexpr int LPR = D / EPL;
-  static_assert(LPR == 16, "fast path needs 256-byte rows");
+  constexpr int ROW_BYTES = D * (int)sizeof(T);
+  constexpr int VB = ROW_BYTES / 16;       // bytes of a row per lane
+  static_assert(VB == 8 || VB == 16 || VB == 32, "rows of 128, 256 or 512 bytes");
+  using Vec = RowVec<VB>;
+  constexpr int EPL = VB / (int)sizeof(T);  // elements of a row per lane
+  constexpr int LPR = 16;                  // lanes per row (one DPP row)
   constexpr int RPI = 64 / LPR;            // rows per load instruction
   constexpr int NI = kBlockRows / RPI;     // load instructions per block
-  constexpr int ROW_BYTES = D * (int)sizeof(T);
   constexpr int NG = WAVES / WPG;          // head groups per workgroup
   static_assert(NG * WPG == WAVES, "waves must split evenly into head groups");
   constexpr int G = NG * HPW;              // query heads per K/V head
@@ -331,23 +415,21 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     const int64_t qrow_bytes = (((int64_t)it.req * a.num_heads + qh0 + j) * D) * (int64_t)sizeof(T);
-    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + qrow_bytes +
-                                                    c * 16);
-    KV::unpack(u, qf[j]);
+    unpack_row<T>(Vec::load(static_cast<const char*>(a.q) + qrow_bytes + c * VB), qf[j]);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qf[j][e] *= a.scale_log2e;
   }
 
-  uint4 knew = make_uint4(0, 0, 0, 0), vnew = make_uint4(0, 0, 0, 0);
+  Vec knew = Vec::zero(), vnew = Vec::zero();
   if (fused) {
-    knew = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + kvrow_bytes + c * 16);
-    vnew = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + kvrow_bytes + c * 16);
+    knew = Vec::load(static_cast<const char*>(a.k_new) + kvrow_bytes + c * VB);
+    vnew = Vec::load(static_cast<const char*>(a.v_new) + kvrow_bytes + c * VB);
     if (wave == 0 && g == 0 && tile == 0) {
       const int pos = t - 1;
       const int64_t slot = (int64_t)pt[pos / S] * a.page_bytes + head_off +
-                           (int64_t)(pos % S) * ROW_BYTES + c * 16;
-      *reinterpret_cast<uint4*>(a.k_layer + slot) = knew;
-      *reinterpret_cast<uint4*>(a.v_layer + slot) = vnew;
+                           (int64_t)(pos % S) * ROW_BYTES + c * VB;
+      knew.store(a.k_layer + slot);
+      vnew.store(a.v_layer + slot);
     }
   }
 
@@ -361,16 +443,16 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
   // (scalar registers) and each load adds one unsigned 32-bit lane offset.
   uint32_t lane_off[NI];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) lane_off[i] = (uint32_t)((i * RPI + g) * ROW_BYTES + c * 16);
-  auto load_block = [&](int b, int32_t page, uint4* kk, uint4* vv) {
+  for (int i = 0; i < NI; ++i) lane_off[i] = (uint32_t)((i * RPI + g) * ROW_BYTES + c * VB);
+  auto load_block = [&](int b, int32_t page, Vec* kk, Vec* vv) {
     const int row0 = b * kBlockRows;
     const int64_t base = (int64_t)page * a.page_bytes + head_off + (int64_t)(row0 % S) * ROW_BYTES;
     const auto rk = block_rsrc(a.k_layer + base, kBlockRows * ROW_BYTES);
     const auto rv = block_rsrc(a.v_layer + base, kBlockRows * ROW_BYTES);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      kk[i] = load_b128(rk, lane_off[i]);
-      vv[i] = load_b128(rv, lane_off[i]);
+      kk[i] = Vec::load(rk, lane_off[i]);
+      vv[i] = Vec::load(rv, lane_off[i]);
     }
   };
 
@@ -386,7 +468,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
 
   // EDGE is a compile-time tag: the masked variant exists only as its own
   // code path, entered by a scalar branch for the request's last block.
-  auto step = [&](int b, uint4* kk, uint4* vv, auto edge_tag) {
+  auto step = [&](int b, Vec* kk, Vec* vv, auto edge_tag) {
     constexpr bool edge = decltype(edge_tag)::value;
     bool valid[NI];
 #pragma unroll
@@ -399,15 +481,15 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
         const int row = b * kBlockRows + i * RPI + g;
         const bool is_new = fused && row == t - 1;
         valid[i] = row < t;
-        kk[i] = select4(is_new, knew, kk[i]);
-        vv[i] = select4(valid[i], select4(is_new, vnew, vv[i]), make_uint4(0, 0, 0, 0));
+        kk[i] = Vec::select(is_new, knew, kk[i]);
+        vv[i] = Vec::select(valid[i], Vec::select(is_new, vnew, vv[i]), Vec::zero());
       }
     }
     float s[HPW][NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float kf[EPL];
-      KV::unpack(kk[i], kf);
+      unpack_row<T>(kk[i], kf);
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
         float d = 0.f;
@@ -441,7 +523,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float vf[EPL];
-      KV::unpack(vv[i], vf);
+      unpack_row<T>(vv[i], vf);
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
 #pragma unroll
@@ -463,7 +545,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
     const int first = it.blk_begin + sub;
     if (first < end) {
       const int wave_last = first + ((end - 1 - first) / WPG) * WPG;
-      uint4 ka[NI], va[NI], kb[NI], vb[NI];
+      Vec ka[NI], va[NI], kb[NI], vb[NI];
       load_block(first, page_of(first), ka, va);
       int32_t p_next = page_of(min(first + WPG, wave_last));
       for (int b = first;; b += 2 * WPG) {
@@ -544,7 +626,8 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
         for (int w = 0; w < WPG; ++w) x = fmaf(s_acc[w0 + w][j][c * EPL + e], wt[w], x);
         o[e] = x;
       }
-      finish_chunk<EPL, 1, D / 64>(a, it, rq, qh0 + j, lane, lane < LPR, c * EPL, mx, lsum, o);
+      finish_chunk<EPL, 1, (D + 63) / 64>(a, it, rq, qh0 + j, lane, lane < LPR, c * EPL, mx, lsum,
+                                          o);
     }
   }
 }
@@ -1084,9 +1167,11 @@ hipError_t launch_fast_shape(const AttnArgs& a, int num_items, hipStream_t strea
 // each K/V block is loaded once and serves all of its query heads; the waves
 // split the chunk's blocks.  Shares of 8 and 16 split over 2 and 4 head groups
 // of four (each block loaded by 2 or 4 waves): more heads per wave would
-// exceed the register file.
+// exceed the register file.  512-byte rows hold twice the registers per
+// block, so there a wave carries at most two heads and shares stop at 8.
 template <typename T, int D>
 hipError_t launch_fast(const AttnArgs& a, int share, int num_items, hipStream_t stream) {
+  constexpr bool wide = D * sizeof(T) == 512;
   switch (share) {
     case 1:
       return a.waves == 8 ? launch_fast_shape<T, D, 8, 1, 8>(a, num_items, stream)
@@ -1094,12 +1179,24 @@ hipError_t launch_fast(const AttnArgs& a, int share, int num_items, hipStream_t 
     case 2:
       return launch_fast_shape<T, D, 4, 2, 4>(a, num_items, stream);
     case 4:
-      return launch_fast_shape<T, D, 4, 4, 4>(a, num_items, stream);
+      if constexpr (wide) return launch_fast_shape<T, D, 4, 2, 2>(a, num_items, stream);
+      else return launch_fast_shape<T, D, 4, 4, 4>(a, num_items, stream);
     case 8:
-      return launch_fast_shape<T, D, 4, 4, 2>(a, num_items, stream);
+      if constexpr (wide) return launch_fast_shape<T, D, 4, 2, 1>(a, num_items, stream);
+      else return launch_fast_shape<T, D, 4, 4, 2>(a, num_items, stream);
     default:
-      return launch_fast_shape<T, D, 4, 4, 1>(a, num_items, stream);
+      if constexpr (wide) return hipErrorInvalidValue;  // shares of wide rows stop at 8
+      else return launch_fast_shape<T, D, 4, 4, 1>(a, num_items, stream);
   }
+}
+
+// Row bytes of the fast path's widths (0 when the width has no fast shape).
+static int fast_row_bytes(int dtype, int head_width) {
+  if (dtype == kDtypeF32 && (head_width == 32 || head_width == 64 || head_width == 128))
+    return head_width * 4;
+  if (dtype == kDtypeBF16 && (head_width == 64 || head_width == 128 || head_width == 256))
+    return head_width * 2;
+  return 0;
 }
 
 template <typename T>
@@ -1129,9 +1226,7 @@ bool group_mfma_supported(int dtype, int head_width, int page_size, int group) {
 
 bool fast_path_supported(int dtype, int head_width, int page_size, int group) {
   if (page_size % kBlockRows != 0 || group < 1) return false;
-  if (dtype == kDtypeF32) return head_width == 64;
-  if (dtype == kDtypeBF16) return head_width == 128;
-  return false;
+  return fast_row_bytes(dtype, head_width) != 0;
 }
 
 hipError_t launch_attention(const AttnArgs& args, int dtype, int num_items, hipStream_t stream,
@@ -1165,10 +1260,22 @@ hipError_t launch_attention(const AttnArgs& args, int dtype, int num_items, hipS
   const bool fast = fast_path_supported(dtype, a.head_width, a.page_size, group);
   if (path_out) *path_out = fast ? KernelPath::kFast : KernelPath::kGeneric;
   if (fast) {
-    const int share = head_share(group, {16, 8, 4, 2, 1});
+    const int share = fast_row_bytes(dtype, a.head_width) == 512
+                          ? head_share(group, {8, 4, 2, 1})
+                          : head_share(group, {16, 8, 4, 2, 1});
     a.head_tiles = group / share;
-    return dtype == kDtypeF32 ? launch_fast<float, 64>(a, share, num_items, stream)
-                              : launch_fast<bf16_t, 128>(a, share, num_items, stream);
+    if (dtype == kDtypeF32) {
+      switch (a.head_width) {
+        case 32: return launch_fast<float, 32>(a, share, num_items, stream);
+        case 64: return launch_fast<float, 64>(a, share, num_items, stream);
+        default: return launch_fast<float, 128>(a, share, num_items, stream);
+      }
+    }
+    switch (a.head_width) {
+      case 64: return launch_fast<bf16_t, 64>(a, share, num_items, stream);
+      case 128: return launch_fast<bf16_t, 128>(a, share, num_items, stream);
+      default: return launch_fast<bf16_t, 256>(a, share, num_items, stream);
+    }
   }
   a.head_tiles = 1;
   return dtype == kDtypeF32 ? launch_generic<float>(a, num_items, stream)

@@ -151,9 +151,14 @@ def test_tiny_fixture_transactions():
 
 # -------------------------------------------------------- batched, small --
 SMALL_CASES = [
-    ("f32", 64, 16), ("bf16", 128, 16), ("bf16", 128, 32),   # fast path
-    ("f32", 40, 16), ("bf16", 256, 16), ("f32", 64, 5), ("bf16", 128, 7),  # generic path
+    # fast path: rows of 256 bytes ...
+    ("f32", 64, 16), ("bf16", 128, 16), ("bf16", 128, 32),
+    # ... 128 and 512 bytes
+    ("bf16", 64, 16), ("f32", 32, 16), ("bf16", 256, 16), ("f32", 128, 32),
+    # generic path: other widths, page sizes that are not a multiple of 16
+    ("f32", 40, 16), ("bf16", 96, 16), ("f32", 64, 5), ("bf16", 128, 7),
 ]
+FAST_WIDTHS = {("f32", 32), ("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128), ("bf16", 256)}
 LENGTHS = [1, 15, 16, 17, 100, 333, 1000]
 
 
@@ -184,8 +189,8 @@ def test_batched_decode_small(dtype, D, S, split, merge):
     pkv.pkv_pool_destroy(pool)
 
 
-@pytest.mark.parametrize("dtype,D,S", [c for c in SMALL_CASES if (c[0], c[1]) in
-                                        (("f32", 64), ("bf16", 128)) and c[2] % 16 == 0])
+@pytest.mark.parametrize("dtype,D,S", [c for c in SMALL_CASES if (c[0], c[1]) in FAST_WIDTHS
+                                        and c[2] % 16 == 0])
 @pytest.mark.parametrize("split,merge", [(0, 2), (2, 2), (2, 0), (-1, 2)])
 def test_eight_wave_workgroups(dtype, D, S, split, merge):
     w = _small(f"w8_{dtype}_{D}_{S}", dtype, D, S, LENGTHS, seed=29)
@@ -255,6 +260,9 @@ GQA_CASES = [
     # workgroup), groups of 12 and 24 (4 and 8 per workgroup), 6 and 3 ...
     ("bf16", 128, 16, 32, 1), ("bf16", 128, 16, 24, 2), ("bf16", 128, 16, 12, 1),
     ("bf16", 128, 16, 6, 1), ("f32", 64, 16, 32, 1), ("f32", 64, 16, 6, 2),
+    # ... rows of 128 and 512 bytes (512: two heads per wave, shares up to 8) ...
+    ("bf16", 64, 16, 8, 1), ("f32", 32, 16, 16, 1), ("f32", 128, 16, 4, 2),
+    ("bf16", 256, 16, 8, 2), ("bf16", 256, 16, 16, 1),
     # ... and the generic kernel: a narrow head, a ragged page
     ("f32", 40, 16, 4, 1), ("bf16", 128, 7, 8, 2),
 ]
