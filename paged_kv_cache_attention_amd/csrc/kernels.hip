@@ -687,15 +687,15 @@ __device__ inline uint32_t word_of(const uint4& u, int i) {
 }
 
 // Ends one chunk for NH heads of a wave at once (lanes 0..15 hold columns
-// col0..col0+7 of each head's context).  Unsplit requests write contexts;
+// col0..col0+NCOL-1 of each head's context).  Unsplit requests write contexts;
 // split ones store all NH partials, order them with one wait, publish them
 // with NH counter increments issued back to back, and merge each head whose
 // last partial this chunk was -- one memory round trip per step instead of
 // one per head.
-template <int NH>
+template <int NH, int NCOL>
 __device__ void finish_heads(const AttnArgs& a, const WorkItem& it, const ReqEntry& rq,
                              const int* heads, int lane, int col0, const float* m,
-                             const float* l, const float (*o)[8]) {
+                             const float* l, const float (*o)[NCOL]) {
   const int D = a.head_width;
   const int H = a.num_heads;
   const bool own = lane < 16;
@@ -706,7 +706,7 @@ __device__ void finish_heads(const AttnArgs& a, const WorkItem& it, const ReqEnt
       float* out = a.out + ((int64_t)it.req * H + heads[k]) * D + col0;
       if (own) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) out[e] = o[k][e] * inv;
+        for (int e = 0; e < NCOL; ++e) out[e] = o[k][e] * inv;
       }
     }
     return;
@@ -717,7 +717,7 @@ __device__ void finish_heads(const AttnArgs& a, const WorkItem& it, const ReqEnt
     float* part = a.partials + ((int64_t)(rq.partial_base + it.split) * H + heads[k]) * (D + 2);
     if (own) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < NCOL; ++e) {
         if (coherent)
           store_part(part + 2 + col0 + e, o[k][e]);
         else
@@ -753,19 +753,23 @@ __device__ void finish_heads(const AttnArgs& a, const WorkItem& it, const ReqEnt
     if (lane == 0)
       (void)__hip_atomic_exchange(a.merge_count + (int64_t)it.req * H + heads[k], 0,
                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    merge_wave<2, true>(a, it.req, rq, heads[k], lane);
+    merge_wave<(16 * NCOL + 63) / 64, true>(a, it.req, rq, heads[k], lane);
   }
 }
 
-template <int G, int W>
-__global__ __launch_bounds__(64 * W, 8 / W) void attend_group_mfma_kernel(AttnArgs a) {
-  constexpr int D = 128;
+template <int G, int W, int D>
+__global__ __launch_bounds__(64 * W, D == 256 ? 1 : 8 / W) void attend_group_mfma_kernel(AttnArgs a) {
   constexpr int ROW_BYTES = D * 2;
+  static_assert(D == 64 || D == 128 || D == 256, "head widths 64, 128 or 256");
+  constexpr int ND = D / 32;     // 32-dim slices of the score product
+  constexpr int NT = D / 16;     // 16-dim tiles of the context (and dims per lane of V)
+  constexpr int VB = 2 * NT;     // bytes of a V row per lane
+  using VVec = RowVec<VB>;
   constexpr int VT_STRIDE = 20;  // bf16 per V^T row (40 B: 16 rows of a read on distinct banks)
   static_assert(G == 4 || G == 8 || G == 16, "groups of 4, 8 or 16 heads");
   static_assert((W == 4 || W == 8) && G % W == 0, "4 or 8 waves, each publishing G / W heads");
   // Per wave: the final partial context [16 rows][D]; while blocks stream,
-  // its first 128 * VT_STRIDE bf16 hold the wave's V^T staging.
+  // its first D * VT_STRIDE bf16 hold the wave's V^T staging.
   __shared__ __attribute__((aligned(16))) float s_acc[W][16][D];
   __shared__ float s_m[W][16], s_l[W][16];
 
@@ -789,16 +793,16 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attend_group_mfma_kernel(AttnAr
   const int64_t kvrow = ((int64_t)it.req * a.num_kv_heads + kvh) * ROW_BYTES;
   uint16_t* vt = reinterpret_cast<uint16_t*>(&s_acc[wave][0][0]);
 
-  bf16x8_t qf[4];
+  bf16x8_t qf[ND];
   {
     const int64_t qrow = ((int64_t)it.req * a.num_heads + qbase + min(ql, G - 1)) * ROW_BYTES;
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc)
+    for (int dc = 0; dc < ND; ++dc)
       qf[dc] = __builtin_bit_cast(
           bf16x8_t, *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + qrow +
                                                     (4 * dc + g) * 16));
   }
-  if (fused && wave == 0 && lane < 16 && tile == 0) {
+  if (fused && wave == 0 && lane < ROW_BYTES / 16 && tile == 0) {
     const int pos = t - 1;
     const int64_t slot = (int64_t)pt[pos / S] * a.page_bytes + head_off +
                          (int64_t)(pos % S) * ROW_BYTES + lane * 16;
@@ -808,25 +812,25 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attend_group_mfma_kernel(AttnAr
         *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + kvrow + lane * 16);
   }
 
-  // K: lane (key ql, dims 32 dc + 8 g); V: lane (keys 4 g + i, dims 8 ql..+7).
-  auto load_block = [&](int b, int32_t page, uint4* kk, uint4* vv) {
+  // K: lane (key ql, dims 32 dc + 8 g); V: lane (keys 4 g + i, dims NT ql..+NT-1).
+  auto load_block = [&](int b, int32_t page, uint4* kk, VVec* vv) {
     const int row0 = b * kBlockRows;
     const int64_t base = (int64_t)page * a.page_bytes + head_off + (int64_t)(row0 % S) * ROW_BYTES;
     const auto rk = block_rsrc(a.k_layer + base, kBlockRows * ROW_BYTES);
     const auto rv = block_rsrc(a.v_layer + base, kBlockRows * ROW_BYTES);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < ND; ++i)
       kk[i] = load_b128(rk, (uint32_t)(ql * ROW_BYTES + (4 * i + g) * 16));
-      vv[i] = load_b128(rv, (uint32_t)((4 * g + i) * ROW_BYTES + ql * 16));
-    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vv[i] = VVec::load(rv, (uint32_t)((4 * g + i) * ROW_BYTES + ql * VB));
   };
 
   float m = -INFINITY, l = 0.f;
-  f32x4_t acc[8];
+  f32x4_t acc[NT];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < NT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](int b, uint4* kk, uint4* vv, auto edge_tag) {
+  auto step = [&](int b, uint4* kk, VVec* vv, auto edge_tag) {
     constexpr bool edge = decltype(edge_tag)::value;
     float valid_k[4];
     if constexpr (edge) {
@@ -836,7 +840,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attend_group_mfma_kernel(AttnAr
       const int row0 = b * kBlockRows;
       if (fused && row0 + ql == t - 1) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < ND; ++i)
           kk[i] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + kvrow +
                                                   (4 * i + g) * 16);
       }
@@ -844,25 +848,24 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attend_group_mfma_kernel(AttnAr
       for (int i = 0; i < 4; ++i) {
         const int key = row0 + 4 * g + i;
         if (fused && key == t - 1)
-          vv[i] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + kvrow +
-                                                  ql * 16);
-        if (key >= t) vv[i] = make_uint4(0, 0, 0, 0);
+          vv[i] = VVec::load(static_cast<const char*>(a.v_new) + kvrow + ql * VB);
+        if (key >= t) vv[i] = VVec::zero();
         valid_k[i] = key < t ? 0.f : -INFINITY;
       }
     }
-    // V^T into this wave's LDS: 8 dims x 4 keys per lane, one 8-byte store per dim
+    // V^T into this wave's LDS: NT dims x 4 keys per lane, one 8-byte store per dim
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < NT; ++e) {
       const int w = e >> 1;
       const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
       uint2 x;
-      x.x = __builtin_amdgcn_perm(word_of(vv[1], w), word_of(vv[0], w), sel);
-      x.y = __builtin_amdgcn_perm(word_of(vv[3], w), word_of(vv[2], w), sel);
-      *reinterpret_cast<uint2*>(&vt[(8 * ql + e) * VT_STRIDE + 4 * g]) = x;
+      x.x = __builtin_amdgcn_perm(vv[1].w[w], vv[0].w[w], sel);
+      x.y = __builtin_amdgcn_perm(vv[3].w[w], vv[2].w[w], sel);
+      *reinterpret_cast<uint2*>(&vt[(NT * ql + e) * VT_STRIDE + 4 * g]) = x;
     }
     f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc)
+    for (int dc = 0; dc < ND; ++dc)
       c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[dc]), qf[dc], c,
                                                    0, 0, 0);
     float sc[4];
@@ -887,7 +890,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attend_group_mfma_kernel(AttnAr
       l *= alpha;
       m = mn;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
+      for (int dt = 0; dt < NT; ++dt) acc[dt] *= alpha;
     }
     float p[4], ps = 0.f;
 #pragma unroll
@@ -902,7 +905,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attend_group_mfma_kernel(AttnAr
     for (int j = 0; j < 4; ++j) pb4[j] = (__bf16)p[j];
     const s16x4_t pb = __builtin_bit_cast(s16x4_t, pb4);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+    for (int dt = 0; dt < NT; ++dt) {
       const uint2 v2 = *reinterpret_cast<const uint2*>(&vt[(16 * dt + ql) * VT_STRIDE + 4 * g]);
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, v2), pb,
                                                           acc[dt], 0, 0, 0);
@@ -936,7 +939,8 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attend_group_mfma_kernel(AttnAr
       };
       auto page_at = [&](int jj) -> int32_t { return __builtin_amdgcn_readlane(pv, jj - j0); };
       auto blk = [&](int jj) { return first + W * jj; };
-      uint4 ka[4], va[4], kb[4], vb[4];
+      uint4 ka[ND], kb[ND];
+      VVec va[4], vb[4];
       fetch_pages(0);
       load_block(first, page_at(0), ka, va);
       int jc = 0;
@@ -967,7 +971,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attend_group_mfma_kernel(AttnAr
   // LDS operations complete in order), then each wave publishes heads
   // wave, wave + 4, ...
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+  for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) s_acc[wave][ql][16 * dt + 4 * g + j] = acc[dt][j];
   if (g == 0) {
@@ -976,9 +980,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attend_group_mfma_kernel(AttnAr
   }
   __syncthreads();
   constexpr int NH = G / W;
-  const int c0 = (lane & 15) * 8;
+  const int c0 = (lane & 15) * NT;
   int heads[NH];
-  float hm[NH], hl[NH], ho[NH][8];
+  float hm[NH], hl[NH], ho[NH][NT];
 #pragma unroll
   for (int k = 0; k < NH; ++k) {
     const int r = wave + W * k;
@@ -993,7 +997,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attend_group_mfma_kernel(AttnAr
       lsum = fmaf(s_l[w][r], wt[w], lsum);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < NT; ++e) {
       float x = 0.f;
 #pragma unroll
       for (int w = 0; w < W; ++w) x = fmaf(s_acc[w][r][c0 + e], wt[w], x);
@@ -1002,7 +1006,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attend_group_mfma_kernel(AttnAr
     hm[k] = mx;
     hl[k] = lsum;
   }
-  finish_heads<NH>(a, it, rq, heads, lane, c0, hm, hl, ho);
+  finish_heads<NH, NT>(a, it, rq, heads, lane, c0, hm, hl, ho);
 }
 
 // ---------------------------------------------------------------------------
@@ -1220,8 +1224,41 @@ static int head_share(int group, std::initializer_list<int> shares) {
 }
 
 bool group_mfma_supported(int dtype, int head_width, int page_size, int group) {
-  return dtype == kDtypeBF16 && head_width == 128 && page_size % kBlockRows == 0 &&
-         group % 4 == 0;
+  return dtype == kDtypeBF16 && (head_width == 64 || head_width == 128 || head_width == 256) &&
+         page_size % kBlockRows == 0 && group % 4 == 0;
+}
+
+// The grouped matrix-core kernel for one head width: 16, 8 or 4 query heads
+// per workgroup; eight waves for shares of 8 and 16 unless PKV_OPT_WAVES asks
+// for four (d_h = 256 stays at four: eight waves' LDS would leave one
+// workgroup per CU).
+template <int D>
+hipError_t launch_group(const AttnArgs& a, int share, dim3 grid, hipStream_t stream) {
+  const bool eight = a.waves != 4 && D != 256;
+  switch (share) {
+    case 4:
+      hipLaunchKernelGGL((attend_group_mfma_kernel<4, 4, D>), grid, dim3(256), 0, stream, a);
+      break;
+    case 8:
+      if constexpr (D != 256) {
+        if (eight) {
+          hipLaunchKernelGGL((attend_group_mfma_kernel<8, 8, D>), grid, dim3(512), 0, stream, a);
+          break;
+        }
+      }
+      hipLaunchKernelGGL((attend_group_mfma_kernel<8, 4, D>), grid, dim3(256), 0, stream, a);
+      break;
+    default:
+      if constexpr (D != 256) {
+        if (eight) {
+          hipLaunchKernelGGL((attend_group_mfma_kernel<16, 8, D>), grid, dim3(512), 0, stream, a);
+          break;
+        }
+      }
+      hipLaunchKernelGGL((attend_group_mfma_kernel<16, 4, D>), grid, dim3(256), 0, stream, a);
+      break;
+  }
+  return hipGetLastError();
 }
 
 bool fast_path_supported(int dtype, int head_width, int page_size, int group) {
@@ -1238,24 +1275,11 @@ hipError_t launch_attention(const AttnArgs& args, int dtype, int num_items, hipS
     const int share = head_share(group, {16, 8, 4});
     a.head_tiles = group / share;
     const dim3 grid(num_items * a.head_tiles, a.num_kv_heads);
-    switch (share) {
-      case 4:
-        hipLaunchKernelGGL((attend_group_mfma_kernel<4, 4>), grid, dim3(256), 0, stream, a);
-        break;
-      case 8:
-        if (a.waves != 4)
-          hipLaunchKernelGGL((attend_group_mfma_kernel<8, 8>), grid, dim3(512), 0, stream, a);
-        else
-          hipLaunchKernelGGL((attend_group_mfma_kernel<8, 4>), grid, dim3(256), 0, stream, a);
-        break;
-      default:
-        if (a.waves != 4)
-          hipLaunchKernelGGL((attend_group_mfma_kernel<16, 8>), grid, dim3(512), 0, stream, a);
-        else
-          hipLaunchKernelGGL((attend_group_mfma_kernel<16, 4>), grid, dim3(256), 0, stream, a);
-        break;
+    switch (a.head_width) {
+      case 64: return launch_group<64>(a, share, grid, stream);
+      case 128: return launch_group<128>(a, share, grid, stream);
+      default: return launch_group<256>(a, share, grid, stream);
     }
-    return hipGetLastError();
   }
   const bool fast = fast_path_supported(dtype, a.head_width, a.page_size, group);
   if (path_out) *path_out = fast ? KernelPath::kFast : KernelPath::kGeneric;

@@ -262,7 +262,8 @@ GQA_CASES = [
     ("bf16", 128, 16, 6, 1), ("f32", 64, 16, 32, 1), ("f32", 64, 16, 6, 2),
     # ... rows of 128 and 512 bytes (512: two heads per wave, shares up to 8) ...
     ("bf16", 64, 16, 8, 1), ("f32", 32, 16, 16, 1), ("f32", 128, 16, 4, 2),
-    ("bf16", 256, 16, 8, 2), ("bf16", 256, 16, 16, 1),
+    ("bf16", 256, 16, 8, 2), ("bf16", 256, 16, 16, 1), ("bf16", 64, 32, 32, 1),
+    ("bf16", 256, 16, 4, 2),
     # ... and the generic kernel: a narrow head, a ragged page
     ("f32", 40, 16, 4, 1), ("bf16", 128, 7, 8, 2),
 ]
@@ -314,22 +315,24 @@ def test_grouped_kv_heads(dtype, D, S, H, Hkv, split, merge):
     pkv.pkv_pool_destroy(pool2)
 
 
-@pytest.mark.parametrize("H,Hkv", [(16, 2), (16, 1), (32, 1), (24, 1), (8, 1)])
+@pytest.mark.parametrize("D", [128, 64, 256])
+@pytest.mark.parametrize("H,Hkv", [(16, 2), (16, 1), (32, 1), (24, 1), (8, 1), (4, 1)])
 @pytest.mark.parametrize("waves", [4, 8])
 @pytest.mark.parametrize("split", [0, 3])
-def test_grouped_workgroup_waves(H, Hkv, waves, split):
-    """The matrix-core grouped kernel with four and with eight waves per
-    workgroup (eight is the default when a workgroup serves 8 or 16 query
-    heads): every context against the oracle, unsplit and split."""
-    w = _small(f"gqa_waves_{H}_{Hkv}", "bf16", 128, 16, LENGTHS, heads=H, kv_heads=Hkv, seed=47,
-               layers=1)
+def test_grouped_workgroup_waves(D, H, Hkv, waves, split):
+    """The matrix-core grouped kernel (bf16, head widths 64, 128 and 256) with
+    four and with eight waves per workgroup (eight is the default when a
+    workgroup serves 8 or 16 query heads, except at width 256): every context
+    against the oracle, unsplit and split."""
+    w = _small(f"gqa_waves_{D}_{H}_{Hkv}", "bf16", D, 16, LENGTHS, heads=H, kv_heads=Hkv,
+               seed=47, layers=1)
     kp, vp = device_pool(w)
     pool = _pool(w, kp, vp, split=split, merge=2)
     pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_WAVES, waves)
     plan = pkv.pkv_plan_create(pool)
     pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
     qh = w.q(0)
-    out = torch.empty((w.n, H, 128), device="cuda")
+    out = torch.empty((w.n, H, D), device="cuda")
     pkv.pkv_plan_decode_attention(plan, 0, rows_to_device(qh, "bf16"), _pt_device(w), out)
     torch.cuda.synchronize()
     for r in range(w.n):
