@@ -23,8 +23,6 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kD = 128;            // head width of this kernel (256-byte bf16 rows)
-constexpr int kRowBytes = kD * 2;
 static_assert(kPrefillTileRows == 128, "four waves of 32 query rows");
 constexpr int kBlockKeys = 64;     // keys per LDS block
 constexpr int kXcds = 8;           // accelerator complex dies of an MI355X
@@ -34,15 +32,6 @@ __device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8
 // Page-table reads that are uniform across a wave go through the scalar data
 // cache (the table is not written while this kernel runs).
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
-
-// Raw buffer access to one 4 KiB head-page: a scalar base in the descriptor,
-// a 32-bit lane offset per load (word 3: 32-bit data format for untyped
-// loads on gfx9-family parts).
-__device__ inline uint4 page_load(const char* page, uint32_t off) {
-  const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(page), 0, 16 * kRowBytes,
-                                                   0x00020000);
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
 
 // Reductions across the four 16-lane rows of a wave on the vector ALU
 // (gfx950 permlane swaps): with both operands x, permlane16_swap returns rows
@@ -80,13 +69,14 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// K and V blocks in LDS: 64 rows of 256 bytes each, row-major, with the
-// 16-byte chunks of row r stored XOR-swizzled by r mod 16.  Sixteen lanes
-// reading one chunk column of sixteen rows (the score operand), or four rows
-// of one 32-byte span each (the transposing value read), then hit distinct
-// banks.  Byte offset of chunk c of row r:
+// K and V blocks in LDS: 64 rows of 2 D bytes each (D / 8 chunks of 16
+// bytes), row-major, with the chunks of row r stored XOR-swizzled by r mod
+// (D / 8).  Lanes reading one chunk column of consecutive rows (the score
+// operand), or four rows of one 32-byte span each (the transposing value
+// read), then spread over the banks.  Byte offset of chunk c of row r:
+template <int D>
 __device__ inline int kv_byte(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ (row & 15)) << 4);
+  return row * (2 * D) + ((chunk ^ (row & (D / 8 - 1))) << 4);
 }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -122,8 +112,15 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 //
 // PAGE16: pages of exactly 16 rows (a row's page and slot are a shift and a
 // mask instead of a division).
-template <bool PAGE16>
+template <bool PAGE16, int D>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
+  static_assert(D == 64 || D == 128, "head widths 64 and 128");
+  constexpr int kRowBytes = 2 * D;
+  constexpr int ND = D / 32;     // 32-dim slices of the score product
+  constexpr int NT = D / 16;     // 16-dim tiles of the context
+  constexpr int NC = D / 8;      // 16-byte chunks per row
+  constexpr int RPI = 64 / NC;   // rows per 1 KiB staging load (4 or 8)
+  constexpr int NPART = 16 / RPI;  // staging loads per wave and block
   // [buffer][0: K, 1: V][64 rows x 256 B], swizzled as kv_byte describes
   __shared__ __attribute__((aligned(16))) char sKV[2][2][kBlockKeys * kRowBytes];
 
@@ -152,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   // last row; their results are not stored).
   const int wrow0 = 32 * wave;
   int my_pos[2];
-  bf16x8_t qf[2][4];
+  bf16x8_t qf[2][ND];
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
     const int row = min(wrow0 + 16 * qs + ql, tile.nq - 1);
@@ -161,37 +158,38 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
                                                       qrow * kRowBytes);
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) qf[qs][dc] = as_bf16x8(src[4 * dc + g]);
+    for (int dc = 0; dc < ND; ++dc) qf[qs][dc] = as_bf16x8(src[4 * dc + g]);
   }
   const int wave_first_pos = pos0 + min(wrow0, tile.nq - 1);
   const int wave_last_pos = pos0 + min(wrow0 + 31, tile.nq - 1);
   const bool wave_active = wrow0 < tile.nq;
 
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-  f32x4_t acc[2][8];
+  f32x4_t acc[2][NT];
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[qs][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < NT; ++dt) acc[qs][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Staging of one 64-key block into buffer b.  Wave w, part i (0..3) covers
-  // block rows 16 i + 4 w .. +3, which lie in one page; lane L takes row
-  // 16 i + 4 w + L/16 and LDS chunk position L%16, i.e. global chunk
-  // (L%16) ^ (row & 15) of that row, and lands at LDS byte base + 16 L.
-  const int lrow = lane >> 4;   // row within the part
-  const int lpos = lane & 15;   // LDS chunk position
+  // Staging of one 64-key block into buffer b.  Wave w, part i covers block
+  // rows RPI (4 i + w) .. +RPI-1 (RPI = 1024 / row bytes), which lie in one
+  // page; lane L takes row RPI (4 i + w) + L / NC and LDS chunk position
+  // L % NC, i.e. global chunk (L % NC) ^ (row mod NC) of that row, and lands
+  // at LDS byte base + 16 L.
+  const int lrow = lane / NC;   // row within the part
+  const int lpos = lane % NC;   // LDS chunk position
   const const_i32_ptr ptc = (const_i32_ptr)pt;
   auto stage = [&](int key0, int b) {
     if (key0 + kBlockKeys <= tile.key_end) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r0 = 16 * i + 4 * wave;          // first block row of the part
+      for (int i = 0; i < NPART; ++i) {
+        const int r0 = RPI * (4 * i + wave);       // first block row of the part
         const int key = key0 + r0;
         const int page_idx = PAGE16 ? key >> 4 : key / S;
         const int slot0 = PAGE16 ? key & 15 : key - page_idx * S;
         const int64_t page = (int64_t)ptc[page_idx] * a.page_bytes + head_off;
         const int r = r0 + lrow;
-        const int voff = (slot0 + lrow) * kRowBytes + ((lpos ^ (r & 15)) << 4);
+        const int voff = (slot0 + lrow) * kRowBytes + ((lpos ^ (r & (NC - 1))) << 4);
         const auto rk = __builtin_amdgcn_make_buffer_rsrc(a.k_layer + page, 0, S * kRowBytes,
                                                           0x00020000);
         const auto rv = __builtin_amdgcn_make_buffer_rsrc(a.v_layer + page, 0, S * kRowBytes,
@@ -204,21 +202,21 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     } else {
       // Partial block: keys clamped to the last row the tile may read (the
       // clamped rows are masked, and finite, so they add nothing).
-      uint4 kx[4], vx[4];
+      uint4 kx[NPART], vx[NPART];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * i + 4 * wave + lrow;
+      for (int i = 0; i < NPART; ++i) {
+        const int r = RPI * (4 * i + wave) + lrow;
         const int key = min(key0 + r, tile.key_end - 1);
         const int page_idx = PAGE16 ? key >> 4 : key / S;
         const int slot = PAGE16 ? key & 15 : key - page_idx * S;
         const int64_t off = (int64_t)pt[page_idx] * a.page_bytes + head_off +
-                            (int64_t)slot * kRowBytes + ((lpos ^ (r & 15)) << 4);
+                            (int64_t)slot * kRowBytes + ((lpos ^ (r & (NC - 1))) << 4);
         kx[i] = *reinterpret_cast<const uint4*>(a.k_layer + off);
         vx[i] = *reinterpret_cast<const uint4*>(a.v_layer + off);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * i + 4 * wave + lrow;
+      for (int i = 0; i < NPART; ++i) {
+        const int r = RPI * (4 * i + wave) + lrow;
         *reinterpret_cast<uint4*>(&sKV[b][0][r * kRowBytes + lpos * 16]) = kx[i];
         *reinterpret_cast<uint4*>(&sKV[b][1][r * kRowBytes + lpos * 16]) = vx[i];
       }
@@ -251,9 +249,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     for (int kt = 0; kt < 4; ++kt) {
       f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dc = 0; dc < 4; ++dc) {
+      for (int dc = 0; dc < ND; ++dc) {
         const bf16x8_t kf =
-            as_bf16x8(*reinterpret_cast<const uint4*>(sK + kv_byte(16 * kt + ql, 4 * dc + g)));
+            as_bf16x8(*reinterpret_cast<const uint4*>(sK + kv_byte<D>(16 * kt + ql, 4 * dc + g)));
         c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][dc], c0, 0, 0, 0);
         c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][dc], c1, 0, 0, 0);
       }
@@ -302,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         for (int j = 0; j < 4; ++j) {
           const float aj = __shfl(alpha, 4 * g + j);
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) acc[qs][dt][j] *= aj;
+          for (int dt = 0; dt < NT; ++dt) acc[qs][dt][j] *= aj;
         }
       }
     }
@@ -335,13 +333,13 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       // + 16), dims 16 dt + 4 (i%4)..+3
       const int vrow = 32 * kc + 4 * g + (ql >> 2);
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
+      for (int dt = 0; dt < NT; ++dt) {
         const int chunk = 2 * dt + ((ql & 3) >> 1);
         const int half = (ql & 1) * 8;
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(sV + kv_byte(vrow, chunk) + half));
+            (lds_s16x4_t*)(sV + kv_byte<D>(vrow, chunk) + half));
         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(sV + kv_byte(vrow + 16, chunk) + half));
+            (lds_s16x4_t*)(sV + kv_byte<D>(vrow + 16, chunk) + half));
         const bf16x8_t vf = __builtin_bit_cast(
             bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[0], vf, acc[0][dt], 0, 0, 0);
@@ -358,9 +356,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       const int row = wrow0 + 16 * qs + 4 * g + j;
       const float inv = 1.0f / __shfl(l[qs], 4 * g + j);
       if (row < tile.nq) {
-        float* o = a.out + ((int64_t)(tile.off + tile.i0 + row) * a.num_heads + h) * kD;
+        float* o = a.out + ((int64_t)(tile.off + tile.i0 + row) * a.num_heads + h) * D;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[16 * dt + ql] = acc[qs][dt][j] * inv;
+        for (int dt = 0; dt < NT; ++dt) o[16 * dt + ql] = acc[qs][dt][j] * inv;
       }
     }
 }
@@ -369,7 +367,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
 // K/V head), 16 bytes per lane.  It runs before the attention launch, which
 // reads the chunk's keys back from the pages (4 KiB contiguous per 16 keys
 // of a head, where the packed inputs put consecutive keys H_kv rows apart).
+template <int D>
 __global__ __launch_bounds__(256) void prefill_append_kernel(PrefillArgs a) {
+  constexpr int kRowBytes = 2 * D;
   const PrefillTile tile = a.tiles[blockIdx.x];
   const int kvh = blockIdx.y;
   const int S = a.page_size;
@@ -392,23 +392,32 @@ __global__ __launch_bounds__(256) void prefill_append_kernel(PrefillArgs a) {
 }  // namespace
 
 bool prefill_fast_supported(int dtype, int head_width, int page_size) {
-  return dtype == kDtypeBF16 && head_width == kD && page_size % 16 == 0;
+  return dtype == kDtypeBF16 && (head_width == 64 || head_width == 128) && page_size % 16 == 0;
 }
 
 hipError_t launch_prefill_append(const PrefillArgs& a, int num_tiles, hipStream_t stream) {
-  hipLaunchKernelGGL(prefill_append_kernel, dim3(num_tiles, a.num_kv_heads), dim3(256), 0, stream,
-                     a);
+  const dim3 grid(num_tiles, a.num_kv_heads);
+  if (a.head_bytes / a.page_size == 128)
+    hipLaunchKernelGGL(prefill_append_kernel<64>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_append_kernel<128>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_prefill_width(const PrefillArgs& a, int num_tiles, hipStream_t stream) {
+  if (a.page_size == 16)
+    hipLaunchKernelGGL((prefill_mfma_kernel<true, D>), dim3(num_tiles * a.num_heads), dim3(256),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_mfma_kernel<false, D>), dim3(num_tiles * a.num_heads), dim3(256),
+                       0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_attention(const PrefillArgs& a, int num_tiles, hipStream_t stream) {
-  if (a.page_size == 16)
-    hipLaunchKernelGGL(prefill_mfma_kernel<true>, dim3(num_tiles * a.num_heads), dim3(256), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL(prefill_mfma_kernel<false>, dim3(num_tiles * a.num_heads), dim3(256), 0,
-                       stream, a);
-  return hipGetLastError();
+  return a.head_bytes / a.page_size == 128 ? launch_prefill_width<64>(a, num_tiles, stream)
+                                           : launch_prefill_width<128>(a, num_tiles, stream);
 }
 
 }  // namespace pkv
