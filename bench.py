@@ -41,21 +41,21 @@ HBM_PEAK_GBS = 8000.0
 # file under csrc/).
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
-    "batch32_fp32_l12": {"source": "kernels.hip", "sha256_16": "c2afc447ff1e6120",
-                         "fetch_kib": 44774.7, "write_kib": 2017.0,
-                         "algorithmic_bytes": 88971264},
-    "batch256_bf16": {"source": "kernels.hip", "sha256_16": "c2afc447ff1e6120",
-                      "fetch_kib": 4761861.3, "write_kib": 4337.9,
-                      "algorithmic_bytes": 9718775808},
-    "batch256_gqa8_bf16": {"source": "kernels.hip", "sha256_16": "c2afc447ff1e6120",
-                           "fetch_kib": 1192872.1, "write_kib": 4096.6,
-                           "algorithmic_bytes": 2434412544},
-    "batch256_mqa_bf16": {"source": "kernels.hip", "sha256_16": "c2afc447ff1e6120",
-                          "fetch_kib": 152139.4, "write_kib": 4096.0,
-                          "algorithmic_bytes": 309806592},
-    "prefill32_bf16": {"source": "prefill.hip", "sha256_16": "abea1b0f35d52af6",
-                       "fetch_kib": 664078.7, "write_kib": 518320.0,
-                       "algorithmic_bytes": 1854562304},
+    "batch32_fp32_l12": {"source": "kernels.hip", "sha256_16": "12b65e9a7ab7d3bd",
+                       "fetch_kib": 44765.1, "write_kib": 2017.0,
+                       "algorithmic_bytes": 88971264},
+    "batch256_bf16": {"source": "kernels.hip", "sha256_16": "12b65e9a7ab7d3bd",
+                    "fetch_kib": 4761990.5, "write_kib": 4351.7,
+                    "algorithmic_bytes": 9718775808},
+    "batch256_gqa8_bf16": {"source": "kernels.hip", "sha256_16": "12b65e9a7ab7d3bd",
+                         "fetch_kib": 1193063.3, "write_kib": 4096.8,
+                         "algorithmic_bytes": 2434412544},
+    "batch256_mqa_bf16": {"source": "kernels.hip", "sha256_16": "12b65e9a7ab7d3bd",
+                        "fetch_kib": 152361.1, "write_kib": 4096.0,
+                        "algorithmic_bytes": 309806592},
+    "prefill32_bf16": {"source": "prefill.hip", "sha256_16": "75e54f88af0cf56b",
+                     "fetch_kib": 663788.8, "write_kib": 518320.1,
+                     "algorithmic_bytes": 1854562304},
 }
 
 
@@ -330,15 +330,16 @@ def step_spread(step, steps: int) -> dict:
 
 def dominant_kernel(w) -> str:
     """The attention kernel the library dispatches for a decode workload: the
-    matrix-core grouped kernel for bf16 d_h=128 when a multiple of 4 query
-    heads share a K/V head (16, 8 or 4 of them per workgroup; template
-    arguments: heads, waves per workgroup), else the vector fast path."""
+    matrix-core grouped kernel for bf16 d_h of 64, 128 or 256 when a
+    multiple of 4 query heads share a K/V head (template arguments: heads per
+    workgroup, waves per workgroup, d_h), else the vector fast path."""
     group = w.heads // w.hkv
-    if w.dtype == "bf16" and w.head_width == 128 and w.page_size % 16 == 0 and group % 4 == 0:
+    D = w.head_width
+    if w.dtype == "bf16" and D in (64, 128, 256) and w.page_size % 16 == 0 and group % 4 == 0:
         share = next(s for s in (16, 8, 4) if group % s == 0)
-        return f"attend_group_mfma_kernel<{share},{8 if share >= 8 else 4}>"
-    return ("attend_fast_kernel<float,64>" if w.dtype == "f32" else
-            "attend_fast_kernel<bf16,128>")
+        waves = 8 if share >= 8 and D != 256 else 4
+        return f"attend_group_mfma_kernel<{share},{waves},{D}>"
+    return f"attend_fast_kernel<{'float' if w.dtype == 'f32' else 'bf16'},{D}>"
 
 
 def prefill_bench(args, w):
