@@ -84,7 +84,8 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Workgroup: 4 waves on one tile (request, up to 128 consecutive chunk rows)
-// and one query head; each wave owns 32 query rows as two sets of 16.  Every
+// and one query head; each wave owns 32 query rows as two sets of 16 (at head
+// width 256: 8 waves of one set each, see prefill_waves).  Every
 // 64-key block of the rows the tile can see (0 .. the tile's last position)
 // goes to LDS by direct buffer-to-LDS loads (no registers, no stores), into
 // one of two buffers while the other one is computed on: one barrier per
@@ -112,15 +113,22 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 //
 // PAGE16: pages of exactly 16 rows (a row's page and slot are a shift and a
 // mask instead of a division).
+// Waves of a prefill workgroup: four with two 16-row query sets each, or, at
+// head width 256 (whose context and query registers are twice as many),
+// eight with one set each; either way a workgroup covers a 128-row tile.
+constexpr int prefill_waves(int D) { return D == 256 ? 8 : 4; }
+
 template <bool PAGE16, int D>
-__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
-  static_assert(D == 64 || D == 128, "head widths 64 and 128");
+__global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(PrefillArgs a) {
+  static_assert(D == 64 || D == 128 || D == 256, "head widths 64, 128 and 256");
+  constexpr int WAVES = prefill_waves(D);
+  constexpr int QS = 8 / WAVES;  // 16-row query sets per wave
   constexpr int kRowBytes = 2 * D;
   constexpr int ND = D / 32;     // 32-dim slices of the score product
   constexpr int NT = D / 16;     // 16-dim tiles of the context
   constexpr int NC = D / 8;      // 16-byte chunks per row
   constexpr int RPI = 64 / NC;   // rows per 1 KiB staging load (4 or 8)
-  constexpr int NPART = 16 / RPI;  // staging loads per wave and block
+  constexpr int NPART = 64 / RPI / WAVES;  // staging loads per wave and block
   // [buffer][0: K, 1: V][64 rows x 256 B], swizzled as kv_byte describes
   __shared__ __attribute__((aligned(16))) char sKV[2][2][kBlockKeys * kRowBytes];
 
@@ -147,11 +155,11 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
 
   // This lane's two query rows (rows past the tile's count attend like its
   // last row; their results are not stored).
-  const int wrow0 = 32 * wave;
-  int my_pos[2];
-  bf16x8_t qf[2][ND];
+  const int wrow0 = 16 * QS * wave;
+  int my_pos[QS];
+  bf16x8_t qf[QS][ND];
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
+  for (int qs = 0; qs < QS; ++qs) {
     const int row = min(wrow0 + 16 * qs + ql, tile.nq - 1);
     my_pos[qs] = pos0 + row;
     const int64_t qrow = (int64_t)(tile.off + tile.i0 + row) * a.num_heads + h;
@@ -161,19 +169,24 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     for (int dc = 0; dc < ND; ++dc) qf[qs][dc] = as_bf16x8(src[4 * dc + g]);
   }
   const int wave_first_pos = pos0 + min(wrow0, tile.nq - 1);
-  const int wave_last_pos = pos0 + min(wrow0 + 31, tile.nq - 1);
+  const int wave_last_pos = pos0 + min(wrow0 + 16 * QS - 1, tile.nq - 1);
   const bool wave_active = wrow0 < tile.nq;
 
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-  f32x4_t acc[2][NT];
+  float m[QS], l[QS];
+  f32x4_t acc[QS][NT];
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs)
+  for (int qs = 0; qs < QS; ++qs) {
+    m[qs] = -INFINITY;
+    l[qs] = 0.f;
+  }
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
     for (int dt = 0; dt < NT; ++dt) acc[qs][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Staging of one 64-key block into buffer b.  Wave w, part i covers block
-  // rows RPI (4 i + w) .. +RPI-1 (RPI = 1024 / row bytes), which lie in one
-  // page; lane L takes row RPI (4 i + w) + L / NC and LDS chunk position
+  // rows RPI (WAVES i + w) .. +RPI-1 (RPI = 1024 / row bytes), which lie in
+  // one page; lane L takes row RPI (WAVES i + w) + L / NC and LDS chunk position
   // L % NC, i.e. global chunk (L % NC) ^ (row mod NC) of that row, and lands
   // at LDS byte base + 16 L.
   const int lrow = lane / NC;   // row within the part
@@ -183,7 +196,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     if (key0 + kBlockKeys <= tile.key_end) {
 #pragma unroll
       for (int i = 0; i < NPART; ++i) {
-        const int r0 = RPI * (4 * i + wave);       // first block row of the part
+        const int r0 = RPI * (WAVES * i + wave);   // first block row of the part
         const int key = key0 + r0;
         const int page_idx = PAGE16 ? key >> 4 : key / S;
         const int slot0 = PAGE16 ? key & 15 : key - page_idx * S;
@@ -205,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       uint4 kx[NPART], vx[NPART];
 #pragma unroll
       for (int i = 0; i < NPART; ++i) {
-        const int r = RPI * (4 * i + wave) + lrow;
+        const int r = RPI * (WAVES * i + wave) + lrow;
         const int key = min(key0 + r, tile.key_end - 1);
         const int page_idx = PAGE16 ? key >> 4 : key / S;
         const int slot = PAGE16 ? key & 15 : key - page_idx * S;
@@ -216,7 +229,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < NPART; ++i) {
-        const int r = RPI * (4 * i + wave) + lrow;
+        const int r = RPI * (WAVES * i + wave) + lrow;
         *reinterpret_cast<uint4*>(&sKV[b][0][r * kRowBytes + lpos * 16]) = kx[i];
         *reinterpret_cast<uint4*>(&sKV[b][1][r * kRowBytes + lpos * 16]) = vx[i];
       }
@@ -244,27 +257,29 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     if (!wave_active || wave_last_pos < key0) continue;
 
     // ---- scores S^T = K Q^T: s[qs][kt][j] = q . k(key0 + 16 kt + 4 g + j) ----
-    float s[2][4][4];
+    float s[QS][4][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t c[QS];
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) c[qs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dc = 0; dc < ND; ++dc) {
         const bf16x8_t kf =
             as_bf16x8(*reinterpret_cast<const uint4*>(sK + kv_byte<D>(16 * kt + ql, 4 * dc + g)));
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][dc], c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][dc], c1, 0, 0, 0);
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs)
+          c[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qs][dc], c[qs], 0, 0, 0);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {  // raw q.k; the log2 scale joins in the exponent
-        s[0][kt][j] = c0[j];
-        s[1][kt][j] = c1[j];
-      }
+      for (int j = 0; j < 4; ++j)  // raw q.k; the log2 scale joins in the exponent
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) s[qs][kt][j] = c[qs][j];
     }
     // causal mask where the block reaches past this wave's first position
     if (key0 + kBlockKeys - 1 > wave_first_pos) {
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
+      for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -273,9 +288,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     }
     // Block maxima in scaled log2 units (the scale is positive, so the
     // maximum of the raw products scales to the maximum of the scores).
-    float cand[2];
+    float cand[QS];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
+    for (int qs = 0; qs < QS; ++qs) {
       float mb = s[qs][0][0];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
@@ -289,9 +304,12 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     // most 2^kSlack, which float32 sums and bf16 weights carry exactly as
     // well.  The first block always moves them from -inf.
     constexpr float kSlack = 8.f;
-    if (__builtin_expect(__any(cand[0] > m[0] + kSlack || cand[1] > m[1] + kSlack), 0)) {
+    bool grow = false;
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
+    for (int qs = 0; qs < QS; ++qs) grow = grow || cand[qs] > m[qs] + kSlack;
+    if (__builtin_expect(__any(grow), 0)) {
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) {
         const float mn = fmaxf(m[qs], cand[qs]);
         const float alpha = __builtin_amdgcn_exp2f(m[qs] - mn);
         l[qs] *= alpha;
@@ -305,7 +323,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       }
     }
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
+    for (int qs = 0; qs < QS; ++qs) {
       float ps = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
@@ -319,9 +337,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     // ---- O += P V over two 32-key steps ----
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      bf16x8_t pf[2];
+      bf16x8_t pf[QS];
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
+      for (int qs = 0; qs < QS; ++qs) {
         uint4 pu;
         pu.x = pack_bf16x2(s[qs][2 * kc][0], s[qs][2 * kc][1]);
         pu.y = pack_bf16x2(s[qs][2 * kc][2], s[qs][2 * kc][3]);
@@ -342,15 +360,16 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
             (lds_s16x4_t*)(sV + kv_byte<D>(vrow + 16, chunk) + half));
         const bf16x8_t vf = __builtin_bit_cast(
             bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[0], vf, acc[0][dt], 0, 0, 0);
-        acc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[1], vf, acc[1][dt], 0, 0, 0);
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs)
+          acc[qs][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[qs], vf, acc[qs][dt], 0, 0, 0);
       }
     }
   }
 
   if (!wave_active) return;
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs)
+  for (int qs = 0; qs < QS; ++qs)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = wrow0 + 16 * qs + 4 * g + j;
@@ -392,32 +411,38 @@ __global__ __launch_bounds__(256) void prefill_append_kernel(PrefillArgs a) {
 }  // namespace
 
 bool prefill_fast_supported(int dtype, int head_width, int page_size) {
-  return dtype == kDtypeBF16 && (head_width == 64 || head_width == 128) && page_size % 16 == 0;
+  return dtype == kDtypeBF16 && (head_width == 64 || head_width == 128 || head_width == 256) &&
+         page_size % 16 == 0;
 }
 
 hipError_t launch_prefill_append(const PrefillArgs& a, int num_tiles, hipStream_t stream) {
   const dim3 grid(num_tiles, a.num_kv_heads);
-  if (a.head_bytes / a.page_size == 128)
-    hipLaunchKernelGGL(prefill_append_kernel<64>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(prefill_append_kernel<128>, grid, dim3(256), 0, stream, a);
+  switch (a.head_bytes / a.page_size) {
+    case 128: hipLaunchKernelGGL(prefill_append_kernel<64>, grid, dim3(256), 0, stream, a); break;
+    case 256: hipLaunchKernelGGL(prefill_append_kernel<128>, grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL(prefill_append_kernel<256>, grid, dim3(256), 0, stream, a); break;
+  }
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_prefill_width(const PrefillArgs& a, int num_tiles, hipStream_t stream) {
+  const dim3 block(64 * prefill_waves(D));
   if (a.page_size == 16)
-    hipLaunchKernelGGL((prefill_mfma_kernel<true, D>), dim3(num_tiles * a.num_heads), dim3(256),
-                       0, stream, a);
+    hipLaunchKernelGGL((prefill_mfma_kernel<true, D>), dim3(num_tiles * a.num_heads), block, 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<false, D>), dim3(num_tiles * a.num_heads), dim3(256),
-                       0, stream, a);
+    hipLaunchKernelGGL((prefill_mfma_kernel<false, D>), dim3(num_tiles * a.num_heads), block, 0,
+                       stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_attention(const PrefillArgs& a, int num_tiles, hipStream_t stream) {
-  return a.head_bytes / a.page_size == 128 ? launch_prefill_width<64>(a, num_tiles, stream)
-                                           : launch_prefill_width<128>(a, num_tiles, stream);
+  switch (a.head_bytes / a.page_size) {
+    case 128: return launch_prefill_width<64>(a, num_tiles, stream);
+    case 256: return launch_prefill_width<128>(a, num_tiles, stream);
+    default: return launch_prefill_width<256>(a, num_tiles, stream);
+  }
 }
 
 }  // namespace pkv

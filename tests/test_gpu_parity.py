@@ -435,8 +435,9 @@ PREFILL_CASES = [
     # dtype, D, S, H, H_kv: matrix-core path (16- and 32-token pages) ...
     ("bf16", 128, 16, 4, 4), ("bf16", 128, 16, 8, 2), ("bf16", 128, 32, 4, 1),
     ("bf16", 64, 16, 4, 4), ("bf16", 64, 16, 8, 2), ("bf16", 64, 32, 4, 1),
+    ("bf16", 256, 16, 2, 1), ("bf16", 256, 32, 4, 2),
     # ... and per-row decode kernels
-    ("f32", 64, 16, 3, 3), ("f32", 40, 16, 2, 1), ("bf16", 128, 7, 2, 2), ("bf16", 256, 16, 2, 1),
+    ("f32", 64, 16, 3, 3), ("f32", 40, 16, 2, 1), ("bf16", 128, 7, 2, 2), ("bf16", 96, 16, 2, 2),
 ]
 PREFILL_CHUNKS = [(0, 1), (0, 37), (5, 20), (16, 16), (100, 70), (1000, 33), (0, 300)]
 
@@ -474,7 +475,7 @@ def test_prefill_rejects_ranges_outside_the_table():
 
 
 @pytest.mark.parametrize("dtype,D,H,Hkv", [("bf16", 128, 4, 2), ("f32", 64, 2, 2),
-                                           ("bf16", 64, 4, 1)])
+                                           ("bf16", 64, 4, 1), ("bf16", 256, 2, 2)])
 def test_prefill_transactional_chunks(dtype, D, H, Hkv):
     """begin_tokens chunks on several caches (one of them a single token),
     batched append_and_attend per layer, commit; an aborted chunk returns its
