@@ -367,12 +367,15 @@ __device__ inline ItemTile item_tile(int tiles) {
 // for all G).  Multi-head attention is G = 1 (HPW = 1, WPG = WAVES).  A block is one contiguous 4 KiB slab of K and one of V.
 // Lane (g, c): row i*4+g of each of the 4 loads, VB = row bytes / 16 bytes at
 // column c, so one load instruction reads four whole rows and the 16 lanes of
-// a DPP row hold one K/V row (512-byte rows take two 16-byte loads per lane).  Each 16-lane group keeps its own online-softmax state per
+// a DPP row hold one K/V row (512-byte rows take two 16-byte loads per lane).
+// PAD: the head width is narrower than D (rows of a whole number of VB-byte
+// lane shares, e.g. bf16 d_h = 96 in D = 128): row bytes come from the
+// arguments, and the lanes past a row's end load no q, contribute nothing to
+// the row sums and store nothing.  Each 16-lane group keeps its own online-softmax state per
 // query head; groups merge in-wave, the waves of a head group in LDS.
-template <typename T, int D, int WAVES, int HPW, int WPG>
+template <typename T, int D, int WAVES, int HPW, int WPG, bool PAD>
 __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
-  constexpr int ROW_BYTES = D * (int)sizeof(T);
-  constexpr int VB = ROW_BYTES / 16;       // bytes of a row per lane
+  constexpr int VB = D * (int)sizeof(T) / 16;  // bytes of a row per lane
   static_assert(VB == 8 || VB == 16 || VB == 32, "rows of 128, 256 or 512 bytes");
   using Vec = RowVec<VB>;
   constexpr int EPL = VB / (int)sizeof(T);  // elements of a row per lane
@@ -402,11 +405,14 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
   const int qh0 = (kvh * tiles + tile) * G + hg * HPW;  // first query head of this wave
   const int g = lane / LPR;
   const int c = lane % LPR;
+  const int DW = PAD ? a.head_width : D;            // elements of a row
+  const int ROW_BYTES = DW * (int)sizeof(T);
+  const bool lane_on = !PAD || c * VB < ROW_BYTES;  // this lane's share lies in the row
   const int t = rq.seq_len;
   const int S = a.page_size;
   const const_i32_ptr pt = as_const(a.page_table + (int64_t)rq.pt_row * a.pt_stride);
   const int64_t kvrow_bytes =
-      (((int64_t)it.req * a.num_kv_heads + kvh) * D) * (int64_t)sizeof(T);
+      (((int64_t)it.req * a.num_kv_heads + kvh) * DW) * (int64_t)sizeof(T);
   const int64_t head_off = (int64_t)kvh * a.head_bytes;
   const int last_blk = (t - 1) / kBlockRows;
   const bool fused = a.fuse_append != 0 && it.blk_end > last_blk;
@@ -414,14 +420,16 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
   float qf[HPW][EPL];
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
-    const int64_t qrow_bytes = (((int64_t)it.req * a.num_heads + qh0 + j) * D) * (int64_t)sizeof(T);
-    unpack_row<T>(Vec::load(static_cast<const char*>(a.q) + qrow_bytes + c * VB), qf[j]);
+    const int64_t qrow_bytes = (((int64_t)it.req * a.num_heads + qh0 + j) * DW) * (int64_t)sizeof(T);
+    Vec qv = Vec::zero();
+    if (lane_on) qv = Vec::load(static_cast<const char*>(a.q) + qrow_bytes + c * VB);
+    unpack_row<T>(qv, qf[j]);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qf[j][e] *= a.scale_log2e;
   }
 
   Vec knew = Vec::zero(), vnew = Vec::zero();
-  if (fused) {
+  if (fused && lane_on) {
     knew = Vec::load(static_cast<const char*>(a.k_new) + kvrow_bytes + c * VB);
     vnew = Vec::load(static_cast<const char*>(a.v_new) + kvrow_bytes + c * VB);
     if (wave == 0 && g == 0 && tile == 0) {
@@ -495,6 +503,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) d = fmaf(qf[j][e], kf[e], d);
+        if constexpr (PAD) d = lane_on ? d : 0.f;  // bytes past the row may be anything
         s[j][i] = row16_sum(d);
         if constexpr (edge) {
           if (!valid[i]) s[j][i] = -INFINITY;
@@ -1158,9 +1167,9 @@ __global__ __launch_bounds__(256) void patch_kernel(int32_t* arena, PatchBatch b
   if (i < b.count) arena[b.offset[i]] = b.value[i];
 }
 
-template <typename T, int D, int WAVES, int HPW, int WPG>
+template <typename T, int D, int WAVES, int HPW, int WPG, bool PAD = false>
 hipError_t launch_fast_shape(const AttnArgs& a, int num_items, hipStream_t stream) {
-  hipLaunchKernelGGL((attend_fast_kernel<T, D, WAVES, HPW, WPG>),
+  hipLaunchKernelGGL((attend_fast_kernel<T, D, WAVES, HPW, WPG, PAD>),
                      dim3(num_items * a.head_tiles, a.num_kv_heads), dim3(64 * WAVES), 0, stream,
                      a);
   return hipGetLastError();
@@ -1201,6 +1210,25 @@ static int fast_row_bytes(int dtype, int head_width) {
   if (dtype == kDtypeBF16 && (head_width == 64 || head_width == 128 || head_width == 256))
     return head_width * 2;
   return 0;
+}
+
+// For a width without its own fast shape: the fast width D whose rows hold
+// it, when its row is a whole number of that width's lane shares (0 if none).
+static int padded_width(int dtype, int head_width) {
+  const int elt = dtype == kDtypeF32 ? 4 : 2;
+  const int rb = head_width * elt;
+  for (int vb : {8, 16, 32})
+    if (rb <= 16 * vb) return rb % vb == 0 && rb > 8 * vb ? 16 * vb / elt : 0;
+  return 0;
+}
+
+// Padded widths run shares of one or two query heads (larger groups as
+// several workgroups of two).
+template <typename T, int D>
+hipError_t launch_fast_padded(const AttnArgs& a, int share, int num_items, hipStream_t stream) {
+  if (share == 2) return launch_fast_shape<T, D, 4, 2, 4, true>(a, num_items, stream);
+  return a.waves == 8 ? launch_fast_shape<T, D, 8, 1, 8, true>(a, num_items, stream)
+                      : launch_fast_shape<T, D, 4, 1, 4, true>(a, num_items, stream);
 }
 
 template <typename T>
@@ -1263,7 +1291,7 @@ hipError_t launch_group(const AttnArgs& a, int share, dim3 grid, hipStream_t str
 
 bool fast_path_supported(int dtype, int head_width, int page_size, int group) {
   if (page_size % kBlockRows != 0 || group < 1) return false;
-  return fast_row_bytes(dtype, head_width) != 0;
+  return fast_row_bytes(dtype, head_width) != 0 || padded_width(dtype, head_width) != 0;
 }
 
 hipError_t launch_attention(const AttnArgs& args, int dtype, int num_items, hipStream_t stream,
@@ -1283,6 +1311,23 @@ hipError_t launch_attention(const AttnArgs& args, int dtype, int num_items, hipS
   }
   const bool fast = fast_path_supported(dtype, a.head_width, a.page_size, group);
   if (path_out) *path_out = fast ? KernelPath::kFast : KernelPath::kGeneric;
+  if (fast && fast_row_bytes(dtype, a.head_width) == 0) {
+    const int share = head_share(group, {2, 1});
+    a.head_tiles = group / share;
+    const int dp = padded_width(dtype, a.head_width);
+    if (dtype == kDtypeF32) {
+      switch (dp) {
+        case 32: return launch_fast_padded<float, 32>(a, share, num_items, stream);
+        case 64: return launch_fast_padded<float, 64>(a, share, num_items, stream);
+        default: return launch_fast_padded<float, 128>(a, share, num_items, stream);
+      }
+    }
+    switch (dp) {
+      case 64: return launch_fast_padded<bf16_t, 64>(a, share, num_items, stream);
+      case 128: return launch_fast_padded<bf16_t, 128>(a, share, num_items, stream);
+      default: return launch_fast_padded<bf16_t, 256>(a, share, num_items, stream);
+    }
+  }
   if (fast) {
     const int share = fast_row_bytes(dtype, a.head_width) == 512
                           ? head_share(group, {8, 4, 2, 1})

@@ -155,10 +155,13 @@ SMALL_CASES = [
     ("f32", 64, 16), ("bf16", 128, 16), ("bf16", 128, 32),
     # ... 128 and 512 bytes
     ("bf16", 64, 16), ("f32", 32, 16), ("bf16", 256, 16), ("f32", 128, 32),
+    # ... and narrower rows padded to those (lanes past the row end idle)
+    ("bf16", 96, 16), ("bf16", 80, 32), ("bf16", 48, 16), ("f32", 40, 16), ("f32", 96, 16),
     # generic path: other widths, page sizes that are not a multiple of 16
-    ("f32", 40, 16), ("bf16", 96, 16), ("f32", 64, 5), ("bf16", 128, 7),
+    ("bf16", 100, 16), ("f32", 10, 16), ("f32", 64, 5), ("bf16", 128, 7),
 ]
-FAST_WIDTHS = {("f32", 32), ("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128), ("bf16", 256)}
+FAST_WIDTHS = {("f32", 32), ("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128), ("bf16", 256),
+               ("bf16", 96), ("f32", 40)}
 LENGTHS = [1, 15, 16, 17, 100, 333, 1000]
 
 
@@ -264,8 +267,10 @@ GQA_CASES = [
     ("bf16", 64, 16, 8, 1), ("f32", 32, 16, 16, 1), ("f32", 128, 16, 4, 2),
     ("bf16", 256, 16, 8, 2), ("bf16", 256, 16, 16, 1), ("bf16", 64, 32, 32, 1),
     ("bf16", 256, 16, 4, 2),
-    # ... and the generic kernel: a narrow head, a ragged page
-    ("f32", 40, 16, 4, 1), ("bf16", 128, 7, 8, 2),
+    # ... padded widths (shares of two heads) ...
+    ("f32", 40, 16, 4, 1), ("bf16", 96, 16, 8, 2), ("bf16", 80, 16, 2, 1),
+    # ... and the generic kernel: a width without a fast shape, a ragged page
+    ("bf16", 100, 16, 4, 2), ("bf16", 128, 7, 8, 2),
 ]
 
 
