@@ -38,15 +38,9 @@ struct bf16_t {
 template <typename T>
 struct KVTraits;
 
+// Element i of a K/V or q row as float (the generic kernel's scalar reads).
 template <>
 struct KVTraits<float> {
-  static constexpr int kPerVec = 4;  // elements in 16 bytes
-  __device__ static inline void unpack(const uint4& u, float* f) {
-    f[0] = __uint_as_float(u.x);
-    f[1] = __uint_as_float(u.y);
-    f[2] = __uint_as_float(u.z);
-    f[3] = __uint_as_float(u.w);
-  }
   __device__ static inline float load1(const void* p, int64_t i) {
     return static_cast<const float*>(p)[i];
   }
@@ -54,17 +48,6 @@ struct KVTraits<float> {
 
 template <>
 struct KVTraits<bf16_t> {
-  static constexpr int kPerVec = 8;
-  __device__ static inline void unpack(const uint4& u, float* f) {
-    f[0] = __uint_as_float(u.x << 16);
-    f[1] = __uint_as_float(u.x & 0xFFFF0000u);
-    f[2] = __uint_as_float(u.y << 16);
-    f[3] = __uint_as_float(u.y & 0xFFFF0000u);
-    f[4] = __uint_as_float(u.z << 16);
-    f[5] = __uint_as_float(u.z & 0xFFFF0000u);
-    f[6] = __uint_as_float(u.w << 16);
-    f[7] = __uint_as_float(u.w & 0xFFFF0000u);
-  }
   __device__ static inline float load1(const void* p, int64_t i) {
     return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
   }
@@ -121,10 +104,6 @@ __device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const char* base, int bytes)
 __device__ inline uint4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-__device__ inline uint4 select4(bool c, const uint4& a, const uint4& b) {
-  return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
 }
 
 // A lane's share of one K/V row on the fast path: VB bytes (8, 16 or 32) as
@@ -690,10 +669,6 @@ __device__ inline float xor32_sum(float x) {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ inline uint32_t word_of(const uint4& u, int i) {
-  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
-}
 
 // Ends one chunk for NH heads of a wave at once (lanes 0..15 hold columns
 // col0..col0+NCOL-1 of each head's context).  Unsplit requests write contexts;

@@ -55,11 +55,6 @@ __device__ inline float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// 32-bit word i (a compile-time constant after unrolling) of a 16-byte value.
-__device__ inline uint32_t word_of(const uint4& u, int i) {
-  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
-}
-
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   // round to nearest even (the hardware conversion)
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
