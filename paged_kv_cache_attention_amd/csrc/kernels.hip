@@ -741,6 +741,65 @@ __device__ void finish_heads(const AttnArgs& a, const WorkItem& it, const ReqEnt
   }
 }
 
+// The block loop of the grouped matrix-core kernels, for one wave: blocks
+// first, first+W, ..., wave_last of the chunk (index j: block first + W j),
+// the next block's loads always issued before the current one is computed.
+// Only the final block can be the request's last (masked) block, so it is
+// peeled off the loop: the loop body is one unmasked step per buffer and the
+// context stays in the same registers throughout.  Page IDs come 64 blocks
+// at a time in one vector load (lane i: block j0 + i) and are picked out with
+// readlane, so issuing a block's loads never waits on a page-table round
+// trip.  load_block(b, page, Buf&) issues a block's loads; step(b, Buf&,
+// edge_tag) computes it.
+template <int W, typename Buf, typename LoadFn, typename StepFn>
+__device__ __forceinline__ void group_block_loop(const AttnArgs& a, const WorkItem& it,
+                                                 const ReqEntry& rq, int wave, int lane,
+                                                 int last_blk, LoadFn& load_block, StepFn& step) {
+  const int end = it.blk_end;
+  const int first = it.blk_begin + wave;
+  if (first >= end) return;
+  const int S = a.page_size;
+  const int wave_last = first + ((end - 1 - first) / W) * W;
+  const int nj = (wave_last - first) / W + 1;
+  const bool edge = wave_last == last_blk;
+  int32_t pv = 0;
+  int j0 = 0;
+  auto fetch_pages = [&](int jf) {
+    const int bb = min(first + W * (jf + lane), wave_last);
+    pv = a.page_table[(int64_t)rq.pt_row * a.pt_stride + (bb * kBlockRows) / S];
+    j0 = jf;
+    // Complete the load here, so that no later use of pv (after this rare
+    // branch rejoins the loop) waits on the K/V loads in flight.
+    __builtin_amdgcn_s_waitcnt(0);
+  };
+  auto page_at = [&](int jj) -> int32_t { return __builtin_amdgcn_readlane(pv, jj - j0); };
+  auto blk = [&](int jj) { return first + W * jj; };
+  Buf ba, bb;
+  fetch_pages(0);
+  load_block(first, page_at(0), ba);
+  int jc = 0;
+  for (; jc + 2 < nj; jc += 2) {  // blocks jc and jc + 1 both precede the final one
+    if (jc + 2 - j0 > 63) fetch_pages(jc + 1);
+    load_block(blk(jc + 1), page_at(jc + 1), bb);
+    step(blk(jc), ba, std::false_type{});
+    load_block(blk(jc + 2), page_at(jc + 2), ba);
+    step(blk(jc + 1), bb, std::false_type{});
+  }
+  if (jc + 2 == nj) {
+    if (jc + 1 - j0 > 63) fetch_pages(jc + 1);
+    load_block(wave_last, page_at(jc + 1), bb);
+    step(blk(jc), ba, std::false_type{});
+    if (edge)
+      step(wave_last, bb, std::true_type{});
+    else
+      step(wave_last, bb, std::false_type{});
+  } else if (edge) {
+    step(wave_last, ba, std::true_type{});
+  } else {
+    step(wave_last, ba, std::false_type{});
+  }
+}
+
 template <int G, int W, int D>
 __global__ __launch_bounds__(64 * W, D == 256 ? 1 : 8 / W) void attend_group_mfma_kernel(AttnArgs a) {
   constexpr int ROW_BYTES = D * 2;
@@ -797,7 +856,13 @@ __global__ __launch_bounds__(64 * W, D == 256 ? 1 : 8 / W) void attend_group_mfm
   }
 
   // K: lane (key ql, dims 32 dc + 8 g); V: lane (keys 4 g + i, dims NT ql..+NT-1).
-  auto load_block = [&](int b, int32_t page, uint4* kk, VVec* vv) {
+  struct Buf {
+    uint4 k[ND];
+    VVec v[4];
+  };
+  auto load_block = [&](int b, int32_t page, Buf& x) {
+    uint4* kk = x.k;
+    VVec* vv = x.v;
     const int row0 = b * kBlockRows;
     const int64_t base = (int64_t)page * a.page_bytes + head_off + (int64_t)(row0 % S) * ROW_BYTES;
     const auto rk = block_rsrc(a.k_layer + base, kBlockRows * ROW_BYTES);
@@ -814,8 +879,10 @@ __global__ __launch_bounds__(64 * W, D == 256 ? 1 : 8 / W) void attend_group_mfm
 #pragma unroll
   for (int dt = 0; dt < NT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](int b, uint4* kk, VVec* vv, auto edge_tag) {
+  auto step = [&](int b, Buf& x, auto edge_tag) {
     constexpr bool edge = decltype(edge_tag)::value;
+    uint4* kk = x.k;
+    VVec* vv = x.v;
     float valid_k[4];
     if constexpr (edge) {
       // The request's last block: keys >= t are masked and their V rows
@@ -896,60 +963,7 @@ __global__ __launch_bounds__(64 * W, D == 256 ? 1 : 8 / W) void attend_group_mfm
     }
   };
 
-  // Blocks first, first+4, ..., wave_last of this wave (index j: block
-  // first + 4 j), the next block's loads always issued before the current one
-  // is computed.  Only the final block can be the request's last (masked)
-  // block, so it is peeled off the loop: the loop body is one unmasked step
-  // per buffer and the context stays in the same registers throughout.
-  // Page IDs come 64 blocks at a time in one vector load (lane i: block
-  // j0 + i) and are picked out with readlane, so issuing a block's loads
-  // never waits on a page-table round trip.
-  {
-    const int end = it.blk_end;
-    const int first = it.blk_begin + wave;
-    if (first < end) {
-      const int wave_last = first + ((end - 1 - first) / W) * W;
-      const int nj = (wave_last - first) / W + 1;
-      const bool edge = wave_last == last_blk;
-      int32_t pv = 0;
-      int j0 = 0;
-      auto fetch_pages = [&](int jf) {
-        const int bb = min(first + W * (jf + lane), wave_last);
-        pv = a.page_table[(int64_t)rq.pt_row * a.pt_stride + (bb * kBlockRows) / S];
-        j0 = jf;
-        // Complete the load here, so that no later use of pv (after this
-        // rare branch rejoins the loop) waits on the K/V loads in flight.
-        __builtin_amdgcn_s_waitcnt(0);
-      };
-      auto page_at = [&](int jj) -> int32_t { return __builtin_amdgcn_readlane(pv, jj - j0); };
-      auto blk = [&](int jj) { return first + W * jj; };
-      uint4 ka[ND], kb[ND];
-      VVec va[4], vb[4];
-      fetch_pages(0);
-      load_block(first, page_at(0), ka, va);
-      int jc = 0;
-      for (; jc + 2 < nj; jc += 2) {  // blocks jc and jc + 1 both precede the final one
-        if (jc + 2 - j0 > 63) fetch_pages(jc + 1);
-        load_block(blk(jc + 1), page_at(jc + 1), kb, vb);
-        step(blk(jc), ka, va, std::false_type{});
-        load_block(blk(jc + 2), page_at(jc + 2), ka, va);
-        step(blk(jc + 1), kb, vb, std::false_type{});
-      }
-      if (jc + 2 == nj) {
-        if (jc + 1 - j0 > 63) fetch_pages(jc + 1);
-        load_block(wave_last, page_at(jc + 1), kb, vb);
-        step(blk(jc), ka, va, std::false_type{});
-        if (edge)
-          step(wave_last, kb, vb, std::true_type{});
-        else
-          step(wave_last, kb, vb, std::false_type{});
-      } else if (edge) {
-        step(wave_last, ka, va, std::true_type{});
-      } else {
-        step(wave_last, ka, va, std::false_type{});
-      }
-    }
-  }
+  group_block_loop<W, Buf>(a, it, rq, wave, lane, last_blk, load_block, step);
 
   // Combine the four waves through LDS (each wave's V^T staging is done: its
   // LDS operations complete in order), then each wave publishes heads
@@ -958,6 +972,190 @@ __global__ __launch_bounds__(64 * W, D == 256 ? 1 : 8 / W) void attend_group_mfm
   for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) s_acc[wave][ql][16 * dt + 4 * g + j] = acc[dt][j];
+  if (g == 0) {
+    s_m[wave][ql] = m;
+    s_l[wave][ql] = l;
+  }
+  __syncthreads();
+  constexpr int NH = G / W;
+  const int c0 = (lane & 15) * NT;
+  int heads[NH];
+  float hm[NH], hl[NH], ho[NH][NT];
+#pragma unroll
+  for (int k = 0; k < NH; ++k) {
+    const int r = wave + W * k;
+    heads[k] = qbase + r;
+    float mx = s_m[0][r];
+#pragma unroll
+    for (int w = 1; w < W; ++w) mx = fmaxf(mx, s_m[w][r]);
+    float wt[W], lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      wt[w] = s_m[w][r] == -INFINITY ? 0.f : fast_exp2(s_m[w][r] - mx);
+      lsum = fmaf(s_l[w][r], wt[w], lsum);
+    }
+#pragma unroll
+    for (int e = 0; e < NT; ++e) {
+      float x = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) x = fmaf(s_acc[w][r][c0 + e], wt[w], x);
+      ho[k][e] = x;
+    }
+    hm[k] = mx;
+    hl[k] = lsum;
+  }
+  finish_heads<NH, NT>(a, it, rq, heads, lane, c0, hm, hl, ho);
+}
+
+// ---------------------------------------------------------------------------
+// Grouped K/V heads on matrix cores in float32: d_h = 32, 64 or 128, pages of
+// a multiple of 16 rows, G = 4, 8 or 16 query heads per workgroup, W waves
+// interleaving the chunk's blocks as in the bf16 kernel.  Both products run
+// on v_mfma_f32_16x16x4_f32 (A: lane l holds A[l%16][l/16]; B: B[l/16][l%16];
+// C: C[4(l/16)+j][l%16]); since a contraction may visit its index in any
+// order, the orders are chosen so that every operand is a lane's own
+// contiguous data:
+//   S^T = K Q^T, step s (of D/4): k index g <-> dim (D/4) g + s.  Lane
+//     (ql, g) holds dims (D/4) g .. +D/4-1 of key ql's K row and of head
+//     ql's q row, and gets the scores of keys 4g .. 4g+3 for head ql.
+//   O^T += V^T P^T, step s (of 4): k index g <-> key 4g + s, which is the
+//     lane's own score element s; output tile t, row r <-> dim (D/16) r + t,
+//     so lane (ql, g) holds dims (D/16) ql .. +D/16-1 of V rows 4g + s and
+//     accumulates dims (D/16)(4g + j) + t of head ql.
+// No LDS staging: K and V go from memory straight into the MFMA operands.
+template <int G, int W, int D>
+__global__ __launch_bounds__(64 * W, D == 128 ? 1 : 8 / W) void attend_group_f32_kernel(AttnArgs a) {
+  constexpr int ROW_BYTES = D * 4;
+  static_assert(D == 32 || D == 64 || D == 128, "head widths 32, 64 or 128");
+  constexpr int KD = D / 4;      // score steps, and dims of a K or q row per lane
+  constexpr int NT = D / 16;     // context tiles, and dims of a V row per lane
+  using KVec = RowVec<KD * 4>;
+  using VVec = RowVec<NT * 4>;
+  static_assert(G == 4 || G == 8 || G == 16, "groups of 4, 8 or 16 heads");
+  static_assert((W == 4 || W == 8) && G % W == 0, "4 or 8 waves, each publishing G / W heads");
+  __shared__ __attribute__((aligned(16))) float s_acc[W][16][D];
+  __shared__ float s_m[W][16], s_l[W][16];
+
+  const int tiles = a.head_tiles;
+  const ItemTile itl = item_tile(tiles);
+  const WorkItem it = plan_item(a, itl.item);
+  const ReqEntry rq = it.rq;
+  const int kvh = blockIdx.y;
+  const int tile = itl.tile;
+  const int qbase = (kvh * tiles + tile) * G;  // first query head of this workgroup
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ql = lane & 15;
+  const int g = lane >> 4;
+  const int t = rq.seq_len;
+  const int S = a.page_size;
+  const const_i32_ptr pt = as_const(a.page_table + (int64_t)rq.pt_row * a.pt_stride);
+  const int64_t head_off = (int64_t)kvh * a.head_bytes;
+  const int last_blk = (t - 1) / kBlockRows;
+  const bool fused = a.fuse_append != 0 && it.blk_end > last_blk;
+  const int64_t kvrow = ((int64_t)it.req * a.num_kv_heads + kvh) * ROW_BYTES;
+
+  float qf[KD];
+  {
+    const int64_t qrow = ((int64_t)it.req * a.num_heads + qbase + min(ql, G - 1)) * ROW_BYTES;
+    const KVec v = KVec::load(static_cast<const char*>(a.q) + qrow + g * KD * 4);
+#pragma unroll
+    for (int s = 0; s < KD; ++s) qf[s] = __uint_as_float(v.w[s]);
+  }
+  if (fused && wave == 0 && lane < ROW_BYTES / 16 && tile == 0) {
+    const int pos = t - 1;
+    const int64_t slot = (int64_t)pt[pos / S] * a.page_bytes + head_off +
+                         (int64_t)(pos % S) * ROW_BYTES + lane * 16;
+    *reinterpret_cast<uint4*>(a.k_layer + slot) =
+        *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + kvrow + lane * 16);
+    *reinterpret_cast<uint4*>(a.v_layer + slot) =
+        *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + kvrow + lane * 16);
+  }
+
+  struct Buf {
+    KVec k;       // key ql, dims KD g ..
+    VVec v[4];    // keys 4 g + s, dims NT ql ..
+  };
+  auto load_block = [&](int b, int32_t page, Buf& x) {
+    const int row0 = b * kBlockRows;
+    const int64_t base = (int64_t)page * a.page_bytes + head_off + (int64_t)(row0 % S) * ROW_BYTES;
+    const auto rk = block_rsrc(a.k_layer + base, kBlockRows * ROW_BYTES);
+    const auto rv = block_rsrc(a.v_layer + base, kBlockRows * ROW_BYTES);
+    x.k = KVec::load(rk, (uint32_t)(ql * ROW_BYTES + g * KD * 4));
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      x.v[s] = VVec::load(rv, (uint32_t)((4 * g + s) * ROW_BYTES + ql * NT * 4));
+  };
+
+  float m = -INFINITY, l = 0.f;
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](int b, Buf& x, auto edge_tag) {
+    constexpr bool edge = decltype(edge_tag)::value;
+    float valid_k[4];
+    if constexpr (edge) {
+      // The request's last block: keys >= t are masked and their V rows
+      // zeroed (stale bytes may be anything); with a fused append, key t-1
+      // comes from the inputs.
+      const int row0 = b * kBlockRows;
+      if (fused && row0 + ql == t - 1)
+        x.k = KVec::load(static_cast<const char*>(a.k_new) + kvrow + g * KD * 4);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int key = row0 + 4 * g + s;
+        if (fused && key == t - 1)
+          x.v[s] = VVec::load(static_cast<const char*>(a.v_new) + kvrow + ql * NT * 4);
+        if (key >= t) x.v[s] = VVec::zero();
+        valid_k[s] = key < t ? 0.f : -INFINITY;
+      }
+    }
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KD; ++s)
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(x.k.w[s]), qf[s], c, 0, 0, 0);
+    float sc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sc[j] = c[j];
+      if constexpr (edge) sc[j] += valid_k[j];
+    }
+    float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    const float cand = xor32_max(xor16_max(mb)) * a.scale_log2e;
+    // Lazy rescale, as in the bf16 kernel.
+    constexpr float kSlack = 8.f;
+    if (__builtin_expect(__any(cand > m + kSlack), 0)) {
+      const float mn = fmaxf(m, cand);
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+      m = mn;
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) acc[dt] *= alpha;
+    }
+    float p[4], ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = fast_exp2(fmaf(sc[j], a.scale_log2e, -m));
+      ps += p[j];
+    }
+    l += xor32_sum(xor16_sum(ps));
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(x.v[s].w[dt]), p[s],
+                                                       acc[dt], 0, 0, 0);
+  };
+
+  group_block_loop<W, Buf>(a, it, rq, wave, lane, last_blk, load_block, step);
+
+  // Combine the waves through LDS (lane (ql, g) holds dims NT (4 g + j) + dt
+  // of head ql), then each wave publishes heads wave, wave + W, ...
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s_acc[wave][ql][NT * (4 * g + j) + dt] = acc[dt][j];
   if (g == 0) {
     s_m[wave][ql] = m;
     s_l[wave][ql] = l;
@@ -1227,8 +1425,35 @@ static int head_share(int group, std::initializer_list<int> shares) {
 }
 
 bool group_mfma_supported(int dtype, int head_width, int page_size, int group) {
-  return dtype == kDtypeBF16 && (head_width == 64 || head_width == 128 || head_width == 256) &&
-         page_size % kBlockRows == 0 && group % 4 == 0;
+  if (page_size % kBlockRows != 0 || group % 4 != 0) return false;
+  if (dtype == kDtypeBF16) return head_width == 64 || head_width == 128 || head_width == 256;
+  if (dtype == kDtypeF32) return head_width == 32 || head_width == 64 || head_width == 128;
+  return false;
+}
+
+// The float32 grouped matrix-core kernel: shares of 16, 8 or 4 heads, eight
+// waves for shares of 8 and 16 unless PKV_OPT_WAVES asks for four.
+template <int D>
+hipError_t launch_group_f32(const AttnArgs& a, int share, dim3 grid, hipStream_t stream) {
+  const bool eight = a.waves != 4;
+  switch (share) {
+    case 4:
+      hipLaunchKernelGGL((attend_group_f32_kernel<4, 4, D>), grid, dim3(256), 0, stream, a);
+      break;
+    case 8:
+      if (eight)
+        hipLaunchKernelGGL((attend_group_f32_kernel<8, 8, D>), grid, dim3(512), 0, stream, a);
+      else
+        hipLaunchKernelGGL((attend_group_f32_kernel<8, 4, D>), grid, dim3(256), 0, stream, a);
+      break;
+    default:
+      if (eight)
+        hipLaunchKernelGGL((attend_group_f32_kernel<16, 8, D>), grid, dim3(512), 0, stream, a);
+      else
+        hipLaunchKernelGGL((attend_group_f32_kernel<16, 4, D>), grid, dim3(256), 0, stream, a);
+      break;
+  }
+  return hipGetLastError();
 }
 
 // The grouped matrix-core kernel for one head width: 16, 8 or 4 query heads
@@ -1278,6 +1503,13 @@ hipError_t launch_attention(const AttnArgs& args, int dtype, int num_items, hipS
     const int share = head_share(group, {16, 8, 4});
     a.head_tiles = group / share;
     const dim3 grid(num_items * a.head_tiles, a.num_kv_heads);
+    if (dtype == kDtypeF32) {
+      switch (a.head_width) {
+        case 32: return launch_group_f32<32>(a, share, grid, stream);
+        case 64: return launch_group_f32<64>(a, share, grid, stream);
+        default: return launch_group_f32<128>(a, share, grid, stream);
+      }
+    }
     switch (a.head_width) {
       case 64: return launch_group<64>(a, share, grid, stream);
       case 128: return launch_group<128>(a, share, grid, stream);

@@ -266,7 +266,7 @@ GQA_CASES = [
     # ... rows of 128 and 512 bytes (512: two heads per wave, shares up to 8) ...
     ("bf16", 64, 16, 8, 1), ("f32", 32, 16, 16, 1), ("f32", 128, 16, 4, 2),
     ("bf16", 256, 16, 8, 2), ("bf16", 256, 16, 16, 1), ("bf16", 64, 32, 32, 1),
-    ("bf16", 256, 16, 4, 2),
+    ("bf16", 256, 16, 4, 2), ("f32", 128, 16, 8, 1), ("f32", 64, 32, 4, 1),
     # ... padded widths (shares of two heads) ...
     ("f32", 40, 16, 4, 1), ("bf16", 96, 16, 8, 2), ("bf16", 80, 16, 2, 1),
     # ... and the generic kernel: a width without a fast shape, a ragged page
@@ -320,16 +320,17 @@ def test_grouped_kv_heads(dtype, D, S, H, Hkv, split, merge):
     pkv.pkv_pool_destroy(pool2)
 
 
-@pytest.mark.parametrize("D", [128, 64, 256])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("bf16", 256), ("f32", 64),
+                                     ("f32", 32), ("f32", 128)])
 @pytest.mark.parametrize("H,Hkv", [(16, 2), (16, 1), (32, 1), (24, 1), (8, 1), (4, 1)])
 @pytest.mark.parametrize("waves", [4, 8])
 @pytest.mark.parametrize("split", [0, 3])
-def test_grouped_workgroup_waves(D, H, Hkv, waves, split):
-    """The matrix-core grouped kernel (bf16, head widths 64, 128 and 256) with
-    four and with eight waves per workgroup (eight is the default when a
-    workgroup serves 8 or 16 query heads, except at width 256): every context
-    against the oracle, unsplit and split."""
-    w = _small(f"gqa_waves_{D}_{H}_{Hkv}", "bf16", D, 16, LENGTHS, heads=H, kv_heads=Hkv,
+def test_grouped_workgroup_waves(dtype, D, H, Hkv, waves, split):
+    """The matrix-core grouped kernels (bf16 head widths 64, 128, 256; float32
+    32, 64, 128) with four and with eight waves per workgroup (eight is the
+    default when a workgroup serves 8 or 16 query heads, except at bf16 width
+    256): every context against the oracle, unsplit and split."""
+    w = _small(f"gqa_waves_{dtype}_{D}_{H}_{Hkv}", dtype, D, 16, LENGTHS, heads=H, kv_heads=Hkv,
                seed=47, layers=1)
     kp, vp = device_pool(w)
     pool = _pool(w, kp, vp, split=split, merge=2)
@@ -338,10 +339,10 @@ def test_grouped_workgroup_waves(D, H, Hkv, waves, split):
     pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
     qh = w.q(0)
     out = torch.empty((w.n, H, D), device="cuda")
-    pkv.pkv_plan_decode_attention(plan, 0, rows_to_device(qh, "bf16"), _pt_device(w), out)
+    pkv.pkv_plan_decode_attention(plan, 0, rows_to_device(qh, dtype), _pt_device(w), out)
     torch.cuda.synchronize()
     for r in range(w.n):
-        assert max_err(out[r], _oracle_decode(w, 0, r, qh)) <= TOL["bf16"], (r, int(w.lengths[r]))
+        assert max_err(out[r], _oracle_decode(w, 0, r, qh)) <= TOL[dtype], (r, int(w.lengths[r]))
     pkv.pkv_plan_destroy(plan)
     pkv.pkv_pool_destroy(pool)
 
