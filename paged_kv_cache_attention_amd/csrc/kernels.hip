@@ -637,10 +637,12 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
 //     G query rows held in registers.  Lane l gets, for head row l%16, the
 //     scores of keys 4(l/16)..4(l/16)+3.
 //   O^T += V^T P^T on 16x16x16 MFMA: B = P^T is exactly that score layout;
-//     A = 16 dims x 16 keys of V^T, staged transposed in the wave's own LDS
-//     region (a lane loads 4 keys x 8 dims and stores 8 dims x 4 keys).
-//     Lane l accumulates, for head row l%16, dims 16 dt + 4(l/16)..+3, so the
-//     online-softmax rescale never leaves the lane.
+//     A = 16 dims x 16 keys of V^T.  A lane loads keys 4(l/16)..+3 with dims
+//     NT (l%16)..+NT-1 (NT = D/16); taking row r of context tile dt to be
+//     dim NT r + dt makes its A operand those four keys' dim NT (l%16) + dt,
+//     packed from its own registers (no transposition through memory).
+//     Lane l accumulates, for head row l%16, dims NT (4(l/16) + j) + dt, so
+//     the online-softmax rescale never leaves the lane.
 // Waves run independently until the end, then combine through LDS; each wave
 // publishes G / W of the heads (finish_heads: the contexts, or split-K
 // partials and the last-arriver merge, all heads of a wave at once).
@@ -808,11 +810,9 @@ __global__ __launch_bounds__(64 * W, D == 256 ? 1 : 8 / W) void attend_group_mfm
   constexpr int NT = D / 16;     // 16-dim tiles of the context (and dims per lane of V)
   constexpr int VB = 2 * NT;     // bytes of a V row per lane
   using VVec = RowVec<VB>;
-  constexpr int VT_STRIDE = 20;  // bf16 per V^T row (40 B: 16 rows of a read on distinct banks)
   static_assert(G == 4 || G == 8 || G == 16, "groups of 4, 8 or 16 heads");
   static_assert((W == 4 || W == 8) && G % W == 0, "4 or 8 waves, each publishing G / W heads");
-  // Per wave: the final partial context [16 rows][D]; while blocks stream,
-  // its first D * VT_STRIDE bf16 hold the wave's V^T staging.
+  // Per wave: the final partial context [16 rows][D].
   __shared__ __attribute__((aligned(16))) float s_acc[W][16][D];
   __shared__ float s_m[W][16], s_l[W][16];
 
@@ -834,7 +834,6 @@ __global__ __launch_bounds__(64 * W, D == 256 ? 1 : 8 / W) void attend_group_mfm
   const int last_blk = (t - 1) / kBlockRows;
   const bool fused = a.fuse_append != 0 && it.blk_end > last_blk;
   const int64_t kvrow = ((int64_t)it.req * a.num_kv_heads + kvh) * ROW_BYTES;
-  uint16_t* vt = reinterpret_cast<uint16_t*>(&s_acc[wave][0][0]);
 
   bf16x8_t qf[ND];
   {
@@ -904,16 +903,6 @@ __global__ __launch_bounds__(64 * W, D == 256 ? 1 : 8 / W) void attend_group_mfm
         valid_k[i] = key < t ? 0.f : -INFINITY;
       }
     }
-    // V^T into this wave's LDS: NT dims x 4 keys per lane, one 8-byte store per dim
-#pragma unroll
-    for (int e = 0; e < NT; ++e) {
-      const int w = e >> 1;
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
-      uint2 x;
-      x.x = __builtin_amdgcn_perm(vv[1].w[w], vv[0].w[w], sel);
-      x.y = __builtin_amdgcn_perm(vv[3].w[w], vv[2].w[w], sel);
-      *reinterpret_cast<uint2*>(&vt[(NT * ql + e) * VT_STRIDE + 4 * g]) = x;
-    }
     f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dc = 0; dc < ND; ++dc)
@@ -955,23 +944,28 @@ __global__ __launch_bounds__(64 * W, D == 256 ? 1 : 8 / W) void attend_group_mfm
 #pragma unroll
     for (int j = 0; j < 4; ++j) pb4[j] = (__bf16)p[j];
     const s16x4_t pb = __builtin_bit_cast(s16x4_t, pb4);
+    // Value tile dt, row r is dim NT r + dt, so the A operand of lane (ql, g)
+    // -- dim NT ql + dt of keys 4g .. 4g+3 -- is its own V data, packed.
 #pragma unroll
     for (int dt = 0; dt < NT; ++dt) {
-      const uint2 v2 = *reinterpret_cast<const uint2*>(&vt[(16 * dt + ql) * VT_STRIDE + 4 * g]);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, v2), pb,
+      const int w = dt >> 1;
+      const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+      uint2 x;
+      x.x = __builtin_amdgcn_perm(vv[1].w[w], vv[0].w[w], sel);
+      x.y = __builtin_amdgcn_perm(vv[3].w[w], vv[2].w[w], sel);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, x), pb,
                                                           acc[dt], 0, 0, 0);
     }
   };
 
   group_block_loop<W, Buf>(a, it, rq, wave, lane, last_blk, load_block, step);
 
-  // Combine the four waves through LDS (each wave's V^T staging is done: its
-  // LDS operations complete in order), then each wave publishes heads
-  // wave, wave + 4, ...
+  // Combine the waves through LDS (lane (ql, g) holds dims NT (4 g + j) + dt
+  // of head ql), then each wave publishes heads wave, wave + W, ...
 #pragma unroll
   for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s_acc[wave][ql][16 * dt + 4 * g + j] = acc[dt][j];
+    for (int j = 0; j < 4; ++j) s_acc[wave][ql][NT * (4 * g + j) + dt] = acc[dt][j];
   if (g == 0) {
     s_m[wave][ql] = m;
     s_l[wave][ql] = l;
