@@ -317,23 +317,32 @@ __device__ inline void finish_chunk(const AttnArgs& a, const WorkItem& it, const
   merge_wave<MCOLS, true>(a, it.req, rq, h, lane);
 }
 
-// Work item and head tile of a workgroup when the query heads of a K/V head
-// span `tiles` workgroups (grid x = items x tiles).  The tiles of one item
-// sit 8 workgroup IDs apart: workgroups are dealt to the 8 XCDs round-robin,
-// so they share an XCD, start together and read the same K/V blocks at about
-// the same time, and the later reads can hit that XCD's L2.  Bijective: each
-// group of up to 8 items takes 8 x tiles consecutive IDs.
-struct ItemTile {
-  int item, tile;
+// Work item, K/V head and head tile of a workgroup.  The 1-D grid holds one
+// workgroup per (item, K/V head, tile), where `tiles` workgroups share the
+// query heads of a K/V head.  Consecutive (item, K/V head) units walk the K/V
+// heads of one item before the next item, so the plan's longest-first item
+// order holds across the whole grid and the short chunks are dispatched last
+// (a 2-D grid would repeat the whole item order once per K/V head).  The
+// tiles of one unit sit 8 workgroup IDs apart: workgroups are dealt to the 8
+// XCDs round-robin, so they share an XCD, start together and read the same
+// K/V blocks at about the same time, and the later reads can hit that XCD's
+// L2.  Bijective: each group of up to 8 units takes 8 x tiles consecutive IDs.
+struct GridUnit {
+  int item, kvh, tile;
 };
-__device__ inline ItemTile item_tile(int tiles) {
+__device__ inline GridUnit grid_unit(const AttnArgs& a) {
+  const int tiles = a.head_tiles;
   const int id = blockIdx.x;
-  if (tiles == 1) return {id, 0};
-  const int n = gridDim.x / tiles;
-  const int span = 8 * tiles;
-  const int q = id / span, r = id - q * span;
-  const int m = min(8, n - 8 * q);
-  return {8 * q + r % m, r / m};
+  int u = id, tile = 0;
+  if (tiles > 1) {
+    const int n = gridDim.x / tiles;
+    const int span = 8 * tiles;
+    const int q = id / span, r = id - q * span;
+    const int m = min(8, n - 8 * q);
+    u = 8 * q + r % m;
+    tile = r / m;
+  }
+  return {u / a.num_kv_heads, u % a.num_kv_heads, tile};
 }
 
 // ---------------------------------------------------------------------------
@@ -365,15 +374,15 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
   static_assert(NG * WPG == WAVES, "waves must split evenly into head groups");
   constexpr int G = NG * HPW;              // query heads per K/V head
 
-  // Grid y: K/V head kvh; grid x: work item and which of head_tiles
-  // consecutive shares of G query heads this workgroup serves (one share
-  // unless the group exceeds what one workgroup holds or has an odd factor).
+  // Work item, K/V head kvh and which of head_tiles consecutive shares of G
+  // query heads this workgroup serves (one share unless the group exceeds
+  // what one workgroup holds or has an odd factor).
   const int tiles = a.head_tiles;
-  const ItemTile itl = item_tile(tiles);
-  const WorkItem it = plan_item(a, itl.item);
+  const GridUnit gu = grid_unit(a);
+  const WorkItem it = plan_item(a, gu.item);
   const ReqEntry rq = it.rq;
-  const int kvh = blockIdx.y;
-  const int tile = itl.tile;
+  const int kvh = gu.kvh;
+  const int tile = gu.tile;
   const int lane = threadIdx.x & 63;
   // Wave-uniform: block indices, page-table reads and branches stay scalar, so
   // the page lookups go through the scalar cache and never wait on the
@@ -817,11 +826,11 @@ __global__ __launch_bounds__(64 * W, D == 256 ? 1 : 8 / W) void attend_group_mfm
   __shared__ float s_m[W][16], s_l[W][16];
 
   const int tiles = a.head_tiles;  // shares of G query heads per K/V head, as in the fast kernel
-  const ItemTile itl = item_tile(tiles);
-  const WorkItem it = plan_item(a, itl.item);
+  const GridUnit gu = grid_unit(a);
+  const WorkItem it = plan_item(a, gu.item);
   const ReqEntry rq = it.rq;
-  const int kvh = blockIdx.y;
-  const int tile = itl.tile;
+  const int kvh = gu.kvh;
+  const int tile = gu.tile;
   const int qbase = (kvh * tiles + tile) * G;  // first query head of this workgroup
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1031,11 +1040,11 @@ __global__ __launch_bounds__(64 * W, D == 128 ? 1 : 8 / W) void attend_group_f32
   __shared__ float s_m[W][16], s_l[W][16];
 
   const int tiles = a.head_tiles;
-  const ItemTile itl = item_tile(tiles);
-  const WorkItem it = plan_item(a, itl.item);
+  const GridUnit gu = grid_unit(a);
+  const WorkItem it = plan_item(a, gu.item);
   const ReqEntry rq = it.rq;
-  const int kvh = blockIdx.y;
-  const int tile = itl.tile;
+  const int kvh = gu.kvh;
+  const int tile = gu.tile;
   const int qbase = (kvh * tiles + tile) * G;  // first query head of this workgroup
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1337,7 +1346,7 @@ __global__ __launch_bounds__(256) void patch_kernel(int32_t* arena, PatchBatch b
 template <typename T, int D, int WAVES, int HPW, int WPG, bool PAD = false>
 hipError_t launch_fast_shape(const AttnArgs& a, int num_items, hipStream_t stream) {
   hipLaunchKernelGGL((attend_fast_kernel<T, D, WAVES, HPW, WPG, PAD>),
-                     dim3(num_items * a.head_tiles, a.num_kv_heads), dim3(64 * WAVES), 0, stream,
+                     dim3(num_items * a.head_tiles * a.num_kv_heads), dim3(64 * WAVES), 0, stream,
                      a);
   return hipGetLastError();
 }
@@ -1496,7 +1505,7 @@ hipError_t launch_attention(const AttnArgs& args, int dtype, int num_items, hipS
     if (path_out) *path_out = KernelPath::kFast;
     const int share = head_share(group, {16, 8, 4});
     a.head_tiles = group / share;
-    const dim3 grid(num_items * a.head_tiles, a.num_kv_heads);
+    const dim3 grid(num_items * a.head_tiles * a.num_kv_heads);
     if (dtype == kDtypeF32) {
       switch (a.head_width) {
         case 32: return launch_group_f32<32>(a, share, grid, stream);
