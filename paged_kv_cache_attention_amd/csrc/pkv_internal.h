@@ -166,7 +166,7 @@ hipError_t launch_page_copies(char* k_storage, char* v_storage, int64_t layer_by
                               hipStream_t stream);
 bool fast_path_supported(int dtype, int head_width, int page_size, int group);
 
-// Prefill on matrix cores (bf16, head width 128, pages of a multiple of 16
+// Prefill on matrix cores (bf16, head width 64, 128 or 256, pages of a multiple of 16
 // rows): an append launch writes the chunk's rows, then an attention launch
 // runs the causal attention of every (tile, query head).
 bool prefill_fast_supported(int dtype, int head_width, int page_size);
