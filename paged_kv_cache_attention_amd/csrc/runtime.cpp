@@ -431,6 +431,10 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
     return (a.blk_end - a.blk_begin) > (b.blk_end - b.blk_begin);
   });
 
+  // One launch holds a workgroup per (chunk, head) at most.
+  if ((int64_t)items.size() * p->desc.num_heads > std::numeric_limits<int32_t>::max())
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%zu chunks x %d heads exceed one launch", items.size(),
+                p->desc.num_heads);
   // Small unsplit plans are passed inline in the kernel arguments.
   const bool inline_plan = n <= pkv::kInlinePlan && (int64_t)items.size() <= pkv::kInlinePlan &&
                            slots == 0;
