@@ -532,11 +532,12 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
   // Software pipeline over this wave's blocks first, first+WPG, ..., wave_last:
   // the K/V loads of the next block are issued before the current block is
   // computed, and the page ID of the block after that is read one step
-  // ahead.  Look-ahead indices are clamped to wave_last instead of being
-  // guarded by a branch, so every path keeps the same loads in flight and the
-  // wait counts stay exact; the one redundant reload at the end of a wave
-  // hits in L2.  Only a wave's final block can be the request's last block
-  // (the masked "edge" step).
+  // ahead (its index clamped to wave_last, so the read stays inside the
+  // table).  The wave's final block issues no look-ahead load: with chunks
+  // of a few blocks per wave, a clamped reload of the final block would add
+  // a third or half again to the wave's load requests (measured 1-2% on the
+  // launch).  Only a wave's final block can be the request's last block (the
+  // masked "edge" step).
   {
     const int end = it.blk_end;
     const int first = it.blk_begin + sub;
@@ -546,22 +547,22 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
       load_block(first, page_of(first), ka, va);
       int32_t p_next = page_of(min(first + WPG, wave_last));
       for (int b = first;; b += 2 * WPG) {
-        const int b1 = min(b + WPG, wave_last);
-        load_block(b1, p_next, kb, vb);
+        const int b1 = b + WPG;
+        if (b1 <= wave_last) load_block(b1, p_next, kb, vb);
         p_next = page_of(min(b + 2 * WPG, wave_last));
         if (b == last_blk)
           step(b, ka, va, std::true_type{});
         else
           step(b, ka, va, std::false_type{});
-        if (b + WPG > wave_last) break;
-        const int b2 = min(b + 2 * WPG, wave_last);
-        load_block(b2, p_next, ka, va);
+        if (b1 > wave_last) break;
+        const int b2 = b + 2 * WPG;
+        if (b2 <= wave_last) load_block(b2, p_next, ka, va);
         p_next = page_of(min(b + 3 * WPG, wave_last));
         if (b1 == last_blk)
           step(b1, kb, vb, std::true_type{});
         else
           step(b1, kb, vb, std::false_type{});
-        if (b + 2 * WPG > wave_last) break;
+        if (b2 > wave_last) break;
       }
     }
   }
