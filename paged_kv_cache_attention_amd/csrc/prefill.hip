@@ -74,9 +74,30 @@ __device__ inline int kv_byte(int row, int chunk) {
   return row * (2 * D) + ((chunk ^ (row & (D / 8 - 1))) << 4);
 }
 
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+// One 16-byte-per-lane buffer load straight into LDS: lane i's 16 bytes at
+// byte voff(i) of [base, base + bytes) land at LDS byte lds_addr + 16 i
+// (reads past `bytes` return zeros).  Inline assembly rather than the
+// builtin: the compiler cannot tell which of the two LDS buffers a builtin
+// load writes, so it waits for every such load before any LDS read of
+// either buffer, which exposes the staging of block k+1 before block k is
+// computed.  The block loop's own s_waitcnt and barrier order these loads.
+__device__ inline void lds_dma16(const char* base, uint32_t bytes, uint32_t voff,
+                                 uint32_t lds_addr) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const i32x4_t rsrc = {(int32_t)(uint32_t)p, (int32_t)((uint32_t)(p >> 32) & 0xFFFFu),
+                        (int32_t)bytes, 0x00020000};
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+      : "memory");
+}
+
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Workgroup: 4 waves on one tile (request, up to 128 consecutive chunk rows)
 // and one query head; each wave owns 32 query rows as two sets of 16 (at head
@@ -189,23 +210,24 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
   const const_i32_ptr ptc = (const_i32_ptr)pt;
   auto stage = [&](int key0, int b) {
     if (key0 + kBlockKeys <= tile.key_end) {
+      int32_t pg[NPART];
+#pragma unroll
+      for (int i = 0; i < NPART; ++i) {
+        const int key = key0 + RPI * (WAVES * i + wave);
+        pg[i] = ptc[PAGE16 ? key >> 4 : key / S];
+      }
+      const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(&sKV[b][0][0]);
+      const uint32_t lds1 = (uint32_t)reinterpret_cast<uintptr_t>(&sKV[b][1][0]);
 #pragma unroll
       for (int i = 0; i < NPART; ++i) {
         const int r0 = RPI * (WAVES * i + wave);   // first block row of the part
         const int key = key0 + r0;
-        const int page_idx = PAGE16 ? key >> 4 : key / S;
-        const int slot0 = PAGE16 ? key & 15 : key - page_idx * S;
-        const int64_t page = (int64_t)ptc[page_idx] * a.page_bytes + head_off;
+        const int slot0 = PAGE16 ? key & 15 : key - (key / S) * S;
+        const int64_t page = (int64_t)pg[i] * a.page_bytes + head_off;
         const int r = r0 + lrow;
-        const int voff = (slot0 + lrow) * kRowBytes + ((lpos ^ (r & (NC - 1))) << 4);
-        const auto rk = __builtin_amdgcn_make_buffer_rsrc(a.k_layer + page, 0, S * kRowBytes,
-                                                          0x00020000);
-        const auto rv = __builtin_amdgcn_make_buffer_rsrc(a.v_layer + page, 0, S * kRowBytes,
-                                                          0x00020000);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)&sKV[b][0][r0 * kRowBytes], 16,
-                                                 voff, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&sKV[b][1][r0 * kRowBytes], 16,
-                                                 voff, 0, 0, 0);
+        const uint32_t voff = (slot0 + lrow) * kRowBytes + ((lpos ^ (r & (NC - 1))) << 4);
+        lds_dma16(a.k_layer + page, S * kRowBytes, voff, lds0 + r0 * kRowBytes);
+        lds_dma16(a.v_layer + page, S * kRowBytes, voff, lds1 + r0 * kRowBytes);
       }
     } else {
       // Partial block: keys clamped to the last row the tile may read (the
