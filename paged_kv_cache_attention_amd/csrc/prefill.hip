@@ -120,9 +120,10 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 // lane 4k + j/4 addresses, k = 0..3; lane i addressing key base + i/4, dims
 // 16 dt + 4 (i%4)..+3 then hands lane j the dim 16 dt + j of keys base..+3).
 // Each K or V fragment read from LDS feeds the MFMAs of both query sets.
-// Online softmax per query in log2 units; the running maximum and sum are
-// reduced across the four lane groups with permlane swaps, and the maximum
-// moves lazily (only by more than 2^8 in weight).  The context accumulates in
+// Online softmax per query in log2 units; the running maximum is reduced
+// across the four lane groups with permlane swaps and moves lazily (only by
+// more than 2^8 in weight); the running sum comes from the matrix cores
+// (head width <= 128) or the same swaps (256).  The context accumulates in
 // the MFMA output layout (lane l: rows 4(l/16)..+3, column l%16 of each
 // 16-column tile), whose per-row scale factors come from the owning lanes by
 // shuffle.
@@ -188,12 +189,21 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
   const int wave_last_pos = pos0 + min(wrow0 + 16 * QS - 1, tile.nq - 1);
   const bool wave_active = wrow0 < tile.nq;
 
+  // Row sums of the weights.  Up to head width 128 they come from a matrix
+  // product of the bf16 weights with a block of ones, so they sit in the
+  // context's row layout and sum exactly the weights the value product used
+  // (two reductions across lane groups and ~40 vector instructions per block
+  // fewer); at 256, where that product measured slower, from a lane-group
+  // reduction of the float32 weights.
+  constexpr bool kOnesSum = D <= 128;
   float m[QS], l[QS];
+  f32x4_t lsum[QS];
   f32x4_t acc[QS][NT];
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs) {
     m[qs] = -INFINITY;
     l[qs] = 0.f;
+    lsum[qs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs)
@@ -334,6 +344,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float aj = __shfl(alpha, 4 * g + j);
+          lsum[qs][j] *= aj;
 #pragma unroll
           for (int dt = 0; dt < NT; ++dt) acc[qs][dt][j] *= aj;
         }
@@ -347,9 +358,9 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           s[qs][kt][j] = __builtin_amdgcn_exp2f(fmaf(s[qs][kt][j], a.scale_log2e, -m[qs]));
-          ps += s[qs][kt][j];
+          if constexpr (!kOnesSum) ps += s[qs][kt][j];
         }
-      l[qs] += xor32_sum(xor16_sum(ps));
+      if constexpr (!kOnesSum) l[qs] += xor32_sum(xor16_sum(ps));
     }
     // ---- O += P V over two 32-key steps ----
 #pragma unroll
@@ -363,6 +374,10 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
         pu.z = pack_bf16x2(s[qs][2 * kc + 1][0], s[qs][2 * kc + 1][1]);
         pu.w = pack_bf16x2(s[qs][2 * kc + 1][2], s[qs][2 * kc + 1][3]);
         pf[qs] = as_bf16x8(pu);
+        if constexpr (kOnesSum)
+          lsum[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              pf[qs], as_bf16x8(uint4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}),
+              lsum[qs], 0, 0, 0);
       }
       // transposing reads: lane (g, i) addresses key 32 kc + 4 g + i/4 (and
       // + 16), dims 16 dt + 4 (i%4)..+3
@@ -390,7 +405,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = wrow0 + 16 * qs + 4 * g + j;
-      const float inv = 1.0f / __shfl(l[qs], 4 * g + j);
+      const float inv = 1.0f / (kOnesSum ? lsum[qs][j] : __shfl(l[qs], 4 * g + j));
       if (row < tile.nq) {
         float* o = a.out + ((int64_t)(tile.off + tile.i0 + row) * a.num_heads + h) * D;
 #pragma unroll
