@@ -42,19 +42,19 @@ HBM_PEAK_GBS = 8000.0
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
     "batch32_fp32_l12": {"source": "kernels.hip", "sha256_16": "133e1ec9db657ded",
-        "fetch_kib": 44577.4, "write_kib": 2016.9,
+        "fetch_kib": 44579.0, "write_kib": 2016.9,
         "algorithmic_bytes": 88971264},
     "batch256_bf16": {"source": "kernels.hip", "sha256_16": "133e1ec9db657ded",
-        "fetch_kib": 4761735.9, "write_kib": 4337.9,
+        "fetch_kib": 4761711.8, "write_kib": 4344.5,
         "algorithmic_bytes": 9718775808},
     "batch256_gqa8_bf16": {"source": "kernels.hip", "sha256_16": "133e1ec9db657ded",
-        "fetch_kib": 1194158.1, "write_kib": 4097.0,
+        "fetch_kib": 1194183.0, "write_kib": 4096.9,
         "algorithmic_bytes": 2434412544},
     "batch256_mqa_bf16": {"source": "kernels.hip", "sha256_16": "133e1ec9db657ded",
-        "fetch_kib": 151913.3, "write_kib": 4096.0,
+        "fetch_kib": 151923.6, "write_kib": 4096.0,
         "algorithmic_bytes": 309806592},
-    "prefill32_bf16": {"source": "prefill.hip", "sha256_16": "d57900f82795861b",
-        "fetch_kib": 726135.2, "write_kib": 518320.3,
+    "prefill32_bf16": {"source": "prefill.hip", "sha256_16": "e74f038f9ebf466f",
+        "fetch_kib": 724398.0, "write_kib": 518320.3,
         "algorithmic_bytes": 1854562304},
 }
 
