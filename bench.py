@@ -19,8 +19,9 @@ and sums each launch's algorithmic bytes.
 Other workloads (--workload): batch256_bf16, skewed64_bf16 (single-layer
 batched decode over existing rows), batch256_gqa8_bf16 and batch256_mqa_bf16
 (the same batch with 32 query heads sharing 8 K/V heads, or one), fullstep128_bf16_l32 (32 layers, 128
-requests, bf16, 1% seeded aborts), prefill32_bf16 (batched prefill chunks,
-reported in TFLOP/s against the bf16 matrix-core peak) and tiny (the latency-bound fixture:
+requests, bf16, 1% seeded aborts), prefill32_bf16 and prefill32_fp32 (batched
+prefill chunks, reported in TFLOP/s against the matrix-core peak of their
+dtype) and tiny (the latency-bound fixture:
 token-at-a-time steps of one request, reported in steps/s and us/step).
 """
 from __future__ import annotations
@@ -305,7 +306,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense matrix-core peaks
 
 
 def step_spread(step, steps: int) -> dict:
@@ -347,7 +348,8 @@ def prefill_bench(args, w):
     attends causally over its prefix and itself, in one pkv_prefill_attention
     call (append launch + matrix-core attention launch).  Reported in TFLOP/s
     of the score and value products (4 d_h per new row, head and attended
-    row); the roofline is the attention kernel against bf16 dense MFMA."""
+    row); the roofline is the attention kernel against the dense matrix-core
+    peak of the pool's dtype (bf16 2.5 PFLOP/s, float32 157.3 TFLOP/s)."""
     import torch
 
     import paged_kv_cache_attention_amd as pkv
@@ -430,11 +432,11 @@ def prefill_bench(args, w):
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "prefill_mfma_kernel",
+            "kernel": "prefill_f32_kernel" if w.dtype == "f32" else "prefill_mfma_kernel",
             "achieved": round(achieved, 1),
-            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "peak": MFMA_PEAK_TFLOPS[w.dtype],
             "unit": "TFLOP/s",
-            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "frac": round(achieved / MFMA_PEAK_TFLOPS[w.dtype], 4),
             "avg_launch_us": round(avg_s * 1e6, 2),
             "flops_per_launch": int(prof.prefill_flops / max(1, launches)) if prof else 0,
             "launches_timed": int(launches),

@@ -122,6 +122,7 @@ struct PrefillArgs {
   int64_t page_bytes;
   int64_t head_bytes;
   float scale_log2e;
+  int32_t dtype;          // kDtypeF32 or kDtypeBF16
 };
 
 struct PatchBatch {
@@ -166,9 +167,10 @@ hipError_t launch_page_copies(char* k_storage, char* v_storage, int64_t layer_by
                               hipStream_t stream);
 bool fast_path_supported(int dtype, int head_width, int page_size, int group);
 
-// Prefill on matrix cores (bf16, head width 64, 128 or 256, pages of a multiple of 16
-// rows): an append launch writes the chunk's rows, then an attention launch
-// runs the causal attention of every (tile, query head).
+// Prefill on matrix cores (bf16 head width 64, 128 or 256; float32 32, 64 or
+// 128; pages of a multiple of 16 rows): an append launch writes the chunk's
+// rows, then an attention launch runs the causal attention of every (tile,
+// query head).
 bool prefill_fast_supported(int dtype, int head_width, int page_size);
 hipError_t launch_prefill_append(const PrefillArgs& a, int num_tiles, hipStream_t stream);
 hipError_t launch_prefill_attention(const PrefillArgs& a, int num_tiles, hipStream_t stream);

@@ -135,6 +135,17 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 // eight with one set each; either way a workgroup covers a 128-row tile.
 constexpr int prefill_waves(int D) { return D == 256 ? 8 : 4; }
 
+// Work item (query head, tile) of this workgroup: consecutive items share a
+// request's K/V (the tile list is grouped by request).  Workgroups go to the
+// eight XCDs round-robin, each with its own L2, so each XCD gets a contiguous
+// range of items: tiles that re-read the same K/V rows then share one L2.
+__device__ inline int prefill_item() {
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int per = nwg / kXcds, rem = nwg % kXcds;
+  return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
 template <bool PAGE16, int D>
 __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(PrefillArgs a) {
   static_assert(D == 64 || D == 128 || D == 256, "head widths 64, 128 and 256");
@@ -149,14 +160,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
   // [buffer][0: K, 1: V][64 rows x 256 B], swizzled as kv_byte describes
   __shared__ __attribute__((aligned(16))) char sKV[2][2][kBlockKeys * kRowBytes];
 
-  // Work item (query head, tile): consecutive items share a request's K/V
-  // (the tile list is grouped by request).  Workgroups go to the eight XCDs
-  // round-robin, each with its own L2, so each XCD gets a contiguous range of
-  // items: tiles that re-read the same K/V rows then share one L2.
-  const int nwg = gridDim.x;
-  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  const int per = nwg / kXcds, rem = nwg % kXcds;
-  const int item = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  const int item = prefill_item();
   const int h = item / a.num_tiles;
   const PrefillTile tile = a.tiles[item - h * a.num_tiles];
   const int kvh = h / (a.num_heads / a.num_kv_heads);
@@ -414,13 +418,263 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Float32 prefill on matrix cores (v_mfma_f32_16x16x4_f32), head widths 32,
+// 64 and 128.  Same tiles, work items, staging and online softmax as the
+// bf16 kernel; what differs is the operand layout of 4-deep float32 steps:
+//
+// Scores S^T = K Q^T, one 16-key tile kt at a time.  For dims 16 q .. 16 q +
+// 15 a lane group g supplies dims 16 q + 4 g + t at step t = 0..3, so lane l
+// reads four consecutive floats of key 16 kt + l%16 (one 16-byte LDS read
+// for four steps) and its query's matching four floats from registers; lane
+// l then holds the scores of query l%16 for keys 16 kt + 4 g + j.
+// Context O^T = V^T P^T, step j of tile kt taking keys 16 kt + 4 g + j from
+// lane group g: the B operand is the lane's own weight for that key and the
+// A operand one float of V (key 16 kt + 4 g + j, dim 16 dt + l%16).  Lane l
+// accumulates dims 16 dt + 4 g + (0..3) of query l%16, so the softmax's
+// per-query rescale is a lane's own scalar and the output row a 16-byte
+// store.  K and V sit row-major in LDS, 16-byte chunks XOR-swizzled by row
+// so both read patterns spread over the banks.  Weights stay float32.
+//
+// Keys per LDS block: 64, or 32 at head width 128 (rows of 512 bytes), so
+// two buffers of K and V take at most 64 KiB.  Four waves of two 16-row
+// query sets, or at head width 128 (twice the context and query registers)
+// eight waves of one set; either way a 128-row tile.
+constexpr int prefill_f32_waves(int D) { return D == 128 ? 8 : 4; }
+
+template <bool PAGE16, int D>
+__global__ __launch_bounds__(64 * prefill_f32_waves(D), 2) void prefill_f32_kernel(PrefillArgs a) {
+  static_assert(D == 32 || D == 64 || D == 128, "head widths 32, 64 and 128");
+  constexpr int WAVES = prefill_f32_waves(D);
+  constexpr int QS = 8 / WAVES;            // 16-row query sets per wave
+  constexpr int KB = D == 128 ? 32 : 64;   // keys per LDS block
+  constexpr int KT = KB / 16;              // 16-key tiles per block
+  constexpr int kRowBytes = 4 * D;
+  constexpr int NC = D / 4;                // 16-byte chunks per row
+  constexpr int NQ = D / 16;               // 16-dim groups of the score product
+  constexpr int NT = D / 16;               // 16-dim tiles of the context
+  constexpr int RPI = 64 / NC;             // rows per 1 KiB staging load
+  constexpr int NPART = KB / RPI / WAVES;  // staging loads per wave and block
+  static_assert(NPART >= 1 && 16 % RPI == 0, "a staging load stays inside one page");
+  __shared__ __attribute__((aligned(16))) char sKV[2][2][KB * kRowBytes];
+  auto chunk_byte = [](int row, int chunk) {
+    return row * kRowBytes + ((chunk ^ (row & (NC - 1))) << 4);
+  };
+
+  const int item = prefill_item();
+  const int h = item / a.num_tiles;
+  const PrefillTile tile = a.tiles[item - h * a.num_tiles];
+  const int kvh = h / (a.num_heads / a.num_kv_heads);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ql = lane & 15;
+  const int g = lane >> 4;
+  const int S = a.page_size;
+  const int32_t* pt = a.page_table + (int64_t)tile.pt_row * a.pt_stride;
+  const const_i32_ptr ptc = (const_i32_ptr)pt;
+  const int64_t head_off = (int64_t)kvh * a.head_bytes;
+  const int pos0 = tile.start + tile.i0;
+
+  // This lane's query rows (rows past the tile's count attend like its last
+  // row; their results are not stored) and their dims 16 q + 4 g .. + 3.
+  const int wrow0 = 16 * QS * wave;
+  int my_pos[QS];
+  f32x4_t qf[QS][NQ];
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    const int row = min(wrow0 + 16 * qs + ql, tile.nq - 1);
+    my_pos[qs] = pos0 + row;
+    const float* src = static_cast<const float*>(a.q) +
+                       ((int64_t)(tile.off + tile.i0 + row) * a.num_heads + h) * D;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) qf[qs][q] = *reinterpret_cast<const f32x4_t*>(src + 16 * q + 4 * g);
+  }
+  const int wave_first_pos = pos0 + min(wrow0, tile.nq - 1);
+  const int wave_last_pos = pos0 + min(wrow0 + 16 * QS - 1, tile.nq - 1);
+  const bool wave_active = wrow0 < tile.nq;
+
+  float m[QS], l[QS];
+  f32x4_t acc[QS][NT];
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    m[qs] = -INFINITY;
+    l[qs] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) acc[qs][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Staging of one KB-key block into buffer b, as in the bf16 kernel: wave
+  // w, part i covers block rows RPI (WAVES i + w) .. +RPI-1, inside one page;
+  // lane L takes row RPI (WAVES i + w) + L / NC and LDS chunk position L % NC.
+  const int lrow = lane / NC;
+  const int lpos = lane % NC;
+  auto stage = [&](int key0, int b) {
+    if (key0 + KB <= tile.key_end) {
+      int32_t pg[NPART];
+#pragma unroll
+      for (int i = 0; i < NPART; ++i) {
+        const int key = key0 + RPI * (WAVES * i + wave);
+        pg[i] = ptc[PAGE16 ? key >> 4 : key / S];
+      }
+      const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(&sKV[b][0][0]);
+      const uint32_t lds1 = (uint32_t)reinterpret_cast<uintptr_t>(&sKV[b][1][0]);
+#pragma unroll
+      for (int i = 0; i < NPART; ++i) {
+        const int r0 = RPI * (WAVES * i + wave);
+        const int key = key0 + r0;
+        const int slot0 = PAGE16 ? key & 15 : key - (key / S) * S;
+        const int64_t page = (int64_t)pg[i] * a.page_bytes + head_off;
+        const int r = r0 + lrow;
+        const uint32_t voff = (slot0 + lrow) * kRowBytes + ((lpos ^ (r & (NC - 1))) << 4);
+        lds_dma16(a.k_layer + page, S * kRowBytes, voff, lds0 + r0 * kRowBytes);
+        lds_dma16(a.v_layer + page, S * kRowBytes, voff, lds1 + r0 * kRowBytes);
+      }
+    } else {
+      // Partial block: keys clamped to the last row the tile may read (the
+      // clamped rows are masked, and finite, so they add nothing).
+      uint4 kx[NPART], vx[NPART];
+#pragma unroll
+      for (int i = 0; i < NPART; ++i) {
+        const int r = RPI * (WAVES * i + wave) + lrow;
+        const int key = min(key0 + r, tile.key_end - 1);
+        const int page_idx = PAGE16 ? key >> 4 : key / S;
+        const int slot = PAGE16 ? key & 15 : key - page_idx * S;
+        const int64_t off = (int64_t)pt[page_idx] * a.page_bytes + head_off +
+                            (int64_t)slot * kRowBytes + ((lpos ^ (r & (NC - 1))) << 4);
+        kx[i] = *reinterpret_cast<const uint4*>(a.k_layer + off);
+        vx[i] = *reinterpret_cast<const uint4*>(a.v_layer + off);
+      }
+#pragma unroll
+      for (int i = 0; i < NPART; ++i) {
+        const int r = RPI * (WAVES * i + wave) + lrow;
+        *reinterpret_cast<uint4*>(&sKV[b][0][r * kRowBytes + lpos * 16]) = kx[i];
+        *reinterpret_cast<uint4*>(&sKV[b][1][r * kRowBytes + lpos * 16]) = vx[i];
+      }
+    }
+  };
+  stage(0, 0);
+
+  const int nblocks = (tile.key_end + KB - 1) / KB;
+  for (int kb = 0; kb < nblocks; ++kb) {
+    const int key0 = kb * KB;
+    const int b = kb & 1;
+    // This wave's loads and stores into buffer b are complete; the barrier
+    // then makes every wave's visible and ends all reads of buffer b ^ 1.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kb + 1 < nblocks) stage(key0 + KB, b ^ 1);
+    const char* sK = sKV[b][0];
+    const char* sV = sKV[b][1];
+    // Causal skip, as in the bf16 kernel (block 0 is never skipped).
+    if (!wave_active || wave_last_pos < key0) continue;
+
+    // ---- scores: s[qs][kt][j] = q . k(key0 + 16 kt + 4 g + j) ----
+    float s[QS][KT][4];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      f32x4_t c[QS];
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) c[qs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const f32x4_t kf =
+            *reinterpret_cast<const f32x4_t*>(sK + chunk_byte(16 * kt + ql, 4 * q + g));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int qs = 0; qs < QS; ++qs)
+            c[qs] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], qf[qs][q][t], c[qs], 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) s[qs][kt][j] = c[qs][j];
+    }
+    if (key0 + KB - 1 > wave_first_pos) {
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (key0 + 16 * kt + 4 * g + j > my_pos[qs]) s[qs][kt][j] = -INFINITY;
+    }
+    float cand[QS];
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      float mb = s[qs][0][0];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mb = fmaxf(mb, s[qs][kt][j]);
+      cand[qs] = xor32_max(xor16_max(mb)) * a.scale_log2e;
+    }
+    // Lazy rescale, as in the bf16 kernel; a lane's context belongs to its
+    // own query, so the factor needs no exchange.
+    constexpr float kSlack = 8.f;
+    bool grow = false;
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) grow = grow || cand[qs] > m[qs] + kSlack;
+    if (__builtin_expect(__any(grow), 0)) {
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) {
+        const float mn = fmaxf(m[qs], cand[qs]);
+        const float alpha = __builtin_amdgcn_exp2f(m[qs] - mn);
+        l[qs] *= alpha;
+        m[qs] = mn;
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) acc[qs][dt] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      float ps = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s[qs][kt][j] = __builtin_amdgcn_exp2f(fmaf(s[qs][kt][j], a.scale_log2e, -m[qs]));
+          ps += s[qs][kt][j];
+        }
+      l[qs] += xor32_sum(xor16_sum(ps));
+    }
+    // ---- O^T += V^T P^T, 4 keys per step ----
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int vrow = 16 * kt + 4 * g + j;
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) {
+          const float vf = *reinterpret_cast<const float*>(
+              sV + chunk_byte(vrow, 4 * dt + (ql >> 2)) + 4 * (ql & 3));
+#pragma unroll
+          for (int qs = 0; qs < QS; ++qs)
+            acc[qs][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf, s[qs][kt][j], acc[qs][dt], 0, 0, 0);
+        }
+      }
+  }
+
+  if (!wave_active) return;
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    const int row = wrow0 + 16 * qs + ql;
+    if (row < tile.nq) {
+      const float inv = 1.0f / l[qs];
+      float* o = a.out + ((int64_t)(tile.off + tile.i0 + row) * a.num_heads + h) * D + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt)
+        *reinterpret_cast<f32x4_t*>(o + 16 * dt) = acc[qs][dt] * inv;
+    }
+  }
+}
+
 // Writes the chunk's new K/V rows into their slots: one workgroup per (tile,
 // K/V head), 16 bytes per lane.  It runs before the attention launch, which
 // reads the chunk's keys back from the pages (4 KiB contiguous per 16 keys
 // of a head, where the packed inputs put consecutive keys H_kv rows apart).
-template <int D>
+template <int kRowBytes>
 __global__ __launch_bounds__(256) void prefill_append_kernel(PrefillArgs a) {
-  constexpr int kRowBytes = 2 * D;
   const PrefillTile tile = a.tiles[blockIdx.x];
   const int kvh = blockIdx.y;
   const int S = a.page_size;
@@ -443,17 +697,31 @@ __global__ __launch_bounds__(256) void prefill_append_kernel(PrefillArgs a) {
 }  // namespace
 
 bool prefill_fast_supported(int dtype, int head_width, int page_size) {
-  return dtype == kDtypeBF16 && (head_width == 64 || head_width == 128 || head_width == 256) &&
-         page_size % 16 == 0;
+  if (page_size % 16 != 0) return false;
+  if (dtype == kDtypeBF16) return head_width == 64 || head_width == 128 || head_width == 256;
+  return dtype == kDtypeF32 && (head_width == 32 || head_width == 64 || head_width == 128);
 }
 
+// Rows of 128, 256 or 512 bytes (both dtypes' widths above).
 hipError_t launch_prefill_append(const PrefillArgs& a, int num_tiles, hipStream_t stream) {
   const dim3 grid(num_tiles, a.num_kv_heads);
   switch (a.head_bytes / a.page_size) {
-    case 128: hipLaunchKernelGGL(prefill_append_kernel<64>, grid, dim3(256), 0, stream, a); break;
-    case 256: hipLaunchKernelGGL(prefill_append_kernel<128>, grid, dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL(prefill_append_kernel<256>, grid, dim3(256), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL(prefill_append_kernel<128>, grid, dim3(256), 0, stream, a); break;
+    case 256: hipLaunchKernelGGL(prefill_append_kernel<256>, grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL(prefill_append_kernel<512>, grid, dim3(256), 0, stream, a); break;
   }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_prefill_f32(const PrefillArgs& a, int num_tiles, hipStream_t stream) {
+  const dim3 block(64 * prefill_f32_waves(D));
+  if (a.page_size == 16)
+    hipLaunchKernelGGL((prefill_f32_kernel<true, D>), dim3(num_tiles * a.num_heads), block, 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((prefill_f32_kernel<false, D>), dim3(num_tiles * a.num_heads), block, 0,
+                       stream, a);
   return hipGetLastError();
 }
 
@@ -470,6 +738,13 @@ hipError_t launch_prefill_width(const PrefillArgs& a, int num_tiles, hipStream_t
 }
 
 hipError_t launch_prefill_attention(const PrefillArgs& a, int num_tiles, hipStream_t stream) {
+  if (a.dtype == kDtypeF32) {
+    switch (a.head_bytes / a.page_size) {
+      case 128: return launch_prefill_f32<32>(a, num_tiles, stream);
+      case 256: return launch_prefill_f32<64>(a, num_tiles, stream);
+      default: return launch_prefill_f32<128>(a, num_tiles, stream);
+    }
+  }
   switch (a.head_bytes / a.page_size) {
     case 128: return launch_prefill_width<64>(a, num_tiles, stream);
     case 256: return launch_prefill_width<128>(a, num_tiles, stream);

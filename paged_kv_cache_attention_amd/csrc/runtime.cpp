@@ -671,6 +671,7 @@ pkv_status run_prefill_tiles(pkv_pool* p, int32_t n, const int32_t* rows, const 
   a.page_bytes = p->page_bytes;
   a.head_bytes = p->head_bytes;
   a.scale_log2e = (float)(1.4426950408889634 / std::sqrt((double)p->desc.head_width));
+  a.dtype = p->desc.kv_dtype;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (p->profiling) {
     e0 = take_event(p);

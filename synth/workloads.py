@@ -282,12 +282,28 @@ def prefill32_bf16() -> Workload:
     return _finish(w)
 
 
+def prefill32_fp32() -> Workload:
+    """Batched float32 prefill in the geometry of the 12-layer float32 step:
+    32 requests, one layer, H=12, D=64, 16-token pages, fp32; chunks of
+    U[256, 2048] new rows after retained prefixes of U[0, 2048] rows, drawn as
+    for the bf16 prefill but from their own seed."""
+    seed = 7
+    prefix = uniform_ints(stream_key(seed, TAG_LENGTHS, 0), 32, 0, 2048)
+    chunks = uniform_ints(stream_key(seed, TAG_LENGTHS, 1), 32, 256, 2048)
+    lengths = prefix + chunks
+    P = int(pages_needed(lengths, 16).sum()) + 32
+    w = Workload("prefill32_fp32", seed, 32, 1, 12, 64, 16, P, "f32", lengths,
+                 appends=True, description=prefill32_fp32.__doc__, chunks=chunks)
+    return _finish(w)
+
+
 WORKLOADS = {
     "batch32_fp32_l12": batch32_fp32,
     "batch256_bf16": batch256_bf16,
     "batch256_gqa8_bf16": batch256_gqa8_bf16,
     "batch256_mqa_bf16": batch256_mqa_bf16,
     "prefill32_bf16": prefill32_bf16,
+    "prefill32_fp32": prefill32_fp32,
     "skewed64_bf16": skewed64_bf16,
     "fullstep128_bf16_l32": fullstep128_bf16,
 }

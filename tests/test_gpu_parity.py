@@ -442,8 +442,10 @@ PREFILL_CASES = [
     ("bf16", 128, 16, 4, 4), ("bf16", 128, 16, 8, 2), ("bf16", 128, 32, 4, 1),
     ("bf16", 64, 16, 4, 4), ("bf16", 64, 16, 8, 2), ("bf16", 64, 32, 4, 1),
     ("bf16", 256, 16, 2, 1), ("bf16", 256, 32, 4, 2),
+    ("f32", 64, 16, 3, 3), ("f32", 64, 32, 4, 2), ("f32", 32, 16, 4, 1), ("f32", 32, 32, 2, 2),
+    ("f32", 128, 16, 2, 2), ("f32", 128, 32, 4, 1),
     # ... and per-row decode kernels
-    ("f32", 64, 16, 3, 3), ("f32", 40, 16, 2, 1), ("bf16", 128, 7, 2, 2), ("bf16", 96, 16, 2, 2),
+    ("f32", 40, 16, 2, 1), ("f32", 64, 7, 2, 2), ("bf16", 128, 7, 2, 2), ("bf16", 96, 16, 2, 2),
 ]
 PREFILL_CHUNKS = [(0, 1), (0, 37), (5, 20), (16, 16), (100, 70), (1000, 33), (0, 300)]
 
@@ -481,7 +483,8 @@ def test_prefill_rejects_ranges_outside_the_table():
 
 
 @pytest.mark.parametrize("dtype,D,H,Hkv", [("bf16", 128, 4, 2), ("f32", 64, 2, 2),
-                                           ("bf16", 64, 4, 1), ("bf16", 256, 2, 2)])
+                                           ("bf16", 64, 4, 1), ("bf16", 256, 2, 2),
+                                           ("f32", 128, 4, 1), ("f32", 32, 2, 2)])
 def test_prefill_transactional_chunks(dtype, D, H, Hkv):
     """begin_tokens chunks on several caches (one of them a single token),
     batched append_and_attend per layer, commit; an aborted chunk returns its
@@ -543,22 +546,25 @@ def test_prefill_transactional_chunks(dtype, D, H, Hkv):
     pkv.pkv_pool_destroy(pool)
 
 
-def test_prefill32_bf16_full_sampled():
-    """The full prefill workload (32 chunks of 256-2048 rows over prefixes of
-    0-2048, H=32, d_h=128, bf16) in the bench's call; sampled (row, head)
-    contexts against the oracle, sampled page writes bit-exact."""
+@pytest.mark.parametrize("name", ["prefill32_bf16", "prefill32_fp32"])
+def test_prefill32_full_sampled(name):
+    """The full prefill workloads (32 chunks of 256-2048 rows over prefixes of
+    0-2048; H=32, d_h=128, bf16, and H=12, d_h=64, fp32) in the bench's call;
+    sampled (row, head) contexts against the oracle, sampled page writes
+    bit-exact."""
     from synth import gpu as sgpu
-    w = W.prefill32_bf16()
+    w = W.WORKLOADS[name]()
+    dt = sgpu.torch_dtype(w.dtype)
     H, Hkv, D, S = w.heads, w.hkv, w.head_width, w.page_size
     T = int(w.chunks.sum())
     kp, vp = device_pool(w)
     keys = [synth.stream_key(w.seed, tag, 0, 1000) for tag in (synth.TAG_Q, synth.TAG_K,
                                                                    synth.TAG_V)]
-    q = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
-    k = torch.empty((T, Hkv, D), dtype=torch.bfloat16, device="cuda")
-    v = torch.empty((T, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((T, H, D), dtype=dt, device="cuda")
+    k = torch.empty((T, Hkv, D), dtype=dt, device="cuda")
+    v = torch.empty((T, Hkv, D), dtype=dt, device="cuda")
     for t, key in zip((q, k, v), keys):
-        sgpu.fill_normal(t, key, "bf16")
+        sgpu.fill_normal(t, key, w.dtype)
     pool = _pool(w, kp, vp)
     out = torch.full((T, H, D), float("nan"), device="cuda")
     pkv.pkv_prefill_attention(pool, 0, _pt_device(w), w.pt_stride, w.starts.tolist(),
@@ -571,7 +577,7 @@ def test_prefill32_bf16_full_sampled():
     def rows(key, first, n, heads, head):
         idx = (((first + np.arange(n, dtype=np.uint64))[:, None] * np.uint64(heads) +
                 np.uint64(head)) * np.uint64(D) + np.arange(D, dtype=np.uint64)).ravel()
-        return synth.normals_at(key, idx, "bf16").reshape(n, D)
+        return synth.normals_at(key, idx, w.dtype).reshape(n, D)
 
     picks = {int(np.argmax(w.chunks)), int(np.argmin(w.chunks)), int(np.argmax(w.starts))}
     for r in sorted(picks):
@@ -580,16 +586,16 @@ def test_prefill32_bf16_full_sampled():
             j = int(offs[r]) + i
             pos = st + i
             page, slot = w.page_tables[r][pos // S], pos % S
-            assert np.array_equal(to_bits(kp[0, page, :, slot, :], "bf16"),
+            assert np.array_equal(to_bits(kp[0, page, :, slot, :], w.dtype),
                                   np.stack([rows(keys[1], j, 1, Hkv, h)[0] for h in range(Hkv)]))
-            for h in (0, 13, H - 1):
+            for h in sorted({0, min(13, H - 1), H - 1}):
                 K = np.concatenate([oracle.kv_to_f64(oracle.gather_prefix(kpg, w.page_tables[r], st, S, h)).reshape(-1, D),
                                     oracle.kv_to_f64(rows(keys[1], int(offs[r]), i + 1, Hkv, h))])
                 V = np.concatenate([oracle.kv_to_f64(oracle.gather_prefix(vpg, w.page_tables[r], st, S, h)).reshape(-1, D),
                                     oracle.kv_to_f64(rows(keys[2], int(offs[r]), i + 1, Hkv, h))])
                 ref = oracle.attend(rows(keys[0], j, 1, H, h)[0], K, V)
                 err = float(np.max(np.abs(out[j, h].cpu().numpy().astype(np.float64) - ref)))
-                assert err <= TOL["bf16"], (r, i, h, err)
+                assert err <= TOL[w.dtype], (r, i, h, err)
     pkv.pkv_pool_destroy(pool)
 
 
