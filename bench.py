@@ -46,17 +46,20 @@ MEASURED_TRAFFIC = {
         "fetch_kib": 44579.0, "write_kib": 2016.9,
         "algorithmic_bytes": 88971264},
     "batch256_bf16": {"source": "kernels.hip", "sha256_16": "133e1ec9db657ded",
-        "fetch_kib": 4761711.8, "write_kib": 4344.5,
+        "fetch_kib": 4761703.0, "write_kib": 4343.8,
         "algorithmic_bytes": 9718775808},
     "batch256_gqa8_bf16": {"source": "kernels.hip", "sha256_16": "133e1ec9db657ded",
-        "fetch_kib": 1194183.0, "write_kib": 4096.9,
+        "fetch_kib": 1194148.8, "write_kib": 4096.8,
         "algorithmic_bytes": 2434412544},
     "batch256_mqa_bf16": {"source": "kernels.hip", "sha256_16": "133e1ec9db657ded",
-        "fetch_kib": 151923.6, "write_kib": 4096.0,
+        "fetch_kib": 151861.4, "write_kib": 4096.0,
         "algorithmic_bytes": 309806592},
-    "prefill32_bf16": {"source": "prefill.hip", "sha256_16": "e74f038f9ebf466f",
-        "fetch_kib": 724398.0, "write_kib": 518320.3,
+    "prefill32_bf16": {"source": "prefill.hip", "sha256_16": "64e07feb42ad9f32",
+        "fetch_kib": 723120.0, "write_kib": 518320.2,
         "algorithmic_bytes": 1854562304},
+    "prefill32_fp32": {"source": "prefill.hip", "sha256_16": "64e07feb42ad9f32",
+        "fetch_kib": 292600.8, "write_kib": 97857.0,
+        "algorithmic_bytes": 575582208},
 }
 
 
