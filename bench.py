@@ -191,6 +191,7 @@ def main():
             pkv.pkv_begin_token_batched(all_caches)
             live = list(range(n))
             live_arr = all_caches
+            idx = None
             kv_bytes = 0
             t_sum = sum(lens) + n
             for layer in range(L):
@@ -200,10 +201,14 @@ def main():
                     live = [r for r in live if abort[r] != layer]
                     live_arr = pkv.pkv_cache_array([caches[r] for r in live])
                     t_sum = sum(lens[r] + 1 for r in live)
+                    # the live rows' index, uploaded once per abort from
+                    # pinned memory without waiting for the stream (a
+                    # pageable upload would drain it at every later layer)
+                    idx = torch.tensor(live, dtype=torch.int64).pin_memory().to(
+                        "cuda", non_blocking=True)
                 if len(live) == n:
                     q, k, v, o = q_all[layer], k_all[layer], v_all[layer], out
                 else:
-                    idx = torch.tensor(live, device="cuda")
                     q, k, v = q_all[layer][idx], k_all[layer][idx], v_all[layer][idx]
                     o = out[:len(live)]
                 kv_bytes += t_sum * Hkv * 2 * D * elt
