@@ -1026,7 +1026,7 @@ def test_fullstep128_bf16_l32_transactional():
 # ------------------------------------------------------ randomized sweep --
 def _random_case(rng):
     dtype = ["f32", "bf16"][rng.integers(2)]
-    D = int(rng.choice([64, 128, 40, 96] if dtype == "f32" else [128, 128, 64, 80]))
+    D = int(rng.choice([64, 128, 40, 96, 32] if dtype == "f32" else [128, 128, 64, 80, 256]))
     S = int(rng.choice([16, 16, 32, 8, 5]))
     H = int(rng.choice([1, 2, 4, 6, 8, 16]))
     divisors = [d for d in range(1, H + 1) if H % d == 0]
