@@ -281,9 +281,9 @@ pkv_status flush_patches(pkv_pool* p, hipStream_t stream) {
 // Workgroup shape and split-K chunk size (in 16-row blocks) of a plan.
 //
 // Waves per workgroup: PKV_OPT_WAVES, or 0 to let the launcher choose per
-// kernel (four for the vector kernels; eight for the matrix-core kernel when
-// a workgroup serves 8 or 16 query heads, whose requests then finish in half
-// the block steps per wave).
+// kernel (four for the vector kernels, eight for a small multi-head batch as
+// below; eight for the matrix-core kernel when a workgroup serves 8 or 16
+// query heads, whose requests then finish in half the block steps per wave).
 // Requests split into chunks sized for about kTargetChunks (chunk, query
 // head) units -- four resident rounds of 256 CUs x 4 workgroups -- so a batch
 // with few (request, head) pairs still fills the GPU and one long context
@@ -294,7 +294,7 @@ struct SplitChoice {
   int32_t waves;
 };
 
-SplitChoice choose_split(const pkv_pool* p, int64_t total_blocks) {
+SplitChoice choose_split(const pkv_pool* p, int32_t n, int64_t total_blocks) {
   // Work is counted in (block, query head) units: a workgroup serving a K/V
   // head does the work of its whole group, so grouped heads split like the
   // multi-head case (measured: splitting them further only adds partial
@@ -307,6 +307,16 @@ SplitChoice choose_split(const pkv_pool* p, int64_t total_blocks) {
   const int64_t work = total_blocks * H;  // (block, head) units
   int64_t c = 8;
   while (c < 512 && c * kTargetChunks < work) c *= 2;
+  // A small multi-head batch with enough (request, head) pairs for an
+  // eight-wave workgroup on every CU: 32-block chunks over eight waves (four
+  // blocks per wave) instead of 8-block chunks over four, so fewer requests
+  // split and fewer partials are published and merged for the same loads in
+  // flight (measured on the 12-layer float32 step: 24.5 -> 23.7 us per
+  // launch; 16-, 24-, 48- and 64-block chunks over eight waves were slower).
+  // A batch with fewer pairs keeps the finer split, which is shorter per wave.
+  if (c == 8 && waves == 0 && p->desc.num_kv_heads == H &&
+      (total_blocks / 32 + n / 2) * H >= 256)
+    return {32, 8};
   return {(int32_t)c, waves};
 }
 
@@ -400,7 +410,7 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
   pkv_status st = ensure_device(p);
   if (st != PKV_OK) return st;
 
-  const SplitChoice choice = choose_split(p, total_blocks);
+  const SplitChoice choice = choose_split(p, n, total_blocks);
   const int32_t chunk = choice.chunk;
   const bool upload = !p->host_only;
   std::vector<ReqEntry> reqs(n);
