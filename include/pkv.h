@@ -152,7 +152,8 @@ typedef enum pkv_option {
                                merge kernel after it                            */
   PKV_OPT_PROFILING = 3,    /* 1: record kernel timing events; 0: stop         */
   PKV_OPT_WAVES = 4         /* waves per workgroup of the fast paths: 4, 8, or
-                               0 (default) to choose per kernel                 */
+                               0 (default) to choose per kernel and batch (the
+                               plan then picks its split as well)               */
 } pkv_option;
 
 /* Library version "major.minor.patch"; static string. */
