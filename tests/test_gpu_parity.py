@@ -815,12 +815,15 @@ def _sampled(n, extra=()):
 
 
 @pytest.mark.parametrize("merge", MERGES)
-def test_batch32_fp32_l12_full_step(merge):
+@pytest.mark.parametrize("split", [0, 4])
+def test_batch32_fp32_l12_full_step(merge, split):
     """32 requests x 12 layers, H=12, d_h=64, fp32, 4096-page pool: one decode
-    step (fused append + attend per layer) under the launch the bench times."""
+    step (fused append + attend per layer) under the plan the bench uses
+    (split 0: the library's own choice, 32-block chunks over eight waves for
+    this batch) and under 4-block chunks (many split requests)."""
     w = W.batch32_fp32()
     kp, vp = device_pool(w)
-    pool = _pool(w, kp, vp, merge=merge, split=4)
+    pool = _pool(w, kp, vp, merge=merge, split=split)
     plan = pkv.pkv_plan_create(pool)
     pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
     pt = _pt_device(w)
