@@ -313,8 +313,10 @@ SplitChoice choose_split(const pkv_pool* p, int32_t n, int64_t total_blocks) {
   // split and fewer partials are published and merged for the same loads in
   // flight (measured on the 12-layer float32 step: 24.5 -> 23.7 us per
   // launch; 16-, 24-, 48- and 64-block chunks over eight waves were slower).
-  // A batch with fewer pairs keeps the finer split, which is shorter per wave.
+  // A batch with fewer pairs keeps the finer split, which is shorter per wave;
+  // the one-wave generic kernel keeps it too.
   if (c == 8 && waves == 0 && p->desc.num_kv_heads == H &&
+      pkv::fast_path_supported(p->desc.kv_dtype, p->desc.head_width, p->desc.page_size, 1) &&
       (total_blocks / 32 + n / 2) * H >= 256)
     return {32, 8};
   return {(int32_t)c, waves};

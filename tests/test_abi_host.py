@@ -285,11 +285,11 @@ def test_automatic_split_targets_4096_chunks():
 
 
 def test_small_multihead_batch_takes_32_block_chunks():
-    # 32 requests x 12 heads, 32 blocks each: 12288 (block, head) units, the
-    # finest default split (8-block chunks), yet (1024/32 + 16) x 12 pairs >=
-    # 256 -> 32-block chunks over eight waves: one chunk per request, two for
-    # a 33-block request.
-    p = make_pool(pages=4200, ctx=16 * 1024, heads=12, caches=40)
+    # 32 requests x 12 heads of width 64 (the vector fast kernel), 32 blocks
+    # each: 12288 (block, head) units, the finest default split (8-block
+    # chunks), yet (1024/32 + 16) x 12 pairs >= 256 -> 32-block chunks over
+    # eight waves: one chunk per request, two for a 33-block request.
+    p = make_pool(pages=4200, ctx=16 * 1024, heads=12, width=64, caches=40)
     plan = pkv.pkv_plan_create(p)
     pkv.pkv_plan_build(plan, [16 * 32] * 32, 1024, stream=0)
     assert pkv.pkv_plan_num_chunks(plan) == 32
@@ -302,10 +302,17 @@ def test_small_multihead_batch_takes_32_block_chunks():
     pkv.pkv_plan_destroy(plan)
     pkv.pkv_pool_destroy(p)
     # too few (request, head) pairs: (64/32 + 0) x 12 < 256 -> 8-block chunks
-    p = make_pool(pages=4200, ctx=16 * 1024, heads=12)
+    p = make_pool(pages=4200, ctx=16 * 1024, heads=12, width=64)
     plan = pkv.pkv_plan_create(p)
     pkv.pkv_plan_build(plan, [16 * 64], 1024, stream=0)
     assert pkv.pkv_plan_num_chunks(plan) == 8
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(p)
+    # a width the one-wave generic kernel runs keeps 8-block chunks
+    p = make_pool(pages=4200, ctx=16 * 1024, heads=12, width=2, caches=40)
+    plan = pkv.pkv_plan_create(p)
+    pkv.pkv_plan_build(plan, [16 * 32] * 32, 1024, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 32 * 4
     pkv.pkv_plan_destroy(plan)
     pkv.pkv_pool_destroy(p)
 
