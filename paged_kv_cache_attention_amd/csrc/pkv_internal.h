@@ -37,9 +37,10 @@ struct WorkItem {
   ReqEntry rq;
 };
 
-// Plans of at most this many requests and work items, none split, are
-// passed inline in the kernel arguments.
-constexpr int kInlinePlan = 16;
+// Plans of at most this many requests and work items are passed inline in
+// the kernel arguments (2.75 KiB of the argument block).
+constexpr int kInlineReqs = 48;
+constexpr int kInlineItems = 64;
 
 struct AttnArgs {
   const void* q;          // [n][H][D] pool dtype
@@ -67,11 +68,11 @@ struct AttnArgs {
   int64_t page_bytes;     // H_kv * S * D * elt
   int64_t head_bytes;     // S * D * elt
   float scale_log2e;      // log2(e) / sqrt(D)
-  // Small plans without split requests travel in the arguments themselves
-  // (no upload before the launch): num_inline > 0 replaces reqs and items.
+  // Small plans travel in the arguments themselves (no upload before the
+  // launch): num_inline > 0 replaces reqs and items.
   int32_t num_inline;
-  ReqEntry inline_reqs[kInlinePlan];
-  WorkItem inline_items[kInlinePlan];
+  ReqEntry inline_reqs[kInlineReqs];
+  WorkItem inline_items[kInlineItems];
 };
 
 // The work item of this workgroup and request entry r of the plan.  The item

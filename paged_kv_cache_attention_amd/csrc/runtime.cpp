@@ -96,9 +96,11 @@ struct pkv_plan {
   int32_t waves = 0;
   bool any_split = false;
   bool inline_plan = false;    // reqs/items go in the kernel arguments
+  bool meta_uploaded = false;  // reqs/items/merge list are in d_meta
   uint64_t rows_attended = 0;  // sum of t_r
   std::vector<ReqEntry> reqs;
   std::vector<WorkItem> items;
+  std::vector<int32_t> merge_list;  // requests with nsplit > 1
   std::vector<int64_t> key;  // (pt_row, seq_len) pairs of the last build
   char* d_meta = nullptr;
   size_t d_meta_cap = 0;
@@ -389,6 +391,16 @@ pkv_status upload_meta(pkv_plan* pl, const MetaPart* parts, int nparts, hipStrea
   return PKV_OK;
 }
 
+// Copies the plan's requests, work items and merge list to the device.
+pkv_status upload_plan_meta(pkv_plan* pl, hipStream_t stream) {
+  const MetaPart parts[3] = {{pl->reqs.data(), pl->reqs.size() * sizeof(ReqEntry)},
+                             {pl->items.data(), pl->items.size() * sizeof(WorkItem)},
+                             {pl->merge_list.data(), pl->merge_list.size() * sizeof(int32_t)}};
+  pkv_status st = upload_meta(pl, parts, 3, stream);
+  if (st == PKV_OK) pl->meta_uploaded = true;
+  return st;
+}
+
 // Builds the split plan for n requests (rows[r] selects the page-table row,
 // lens[r] the attended length) and uploads it on the stream.
 pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_t* lens,
@@ -447,10 +459,11 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
   if ((int64_t)items.size() * p->desc.num_heads > std::numeric_limits<int32_t>::max())
     return fail(PKV_ERR_INVALID_ARGUMENT, "%zu chunks x %d heads exceed one launch", items.size(),
                 p->desc.num_heads);
-  // Small unsplit plans are passed inline in the kernel arguments.
-  const bool inline_plan = n <= pkv::kInlinePlan && (int64_t)items.size() <= pkv::kInlinePlan &&
-                           slots == 0;
-  if (upload && !inline_plan) {
+  // Small plans are passed inline in the kernel arguments, so the launch
+  // needs no upload; the device copy is made only if a separate merge
+  // kernel needs it (upload_plan_meta).
+  const bool inline_plan = n <= pkv::kInlineReqs && (int64_t)items.size() <= pkv::kInlineItems;
+  if (upload) {
   const size_t part_floats = (size_t)slots * p->desc.num_heads * (p->desc.head_width + 2);
   if (part_floats > pl->partials_cap) {
     const size_t cap = std::max(part_floats, pl->partials_cap * 2);
@@ -481,20 +494,22 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
     pl->d_counters = static_cast<int32_t*>(d);
     pl->counters_cap = cap;
   }
-  const MetaPart parts[3] = {{reqs.data(), reqs.size() * sizeof(ReqEntry)},
-                             {items.data(), items.size() * sizeof(WorkItem)},
-                             {merge_list.data(), merge_list.size() * sizeof(int32_t)}};
-  if ((st = upload_meta(pl, parts, 3, stream)) != PKV_OK) return st;
   }  // upload
 
   pl->reqs = std::move(reqs);
   pl->items = std::move(items);
+  pl->merge_list = std::move(merge_list);
+  pl->meta_uploaded = false;
+  // The device copy is also made now when this pool's separate merge kernel
+  // will need it, so a launch captured into a graph finds it there.
+  const bool need_meta = !inline_plan || (slots > 0 && p->merge_mode == pkv::kMergeSeparate);
+  if (upload && need_meta && (st = upload_plan_meta(pl, stream)) != PKV_OK) return st;
   pl->key = std::move(key);
   pl->n = n;
   pl->pt_stride = pt_stride;
   pl->num_items = (int32_t)pl->items.size();
   pl->total_splits = slots;
-  pl->num_split_reqs = (int32_t)merge_list.size();
+  pl->num_split_reqs = (int32_t)pl->merge_list.size();
   pl->waves = choice.waves;
   pl->any_split = slots > 0;
   pl->inline_plan = inline_plan;
@@ -595,6 +610,14 @@ pkv_status run_attention(pkv_plan* pl, int32_t layer, const int32_t* page_table,
     p->profile.algorithmic_bytes += launch_bytes(pl, fuse);
   }
   if (pl->any_split && p->merge_mode == pkv::kMergeSeparate) {
+    // The merge kernel reads the plan from the device: an inline plan built
+    // before the pool switched to this mode is copied there once, on the
+    // stream ahead of the merge.
+    if (!pl->meta_uploaded) {
+      pkv_status st = upload_plan_meta(pl, stream);
+      if (st != PKV_OK) return st;
+      a = make_args(pl, layer, page_table, q, k, v, out, fuse);
+    }
     if (p->profiling) {
       e0 = take_event(p);
       e1 = take_event(p);
