@@ -43,22 +43,22 @@ HBM_PEAK_GBS = 8000.0
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
     "batch32_fp32_l12": {"source": "kernels.hip", "sha256_16": "133e1ec9db657ded",
-        "fetch_kib": 44368.0, "write_kib": 670.4,
+        "fetch_kib": 44364.1, "write_kib": 670.4,
         "algorithmic_bytes": 88971264},
     "batch256_bf16": {"source": "kernels.hip", "sha256_16": "133e1ec9db657ded",
-        "fetch_kib": 4761707.6, "write_kib": 4345.4,
+        "fetch_kib": 4761694.4, "write_kib": 4336.1,
         "algorithmic_bytes": 9718775808},
     "batch256_gqa8_bf16": {"source": "kernels.hip", "sha256_16": "133e1ec9db657ded",
-        "fetch_kib": 1194148.0, "write_kib": 4096.6,
+        "fetch_kib": 1194160.1, "write_kib": 4096.9,
         "algorithmic_bytes": 2434412544},
     "batch256_mqa_bf16": {"source": "kernels.hip", "sha256_16": "133e1ec9db657ded",
-        "fetch_kib": 151928.4, "write_kib": 4096.0,
+        "fetch_kib": 151902.3, "write_kib": 4096.0,
         "algorithmic_bytes": 309806592},
     "prefill32_bf16": {"source": "prefill.hip", "sha256_16": "64e07feb42ad9f32",
-        "fetch_kib": 723061.3, "write_kib": 518320.2,
+        "fetch_kib": 724448.3, "write_kib": 518320.2,
         "algorithmic_bytes": 1854562304},
     "prefill32_fp32": {"source": "prefill.hip", "sha256_16": "64e07feb42ad9f32",
-        "fetch_kib": 292772.1, "write_kib": 97857.0,
+        "fetch_kib": 293500.7, "write_kib": 97857.0,
         "algorithmic_bytes": 575582208},
 }
 
