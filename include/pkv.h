@@ -321,8 +321,9 @@ pkv_status pkv_plan_create(pkv_pool* pool, pkv_plan** out);
 pkv_status pkv_plan_destroy(pkv_plan* plan);
 
 /* seq_lens: host array of n attended lengths t_r >= 1 (the newest row
- * included), each at most pt_stride * page_size.  Uploads the plan on the
- * stream.  Errors: INVALID_ARGUMENT (n < 1, t_r < 1 or too long); ALLOC. */
+ * included), each at most pt_stride * page_size.  A plan of at most 48
+ * requests and 64 work items travels in the kernel arguments; a larger one
+ * (or one the separate merge kernel reads) is uploaded on the stream.  Errors: INVALID_ARGUMENT (n < 1, t_r < 1 or too long); ALLOC. */
 pkv_status pkv_plan_build(pkv_plan* plan, int32_t n, const int32_t* seq_lens,
                           int32_t pt_stride, void* stream);
 
