@@ -151,8 +151,10 @@ typedef enum pkv_option {
                                inside the attention kernel; 0: a separate
                                merge kernel after it                            */
   PKV_OPT_PROFILING = 3,    /* 1: record kernel timing events; 0: stop         */
-  PKV_OPT_WAVES = 4         /* waves per workgroup of the fast paths: 4, 8, or
-                               0 (default) to choose per kernel and batch (the
+  PKV_OPT_WAVES = 4         /* waves per workgroup of the fast paths: 4, 8,
+                               16 (the multi-head kernel for d_h <= 64; other
+                               kernels then take 8), or 0
+                               (default) to choose per kernel and batch (the
                                plan then picks its split as well)               */
 } pkv_option;
 

@@ -1359,12 +1359,15 @@ hipError_t launch_fast_shape(const AttnArgs& a, int num_items, hipStream_t strea
 // of four (each block loaded by 2 or 4 waves): more heads per wave would
 // exceed the register file.  512-byte rows hold twice the registers per
 // block, so there a wave carries at most two heads and shares stop at 8.
+// One head per workgroup runs on 4, 8 or (d_h <= 64) 16 waves.
 template <typename T, int D>
 hipError_t launch_fast(const AttnArgs& a, int share, int num_items, hipStream_t stream) {
   constexpr bool wide = D * sizeof(T) == 512;
   switch (share) {
     case 1:
-      return a.waves == 8 ? launch_fast_shape<T, D, 8, 1, 8>(a, num_items, stream)
+      if constexpr (D <= 64)
+        if (a.waves == 16) return launch_fast_shape<T, D, 16, 1, 16>(a, num_items, stream);
+      return a.waves >= 8 ? launch_fast_shape<T, D, 8, 1, 8>(a, num_items, stream)
                           : launch_fast_shape<T, D, 4, 1, 4>(a, num_items, stream);
     case 2:
       return launch_fast_shape<T, D, 4, 2, 4>(a, num_items, stream);
@@ -1404,7 +1407,7 @@ static int padded_width(int dtype, int head_width) {
 template <typename T, int D>
 hipError_t launch_fast_padded(const AttnArgs& a, int share, int num_items, hipStream_t stream) {
   if (share == 2) return launch_fast_shape<T, D, 4, 2, 4, true>(a, num_items, stream);
-  return a.waves == 8 ? launch_fast_shape<T, D, 8, 1, 8, true>(a, num_items, stream)
+  return a.waves >= 8 ? launch_fast_shape<T, D, 8, 1, 8, true>(a, num_items, stream)
                       : launch_fast_shape<T, D, 4, 1, 4, true>(a, num_items, stream);
 }
 

@@ -283,8 +283,8 @@ pkv_status flush_patches(pkv_pool* p, hipStream_t stream) {
 // Workgroup shape and split-K chunk size (in 16-row blocks) of a plan.
 //
 // Waves per workgroup: PKV_OPT_WAVES, or 0 to let the launcher choose per
-// kernel (four for the vector kernels, eight for a small multi-head batch as
-// below; eight for the matrix-core kernel when a workgroup serves 8 or 16
+// kernel (four for the vector kernels, eight or sixteen for a small
+// multi-head batch as below; eight for the matrix-core kernel when a workgroup serves 8 or 16
 // query heads, whose requests then finish in half the block steps per wave).
 // Requests split into chunks sized for about kTargetChunks (chunk, query
 // head) units -- four resident rounds of 256 CUs x 4 workgroups -- so a batch
@@ -315,12 +315,21 @@ SplitChoice choose_split(const pkv_pool* p, int32_t n, int64_t total_blocks) {
   // split and fewer partials are published and merged for the same loads in
   // flight (measured on the 12-layer float32 step: 24.5 -> 23.7 us per
   // launch; 16-, 24-, 48- and 64-block chunks over eight waves were slower).
+  // For d_h <= 64 the same test at 64-block chunks picks sixteen-wave
+  // workgroups instead: still four blocks per wave, but half the chunks, so
+  // requests of up to 64 blocks stay whole and publish no partials (measured
+  // on the same step: 24.2 -> 22.6 us per launch, where 32- and 48-block
+  // chunks over sixteen waves and whole requests over eight were slower).
+  // Sixteen waves are built for d_h <= 64 only, whose kernels fit the 128
+  // registers a 1024-lane workgroup leaves per lane (bf16 d_h = 128 would
+  // spill).
   // A batch with fewer pairs keeps the finer split, which is shorter per wave;
   // the one-wave generic kernel keeps it too.
-  if (c == 8 && waves == 0 && p->desc.num_kv_heads == H &&
-      pkv::fast_path_supported(p->desc.kv_dtype, p->desc.head_width, p->desc.page_size, 1) &&
-      (total_blocks / 32 + n / 2) * H >= 256)
-    return {32, 8};
+  const bool small_mha = c == 8 && waves == 0 && p->desc.num_kv_heads == H &&
+      pkv::fast_path_supported(p->desc.kv_dtype, p->desc.head_width, p->desc.page_size, 1);
+  if (small_mha && p->desc.head_width <= 64 && (total_blocks / 64 + n / 2) * H >= 256)
+    return {64, 16};
+  if (small_mha && (total_blocks / 32 + n / 2) * H >= 256) return {32, 8};
   return {(int32_t)c, waves};
 }
 
@@ -961,7 +970,7 @@ pkv_status pkv_pool_set_option(pkv_pool* p, int32_t option, int64_t value) {
       p->merge_mode = (int32_t)value;
       return ok();
     case PKV_OPT_WAVES:
-      if (value != 0 && value != 4 && value != 8)
+      if (value != 0 && value != 4 && value != 8 && value != 16)
         return fail(PKV_ERR_INVALID_ARGUMENT, "waves %lld", (long long)value);
       p->waves_option = (int32_t)value;
       p->txn_plan.key.clear();

@@ -284,21 +284,32 @@ def test_automatic_split_targets_4096_chunks():
     pkv.pkv_pool_destroy(p)
 
 
-def test_small_multihead_batch_takes_32_block_chunks():
+def test_small_multihead_batch_takes_whole_requests_or_32_block_chunks():
     # 32 requests x 12 heads of width 64 (the vector fast kernel), 32 blocks
     # each: 12288 (block, head) units, the finest default split (8-block
-    # chunks), yet (1024/32 + 16) x 12 pairs >= 256 -> 32-block chunks over
-    # eight waves: one chunk per request, two for a 33-block request.
+    # chunks), yet (1024/64 + 16) x 12 pairs >= 256 -> 64-block chunks over
+    # sixteen waves: whole requests, a 33-block request included.
     p = make_pool(pages=4200, ctx=16 * 1024, heads=12, width=64, caches=40)
     plan = pkv.pkv_plan_create(p)
     pkv.pkv_plan_build(plan, [16 * 32] * 32, 1024, stream=0)
     assert pkv.pkv_plan_num_chunks(plan) == 32
     pkv.pkv_plan_build(plan, [16 * 32] * 31 + [16 * 33], 1024, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 32
+    # a 65-block request takes two chunks
+    pkv.pkv_plan_build(plan, [16 * 32] * 31 + [16 * 65], 1024, stream=0)
     assert pkv.pkv_plan_num_chunks(plan) == 31 + 2
     # an explicit waves option keeps the 8-block chunks
     pkv.pkv_pool_set_option(p, pkv.PKV_OPT_WAVES, 4)
     pkv.pkv_plan_build(plan, [16 * 32] * 32, 1024, stream=0)
     assert pkv.pkv_plan_num_chunks(plan) == 32 * 4
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(p)
+    # width 128: no sixteen-wave kernel -> (1057/32 + 16) x 12 >= 256 ->
+    # 32-block chunks over eight waves, two for a 33-block request
+    p = make_pool(pages=4200, ctx=16 * 1024, heads=12, width=128, caches=40)
+    plan = pkv.pkv_plan_create(p)
+    pkv.pkv_plan_build(plan, [16 * 32] * 31 + [16 * 33], 1024, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 31 + 2
     pkv.pkv_plan_destroy(plan)
     pkv.pkv_pool_destroy(p)
     # too few (request, head) pairs: (64/32 + 0) x 12 < 256 -> 8-block chunks

@@ -195,11 +195,14 @@ def test_batched_decode_small(dtype, D, S, split, merge):
 @pytest.mark.parametrize("dtype,D,S", [c for c in SMALL_CASES if (c[0], c[1]) in FAST_WIDTHS
                                         and c[2] % 16 == 0])
 @pytest.mark.parametrize("split,merge", [(0, 2), (2, 2), (2, 0), (-1, 2)])
-def test_eight_wave_workgroups(dtype, D, S, split, merge):
+@pytest.mark.parametrize("waves", [8, 16])
+def test_eight_and_sixteen_wave_workgroups(dtype, D, S, split, merge, waves):
+    """Multi-head workgroups of eight and of sixteen waves (sixteen runs for
+    d_h <= 64; wider rows take eight), unsplit and split, both merge modes."""
     w = _small(f"w8_{dtype}_{D}_{S}", dtype, D, S, LENGTHS, seed=29)
     kp, vp = device_pool(w)
     pool = _pool(w, kp, vp, split=split, merge=merge)
-    pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_WAVES, 8)
+    pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_WAVES, waves)
     plan = pkv.pkv_plan_create(pool)
     pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
     pt = _pt_device(w)
@@ -819,8 +822,8 @@ def _sampled(n, extra=()):
 def test_batch32_fp32_l12_full_step(merge, split):
     """32 requests x 12 layers, H=12, d_h=64, fp32, 4096-page pool: one decode
     step (fused append + attend per layer) under the plan the bench uses
-    (split 0: the library's own choice, 32-block chunks over eight waves for
-    this batch) and under 4-block chunks (many split requests)."""
+    (split 0: the library's own choice, whole requests over sixteen waves
+    for this batch) and under 4-block chunks (many split requests)."""
     w = W.batch32_fp32()
     kp, vp = device_pool(w)
     pool = _pool(w, kp, vp, merge=merge, split=split)
