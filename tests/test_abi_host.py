@@ -328,6 +328,22 @@ def test_small_multihead_batch_takes_whole_requests_or_32_block_chunks():
     pkv.pkv_pool_destroy(p)
 
 
+def test_waves_option_values():
+    # 0, 4, 8 and 16 are accepted; anything else is rejected and leaves the
+    # option unchanged (16 explicit waves keep the finest default split)
+    p = make_pool(pages=4200, ctx=16 * 1024, heads=12, width=64, caches=40)
+    for v in (0, 4, 8, 16):
+        pkv.pkv_pool_set_option(p, pkv.PKV_OPT_WAVES, v)
+    for v in (1, 2, 12, 32, -1):
+        assert status_of(pkv.pkv_pool_set_option, p, pkv.PKV_OPT_WAVES, v) == \
+            Status.INVALID_ARGUMENT
+    plan = pkv.pkv_plan_create(p)
+    pkv.pkv_plan_build(plan, [16 * 32] * 32, 1024, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 32 * 4
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(p)
+
+
 def test_split_counts_query_heads_of_grouped_pools():
     # 8 query heads sharing 2 K/V heads: 64 requests of 512 blocks are
     # 262144 (block, query head) units -> 64-block chunks, 8 per request
