@@ -38,6 +38,12 @@
  *  - Device outputs are float32; K/V, q, k and v use the pool dtype.  Every
  *    device pointer must be 16-byte aligned (INVALID_ARGUMENT otherwise).
  *  - Gathered K/V tensors are never exposed; only the pool and the context.
+ *  - Device memory the library owns (the page-table arena, plan buffers) is
+ *    allocated on first use and grows by doubling; a replaced buffer stays
+ *    allocated until its plan or pool is destroyed, because freeing device
+ *    memory waits for the whole device.  No call except the destroys (and
+ *    pkv_pool_get_profile, which waits for its timing events) waits for the
+ *    device; pkv_plan_build waits only for its own previous upload's copy.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -158,10 +164,15 @@ typedef enum pkv_option {
                                plan then picks its split as well)               */
 } pkv_option;
 
-/* Library version "major.minor.patch"; static string. */
+/* Library version "major.minor.patch"; static string.  ("Incremental
+ * Serving", Stable C and Python sessions: the C surface reports its ABI
+ * version.) */
 const char* pkv_version(void);
 
-/* Message for the last error on this thread ("" if none); owned by the library. */
+/* Message for the last error on this thread ("" if none); owned by the
+ * library, valid until the next call on this thread.  ("Incremental
+ * Serving", Stable C and Python sessions: status codes plus a last-error
+ * string, no exceptions across the ABI.) */
 const char* pkv_last_error(void);
 
 /* ------------------------------------------------------------------ pool -- */
@@ -171,24 +182,37 @@ const char* pkv_last_error(void);
  * "Incremental Serving", section "Stable C and Python sessions". */
 void pkv_pool_desc_init(pkv_pool_desc* desc);
 
-/* Creates a pool over caller storage.  The free list holds every page ID in
- * a seeded random order.  Touches no device: device resources are created on
- * the first device call, on the device current at that moment.
+/* Creates a pool over caller storage ("Incremental Serving", Paged KV-cache
+ * layout: one shared pool of per-layer key and value pages, one physical page
+ * ID valid in every layer, a block count of 0 sizing the pool for one
+ * maximum context).  The free list holds every page ID in a seeded random
+ * order.  Touches no device: device resources are created on the first
+ * device call, on the device current at that moment.  *out is owned by the
+ * caller until pkv_pool_destroy.
  * Errors: INVALID_ARGUMENT (null desc/out/storage, storage not 16-byte
  * aligned, non-positive sizes, head_width > 1024, unknown dtype or flags);
  * ALLOC. */
 pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out);
 
-/* Destroys the pool.  Errors: BAD_STATE while any cache or plan of the pool
- * is alive or any raw page is leased. */
+/* Destroys the pool and frees its device memory (which waits for the
+ * device).  ("Incremental Serving", Stable C and Python sessions: a shared
+ * object is rejected while anything created from it is alive.)  Errors:
+ * BAD_STATE while any cache or plan of the pool is alive or any raw page is
+ * leased. */
 pkv_status pkv_pool_destroy(pkv_pool* pool);
 
-/* The resolved geometry (num_pages, max_caches filled in). */
+/* The resolved geometry (num_pages, max_caches filled in; "Incremental
+ * Serving", Paged KV-cache layout).  Errors: INVALID_ARGUMENT (null). */
 pkv_status pkv_pool_get_desc(const pkv_pool* pool, pkv_pool_desc* out);
 
+/* Work counters (learn_llm ch.38, section "Count attention-score cells, not
+ * total runtime": appends and cached score cells of committed tokens) and the
+ * pool's page occupancy.  Errors: INVALID_ARGUMENT (null). */
 pkv_status pkv_pool_get_counters(const pkv_pool* pool, pkv_counters* out);
 
-/* Sets one pkv_option.  Errors: INVALID_ARGUMENT (unknown option or value). */
+/* Sets one pkv_option; a plan built before an option that changes chunking
+ * or workgroup shape (split blocks, waves, merge mode) is rebuilt by its
+ * next build.  Errors: INVALID_ARGUMENT (unknown option or value). */
 pkv_status pkv_pool_set_option(pkv_pool* pool, int32_t option, int64_t value);
 
 /* Waits for the recorded timing events, sums them into *out and, if reset,
@@ -196,42 +220,56 @@ pkv_status pkv_pool_set_option(pkv_pool* pool, int32_t option, int64_t value);
 pkv_status pkv_pool_get_profile(pkv_pool* pool, pkv_profile* out, int32_t reset);
 
 /* Raw page lease/release, for callers that keep their own page tables and
- * use the batched calls below.  Errors: OUT_OF_PAGES; INVALID_ARGUMENT for a
- * page that is out of range or not raw-leased. */
+ * use the batched calls below ("Incremental Serving", Paged KV-cache layout:
+ * pages are leased from the shared pool and returned to it).  *page receives
+ * a physical page ID in [0, num_pages).  Errors: OUT_OF_PAGES;
+ * INVALID_ARGUMENT for a page that is out of range or not raw-leased. */
 pkv_status pkv_page_lease(pkv_pool* pool, int32_t* page);
 pkv_status pkv_page_release(pkv_pool* pool, int32_t page);
 
 /* ------------------------------------------------------- request caches -- */
 
-/* Creates an empty request cache (length 0, no pages).  max_context <= the
- * pool's.  Errors: INVALID_ARGUMENT; BAD_STATE when max_caches caches live. */
+/* Creates an empty request cache (length 0, no pages): a request-local
+ * logical-to-physical page table over the pool ("Incremental Serving", Paged
+ * KV-cache layout).  max_context <= the pool's.  *out is owned by the caller
+ * until pkv_cache_destroy.  Errors: INVALID_ARGUMENT; BAD_STATE when
+ * max_caches caches live. */
 pkv_status pkv_cache_create(pkv_pool* pool, int32_t max_context, pkv_cache** out);
 
-/* Returns every page (a pending token's included) and frees the handle. */
+/* Returns every page (a pending token's included) and frees the handle
+ * ("Incremental Serving", Paged KV-cache layout: pages return to the pool
+ * when a cache is destroyed).  Errors: INVALID_ARGUMENT (null). */
 pkv_status pkv_cache_destroy(pkv_cache* cache);
 
-/* Length back to 0, every page returned, handle kept.  Pages return in the
- * reverse of their lease order, so replaying the same tokens leases the same
- * pages again.  Errors: BAD_STATE while a token is pending. */
+/* Length back to 0, every page returned, handle kept ("Incremental
+ * Serving", Paged KV-cache layout: pages return on reset; learn_llm ch.38:
+ * reset keeps the allocation).  Pages return in the reverse of their lease
+ * order, so replaying the same tokens leases the same pages again.  Errors:
+ * BAD_STATE while a token is pending. */
 pkv_status pkv_cache_reset(pkv_cache* cache);
 
-/* Committed length, maximum context, page size (tokens). -1 for a null cache. */
+/* Committed length, maximum context, page size (tokens); -1 for a null
+ * cache ("Incremental Serving", Stable C and Python sessions: a session
+ * reports its size, capacity and block size). */
 int32_t pkv_cache_size(const pkv_cache* cache);
 int32_t pkv_cache_capacity(const pkv_cache* cache);
 int32_t pkv_cache_block_size(const pkv_cache* cache);
 
 /* Copies the logical page table (pages held, a pending token's included) into
- * out[0..cap); *n_out receives the number of entries.  Errors:
- * INVALID_ARGUMENT when cap is too small (nothing written). */
+ * out[0..cap) (host memory); *n_out receives the number of entries
+ * ("Incremental Serving", Paged KV-cache layout: the request-local table).
+ * Errors: INVALID_ARGUMENT when cap is too small (nothing written). */
 pkv_status pkv_cache_page_table(const pkv_cache* cache, int32_t* out, int32_t cap,
                                 int32_t* n_out);
 
 /* Extends the committed length by n_tokens rows whose K/V bytes the caller
- * writes itself (a bulk prefill writer), leasing the pages they need.  When
- * the last page is shared and partly filled, its private copy is made on the
- * null stream and completed before the call returns.
+ * writes itself (a bulk prefill writer), leasing the pages they need
+ * ("Incremental Serving", Paged KV-cache layout: pages are leased as a
+ * sequence grows).  When the last page is shared and partly filled, its
+ * private copy is enqueued on `stream` (a hipStream_t, NULL = the default
+ * stream): rows the caller then writes on that stream land after the copy.
  * Errors: BAD_STATE (token pending), CAPACITY_EXHAUSTED, OUT_OF_PAGES. */
-pkv_status pkv_cache_grow(pkv_cache* cache, int32_t n_tokens);
+pkv_status pkv_cache_grow(pkv_cache* cache, int32_t n_tokens, void* stream);
 
 /* A new cache that shares the first n_tokens rows of src (0 <= n_tokens <=
  * its committed length): it holds references to src's first
@@ -240,7 +278,7 @@ pkv_status pkv_cache_grow(pkv_cache* cache, int32_t n_tokens);
  * positions >= length); the first write into a shared, partly filled page
  * -- by either cache -- first gives the writer a private copy of that page
  * (every layer's K and V), queued on the stream of the writer's next layer
- * call (or completed before pkv_cache_grow returns), and abort undoes it.
+ * call (or of pkv_cache_grow), and abort undoes it.
  * A page returns to the free list when its last holder lets it go.
  * ("Incremental Serving", Current scope: paged storage alone does not share
  * pages between matching prompts or manage prefixes by copy-on-write; this
@@ -253,8 +291,12 @@ pkv_status pkv_cache_fork(const pkv_cache* src, int32_t n_tokens, int32_t max_co
 
 /* --------------------------------------------------- token transaction -- */
 
-/* Reserves position = length; leases a page when the position starts one.
- * Errors: BAD_STATE (already pending), CAPACITY_EXHAUSTED, OUT_OF_PAGES. */
+/* Reserves position = length; leases a page when the position starts one
+ * ("Incremental Serving", Request flow: begin reserves the next logical
+ * position; Paged KV-cache layout: lazy lease; Stable C and Python sessions:
+ * a full context is reported, not cropped).  *position (may be null)
+ * receives the position.  Errors: BAD_STATE (already pending),
+ * CAPACITY_EXHAUSTED, OUT_OF_PAGES. */
 pkv_status pkv_begin_token(pkv_cache* cache, int32_t* position);
 
 /* Reserves a chunk of count >= 1 positions length..length+count-1 as one
@@ -270,7 +312,11 @@ pkv_status pkv_begin_token(pkv_cache* cache, int32_t* position);
  * capacity), OUT_OF_PAGES. */
 pkv_status pkv_begin_tokens(pkv_cache* cache, int32_t count, int32_t* position);
 
-/* One layer of the pending token (or chunk of count tokens): writes k and v
+/* One layer of the pending token (or chunk of count tokens) ("Incremental
+ * Serving", Request flow: each layer appends its K/V row, then attends;
+ * learn_llm ch.38, "Prepare every block, then commit every cache together":
+ * the query scores the retained rows and the new one, len+1 rows, with
+ * dot(q, k)/sqrt(d_h), stable softmax, weighted value rows): writes k and v
  * ([count,H_kv,d_h], pool dtype, device) into the pool at the pending
  * positions, then attends with q ([count,H,d_h]), row i over rows
  * 0..length+i, writing out ([count,H,d_h] float32).  For one token these are
@@ -280,31 +326,41 @@ pkv_status pkv_begin_tokens(pkv_cache* cache, int32_t count, int32_t* position);
 pkv_status pkv_append_and_attend(pkv_cache* cache, int32_t layer, const void* q,
                                  const void* k, const void* v, float* out, void* stream);
 
-/* Makes the pending position(s) visible.  Errors: BAD_STATE (nothing
- * pending, or some layer not appended; the caller may then abort). */
+/* Makes the pending position(s) visible ("Incremental Serving", Request
+ * flow; learn_llm ch.38: every block prepares before any cache commits, so
+ * all layers must have appended).  Errors: BAD_STATE (nothing pending, or
+ * some layer not appended; the caller may then abort). */
 pkv_status pkv_commit_token(pkv_cache* cache);
 
-/* Drops the pending token or chunk: length unchanged, the pages leased by
- * its begin returned.  Errors: BAD_STATE (nothing pending). */
+/* Drops the pending token or chunk: length unchanged ("Incremental Serving",
+ * Request flow), the pages leased by its begin returned (learn_llm ch.38:
+ * a rejected step commits no state change).  Rows written into the pages by
+ * the aborted layers stay as unspecified bytes beyond the length.  Errors:
+ * BAD_STATE (nothing pending). */
 pkv_status pkv_abort_token(pkv_cache* cache);
 
 /* begin_token on n caches of one pool, all or none: on any error no cache
- * changes.  positions (may be null) receives the n reserved positions.
+ * changes ("Incremental Serving", Request flow, for a batch of requests;
+ * learn_llm ch.38: rejected operations leave committed state unchanged).  positions (may be null) receives the n reserved positions.
  * Errors: as pkv_begin_token (the first failing cache is named in the
  * message); OUT_OF_PAGES when the n begins together need more pages than are
  * free; INVALID_ARGUMENT for a repeated cache or mixed pools. */
 pkv_status pkv_begin_token_batched(pkv_cache* const* caches, int32_t n, int32_t* positions);
 
 /* begin_tokens on n caches, counts[i] positions for caches[i] (counts may be
- * null: one each), all or none.  Errors: as pkv_begin_tokens, and
+ * null: one each; host array), all or none ("Incremental Serving", Request
+ * flow and Paged KV-cache layout's batched prefill).  Errors: as pkv_begin_tokens, and
  * OUT_OF_PAGES when the begins together need more pages than are free. */
 pkv_status pkv_begin_tokens_batched(pkv_cache* const* caches, int32_t n, const int32_t* counts,
                                     int32_t* positions);
 
-/* commit_token on n caches, all or none.  Errors: as pkv_commit_token. */
+/* commit_token on n caches, all or none ("Incremental Serving", Request
+ * flow; learn_llm ch.38: commit every cache together).  Errors: as
+ * pkv_commit_token. */
 pkv_status pkv_commit_token_batched(pkv_cache* const* caches, int32_t n);
 
-/* The same layer step for n pending caches of one pool in one launch set:
+/* The same layer step for n pending caches of one pool in one launch set
+ * (the Request flow of "Incremental Serving" for many requests at once):
  * q is [T,H,d_h], k and v are [T,H_kv,d_h] (pool dtype), out is [T,H,d_h]
  * float32, where T sums the caches' pending counts (T = n for single
  * tokens) and the rows of caches[i] follow those of caches[0..i).  All
@@ -317,40 +373,60 @@ pkv_status pkv_append_and_attend_batched(pkv_cache* const* caches, int32_t n, in
 /* ------------------------------------------- batched calls on page tables -- */
 
 /* A split plan: per-request attended lengths turned into a device work list
- * (split-K chunks, longest first) plus partial buffers.  Build it once per
- * decode step and reuse it for every layer. */
+ * (split-K chunks, longest first) plus partial buffers ("Rollout Serving,
+ * Caching, and Batching", batching section: ragged lengths in one batch and
+ * length-aware grouping).  Build it once per decode step and reuse it for
+ * every layer.  The plan owns its device buffers; destroying it frees them
+ * (which waits for the device).  Errors: INVALID_ARGUMENT (null; destroy of
+ * a library-internal plan); ALLOC. */
 pkv_status pkv_plan_create(pkv_pool* pool, pkv_plan** out);
 pkv_status pkv_plan_destroy(pkv_plan* plan);
 
 /* seq_lens: host array of n attended lengths t_r >= 1 (the newest row
- * included), each at most pt_stride * page_size.  A plan of at most 48
+ * included), each at most pt_stride * page_size (learn_llm ch.38: the
+ * newest query reads the whole retained prefix, which grows with t).  A plan of at most 48
  * requests and 64 work items travels in the kernel arguments; a larger one
  * (or one the separate merge kernel reads) is uploaded on the stream.  Errors: INVALID_ARGUMENT (n < 1, t_r < 1 or too long); ALLOC. */
 pkv_status pkv_plan_build(pkv_plan* plan, int32_t n, const int32_t* seq_lens,
                           int32_t pt_stride, void* stream);
 
-/* Number of split chunks of the built plan (0 if not built). */
+/* Number of split chunks of the built plan (0 if not built or null). */
 int32_t pkv_plan_num_chunks(const pkv_plan* plan);
 
-/* Batched decode attention: for each request r, q[r] ([H,d_h], pool dtype)
- * attends to rows 0..t_r-1 of its pages; page_table is a device int32
- * array [n][pt_stride] of physical page IDs (request r's logical page i at
- * page_table[r*pt_stride + i]).  out: [n,H,d_h] float32, device. */
+/* Batched decode attention (learn_llm ch.38, the incremental mixture:
+ * softmax(q K^T / sqrt(d_h)) V for the newest query; "Incremental Serving",
+ * Paged KV-cache layout: rows reached through a logical-to-physical page
+ * table): for each request r, q[r] ([H,d_h], pool dtype, device) attends to
+ * rows 0..t_r-1 of its pages; page_table is a device int32 array
+ * [n][pt_stride] of physical page IDs (request r's logical page i at
+ * page_table[r*pt_stride + i], each in [0, num_pages); entries past the
+ * request's pages are never read).  out: [n,H,d_h] float32, device.
+ * Errors: INVALID_ARGUMENT (null or misaligned pointer, layer out of
+ * range), BAD_STATE (plan not built), DEVICE. */
 pkv_status pkv_plan_decode_attention(pkv_plan* plan, int32_t layer, const void* q,
                                      const int32_t* page_table, float* out, void* stream);
 
-/* Batched append: writes k[r], v[r] ([n,H_kv,d_h], pool dtype) into row
- * t_r-1 of each request's pages (a byte copy). */
+/* Batched append ("Incremental Serving", Request flow: the new K/V row
+ * becomes part of the cache; Paged KV-cache layout: row j at page
+ * pt[j / S], slot j % S): writes k[r], v[r] ([n,H_kv,d_h], pool dtype,
+ * device) into row t_r-1 of each request's pages, a byte copy.  Errors: as
+ * pkv_plan_decode_attention. */
 pkv_status pkv_plan_kv_append(pkv_plan* plan, int32_t layer, const int32_t* page_table,
                               const void* k, const void* v, void* stream);
 
-/* Both in one launch: append row t_r-1, then attend over rows 0..t_r-1. */
+/* Both in one launch: append row t_r-1, then attend over rows 0..t_r-1 (the
+ * append-then-attend order of "Incremental Serving", Request flow).  Errors:
+ * as pkv_plan_decode_attention. */
 pkv_status pkv_plan_append_and_attend(pkv_plan* plan, int32_t layer,
                                       const int32_t* page_table, const void* q,
                                       const void* k, const void* v, float* out,
                                       void* stream);
 
-/* One-call forms that build an internal plan from host seq_lens. */
+/* One-call form of pkv_plan_decode_attention that builds the pool's
+ * internal plan from host seq_lens (t_r >= 1, at most pt_stride * page_size;
+ * an empty prefix has no softmax, so t_r = 0 is rejected).  Errors:
+ * INVALID_ARGUMENT (n < 1, a length out of range, null or misaligned
+ * pointer), ALLOC, DEVICE. */
 pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, int32_t n, const void* q,
                                 const int32_t* page_table, int32_t pt_stride,
                                 const int32_t* seq_lens, float* out, void* stream);
@@ -370,8 +446,10 @@ pkv_status pkv_prefill_attention(pkv_pool* pool, int32_t layer, int32_t n,
                                  const int32_t* starts, const int32_t* counts, const void* q,
                                  const void* k, const void* v, float* out, void* stream);
 
-/* positions: host array of n row indices; row positions[r] of request r is
- * written, so positions[r] < pt_stride * page_size. */
+/* One-call form of pkv_plan_kv_append ("Incremental Serving", Request flow
+ * and Paged KV-cache layout): positions is a host array of n row indices;
+ * row positions[r] of request r is written, so 0 <= positions[r] <
+ * pt_stride * page_size.  Errors: INVALID_ARGUMENT. */
 pkv_status pkv_kv_append(pkv_pool* pool, int32_t layer, int32_t n,
                          const int32_t* page_table, int32_t pt_stride,
                          const int32_t* positions, const void* k, const void* v,

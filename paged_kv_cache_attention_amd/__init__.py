@@ -17,7 +17,9 @@ import os
 import torch  # noqa: F401  (loads the HIP runtime the library must share)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpkv.so")
+# PKV_LIBRARY names another build of the same library to load instead (the
+# CPU tests use it for the build whose host runtime carries sanitizers).
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(_HERE, "libpkv.so")
 
 PKV_OK = 0
 PKV_ERR_INVALID_ARGUMENT = 1
@@ -122,7 +124,7 @@ SIGNATURES = {
     "pkv_cache_block_size": (_I32, [_P]),
     "pkv_cache_page_table": (_I32, [_P, _PI32, _I32, _PI32]),
     "pkv_cache_fork": (_I32, [_P, _I32, _I32, ctypes.POINTER(_P)]),
-    "pkv_cache_grow": (_I32, [_P, _I32]),
+    "pkv_cache_grow": (_I32, [_P, _I32, _P]),
     "pkv_begin_token": (_I32, [_P, _PI32]),
     "pkv_append_and_attend": (_I32, [_P, _I32, _P, _P, _P, _P, _P]),
     "pkv_commit_token": (_I32, [_P]),
@@ -302,8 +304,8 @@ def pkv_cache_fork(src: int, n_tokens: int, max_context: int) -> int:
     return h.value
 
 
-def pkv_cache_grow(cache: int, n_tokens: int) -> None:
-    _check(_lib.pkv_cache_grow(cache, n_tokens), "pkv_cache_grow")
+def pkv_cache_grow(cache: int, n_tokens: int, stream=None) -> None:
+    _check(_lib.pkv_cache_grow(cache, n_tokens, _stream(stream)), "pkv_cache_grow")
 
 
 # -------------------------------------------------------------- transaction --

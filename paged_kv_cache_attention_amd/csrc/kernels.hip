@@ -14,7 +14,8 @@
 //
 // Arithmetic: float32 throughout (bf16 K/V widen exactly; the grouped-head
 // matrix path multiplies bf16 operands exactly and rounds the softmax weights
-// to bf16 for the value product).  Scores are kept in
+// to bf16 for the value product, summing the same rounded weights for the
+// normaliser).  Scores are kept in
 // log2 units (q is pre-multiplied by log2(e)/sqrt(d_h)) so every exponential is
 // one v_exp_f32.  Softmax is online: each lane group keeps a running maximum m,
 // a running sum l of 2^(s-m) and an accumulator of 2^(s-m) v; groups, waves and
@@ -52,6 +53,26 @@ struct KVTraits<bf16_t> {
     return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
   }
 };
+
+// The work item of this workgroup and request entry r of the plan.  The item
+// is uniform across the workgroup; readfirstlane keeps its fields in scalar
+// registers whichever source it came from.
+__device__ inline WorkItem plan_item(const AttnArgs& a, int idx) {
+  WorkItem w = a.num_inline ? a.inline_items[idx] : a.items[idx];
+  w.req = __builtin_amdgcn_readfirstlane(w.req);
+  w.blk_begin = __builtin_amdgcn_readfirstlane(w.blk_begin);
+  w.blk_end = __builtin_amdgcn_readfirstlane(w.blk_end);
+  w.split = __builtin_amdgcn_readfirstlane(w.split);
+  w.rq.pt_row = __builtin_amdgcn_readfirstlane(w.rq.pt_row);
+  w.rq.seq_len = __builtin_amdgcn_readfirstlane(w.rq.seq_len);
+  w.rq.nsplit = __builtin_amdgcn_readfirstlane(w.rq.nsplit);
+  w.rq.partial_base = __builtin_amdgcn_readfirstlane(w.rq.partial_base);
+  return w;
+}
+__device__ inline WorkItem plan_item(const AttnArgs& a) { return plan_item(a, blockIdx.x); }
+__device__ inline ReqEntry plan_req(const AttnArgs& a, int r) {
+  return a.num_inline ? a.inline_reqs[r] : a.reqs[r];
+}
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -892,11 +913,12 @@ __global__ __launch_bounds__(64 * W, D == 256 ? 1 : 8 / W) void attend_group_mfm
     constexpr bool edge = decltype(edge_tag)::value;
     uint4* kk = x.k;
     VVec* vv = x.v;
-    float valid_k[4];
+    bool valid_k[4] = {true, true, true, true};
     if constexpr (edge) {
       // The request's last block: keys >= t are masked and their V rows
-      // zeroed (stale bytes may be anything); with a fused append, key t-1
-      // comes from the inputs.
+      // zeroed (stale bytes may be anything, NaN and Inf patterns included:
+      // a masked score is replaced, never added to); with a fused append,
+      // key t-1 comes from the inputs.
       const int row0 = b * kBlockRows;
       if (fused && row0 + ql == t - 1) {
 #pragma unroll
@@ -910,7 +932,7 @@ __global__ __launch_bounds__(64 * W, D == 256 ? 1 : 8 / W) void attend_group_mfm
         if (fused && key == t - 1)
           vv[i] = VVec::load(static_cast<const char*>(a.v_new) + kvrow + ql * VB);
         if (key >= t) vv[i] = VVec::zero();
-        valid_k[i] = key < t ? 0.f : -INFINITY;
+        valid_k[i] = key < t;
       }
     }
     f32x4_t c = {0.f, 0.f, 0.f, 0.f};
@@ -920,10 +942,7 @@ __global__ __launch_bounds__(64 * W, D == 256 ? 1 : 8 / W) void attend_group_mfm
                                                    0, 0, 0);
     float sc[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sc[j] = c[j];
-      if constexpr (edge) sc[j] += valid_k[j];
-    }
+    for (int j = 0; j < 4; ++j) sc[j] = (!edge || valid_k[j]) ? c[j] : -INFINITY;
     float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     const float cand = xor32_max(xor16_max(mb)) * a.scale_log2e;
     // Lazy rescale: a head's running maximum moves (and its context and sum
@@ -942,17 +961,18 @@ __global__ __launch_bounds__(64 * W, D == 256 ? 1 : 8 / W) void attend_group_mfm
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt) acc[dt] *= alpha;
     }
-    float p[4], ps = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p[j] = fast_exp2(fmaf(sc[j], a.scale_log2e, -m));
-      ps += p[j];
-    }
-    l += xor32_sum(xor16_sum(ps));
+    // The weights are rounded to bf16 for the value product, and the running
+    // sum adds those same rounded weights, so numerator and denominator use
+    // one set of weights (the softmax normalises exactly what it mixes).
     typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
     bf16x4_t pb4;
+    float ps = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pb4[j] = (__bf16)p[j];
+    for (int j = 0; j < 4; ++j) {
+      pb4[j] = (__bf16)fast_exp2(fmaf(sc[j], a.scale_log2e, -m));
+      ps += (float)pb4[j];
+    }
+    l += xor32_sum(xor16_sum(ps));
     const s16x4_t pb = __builtin_bit_cast(s16x4_t, pb4);
     // Value tile dt, row r is dim NT r + dt, so the A operand of lane (ql, g)
     // -- dim NT ql + dt of keys 4g .. 4g+3 -- is its own V data, packed.
@@ -1098,11 +1118,12 @@ __global__ __launch_bounds__(64 * W, D == 128 ? 1 : 8 / W) void attend_group_f32
 
   auto step = [&](int b, Buf& x, auto edge_tag) {
     constexpr bool edge = decltype(edge_tag)::value;
-    float valid_k[4];
+    bool valid_k[4] = {true, true, true, true};
     if constexpr (edge) {
-      // The request's last block: keys >= t are masked and their V rows
-      // zeroed (stale bytes may be anything); with a fused append, key t-1
-      // comes from the inputs.
+      // The request's last block: keys >= t are masked (their scores
+      // replaced, so NaN or Inf bytes in unwritten slots cannot reach the
+      // sums) and their V rows zeroed; with a fused append, key t-1 comes
+      // from the inputs.
       const int row0 = b * kBlockRows;
       if (fused && row0 + ql == t - 1)
         x.k = KVec::load(static_cast<const char*>(a.k_new) + kvrow + g * KD * 4);
@@ -1112,7 +1133,7 @@ __global__ __launch_bounds__(64 * W, D == 128 ? 1 : 8 / W) void attend_group_f32
         if (fused && key == t - 1)
           x.v[s] = VVec::load(static_cast<const char*>(a.v_new) + kvrow + ql * NT * 4);
         if (key >= t) x.v[s] = VVec::zero();
-        valid_k[s] = key < t ? 0.f : -INFINITY;
+        valid_k[s] = key < t;
       }
     }
     f32x4_t c = {0.f, 0.f, 0.f, 0.f};
@@ -1121,10 +1142,7 @@ __global__ __launch_bounds__(64 * W, D == 128 ? 1 : 8 / W) void attend_group_f32
       c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(x.k.w[s]), qf[s], c, 0, 0, 0);
     float sc[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sc[j] = c[j];
-      if constexpr (edge) sc[j] += valid_k[j];
-    }
+    for (int j = 0; j < 4; ++j) sc[j] = (!edge || valid_k[j]) ? c[j] : -INFINITY;
     float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     const float cand = xor32_max(xor16_max(mb)) * a.scale_log2e;
     // Lazy rescale, as in the bf16 kernel.
@@ -1344,6 +1362,11 @@ __global__ __launch_bounds__(256) void patch_kernel(int32_t* arena, PatchBatch b
   if (i < b.count) arena[b.offset[i]] = b.value[i];
 }
 
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* p, int64_t count) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256)
+    p[i] = 0;
+}
+
 template <typename T, int D, int WAVES, int HPW, int WPG, bool PAD = false>
 hipError_t launch_fast_shape(const AttnArgs& a, int num_items, hipStream_t stream) {
   hipLaunchKernelGGL((attend_fast_kernel<T, D, WAVES, HPW, WPG, PAD>),
@@ -1493,6 +1516,16 @@ hipError_t launch_group(const AttnArgs& a, int share, dim3 grid, hipStream_t str
       hipLaunchKernelGGL((attend_group_mfma_kernel<16, 4, D>), grid, dim3(256), 0, stream, a);
       break;
   }
+  return hipGetLastError();
+}
+
+bool fast_width_native(int dtype, int head_width) { return fast_row_bytes(dtype, head_width) != 0; }
+
+hipError_t launch_zero_i32(int32_t* p, int64_t count, hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  const int64_t blocks = (count + 255) / 256;
+  hipLaunchKernelGGL(zero_i32_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0,
+                     stream, p, count);
   return hipGetLastError();
 }
 

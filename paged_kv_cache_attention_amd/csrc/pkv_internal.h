@@ -75,26 +75,6 @@ struct AttnArgs {
   WorkItem inline_items[kInlineItems];
 };
 
-// The work item of this workgroup and request entry r of the plan.  The item
-// is uniform across the workgroup; readfirstlane keeps its fields in scalar
-// registers whichever source it came from.
-__device__ inline WorkItem plan_item(const AttnArgs& a, int idx) {
-  WorkItem w = a.num_inline ? a.inline_items[idx] : a.items[idx];
-  w.req = __builtin_amdgcn_readfirstlane(w.req);
-  w.blk_begin = __builtin_amdgcn_readfirstlane(w.blk_begin);
-  w.blk_end = __builtin_amdgcn_readfirstlane(w.blk_end);
-  w.split = __builtin_amdgcn_readfirstlane(w.split);
-  w.rq.pt_row = __builtin_amdgcn_readfirstlane(w.rq.pt_row);
-  w.rq.seq_len = __builtin_amdgcn_readfirstlane(w.rq.seq_len);
-  w.rq.nsplit = __builtin_amdgcn_readfirstlane(w.rq.nsplit);
-  w.rq.partial_base = __builtin_amdgcn_readfirstlane(w.rq.partial_base);
-  return w;
-}
-__device__ inline WorkItem plan_item(const AttnArgs& a) { return plan_item(a, blockIdx.x); }
-__device__ inline ReqEntry plan_req(const AttnArgs& a, int r) {
-  return a.num_inline ? a.inline_reqs[r] : a.reqs[r];
-}
-
 // One prefill work tile: up to kPrefillTileRows consecutive rows of one
 // request's chunk.
 struct PrefillTile {
@@ -167,6 +147,12 @@ hipError_t launch_page_copies(char* k_storage, char* v_storage, int64_t layer_by
                               int64_t page_bytes, int32_t num_layers, const CopyBatch& b,
                               hipStream_t stream);
 bool fast_path_supported(int dtype, int head_width, int page_size, int group);
+// Whether the head width has a vector fast-path shape of its own (rows of
+// 128, 256 or 512 bytes), as opposed to running a wider shape padded.
+bool fast_width_native(int dtype, int head_width);
+// Writes zero to count int32 values on the stream (a kernel, so that the
+// clear is ordered with the launches that follow on any stream kind).
+hipError_t launch_zero_i32(int32_t* p, int64_t count, hipStream_t stream);
 
 // Prefill on matrix cores (bf16 head width 64, 128 or 256; float32 32, 64 or
 // 128; pages of a multiple of 16 rows): an append launch writes the chunk's

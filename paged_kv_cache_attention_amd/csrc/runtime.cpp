@@ -112,6 +112,12 @@ struct pkv_plan {
   size_t h_stage_cap = 0;
   hipEvent_t ev = nullptr;
   bool ev_pending = false;
+  // Buffers replaced by a larger one.  Work already enqueued may still read
+  // them, and freeing device or pinned memory waits for the whole device, so
+  // they stay allocated until the plan is released (capacities double, so
+  // together they stay below the final buffers' size).
+  std::vector<void*> retired_dev;
+  std::vector<void*> retired_host;
 };
 
 struct pkv_cache {
@@ -158,6 +164,7 @@ struct pkv_pool {
   pkv_counters counters{};
   int32_t merge_mode = pkv::kMergeLastArriver;
   int32_t waves_option = 0;
+  uint64_t opt_gen = 0;  // bumped by every option that changes a plan's shape
   bool profiling = false;
   enum TimedKind { kTimedAttention, kTimedMerge, kTimedPrefill };
   struct Timed {
@@ -199,7 +206,7 @@ void record_patch(pkv_cache* c, int32_t logical, int32_t page) {
   p->patches.emplace_back(c->slot * p->arena_stride + logical, page);
 }
 
-pkv_status ensure_device(pkv_pool* p) {
+pkv_status ensure_device(pkv_pool* p, hipStream_t stream) {
   if (p->host_only) return PKV_OK;
   int dev = 0;
   PKV_HIP_TRY(hipGetDevice(&dev));
@@ -213,9 +220,11 @@ pkv_status ensure_device(pkv_pool* p) {
   void* arena = nullptr;
   if (hipMalloc(&arena, bytes) != hipSuccess)
     return fail(PKV_ERR_ALLOC, "device page-table arena of %zu bytes", bytes);
-  if (hipMemset(arena, 0, bytes) != hipSuccess) {
+  // Cleared on the caller's stream, ahead of the patches that fill it.
+  if (pkv::launch_zero_i32(static_cast<int32_t*>(arena), (int64_t)(bytes / sizeof(int32_t)),
+                           stream) != hipSuccess) {
     (void)hipFree(arena);
-    return fail(PKV_ERR_DEVICE, "hipMemset of the page-table arena failed");
+    return fail(PKV_ERR_DEVICE, "clearing the page-table arena failed");
   }
   p->d_arena = static_cast<int32_t*>(arena);
   p->device = dev;
@@ -327,13 +336,23 @@ SplitChoice choose_split(const pkv_pool* p, int32_t n, int64_t total_blocks) {
   // the one-wave generic kernel keeps it too.
   const bool small_mha = c == 8 && waves == 0 && p->desc.num_kv_heads == H &&
       pkv::fast_path_supported(p->desc.kv_dtype, p->desc.head_width, p->desc.page_size, 1);
-  if (small_mha && p->desc.head_width <= 64 && (total_blocks / 64 + n / 2) * H >= 256)
+  // Sixteen waves exist for the native row widths only (a padded width runs
+  // a wider shape, which has no sixteen-wave form), so padded widths take
+  // the eight-wave choice below.
+  if (small_mha && p->desc.head_width <= 64 &&
+      pkv::fast_width_native(p->desc.kv_dtype, p->desc.head_width) &&
+      (total_blocks / 64 + n / 2) * H >= 256)
     return {64, 16};
   if (small_mha && (total_blocks / 32 + n / 2) * H >= 256) return {32, 8};
   return {(int32_t)c, waves};
 }
 
+// Frees the plan's buffers (at destroy: these frees wait for the device).
 void plan_release(pkv_plan* pl) {
+  for (void* d : pl->retired_dev) (void)hipFree(d);
+  for (void* h : pl->retired_host) (void)hipHostFree(h);
+  pl->retired_dev.clear();
+  pl->retired_host.clear();
   if (pl->ev) {
     (void)hipEventSynchronize(pl->ev);
     (void)hipEventDestroy(pl->ev);
@@ -360,7 +379,7 @@ struct MetaPart {
 // Copies the parts, back to back, into the plan's device metadata buffer on
 // the stream, through pinned host staging.  The staging buffer is reused only
 // after the previous upload's copy has completed (an event on the stream);
-// growing the device buffer waits for the device to finish with the old one.
+// a grown device buffer replaces the old one, which is kept (see retired_dev).
 pkv_status upload_meta(pkv_plan* pl, const MetaPart* parts, int nparts, hipStream_t stream) {
   size_t bytes = 0;
   for (int i = 0; i < nparts; ++i) bytes += parts[i].bytes;
@@ -373,10 +392,7 @@ pkv_status upload_meta(pkv_plan* pl, const MetaPart* parts, int nparts, hipStrea
     const size_t cap = std::max(bytes, pl->d_meta_cap * 2);
     void* d = nullptr;
     if (hipMalloc(&d, cap) != hipSuccess) return fail(PKV_ERR_ALLOC, "plan buffer %zu bytes", cap);
-    if (pl->d_meta) {
-      (void)hipDeviceSynchronize();
-      (void)hipFree(pl->d_meta);
-    }
+    if (pl->d_meta) pl->retired_dev.push_back(pl->d_meta);
     pl->d_meta = static_cast<char*>(d);
     pl->d_meta_cap = cap;
   }
@@ -385,7 +401,7 @@ pkv_status upload_meta(pkv_plan* pl, const MetaPart* parts, int nparts, hipStrea
     void* h = nullptr;
     if (hipHostMalloc(&h, cap, hipHostMallocDefault) != hipSuccess)
       return fail(PKV_ERR_ALLOC, "pinned staging %zu bytes", cap);
-    if (pl->h_stage) (void)hipHostFree(pl->h_stage);
+    if (pl->h_stage) pl->retired_host.push_back(pl->h_stage);
     pl->h_stage = static_cast<char*>(h);
     pl->h_stage_cap = cap;
   }
@@ -423,14 +439,17 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
                   (long long)max_len);
     total_blocks += (lens[r] + pkv::kBlockRows - 1) / pkv::kBlockRows;
   }
-  std::vector<int64_t> key(2 * (size_t)n + 1);
+  // The key holds the options generation too: a plan built before an option
+  // changed its chunking or workgroup shape is rebuilt.
+  std::vector<int64_t> key(2 * (size_t)n + 2);
   key[0] = pt_stride;
+  key[1] = (int64_t)p->opt_gen;
   for (int32_t r = 0; r < n; ++r) {
-    key[1 + 2 * r] = rows[r];
-    key[2 + 2 * r] = lens[r];
+    key[2 + 2 * r] = rows[r];
+    key[3 + 2 * r] = lens[r];
   }
   if (pl->built && key == pl->key) return PKV_OK;  // identical plan already on the device
-  pkv_status st = ensure_device(p);
+  pkv_status st = ensure_device(p, stream);
   if (st != PKV_OK) return st;
 
   const SplitChoice choice = choose_split(p, n, total_blocks);
@@ -479,10 +498,7 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
     void* d = nullptr;
     if (hipMalloc(&d, cap * sizeof(float)) != hipSuccess)
       return fail(PKV_ERR_ALLOC, "partials %zu floats", cap);
-    if (pl->d_partials) {
-      (void)hipDeviceSynchronize();
-      (void)hipFree(pl->d_partials);
-    }
+    if (pl->d_partials) pl->retired_dev.push_back(pl->d_partials);
     pl->d_partials = static_cast<float*>(d);
     pl->partials_cap = cap;
   }
@@ -492,14 +508,12 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
     void* d = nullptr;
     if (hipMalloc(&d, cap * sizeof(int32_t)) != hipSuccess)
       return fail(PKV_ERR_ALLOC, "merge counters %zu", cap);
-    if (hipMemset(d, 0, cap * sizeof(int32_t)) != hipSuccess) {
+    // Zeroed on the stream of the launches that will use them.
+    if (pkv::launch_zero_i32(static_cast<int32_t*>(d), (int64_t)cap, stream) != hipSuccess) {
       (void)hipFree(d);
-      return fail(PKV_ERR_DEVICE, "hipMemset of merge counters failed");
+      return fail(PKV_ERR_DEVICE, "clearing the merge counters failed");
     }
-    if (pl->d_counters) {
-      (void)hipDeviceSynchronize();
-      (void)hipFree(pl->d_counters);
-    }
+    if (pl->d_counters) pl->retired_dev.push_back(pl->d_counters);
     pl->d_counters = static_cast<int32_t*>(d);
     pl->counters_cap = cap;
   }
@@ -658,13 +672,14 @@ pkv_status run_prefill_tiles(pkv_pool* p, int32_t n, const int32_t* rows, const 
                              const void* v, float* out, uint64_t score_rows,
                              hipStream_t stream) {
   pkv_plan* pl = &p->prefill_plan;
-  std::vector<int64_t> key(3 * (size_t)n + 2);
+  std::vector<int64_t> key(3 * (size_t)n + 3);
   key[0] = -1;  // never equal to a decode-plan key (those start with pt_stride)
   key[1] = pt_stride;
+  key[2] = (int64_t)p->opt_gen;
   for (int32_t r = 0; r < n; ++r) {
-    key[2 + 3 * r] = rows[r];
-    key[3 + 3 * r] = starts[r];
-    key[4 + 3 * r] = counts[r];
+    key[3 + 3 * r] = rows[r];
+    key[4 + 3 * r] = starts[r];
+    key[5 + 3 * r] = counts[r];
   }
   if (!(pl->built && key == pl->key)) {
     // Tiles grouped by request (they re-read the request's K/V), requests
@@ -688,7 +703,7 @@ pkv_status run_prefill_tiles(pkv_pool* p, int32_t n, const int32_t* rows, const 
         tiles.push_back(PrefillTile{rows[r], starts[r], offs[r], i0, nq, starts[r] + i0 + nq});
       }
     }
-    pkv_status st = ensure_device(p);
+    pkv_status st = ensure_device(p, stream);
     if (st != PKV_OK) return st;
     const MetaPart part{tiles.data(), tiles.size() * sizeof(PrefillTile)};
     if ((st = upload_meta(pl, &part, 1, stream)) != PKV_OK) return st;
@@ -775,7 +790,7 @@ pkv_status run_prefill(pkv_pool* p, int32_t n, const int32_t* rows, const int32_
   pkv_status st = plan_build(pl, (int32_t)total, vrows.data(), vlens.data(), pt_stride, stream);
   if (st != PKV_OK) return st;
   if (!p->host_only) {
-    AttnArgs a = make_args(pl, layer, page_table, q, k, v, out, false);
+      AttnArgs a = make_args(pl, layer, page_table, q, k, v, out, false);
     PKV_HIP_TRY(pkv::launch_kv_append(a, p->desc.kv_dtype, (int32_t)total, stream));
   }
   // run_attention counts the decode-form K/V reads; this call counted its own
@@ -817,8 +832,8 @@ pkv_status txn_step(pkv_cache* const* caches, int32_t n, int32_t layer, const vo
     if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
       return fail(PKV_ERR_INVALID_ARGUMENT, "a cache appears twice in the batch");
   }
-  if ((st = ensure_device(p)) != PKV_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = ensure_device(p, s)) != PKV_OK) return st;
   if ((st = flush_patches(p, s)) != PKV_OK) return st;
   if (chunked) {
     st = run_prefill(p, n, rows.data(), starts.data(), counts.data(), p->arena_stride, layer,
@@ -961,20 +976,19 @@ pkv_status pkv_pool_set_option(pkv_pool* p, int32_t option, int64_t value) {
     case PKV_OPT_SPLIT_BLOCKS:
       if (value < -1 || value > (1 << 24)) return fail(PKV_ERR_INVALID_ARGUMENT, "split_blocks");
       p->desc.split_blocks = (int32_t)value;
-      p->txn_plan.key.clear();
-      p->call_plan.key.clear();
+      p->opt_gen += 1;
       return ok();
     case PKV_OPT_MERGE_MODE:
       if (value != pkv::kMergeSeparate && value != pkv::kMergeLastArriver)
         return fail(PKV_ERR_INVALID_ARGUMENT, "merge mode %lld", (long long)value);
       p->merge_mode = (int32_t)value;
+      p->opt_gen += 1;
       return ok();
     case PKV_OPT_WAVES:
       if (value != 0 && value != 4 && value != 8 && value != 16)
         return fail(PKV_ERR_INVALID_ARGUMENT, "waves %lld", (long long)value);
       p->waves_option = (int32_t)value;
-      p->txn_plan.key.clear();
-      p->call_plan.key.clear();
+      p->opt_gen += 1;
       return ok();
     case PKV_OPT_PROFILING:
       if (value != 0 && value != 1) return fail(PKV_ERR_INVALID_ARGUMENT, "profiling %lld", (long long)value);
@@ -1096,7 +1110,7 @@ pkv_status pkv_cache_page_table(const pkv_cache* c, int32_t* out, int32_t cap, i
 static bool needs_cow(const pkv_cache* c);
 static int32_t copy_on_write(pkv_cache* c);
 
-pkv_status pkv_cache_grow(pkv_cache* c, int32_t n_tokens) {
+pkv_status pkv_cache_grow(pkv_cache* c, int32_t n_tokens, void* stream) {
   if (!c) return fail(PKV_ERR_INVALID_ARGUMENT, "null cache");
   if (n_tokens < 0) return fail(PKV_ERR_INVALID_ARGUMENT, "negative n_tokens");
   if (c->pending) return fail(PKV_ERR_BAD_STATE, "grow with a pending token");
@@ -1111,14 +1125,16 @@ pkv_status pkv_cache_grow(pkv_cache* c, int32_t n_tokens) {
     return fail(PKV_ERR_OUT_OF_PAGES, "need %d pages, %zu free", need + (cow ? 1 : 0),
                 p->free_stack.size());
   if (cow) {
-    // The caller writes the grown rows itself right after this call, so the
-    // private copy of the shared last page is complete when it returns.
-    pkv_status st = ensure_device(p);
+    // The private copy of the shared last page is enqueued on the caller's
+    // stream, so the rows the caller then writes on that stream land after
+    // it, and it reads the source after every earlier write there.  The
+    // source stays allocated: another holder still has it.
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    pkv_status st = ensure_device(p, s);
     if (st != PKV_OK) return st;
     const int32_t old = c->pages[c->len / S];
     copy_on_write(c);
-    if ((st = flush_copies(p, nullptr)) != PKV_OK) return st;
-    if (!p->host_only) PKV_HIP_TRY(hipStreamSynchronize(nullptr));
+    if ((st = flush_copies(p, s)) != PKV_OK) return st;
     release_page(p, old);
   }
   for (int32_t i = 0; i < need; ++i) {
@@ -1379,18 +1395,19 @@ int32_t pkv_plan_num_chunks(const pkv_plan* pl) {
   return (pl && pl->built) ? pl->num_items : 0;
 }
 
-static pkv_status plan_ready(const pkv_plan* pl, int32_t layer, const int32_t* page_table) {
+static pkv_status plan_ready(const pkv_plan* pl, int32_t layer, const int32_t* page_table,
+                             void* stream) {
   if (!pl) return fail(PKV_ERR_INVALID_ARGUMENT, "null plan");
   if (!pl->built) return fail(PKV_ERR_BAD_STATE, "plan not built");
   pkv_status st = check_layer(pl->pool, layer);
   if (st != PKV_OK) return st;
   if (!page_table) return fail(PKV_ERR_INVALID_ARGUMENT, "page_table is null");
-  return ensure_device(pl->pool);
+  return ensure_device(pl->pool, static_cast<hipStream_t>(stream));
 }
 
 pkv_status pkv_plan_decode_attention(pkv_plan* pl, int32_t layer, const void* q,
                                      const int32_t* page_table, float* out, void* stream) {
-  pkv_status st = plan_ready(pl, layer, page_table);
+  pkv_status st = plan_ready(pl, layer, page_table, stream);
   if (st != PKV_OK) return st;
   if ((st = check_ptr(q, "q")) != PKV_OK || (st = check_ptr(out, "out")) != PKV_OK) return st;
   st = run_attention(pl, layer, page_table, q, nullptr, nullptr, out, false,
@@ -1400,7 +1417,7 @@ pkv_status pkv_plan_decode_attention(pkv_plan* pl, int32_t layer, const void* q,
 
 pkv_status pkv_plan_kv_append(pkv_plan* pl, int32_t layer, const int32_t* page_table,
                               const void* k, const void* v, void* stream) {
-  pkv_status st = plan_ready(pl, layer, page_table);
+  pkv_status st = plan_ready(pl, layer, page_table, stream);
   if (st != PKV_OK) return st;
   if ((st = check_ptr(k, "k")) != PKV_OK || (st = check_ptr(v, "v")) != PKV_OK) return st;
   if (pl->pool->host_only) return ok();
@@ -1413,7 +1430,7 @@ pkv_status pkv_plan_kv_append(pkv_plan* pl, int32_t layer, const int32_t* page_t
 pkv_status pkv_plan_append_and_attend(pkv_plan* pl, int32_t layer, const int32_t* page_table,
                                       const void* q, const void* k, const void* v, float* out,
                                       void* stream) {
-  pkv_status st = plan_ready(pl, layer, page_table);
+  pkv_status st = plan_ready(pl, layer, page_table, stream);
   if (st != PKV_OK) return st;
   if ((st = check_ptr(q, "q")) != PKV_OK || (st = check_ptr(k, "k")) != PKV_OK ||
       (st = check_ptr(v, "v")) != PKV_OK || (st = check_ptr(out, "out")) != PKV_OK)

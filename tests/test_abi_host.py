@@ -328,6 +328,49 @@ def test_small_multihead_batch_takes_whole_requests_or_32_block_chunks():
     pkv.pkv_pool_destroy(p)
 
 
+def test_padded_widths_take_eight_waves_not_sixteen():
+    # float32 d_h = 40 runs the d_h = 64 shape padded, which has no
+    # sixteen-wave form: the small-batch choice is 32-block chunks over eight
+    # waves (a 33-block request in two chunks), where the native d_h = 64
+    # takes 64-block chunks over sixteen (one chunk per request).
+    for width, chunks in ((64, 32), (40, 64)):
+        p = make_pool(pages=4200, ctx=16 * 1024, heads=12, width=width, caches=40)
+        plan = pkv.pkv_plan_create(p)
+        pkv.pkv_plan_build(plan, [16 * 33] * 32, 1024, stream=0)
+        assert pkv.pkv_plan_num_chunks(plan) == chunks, width
+        pkv.pkv_plan_destroy(plan)
+        pkv.pkv_pool_destroy(p)
+
+
+def test_option_change_rebuilds_a_plan_with_the_same_lengths():
+    # a plan keyed on its lengths alone would keep its old chunking
+    p = make_pool(pages=64, ctx=1024, split=2)
+    plan = pkv.pkv_plan_create(p)
+    pkv.pkv_plan_build(plan, [100, 16, 33], 64, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 4 + 1 + 2
+    pkv.pkv_pool_set_option(p, pkv.PKV_OPT_SPLIT_BLOCKS, 4)       # 7 blocks -> 2 chunks
+    pkv.pkv_plan_build(plan, [100, 16, 33], 64, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 2 + 1 + 1
+    pkv.pkv_pool_set_option(p, pkv.PKV_OPT_SPLIT_BLOCKS, -1)      # never split
+    pkv.pkv_plan_build(plan, [100, 16, 33], 64, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 3
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(p)
+    # the waves option picks the split of a small multi-head batch
+    p = make_pool(pages=4200, ctx=16 * 1024, heads=12, width=64, caches=40)
+    plan = pkv.pkv_plan_create(p)
+    pkv.pkv_plan_build(plan, [16 * 32] * 32, 1024, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 32
+    pkv.pkv_pool_set_option(p, pkv.PKV_OPT_WAVES, 4)
+    pkv.pkv_plan_build(plan, [16 * 32] * 32, 1024, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 32 * 4
+    pkv.pkv_pool_set_option(p, pkv.PKV_OPT_WAVES, 0)
+    pkv.pkv_plan_build(plan, [16 * 32] * 32, 1024, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 32
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(p)
+
+
 def test_waves_option_values():
     # 0, 4, 8 and 16 are accepted; anything else is rejected and leaves the
     # option unchanged (16 explicit waves keep the finest default split)
