@@ -25,3 +25,15 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    try:
+        from tests.gpu_support import OBSERVED
+    except Exception:  # pragma: no cover
+        return
+    if not OBSERVED:
+        return
+    terminalreporter.write_sep("-", "largest observed errors against the oracle")
+    for name in sorted(OBSERVED):
+        terminalreporter.write_line(f"{name}: {OBSERVED[name]:.3e}")

@@ -13,7 +13,8 @@ import torch
 import oracle
 import synth
 from synth import workloads as W
-from tests.gpu_support import (TOL, HostPages, device_pool, max_err, rows_to_device, to_bits)
+from tests.gpu_support import (TOL, GeneratorLayer, HostPages, device_pool, max_err, record_err,
+                               rows_to_device, to_bits)
 
 pytestmark = pytest.mark.gpu
 pkv = pytest.importorskip("paged_kv_cache_attention_amd")
@@ -847,12 +848,20 @@ def test_batch32_fp32_l12_full_step(merge, split):
         got_v = to_bits(vp[layer][torch.from_numpy(pages).long(), :, torch.from_numpy(last % 16)
                                   .long(), :], "f32")
         assert np.array_equal(got_k, kh) and np.array_equal(got_v, vh)
-    longest = int(np.argmax(w.lengths))
-    for layer in (0, 5, 11):
-        qh = w.q(layer)
-        for r in _sampled(w.n, extra=[longest, int(np.argmin(w.lengths))]):
-            ref = _oracle_decode(w, layer, r, qh, appended=(w.k_new(layer), w.v_new(layer)))
-            assert max_err(outs[layer][r], ref) <= TOL["f32"], (layer, r)
+    worst = 0.0
+    for layer in range(w.layers):
+        qh, kh, vh = w.q(layer), w.k_new(layer), w.v_new(layer)
+        kg, vg = GeneratorLayer(w, "k", layer), GeneratorLayer(w, "v", layer)
+        if layer == 0:
+            kg.spot_check(w.page_tables[:, 0])
+        for r in range(w.n):
+            t = int(w.lengths[r])
+            ref = oracle.append_and_attend(qh[r], kh[r], vh[r], kg, vg, w.page_tables[r], t - 1,
+                                           w.page_size)
+            err = max_err(outs[layer][r], ref)
+            worst = max(worst, err)
+            assert err <= TOL["f32"], (layer, r)
+    record_err(f"batch32_fp32_l12 full step split {split} merge {merge}", worst)
     pkv.pkv_plan_destroy(plan)
     pkv.pkv_pool_destroy(pool)
 
@@ -885,7 +894,7 @@ def test_last_arriver_merge_is_bitwise_separate_merge():
     for o in outs[pkv.PKV_MERGE_LAST_ARRIVER]:
         assert torch.equal(o, ref)
     qh = w.q(0)
-    for r in _sampled(w.n):
+    for r in range(w.n):
         assert max_err(ref[r], _oracle_decode(w, 0, r, qh)) <= TOL["f32"]
 
 
@@ -944,21 +953,32 @@ def test_bf16_single_layer_full(maker, merge):
     pkv.pkv_plan_decode_attention(plan, 0, rows_to_device(qh, "bf16"), _pt_device(w), out)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
-    longest, shortest = int(np.argmax(w.lengths)), int(np.argmin(w.lengths))
-    for r in _sampled(w.n, extra=[longest, shortest])[:12]:
-        ref = _oracle_decode(w, 0, r, qh)
-        assert max_err(out[r], ref) <= TOL["bf16"], (r, int(w.lengths[r]))
+    kg, vg = GeneratorLayer(w, "k", 0), GeneratorLayer(w, "v", 0)
+    kg.spot_check(w.page_tables[[0, w.n - 1], 0])
+    vg.spot_check(w.page_tables[[0, w.n - 1], 0])
+    got = out.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for r in range(w.n):
+        ref = oracle.paged_decode_attention(qh[r], kg, vg, w.page_tables[r], int(w.lengths[r]),
+                                            w.page_size, num_kv_heads=w.hkv)
+        err = float(np.max(np.abs(got[r] - ref)))
+        worst = max(worst, err)
+        assert err <= TOL["bf16"], (r, int(w.lengths[r]))
+    record_err(f"{w.name} every request merge {merge}", worst)
     pkv.pkv_plan_destroy(plan)
     pkv.pkv_pool_destroy(pool)
 
 
 def test_fullstep128_bf16_l32_transactional():
-    """128 caches x 32 layers, H=32, d_h=128, bf16: begin, batched
-    append_and_attend per layer, commit; seeded aborts; then the aborted
-    requests retry and match a run that never saw the aborted token."""
+    """128 caches x 32 layers, H=32, d_h=128, bf16, every layer's pool filled
+    by the generator: begin, batched append_and_attend per layer, commit;
+    seeded aborts; then the aborted requests retry and match a run that never
+    saw the aborted token.  Every live request is checked against the oracle
+    at eight layers spread over the 32 (its new rows bit-exact in the pages
+    at every layer), and every retried request at the same layers."""
     w = W.fullstep128_bf16(extra_steps=4)
-    checked_layers = [0, 13, 31]
-    kp, vp = device_pool(w, layers=checked_layers)
+    checked_layers = [0, 4, 9, 13, 18, 22, 27, 31]
+    kp, vp = device_pool(w)
     pool = _pool(w, kp, vp, seed=55, max_caches=w.n, max_context=4096)
     caches = [pkv.pkv_cache_create(pool, 4096) for _ in range(w.n)]
     prefix = w.lengths - 1
@@ -966,14 +986,14 @@ def test_fullstep128_bf16_l32_transactional():
         pkv.pkv_cache_grow(c, n)
     tables = [pkv.pkv_cache_page_table(c) for c in caches]
     flat = [p for t in tables for p in t]
-    assert len(flat) == len(set(flat))
+    assert len(flat) == len(set(flat)) and all(0 <= p < w.num_pages for p in flat)
     # find a step with at least one abort
     step = next(s for s in range(100) if (w.abort_layer(s) >= 0).any())
     abort = w.abort_layer(step)
     for c in caches:
         pkv.pkv_begin_token(c)
     tables = [pkv.pkv_cache_page_table(c) for c in caches]
-    outs = {}
+    outs, lives = {}, {}
     live = list(range(w.n))
     for layer in range(w.layers):
         for r in [r for r in live if abort[r] == layer]:
@@ -983,8 +1003,9 @@ def test_fullstep128_bf16_l32_transactional():
         q, k, v = (rows_to_device(x[live], "bf16") for x in (qa, ka, va))
         out = torch.empty((len(live), w.heads, w.head_width), device="cuda")
         pkv.pkv_append_and_attend_batched([caches[r] for r in live], layer, q, k, v, out)
+        lives[layer] = list(live)
         if layer in checked_layers:
-            outs[layer] = (list(live), out)
+            outs[layer] = out
     torch.cuda.synchronize()
     for r in live:
         pkv.pkv_commit_token(caches[r])
@@ -992,36 +1013,54 @@ def test_fullstep128_bf16_l32_transactional():
     assert aborted
     for r in range(w.n):
         assert pkv.pkv_cache_size(caches[r]) == prefix[r] + (0 if r in aborted else 1)
-    for layer in checked_layers:
-        lv, out = outs[layer]
-        qa, ka, va = w.q(layer, step), w.k_new(layer, step), w.v_new(layer, step)
-        kpg, vpg = HostPages(w, "k", layer), HostPages(w, "v", layer)
-        for i in _sampled(len(lv))[:5]:
-            r = lv[i]
-            ref = oracle.append_and_attend(qa[r], ka[r], va[r], kpg, vpg, tables[r],
-                                           int(prefix[r]), 16)
-            assert max_err(out[i], ref) <= TOL["bf16"], (layer, r)
-    # the aborted requests retry with the next step's rows
+    # the committed requests' new rows, bit-exact in the pages of every layer
+    committed = list(live)
+    rows = torch.tensor([tables[r][int(prefix[r]) // 16] for r in committed], device="cuda")
+    slots = torch.tensor([int(prefix[r]) % 16 for r in committed], device="cuda")
+    for layer in range(w.layers):
+        ka, va = w.k_new(layer, step), w.v_new(layer, step)
+        got_k = to_bits(kp[layer][rows, :, slots, :], "bf16")
+        got_v = to_bits(vp[layer][rows, :, slots, :], "bf16")
+        assert np.array_equal(got_k, ka[committed]) and np.array_equal(got_v, va[committed]), layer
+    # the retry of the aborted requests, with the next step's rows
     retry = step + 1
     for r in aborted:
         assert pkv.pkv_begin_token(caches[r]) == prefix[r]
-    layer_outs = {}
+    retry_outs = {}
     for layer in range(w.layers):
         qa, ka, va = w.q(layer, retry), w.k_new(layer, retry), w.v_new(layer, retry)
         q, k, v = (rows_to_device(x[aborted], "bf16") for x in (qa, ka, va))
         out = torch.empty((len(aborted), w.heads, w.head_width), device="cuda")
         pkv.pkv_append_and_attend_batched([caches[r] for r in aborted], layer, q, k, v, out)
-        layer_outs[layer] = out
+        if layer in checked_layers:
+            retry_outs[layer] = out
     torch.cuda.synchronize()
     for r in aborted:
         pkv.pkv_commit_token(caches[r])
+    retry_tables = {r: pkv.pkv_cache_page_table(caches[r]) for r in aborted}
+    worst = 0.0
     for layer in checked_layers:
+        kg, vg = GeneratorLayer(w, "k", layer), GeneratorLayer(w, "v", layer)
+        if layer == checked_layers[-1]:
+            kg.spot_check(tables[0][:2])
+        got = outs[layer].cpu().numpy().astype(np.float64)
+        qa, ka, va = w.q(layer, step), w.k_new(layer, step), w.v_new(layer, step)
+        for i, r in enumerate(lives[layer]):
+            ref = oracle.append_and_attend(qa[r], ka[r], va[r], kg, vg, tables[r],
+                                           int(prefix[r]), 16)
+            err = float(np.max(np.abs(got[i] - ref)))
+            worst = max(worst, err)
+            assert err <= TOL["bf16"], (layer, r)
+        got = retry_outs[layer].cpu().numpy().astype(np.float64)
         qa, ka, va = w.q(layer, retry), w.k_new(layer, retry), w.v_new(layer, retry)
         for i, r in enumerate(aborted):
-            ref = oracle.append_and_attend(qa[r], ka[r], va[r], HostPages(w, "k", layer),
-                                           HostPages(w, "v", layer),
-                                           pkv.pkv_cache_page_table(caches[r]), int(prefix[r]), 16)
-            assert max_err(layer_outs[layer][i], ref) <= TOL["bf16"]
+            ref = oracle.append_and_attend(qa[r], ka[r], va[r], kg, vg, retry_tables[r],
+                                           int(prefix[r]), 16)
+            err = float(np.max(np.abs(got[i] - ref)))
+            worst = max(worst, err)
+            assert err <= TOL["bf16"], ("retry", layer, r)
+        del kg, vg
+    record_err("fullstep128_bf16_l32 live and retried requests", worst)
     cnt = pkv.pkv_pool_get_counters(pool)
     assert cnt.committed_tokens == w.n and cnt.aborted_tokens == len(aborted)
     for c in caches:
