@@ -48,17 +48,23 @@ HBM_PEAK_GBS = 8000.0
 # file under csrc/).
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
-    "batch32_fp32_l12": {"source": "kernels.hip", "sha256_16": "290d3361ae1bcabb",
-        "fetch_kib": 44294.2, "write_kib": 299.2,
-        "algorithmic_bytes": 88971264},
-    "batch256_bf16": {"source": "kernels.hip", "sha256_16": "290d3361ae1bcabb",
-        "fetch_kib": 4761714.8, "write_kib": 4345.9,
+    "fullstep128_bf16_l32": {"source": "kernels.hip", "sha256_16": "620d943fb2d1e74e",
+        "fetch_kib": 2073954.0, "write_kib": 18562.9,
+        "algorithmic_bytes": 4238041600},
+    "batch32_fp32_l12": {"source": "kernels.hip", "sha256_16": "620d943fb2d1e74e",
+        "fetch_kib": 44162.4, "write_kib": 292.0,
+        "algorithmic_bytes": 88676352},
+    "batch256_bf16": {"source": "kernels.hip", "sha256_16": "620d943fb2d1e74e",
+        "fetch_kib": 4761780.4, "write_kib": 4345.3,
         "algorithmic_bytes": 9718775808},
-    "batch256_gqa8_bf16": {"source": "kernels.hip", "sha256_16": "290d3361ae1bcabb",
-        "fetch_kib": 1194139.1, "write_kib": 4097.2,
+    "skewed64_bf16": {"source": "kernels.hip", "sha256_16": "620d943fb2d1e74e",
+        "fetch_kib": 1792457.1, "write_kib": 15723.8,
+        "algorithmic_bytes": 3659710464},
+    "batch256_gqa8_bf16": {"source": "kernels.hip", "sha256_16": "620d943fb2d1e74e",
+        "fetch_kib": 1194386.5, "write_kib": 4097.0,
         "algorithmic_bytes": 2434412544},
-    "batch256_mqa_bf16": {"source": "kernels.hip", "sha256_16": "290d3361ae1bcabb",
-        "fetch_kib": 152003.2, "write_kib": 4096.0,
+    "batch256_mqa_bf16": {"source": "kernels.hip", "sha256_16": "620d943fb2d1e74e",
+        "fetch_kib": 152474.8, "write_kib": 4096.0,
         "algorithmic_bytes": 309806592},
     "prefill32_bf16": {"source": "prefill.hip", "sha256_16": "64e07feb42ad9f32",
         "fetch_kib": 724296.0, "write_kib": 518320.2,
