@@ -431,6 +431,34 @@ pkv_status pkv_decode_attention(pkv_pool* pool, int32_t layer, int32_t n, const 
                                 const int32_t* page_table, int32_t pt_stride,
                                 const int32_t* seq_lens, float* out, void* stream);
 
+/* For callers that cannot allocate memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): pkv_decode_attention
+ * with no allocation of any kind, device or host.  Same arguments, checks,
+ * plan, kernels and result (bit for bit) as pkv_decode_attention; the split
+ * plan, the merge arrival counters and the split-K partials live in a
+ * library-owned device scratch array of PKV_NOALLOC_SCRATCH_BYTES per GPU
+ * (held from library load until the process ends), and the plan is built in
+ * fixed host arrays.  Limits: n <= PKV_NOALLOC_MAX_REQUESTS, at most
+ * PKV_NOALLOC_MAX_CHUNKS split chunks, n * num_heads <=
+ * PKV_NOALLOC_MAX_COUNTERS, and (split chunks) * num_heads * (head_width + 2)
+ * <= PKV_NOALLOC_MAX_PARTIAL_FLOATS; beyond them INVALID_ARGUMENT, with
+ * nothing enqueued.  Every call on one GPU shares that GPU's scratch (and the
+ * host arrays), which keeps the last call's contents: calls must not
+ * overlap -- two calls in flight on different streams, or from different
+ * threads, race.  A plan above 48 requests or 64 chunks is copied into the
+ * scratch from pageable host memory (so the call returns once the copy has
+ * read it); PKV_OPT_PROFILING records nothing for this call.  Errors: as
+ * pkv_decode_attention, and DEVICE. */
+#define PKV_NOALLOC_SCRATCH_BYTES 33554432
+#define PKV_NOALLOC_MAX_REQUESTS 4096
+#define PKV_NOALLOC_MAX_CHUNKS 32768
+#define PKV_NOALLOC_MAX_COUNTERS 262144
+#define PKV_NOALLOC_MAX_PARTIAL_FLOATS 7602176
+pkv_status pkv_decode_attention_noalloc(pkv_pool* pool, int32_t layer, int32_t n,
+                                        const void* q, const int32_t* page_table,
+                                        int32_t pt_stride, const int32_t* seq_lens, float* out,
+                                        void* stream);
+
 /* Batched prefill on caller page tables: request r appends counts[r] >= 1
  * rows at positions starts[r]..starts[r]+counts[r]-1 (starts[r] >= 0, the
  * last position below pt_stride * page_size), then each of them attends

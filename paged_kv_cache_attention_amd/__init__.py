@@ -144,6 +144,7 @@ SIGNATURES = {
     "pkv_plan_append_and_attend": (_I32, [_P, _I32, _P, _P, _P, _P, _P, _P]),
     "pkv_decode_attention": (_I32, [_P, _I32, _I32, _P, _P, _I32, _PI32, _P, _P]),
     "pkv_kv_append": (_I32, [_P, _I32, _I32, _P, _I32, _PI32, _P, _P, _P]),
+    "pkv_decode_attention_noalloc": (_I32, [_P, _I32, _I32, _P, _P, _I32, _PI32, _P, _P]),
 }
 
 
@@ -418,6 +419,21 @@ def pkv_decode_attention(pool: int, layer: int, q, page_table, pt_stride: int, s
            "pkv_decode_attention")
 
 
+PKV_NOALLOC_SCRATCH_BYTES = 33554432
+PKV_NOALLOC_MAX_REQUESTS = 4096
+PKV_NOALLOC_MAX_CHUNKS = 32768
+PKV_NOALLOC_MAX_COUNTERS = 262144
+PKV_NOALLOC_MAX_PARTIAL_FLOATS = 7602176
+
+
+def pkv_decode_attention_noalloc(pool: int, layer: int, q, page_table, pt_stride: int, seq_lens,
+                                 out, stream=None) -> None:
+    arr = _i32_array(seq_lens)
+    _check(_lib.pkv_decode_attention_noalloc(pool, layer, len(seq_lens), _ptr(q),
+                                             _ptr(page_table), pt_stride, arr, _ptr(out),
+                                             _stream(stream)), "pkv_decode_attention_noalloc")
+
+
 def pkv_kv_append(pool: int, layer: int, page_table, pt_stride: int, positions, k, v,
                   stream=None) -> None:
     arr = _i32_array(positions)
@@ -440,4 +456,6 @@ def pkv_prefill_attention(pool: int, layer: int, page_table, pt_stride: int, sta
 __all__ = [n for n in list(globals()) if n.startswith("pkv_")] + [
     "PkvError", "STATUS_NAMES", "PKV_DTYPE_F32", "PKV_DTYPE_BF16", "PKV_POOL_HOST_ONLY",
     "PKV_OPT_SPLIT_BLOCKS", "PKV_OPT_MERGE_MODE", "PKV_OPT_PROFILING", "PKV_OPT_WAVES", "PKV_MERGE_SEPARATE",
-    "PKV_MERGE_LAST_ARRIVER", "LIB_PATH", "SIGNATURES"]
+    "PKV_MERGE_LAST_ARRIVER", "LIB_PATH", "SIGNATURES", "PKV_NOALLOC_SCRATCH_BYTES",
+    "PKV_NOALLOC_MAX_REQUESTS", "PKV_NOALLOC_MAX_CHUNKS", "PKV_NOALLOC_MAX_COUNTERS",
+    "PKV_NOALLOC_MAX_PARTIAL_FLOATS"]

@@ -4,9 +4,9 @@ Run ``python paged_kv_cache_attention_amd/build.py`` (by path: importing the
 package would load the library being rebuilt); both libraries are written
 in-tree next to their sources.
 
-The kernels (kernels.hip, prefill.hip) and the host runtime (runtime.cpp)
-compile to separate objects under ``_build/``, in parallel, and link into
-libpkv.so.  The same kernel objects also link with a copy of the runtime
+The device sources (kernels.hip, prefill.hip, scratch.hip) and the host
+runtime (runtime.cpp) compile to separate objects under ``_build/``, in
+parallel, and link into libpkv.so.  The same kernel objects also link with a copy of the runtime
 built with AddressSanitizer and UndefinedBehaviorSanitizer on the host side
 only (``libpkv_san.so``), for the CPU tests of the allocator and the token
 transaction; device code is never built with a sanitizer.
@@ -40,7 +40,7 @@ SAN_FLAGS = ["-std=c++17", "-O1", "-g", "-fPIC", "-fno-omit-frame-pointer",
 LIBPKV = os.path.join(HERE, "libpkv.so")
 LIBPKV_SAN = os.path.join(HERE, "libpkv_san.so")
 LIBSYNTH = os.path.join(ROOT, "synth", "libsynth.so")
-KERNEL_SOURCES = ("kernels.hip", "prefill.hip")
+KERNEL_SOURCES = ("kernels.hip", "prefill.hip", "scratch.hip")
 
 
 def _run(cmd):
@@ -80,8 +80,8 @@ def _link(objs, target: str) -> str:
 
 
 def build_libpkv(sanitized: bool = True) -> str:
-    """Compiles the three sources in parallel and links libpkv.so (and, with
-    sanitized=True, libpkv_san.so from the same kernel objects)."""
+    """Compiles the sources in parallel and links libpkv.so (and, with
+    sanitized=True, libpkv_san.so from the same device objects)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
         kern = [ex.submit(_compile_device, n) for n in KERNEL_SOURCES]

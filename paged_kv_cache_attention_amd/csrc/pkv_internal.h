@@ -154,6 +154,25 @@ bool fast_width_native(int dtype, int head_width);
 // clear is ordered with the launches that follow on any stream kind).
 hipError_t launch_zero_i32(int32_t* p, int64_t count, hipStream_t stream);
 
+// Device scratch of the allocation-free decode call (scratch.hip): one
+// file-scope array per device, laid out as the plan (requests, work items,
+// split requests), the merge arrival counters and the split-K partials.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr size_t kScratchMetaOffset = 0;
+constexpr size_t kScratchMetaBytes = size_t(2) << 20;
+constexpr size_t kScratchCountersOffset = kScratchMetaBytes;
+constexpr size_t kScratchCountersBytes = size_t(1) << 20;
+constexpr size_t kScratchPartialsOffset = kScratchCountersOffset + kScratchCountersBytes;
+constexpr size_t kScratchPartialsBytes = kScratchBytes - kScratchPartialsOffset;
+constexpr int kScratchMaxReqs = 4096;
+constexpr int kScratchMaxItems = 32768;
+static_assert(kScratchMaxReqs * sizeof(ReqEntry) + kScratchMaxItems * sizeof(WorkItem) +
+                      kScratchMaxReqs * sizeof(int32_t) <= kScratchMetaBytes,
+              "the largest plan fits the scratch's plan region");
+// The scratch's device address on `device`, which must be the current
+// device: looked up once per device, then cached.
+hipError_t scratch_address(int device, void** out);
+
 // Prefill on matrix cores (bf16 head width 64, 128 or 256; float32 32, 64 or
 // 128; pages of a multiple of 16 rows): an append launch writes the chunk's
 // rows, then an attention launch runs the causal attention of every (tile,

@@ -541,26 +541,41 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
   return PKV_OK;
 }
 
-AttnArgs make_args(const pkv_plan* pl, int32_t layer, const int32_t* page_table,
-                   const void* q, const void* k, const void* v, float* out, bool fuse) {
-  const pkv_pool* p = pl->pool;
+// A built plan as the kernels see it: its host copy (for inline plans),
+// where its device copy and buffers are, and its launch shape.
+struct PlanView {
+  const ReqEntry* reqs;
+  int32_t n;
+  const WorkItem* items;
+  int32_t num_items;
+  int32_t pt_stride;
+  int32_t waves;
+  bool inline_plan;
+  const char* d_meta;  // requests, then work items, then split requests
+  float* d_partials;
+  int32_t* d_counters;
+};
+
+AttnArgs make_args_view(const pkv_pool* p, const PlanView& v, int32_t layer,
+                        const int32_t* page_table, const void* q, const void* k,
+                        const void* vv, float* out, bool fuse) {
   AttnArgs a{};
   a.q = q;
   a.k_new = k;
-  a.v_new = v;
+  a.v_new = vv;
   a.out = out;
   a.k_layer = static_cast<char*>(p->desc.k_storage) + (int64_t)layer * p->layer_bytes;
   a.v_layer = static_cast<char*>(p->desc.v_storage) + (int64_t)layer * p->layer_bytes;
   a.page_table = page_table;
-  a.pt_stride = pl->pt_stride;
-  a.reqs = reinterpret_cast<const ReqEntry*>(pl->d_meta);
-  a.items = reinterpret_cast<const WorkItem*>(pl->d_meta + pl->reqs.size() * sizeof(ReqEntry));
-  a.partials = pl->d_partials;
-  a.merge_count = pl->d_counters;
-  a.merge_reqs = reinterpret_cast<const int32_t*>(pl->d_meta + pl->reqs.size() * sizeof(ReqEntry) +
-                                                  pl->items.size() * sizeof(WorkItem));
+  a.pt_stride = v.pt_stride;
+  a.reqs = reinterpret_cast<const ReqEntry*>(v.d_meta);
+  a.items = reinterpret_cast<const WorkItem*>(v.d_meta + (size_t)v.n * sizeof(ReqEntry));
+  a.partials = v.d_partials;
+  a.merge_count = v.d_counters;
+  a.merge_reqs = reinterpret_cast<const int32_t*>(v.d_meta + (size_t)v.n * sizeof(ReqEntry) +
+                                                  (size_t)v.num_items * sizeof(WorkItem));
   a.merge_mode = p->merge_mode;
-  a.waves = pl->waves;
+  a.waves = v.waves;
   a.num_heads = p->desc.num_heads;
   a.num_kv_heads = p->desc.num_kv_heads;
   a.page_size = p->desc.page_size;
@@ -570,12 +585,20 @@ AttnArgs make_args(const pkv_plan* pl, int32_t layer, const int32_t* page_table,
   a.head_bytes = p->head_bytes;
   a.scale_log2e = (float)(1.4426950408889634 / std::sqrt((double)p->desc.head_width));
   a.num_inline = 0;
-  if (pl->inline_plan) {
-    a.num_inline = (int32_t)pl->items.size();
-    std::memcpy(a.inline_reqs, pl->reqs.data(), pl->reqs.size() * sizeof(ReqEntry));
-    std::memcpy(a.inline_items, pl->items.data(), pl->items.size() * sizeof(WorkItem));
+  if (v.inline_plan) {
+    a.num_inline = v.num_items;
+    std::memcpy(a.inline_reqs, v.reqs, (size_t)v.n * sizeof(ReqEntry));
+    std::memcpy(a.inline_items, v.items, (size_t)v.num_items * sizeof(WorkItem));
   }
   return a;
+}
+
+AttnArgs make_args(const pkv_plan* pl, int32_t layer, const int32_t* page_table,
+                   const void* q, const void* k, const void* v, float* out, bool fuse) {
+  const PlanView view{pl->reqs.data(), (int32_t)pl->reqs.size(), pl->items.data(),
+                      (int32_t)pl->items.size(), pl->pt_stride, pl->waves, pl->inline_plan,
+                      pl->d_meta, pl->d_partials, pl->d_counters};
+  return make_args_view(pl->pool, view, layer, page_table, q, k, v, out, fuse);
 }
 
 pkv_status check_ptr(const void* ptr, const char* name) {
@@ -851,6 +874,36 @@ pkv_status txn_step(pkv_cache* const* caches, int32_t n, int32_t layer, const vo
     caches[i]->appended_count += 1;
   }
   return ok();
+}
+
+// ---- the allocation-free decode call's plan --------------------------------
+// Fixed host arrays (no heap): the plan is built here, then copied into the
+// device scratch's plan region in one copy from na_stage.  Shared by every
+// call, like the device scratch itself.
+ReqEntry na_reqs[pkv::kScratchMaxReqs];
+WorkItem na_items[pkv::kScratchMaxItems];
+WorkItem na_tmp[pkv::kScratchMaxItems];
+int32_t na_merge[pkv::kScratchMaxReqs];
+char na_stage[pkv::kScratchMetaBytes];
+
+// Stable sort of items[0..m) by decreasing chunk length, bottom-up merge
+// sort through tmp (no allocation): the order plan_build's stable_sort
+// gives, so both calls launch identical plans.
+void sort_longest_first(WorkItem* items, WorkItem* tmp, int32_t m) {
+  auto len = [](const WorkItem& w) { return w.blk_end - w.blk_begin; };
+  WorkItem* src = items;
+  WorkItem* dst = tmp;
+  for (int32_t width = 1; width < m; width *= 2) {
+    for (int32_t lo = 0; lo < m; lo += 2 * width) {
+      const int32_t mid = std::min(lo + width, m), hi = std::min(lo + 2 * width, m);
+      int32_t i = lo, j = mid, k = lo;
+      while (i < mid && j < hi) dst[k++] = len(src[j]) > len(src[i]) ? src[j++] : src[i++];
+      while (i < mid) dst[k++] = src[i++];
+      while (j < hi) dst[k++] = src[j++];
+    }
+    std::swap(src, dst);
+  }
+  if (src != items) std::memcpy(items, src, (size_t)m * sizeof(WorkItem));
 }
 
 }  // namespace
@@ -1454,6 +1507,106 @@ pkv_status pkv_decode_attention(pkv_pool* p, int32_t layer, int32_t n, const voi
   if ((st = plan_build(&p->call_plan, n, rows.data(), seq_lens, pt_stride, s)) != PKV_OK) return st;
   st = run_attention(&p->call_plan, layer, page_table, q, nullptr, nullptr, out, false, s);
   return st == PKV_OK ? ok() : st;
+}
+
+pkv_status pkv_decode_attention_noalloc(pkv_pool* p, int32_t layer, int32_t n, const void* q,
+                                        const int32_t* page_table, int32_t pt_stride,
+                                        const int32_t* seq_lens, float* out, void* stream) {
+  static_assert(PKV_NOALLOC_SCRATCH_BYTES == pkv::kScratchBytes, "scratch size");
+  static_assert(PKV_NOALLOC_MAX_REQUESTS == pkv::kScratchMaxReqs, "scratch requests");
+  static_assert(PKV_NOALLOC_MAX_CHUNKS == pkv::kScratchMaxItems, "scratch chunks");
+  static_assert(PKV_NOALLOC_MAX_COUNTERS * sizeof(int32_t) == pkv::kScratchCountersBytes,
+                "scratch counters");
+  static_assert(PKV_NOALLOC_MAX_PARTIAL_FLOATS * sizeof(float) == pkv::kScratchPartialsBytes,
+                "scratch partials");
+  if (!p || !seq_lens || n < 1 || pt_stride < 1)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "null pool/seq_lens or non-positive n/pt_stride");
+  pkv_status st = check_layer(p, layer);
+  if (st != PKV_OK) return st;
+  if (!page_table) return fail(PKV_ERR_INVALID_ARGUMENT, "page_table is null");
+  if ((st = check_ptr(q, "q")) != PKV_OK || (st = check_ptr(out, "out")) != PKV_OK) return st;
+  const int64_t H = p->desc.num_heads, D = p->desc.head_width;
+  if (n > pkv::kScratchMaxReqs)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%d requests exceed the scratch's %d", n,
+                pkv::kScratchMaxReqs);
+  if ((int64_t)n * H > PKV_NOALLOC_MAX_COUNTERS)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%d requests x %lld heads exceed the scratch's %d "
+                "merge counters", n, (long long)H, PKV_NOALLOC_MAX_COUNTERS);
+  const int64_t max_len = (int64_t)pt_stride * p->desc.page_size;
+  int64_t total_blocks = 0;
+  uint64_t rows_attended = 0;
+  for (int32_t r = 0; r < n; ++r) {
+    if (seq_lens[r] < 1 || seq_lens[r] > max_len)
+      return fail(PKV_ERR_INVALID_ARGUMENT, "seq_lens[%d]=%d outside [1, %lld]", r, seq_lens[r],
+                  (long long)max_len);
+    total_blocks += (seq_lens[r] + pkv::kBlockRows - 1) / pkv::kBlockRows;
+    rows_attended += (uint64_t)seq_lens[r];
+  }
+  // The plan of pkv_decode_attention, built into the fixed arrays.
+  const SplitChoice choice = choose_split(p, n, total_blocks);
+  int32_t m = 0, slots = 0, nmerge = 0;
+  for (int32_t r = 0; r < n; ++r) {
+    const int32_t blocks = (seq_lens[r] + pkv::kBlockRows - 1) / pkv::kBlockRows;
+    const int32_t nsplit = (int32_t)(((int64_t)blocks + choice.chunk - 1) / choice.chunk);
+    if ((int64_t)m + nsplit > pkv::kScratchMaxItems)
+      return fail(PKV_ERR_INVALID_ARGUMENT, "the plan needs more than the scratch's %d chunks",
+                  pkv::kScratchMaxItems);
+    na_reqs[r] = ReqEntry{r, seq_lens[r], nsplit, nsplit > 1 ? slots : -1};
+    if (nsplit > 1) {
+      slots += nsplit;
+      na_merge[nmerge++] = r;
+    }
+    const int32_t base = blocks / nsplit, extra = blocks % nsplit;
+    int32_t b0 = 0;
+    for (int32_t s = 0; s < nsplit; ++s) {
+      const int32_t b1 = b0 + base + (s < extra ? 1 : 0);
+      na_items[m++] = WorkItem{r, b0, b1, s, na_reqs[r]};
+      b0 = b1;
+    }
+  }
+  if ((int64_t)slots * H * (D + 2) > PKV_NOALLOC_MAX_PARTIAL_FLOATS)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%d split chunks x %lld heads x %lld floats exceed the "
+                "scratch's %d partial floats", slots, (long long)H, (long long)(D + 2),
+                PKV_NOALLOC_MAX_PARTIAL_FLOATS);
+  if ((int64_t)m * H > std::numeric_limits<int32_t>::max())
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%d chunks x %lld heads exceed one launch", m,
+                (long long)H);
+  sort_longest_first(na_items, na_tmp, m);
+  p->counters.kv_bytes_read += rows_attended * (uint64_t)p->desc.num_kv_heads * 2ull *
+                               (uint64_t)D * p->elt;
+  if (p->host_only) return ok();
+
+  int dev = 0;
+  PKV_HIP_TRY(hipGetDevice(&dev));
+  if (p->device >= 0 && dev != p->device)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "pool lives on device %d, current device is %d",
+                p->device, dev);
+  void* base = nullptr;
+  PKV_HIP_TRY(pkv::scratch_address(dev, &base));
+  char* scratch = static_cast<char*>(base);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool inline_plan = n <= pkv::kInlineReqs && m <= pkv::kInlineItems;
+  const bool separate = slots > 0 && p->merge_mode == pkv::kMergeSeparate;
+  char* d_meta = scratch + pkv::kScratchMetaOffset;
+  if (!inline_plan || separate) {
+    // one copy from fixed host memory: requests, work items, split requests
+    const size_t rb = (size_t)n * sizeof(ReqEntry), ib = (size_t)m * sizeof(WorkItem);
+    std::memcpy(na_stage, na_reqs, rb);
+    std::memcpy(na_stage + rb, na_items, ib);
+    std::memcpy(na_stage + rb + ib, na_merge, (size_t)nmerge * sizeof(int32_t));
+    PKV_HIP_TRY(hipMemcpyAsync(d_meta, na_stage, rb + ib + (size_t)nmerge * sizeof(int32_t),
+                               hipMemcpyHostToDevice, s));
+  }
+  int32_t* d_counters = reinterpret_cast<int32_t*>(scratch + pkv::kScratchCountersOffset);
+  if (slots > 0 && !separate)  // the last-arriver merge counts from zero
+    PKV_HIP_TRY(pkv::launch_zero_i32(d_counters, (int64_t)n * H, s));
+  const PlanView view{na_reqs, n, na_items, m, pt_stride, choice.waves, inline_plan, d_meta,
+                      reinterpret_cast<float*>(scratch + pkv::kScratchPartialsOffset),
+                      d_counters};
+  const AttnArgs a = make_args_view(p, view, layer, page_table, q, nullptr, nullptr, out, false);
+  PKV_HIP_TRY(pkv::launch_attention(a, p->desc.kv_dtype, m, s, nullptr));
+  if (separate) PKV_HIP_TRY(pkv::launch_merge(a, nmerge, s));
+  return ok();
 }
 
 pkv_status pkv_prefill_attention(pkv_pool* p, int32_t layer, int32_t n,

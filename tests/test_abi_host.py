@@ -630,3 +630,23 @@ def test_prefill_call_validates_ranges_host_only():
                      0) == Status.INVALID_ARGUMENT   # layer out of range
     assert pkv.pkv_pool_get_counters(p).kv_bytes_read > 0
     pkv.pkv_pool_destroy(p)
+
+
+def test_noalloc_decode_limits_on_host():
+    # the allocation-free call validates like pkv_decode_attention and
+    # rejects plans beyond its fixed scratch before any work
+    p = make_pool(pages=64, ctx=1024, heads=4, width=128, dtype=1)
+    pkv.pkv_decode_attention_noalloc(p, 0, FAKE, FAKE, 64, [100, 16, 33], FAKE, stream=0)
+    assert status_of(pkv.pkv_decode_attention_noalloc, p, 0, FAKE, FAKE, 64, [0], FAKE,
+                     0) == Status.INVALID_ARGUMENT
+    assert status_of(pkv.pkv_decode_attention_noalloc, p, 2, FAKE, FAKE, 64, [5], FAKE,
+                     0) == Status.INVALID_ARGUMENT
+    assert status_of(pkv.pkv_decode_attention_noalloc, p, 0, FAKE, FAKE, 64,
+                     [1] * (pkv.PKV_NOALLOC_MAX_REQUESTS + 1), FAKE, 0) == Status.INVALID_ARGUMENT
+    pkv.pkv_pool_set_option(p, pkv.PKV_OPT_SPLIT_BLOCKS, 1)
+    # 8 x 64 one-block chunks: 512 chunks x 4 heads x 130 floats fit
+    pkv.pkv_decode_attention_noalloc(p, 0, FAKE, FAKE, 64, [1024] * 8, FAKE, stream=0)
+    # 4000 x 64 chunks exceed the scratch's 32768 chunks
+    assert status_of(pkv.pkv_decode_attention_noalloc, p, 0, FAKE, FAKE, 64, [1024] * 4000,
+                     FAKE, 0) == Status.INVALID_ARGUMENT
+    pkv.pkv_pool_destroy(p)
