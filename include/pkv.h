@@ -157,11 +157,19 @@ typedef enum pkv_option {
                                inside the attention kernel; 0: a separate
                                merge kernel after it                            */
   PKV_OPT_PROFILING = 3,    /* 1: record kernel timing events; 0: stop         */
-  PKV_OPT_WAVES = 4         /* waves per workgroup of the fast paths: 4, 8,
+  PKV_OPT_WAVES = 4,        /* waves per workgroup of the fast paths: 4, 8,
                                16 (the multi-head kernel for d_h <= 64; other
                                kernels then take 8), or 0
                                (default) to choose per kernel and batch (the
                                plan then picks its split as well)               */
+  PKV_OPT_VALIDATE = 5      /* 1: debug mode -- before a call that takes a
+                               caller page table enqueues anything, read back
+                               each request's entries up to the last row the
+                               call touches and reject any outside
+                               [0, num_pages) with INVALID_ARGUMENT (this
+                               waits for the stream); 0 (default): the caller
+                               guarantees the entries.  Not applied by the
+                               allocation-free call.                            */
 } pkv_option;
 
 /* Library version "major.minor.patch"; static string.  ("Incremental

@@ -166,6 +166,7 @@ struct pkv_pool {
   int32_t waves_option = 0;
   uint64_t opt_gen = 0;  // bumped by every option that changes a plan's shape
   bool profiling = false;
+  bool validate = false;  // debug: check caller page-table entries before use
   enum TimedKind { kTimedAttention, kTimedMerge, kTimedPrefill };
   struct Timed {
     hipEvent_t start, end;
@@ -605,6 +606,45 @@ pkv_status check_ptr(const void* ptr, const char* name) {
   if (!ptr) return fail(PKV_ERR_INVALID_ARGUMENT, "%s is null", name);
   if (!aligned16(ptr)) return fail(PKV_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
   return PKV_OK;
+}
+
+// Debug validation of a caller's device page table: entries [0, used[i]) of
+// row rows[i] are read back (waiting for the stream, so earlier writes to the
+// table on it are seen) and must name pages of the pool.
+pkv_status validate_table(const pkv_pool* p, const int32_t* page_table, int32_t pt_stride,
+                          int32_t n, const int32_t* rows, const int32_t* used,
+                          hipStream_t stream) {
+  if (!p->validate || p->host_only) return PKV_OK;
+  int32_t max_row = 0;
+  for (int32_t i = 0; i < n; ++i) max_row = std::max(max_row, rows[i]);
+  std::vector<int32_t> host((size_t)(max_row + 1) * pt_stride);
+  PKV_HIP_TRY(hipMemcpyAsync(host.data(), page_table, host.size() * sizeof(int32_t),
+                             hipMemcpyDeviceToHost, stream));
+  PKV_HIP_TRY(hipStreamSynchronize(stream));
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t* row = host.data() + (size_t)rows[i] * pt_stride;
+    for (int32_t j = 0; j < used[i]; ++j)
+      if (row[j] < 0 || row[j] >= p->desc.num_pages)
+        return fail(PKV_ERR_INVALID_ARGUMENT,
+                    "page_table[%d][%d] = %d is not a page of the pool (0..%d); request %d",
+                    rows[i], j, row[j], p->desc.num_pages - 1, i);
+  }
+  return PKV_OK;
+}
+
+// validate_table for a built decode plan: each request reads the pages of
+// its t rows.
+pkv_status validate_plan_table(const pkv_plan* pl, const int32_t* page_table,
+                               hipStream_t stream) {
+  const pkv_pool* p = pl->pool;
+  if (!p->validate || p->host_only) return PKV_OK;
+  std::vector<int32_t> rows(pl->reqs.size()), used(pl->reqs.size());
+  for (size_t i = 0; i < pl->reqs.size(); ++i) {
+    rows[i] = pl->reqs[i].pt_row;
+    used[i] = (pl->reqs[i].seq_len + p->desc.page_size - 1) / p->desc.page_size;
+  }
+  return validate_table(p, page_table, pl->pt_stride, (int32_t)rows.size(), rows.data(),
+                        used.data(), stream);
 }
 
 hipEvent_t take_event(pkv_pool* p) {
@@ -1047,6 +1087,10 @@ pkv_status pkv_pool_set_option(pkv_pool* p, int32_t option, int64_t value) {
       if (value != 0 && value != 1) return fail(PKV_ERR_INVALID_ARGUMENT, "profiling %lld", (long long)value);
       p->profiling = value == 1;
       return ok();
+    case PKV_OPT_VALIDATE:
+      if (value != 0 && value != 1) return fail(PKV_ERR_INVALID_ARGUMENT, "validate %lld", (long long)value);
+      p->validate = value == 1;
+      return ok();
     default:
       return fail(PKV_ERR_INVALID_ARGUMENT, "unknown option %d", option);
   }
@@ -1463,6 +1507,8 @@ pkv_status pkv_plan_decode_attention(pkv_plan* pl, int32_t layer, const void* q,
   pkv_status st = plan_ready(pl, layer, page_table, stream);
   if (st != PKV_OK) return st;
   if ((st = check_ptr(q, "q")) != PKV_OK || (st = check_ptr(out, "out")) != PKV_OK) return st;
+  if ((st = validate_plan_table(pl, page_table, static_cast<hipStream_t>(stream))) != PKV_OK)
+    return st;
   st = run_attention(pl, layer, page_table, q, nullptr, nullptr, out, false,
                      static_cast<hipStream_t>(stream));
   return st == PKV_OK ? ok() : st;
@@ -1473,6 +1519,8 @@ pkv_status pkv_plan_kv_append(pkv_plan* pl, int32_t layer, const int32_t* page_t
   pkv_status st = plan_ready(pl, layer, page_table, stream);
   if (st != PKV_OK) return st;
   if ((st = check_ptr(k, "k")) != PKV_OK || (st = check_ptr(v, "v")) != PKV_OK) return st;
+  if ((st = validate_plan_table(pl, page_table, static_cast<hipStream_t>(stream))) != PKV_OK)
+    return st;
   if (pl->pool->host_only) return ok();
   AttnArgs a = make_args(pl, layer, page_table, nullptr, k, v, nullptr, false);
   PKV_HIP_TRY(pkv::launch_kv_append(a, pl->pool->desc.kv_dtype, pl->n,
@@ -1487,6 +1535,8 @@ pkv_status pkv_plan_append_and_attend(pkv_plan* pl, int32_t layer, const int32_t
   if (st != PKV_OK) return st;
   if ((st = check_ptr(q, "q")) != PKV_OK || (st = check_ptr(k, "k")) != PKV_OK ||
       (st = check_ptr(v, "v")) != PKV_OK || (st = check_ptr(out, "out")) != PKV_OK)
+    return st;
+  if ((st = validate_plan_table(pl, page_table, static_cast<hipStream_t>(stream))) != PKV_OK)
     return st;
   st = run_attention(pl, layer, page_table, q, k, v, out, true, static_cast<hipStream_t>(stream));
   return st == PKV_OK ? ok() : st;
@@ -1505,6 +1555,7 @@ pkv_status pkv_decode_attention(pkv_pool* p, int32_t layer, int32_t n, const voi
   for (int32_t r = 0; r < n; ++r) rows[r] = r;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = plan_build(&p->call_plan, n, rows.data(), seq_lens, pt_stride, s)) != PKV_OK) return st;
+  if ((st = validate_plan_table(&p->call_plan, page_table, s)) != PKV_OK) return st;
   st = run_attention(&p->call_plan, layer, page_table, q, nullptr, nullptr, out, false, s);
   return st == PKV_OK ? ok() : st;
 }
@@ -1621,8 +1672,18 @@ pkv_status pkv_prefill_attention(pkv_pool* p, int32_t layer, int32_t n,
   if ((st = check_ptr(q, "q")) != PKV_OK || (st = check_ptr(k, "k")) != PKV_OK ||
       (st = check_ptr(v, "v")) != PKV_OK || (st = check_ptr(out, "out")) != PKV_OK)
     return st;
-  std::vector<int32_t> rows(n);
-  for (int32_t r = 0; r < n; ++r) rows[r] = r;
+  std::vector<int32_t> rows(n), used(n);
+  for (int32_t r = 0; r < n; ++r) {
+    rows[r] = r;
+    if (counts[r] < 1 || starts[r] < 0 ||
+        (int64_t)starts[r] + counts[r] > (int64_t)pt_stride * p->desc.page_size)
+      return fail(PKV_ERR_INVALID_ARGUMENT, "request %d: rows [%d, %d + %d) outside [0, %lld)", r,
+                  starts[r], starts[r], counts[r], (long long)pt_stride * p->desc.page_size);
+    used[r] = (starts[r] + counts[r] + p->desc.page_size - 1) / p->desc.page_size;
+  }
+  if ((st = validate_table(p, page_table, pt_stride, n, rows.data(), used.data(),
+                           static_cast<hipStream_t>(stream))) != PKV_OK)
+    return st;
   st = run_prefill(p, n, rows.data(), starts, counts, pt_stride, layer, page_table, q, k, v, out,
                    static_cast<hipStream_t>(stream));
   return st == PKV_OK ? ok() : st;
@@ -1646,6 +1707,7 @@ pkv_status pkv_kv_append(pkv_pool* p, int32_t layer, int32_t n, const int32_t* p
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = plan_build(&p->call_plan, n, rows.data(), lens.data(), pt_stride, s)) != PKV_OK)
     return st;
+  if ((st = validate_plan_table(&p->call_plan, page_table, s)) != PKV_OK) return st;
   if (p->host_only) return ok();
   AttnArgs a = make_args(&p->call_plan, layer, page_table, nullptr, k, v, nullptr, false);
   PKV_HIP_TRY(pkv::launch_kv_append(a, p->desc.kv_dtype, n, s));

@@ -650,3 +650,13 @@ def test_noalloc_decode_limits_on_host():
     assert status_of(pkv.pkv_decode_attention_noalloc, p, 0, FAKE, FAKE, 64, [1024] * 4000,
                      FAKE, 0) == Status.INVALID_ARGUMENT
     pkv.pkv_pool_destroy(p)
+
+
+def test_validate_option_values():
+    p = make_pool()
+    for v in (1, 0):
+        pkv.pkv_pool_set_option(p, pkv.PKV_OPT_VALIDATE, v)
+    for v in (2, -1):
+        assert status_of(pkv.pkv_pool_set_option, p, pkv.PKV_OPT_VALIDATE, v) == \
+            Status.INVALID_ARGUMENT
+    pkv.pkv_pool_destroy(p)

@@ -798,6 +798,68 @@ def test_empty_and_oversized_inputs_rejected():
     pkv.pkv_pool_destroy(pool)
 
 
+def test_debug_validation_rejects_bad_page_ids_before_any_work():
+    """With PKV_OPT_VALIDATE, an entry a call would read that is not a page
+    of the pool is rejected before anything is enqueued; entries past the
+    rows a request reads are not looked at.  The pool is declared four pages
+    smaller than its storage, so the rejected IDs (the pool's size and one
+    more) still lie inside the allocation."""
+    w = _small("validate", "bf16", 128, 16, [40, 17, 3], heads=4, layers=1, extra_pages=8)
+    kp, vp = device_pool(w)
+    d = pkv.pkv_pool_desc_init()
+    d.num_layers, d.num_heads, d.head_width, d.page_size = 1, w.heads, 128, 16
+    d.num_pages, d.max_context, d.kv_dtype = w.num_pages - 4, w.pt_stride * 16, pkv.PKV_DTYPE_BF16
+    d.k_storage, d.v_storage = kp.data_ptr(), vp.data_ptr()
+    pool = pkv.pkv_pool_create(d)
+    pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_VALIDATE, 1)
+    good = w.page_tables.copy()
+    # keep every read entry inside the declared pool
+    used = sorted({int(x) for r, t in enumerate(w.lengths.tolist())
+                   for x in good[r][: -(-t // 16)]})
+    remap = {old: i for i, old in enumerate(used)}
+    for r, t in enumerate(w.lengths.tolist()):
+        for j in range(-(-t // 16)):
+            good[r, j] = remap[int(good[r, j])]
+    good[2, 1:] = -7                      # request 2 reads one page: the rest is unread
+    q = rows_to_device(w.q(0), "bf16")
+    k, v = rows_to_device(w.k_new(0), "bf16"), rows_to_device(w.v_new(0), "bf16")
+    pt = torch.from_numpy(good).cuda()
+    out = torch.full((w.n, w.heads, 128), float("nan"), device="cuda")
+    pkv.pkv_decode_attention(pool, 0, q, pt, w.pt_stride, w.lengths.tolist(), out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    T = 12
+    qc, kc, vc = (torch.zeros((T, w.heads, 128), dtype=torch.bfloat16, device="cuda")
+                  for _ in range(3))
+    for bad_value in (w.num_pages - 4, w.num_pages - 3):
+        bad = good.copy()
+        bad[0, 2] = bad_value             # request 0 (40 rows) reads entries 0..2
+        ptb = torch.from_numpy(bad).cuda()
+        sentinel = torch.full((w.n, w.heads, 128), 7.0, device="cuda")
+        sentinel_c = torch.full((T, w.heads, 128), 7.0, device="cuda")
+        plan = pkv.pkv_plan_create(pool)
+        pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
+        calls = [
+            lambda: pkv.pkv_decode_attention(pool, 0, q, ptb, w.pt_stride, w.lengths.tolist(),
+                                             sentinel),
+            lambda: pkv.pkv_kv_append(pool, 0, ptb, w.pt_stride, (w.lengths - 1).tolist(), k, v),
+            lambda: pkv.pkv_prefill_attention(pool, 0, ptb, w.pt_stride, [30, 0, 0], [10, 1, 1],
+                                              qc, kc, vc, sentinel_c),
+            lambda: pkv.pkv_plan_decode_attention(plan, 0, q, ptb, sentinel),
+            lambda: pkv.pkv_plan_kv_append(plan, 0, ptb, k, v),
+            lambda: pkv.pkv_plan_append_and_attend(plan, 0, ptb, q, k, v, sentinel),
+        ]
+        for call in calls:
+            with pytest.raises(pkv.PkvError) as e:
+                call()
+            assert e.value.status == pkv.PKV_ERR_INVALID_ARGUMENT
+            assert "not a page of the pool" in str(e.value)
+        torch.cuda.synchronize()
+        assert bool((sentinel == 7.0).all()) and bool((sentinel_c == 7.0).all())
+        pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(pool)
+
+
 def test_maximum_head_width_generic():
     w = _small("wide", "f32", 1024, 16, [1, 70, 129], heads=2, layers=1)
     kp, vp = device_pool(w)
