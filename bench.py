@@ -51,23 +51,23 @@ HBM_PEAK_GBS = 8000.0
 # file under csrc/).
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
-    "fullstep128_bf16_l32": {"source": "kernels.hip", "sha256_16": "620d943fb2d1e74e",
-        "fetch_kib": 2073954.0, "write_kib": 18562.9,
+    "fullstep128_bf16_l32": {"source": "kernels.hip", "sha256_16": "6eb8f22e35066277",
+        "fetch_kib": 2071995.1, "write_kib": 18504.4,
         "algorithmic_bytes": 4238041600},
-    "batch32_fp32_l12": {"source": "kernels.hip", "sha256_16": "620d943fb2d1e74e",
-        "fetch_kib": 44162.4, "write_kib": 292.0,
+    "batch32_fp32_l12": {"source": "kernels.hip", "sha256_16": "6eb8f22e35066277",
+        "fetch_kib": 44102.3, "write_kib": 292.0,
         "algorithmic_bytes": 88676352},
-    "batch256_bf16": {"source": "kernels.hip", "sha256_16": "620d943fb2d1e74e",
-        "fetch_kib": 4761780.4, "write_kib": 4345.3,
+    "batch256_bf16": {"source": "kernels.hip", "sha256_16": "6eb8f22e35066277",
+        "fetch_kib": 4759803.2, "write_kib": 4125.4,
         "algorithmic_bytes": 9718775808},
-    "skewed64_bf16": {"source": "kernels.hip", "sha256_16": "620d943fb2d1e74e",
-        "fetch_kib": 1792457.1, "write_kib": 15723.8,
+    "skewed64_bf16": {"source": "kernels.hip", "sha256_16": "6eb8f22e35066277",
+        "fetch_kib": 1791420.2, "write_kib": 15720.0,
         "algorithmic_bytes": 3659710464},
-    "batch256_gqa8_bf16": {"source": "kernels.hip", "sha256_16": "620d943fb2d1e74e",
-        "fetch_kib": 1194386.5, "write_kib": 4097.0,
+    "batch256_gqa8_bf16": {"source": "kernels.hip", "sha256_16": "6eb8f22e35066277",
+        "fetch_kib": 1192093.3, "write_kib": 4096.1,
         "algorithmic_bytes": 2434412544},
-    "batch256_mqa_bf16": {"source": "kernels.hip", "sha256_16": "620d943fb2d1e74e",
-        "fetch_kib": 152474.8, "write_kib": 4096.0,
+    "batch256_mqa_bf16": {"source": "kernels.hip", "sha256_16": "6eb8f22e35066277",
+        "fetch_kib": 152582.2, "write_kib": 4096.0,
         "algorithmic_bytes": 309806592},
     "prefill32_bf16": {"source": "prefill.hip", "sha256_16": "64e07feb42ad9f32",
         "fetch_kib": 724296.0, "write_kib": 518320.2,
@@ -391,14 +391,16 @@ def dominant_kernel(w) -> str:
     """The attention kernel the library dispatches for a decode workload: the
     matrix-core grouped kernel for bf16 d_h of 64, 128 or 256 when a
     multiple of 4 query heads share a K/V head (template arguments: heads per
-    workgroup, waves per workgroup, d_h), else the vector fast path."""
+    workgroup, waves per workgroup, d_h), else the vector fast path; ",nt"
+    when its K/V loads are non-temporal (each block read by one workgroup)."""
     group = w.heads // w.hkv
     D = w.head_width
     if w.dtype == "bf16" and D in (64, 128, 256) and w.page_size % 16 == 0 and group % 4 == 0:
         share = next(s for s in (16, 8, 4) if group % s == 0)
         waves = 8 if share >= 8 and D != 256 else 4
-        return f"attend_group_mfma_kernel<{share},{waves},{D}>"
-    return f"attend_fast_kernel<{'float' if w.dtype == 'f32' else 'bf16'},{D}>"
+        nt = ",nt" if group == share else ""
+        return f"attend_group_mfma_kernel<{share},{waves},{D}{nt}>"
+    return f"attend_fast_kernel<{'float' if w.dtype == 'f32' else 'bf16'},{D},nt>"
 
 
 def prefill_bench(args, w, baseline):
