@@ -18,10 +18,14 @@ between device synchronisations, nothing but the steps on the stream).
 the same number of steps in which the library records HIP events on the
 launch stream immediately around every attention kernel (PKV_OPT_PROFILING)
 and sums each launch's algorithmic bytes (for workloads whose step is a
-single launch, the duration comes instead from one event pair around the
-same number of back-to-back launches, free of per-kernel event packets);
-it also repeats the whole-step rate, which the kernel-only rate must not
-fall below.  ``cpu_baseline`` is
+single launch, the duration comes instead from one event pair around
+back-to-back launches, at least as many as the timed steps and at least
+~50 ms of them, free of per-kernel event packets); it also repeats the
+whole-step rate and says whether the kernel-only rate is at least that (for
+short multi-layer launches it can fall just below: the event pair around a
+launch adds about a microsecond to what it measures, e.g. 20.8 us per launch
+against 19.4 us per layer of whole-step wall clock on the 12-layer float32
+step).  ``cpu_baseline`` is
 the float64 oracle on the host's cores, timed before the GPU is touched.
 
 Other workloads (--workload): batch32_fp32_l12 (32 requests, 12 layers,
@@ -284,21 +288,28 @@ def main():
     # time per launch with no event packet between them (per-kernel events
     # cost a few microseconds each).  Multi-layer steps keep the per-kernel
     # events: host work and other kernels sit between their launches.
+    # At least ~50 ms of launches, so a step of tens of microseconds is not
+    # timed over a couple of milliseconds only.
     batch_s = None
+    batch_launches = 0
     if not args.no_kernel_events and not transactional:
+        batch_launches = max(args.steps, int(0.05 / max(elapsed / args.steps, 1e-6)) + 1)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
-        for _ in range(args.steps):
+        for _ in range(batch_launches):
             step(False)
         e1.record(stream)
         torch.cuda.synchronize()
-        batch_s = e0.elapsed_time(e1) / 1e3 / args.steps
+        batch_s = e0.elapsed_time(e1) / 1e3 / batch_launches
     # Pass 3: one stream event between successive steps -> per-step spread.
     spread = step_spread(lambda: step(False), args.steps)
     launches = prof.attention_launches if prof else 0
     event_kern_s = prof.attention_ms / max(1, launches) / 1e3 if prof else 0.0
-    avg_kern_s = batch_s if batch_s is not None else event_kern_s
+    if batch_s is not None:
+        avg_kern_s, timing = batch_s, "one event pair around back-to-back launches"
+    else:
+        avg_kern_s, timing = event_kern_s, "event pair around each attention launch"
     bytes_per_launch = prof.algorithmic_bytes / max(1, launches) if prof else 0.0
     achieved = bytes_per_launch / avg_kern_s / 1e9 if avg_kern_s > 0 else 0.0
     value = kv_total / elapsed / 1e9
@@ -347,11 +358,10 @@ def main():
             "step_frac": round(value / HBM_PEAK_GBS, 4),
             "kernel_rate_at_least_step_rate": bool(achieved >= value),
             "avg_launch_us": round(avg_kern_s * 1e6, 2),
-            "launch_timing": "one event pair around back-to-back launches"
-            if batch_s is not None else "event pair around each attention launch",
+            "launch_timing": timing,
             "avg_launch_us_per_kernel_events": round(event_kern_s * 1e6, 2),
             "bytes_per_launch": int(bytes_per_launch),
-            "launches_timed": int(launches),
+            "launches_timed": int(batch_launches if batch_s is not None else launches),
             "merge_launches": int(prof.merge_launches) if prof else 0,
             "merge_avg_us": round(prof.merge_ms / max(1, prof.merge_launches) * 1e3, 2)
             if prof else 0.0,
@@ -388,19 +398,28 @@ def step_spread(step, steps: int) -> dict:
 
 
 def dominant_kernel(w) -> str:
-    """The attention kernel the library dispatches for a decode workload: the
-    matrix-core grouped kernel for bf16 d_h of 64, 128 or 256 when a
-    multiple of 4 query heads share a K/V head (template arguments: heads per
-    workgroup, waves per workgroup, d_h), else the vector fast path; ",nt"
-    when its K/V loads are non-temporal (each block read by one workgroup)."""
+    """The attention kernel the library dispatches for a decode workload: a
+    grouped matrix-core kernel when a multiple of 4 query heads share a K/V
+    head (bf16 d_h 64/128/256, float32 d_h 32/64/128; template arguments:
+    heads per workgroup, waves per workgroup, d_h), else the vector fast path
+    (type, d_h); ",nt" when its K/V loads are non-temporal, which is when one
+    workgroup serves all the query heads of a K/V head."""
     group = w.heads // w.hkv
     D = w.head_width
-    if w.dtype == "bf16" and D in (64, 128, 256) and w.page_size % 16 == 0 and group % 4 == 0:
+    widths = (64, 128, 256) if w.dtype == "bf16" else (32, 64, 128)
+    if D in widths and w.page_size % 16 == 0 and group % 4 == 0:
         share = next(s for s in (16, 8, 4) if group % s == 0)
-        waves = 8 if share >= 8 and D != 256 else 4
         nt = ",nt" if group == share else ""
-        return f"attend_group_mfma_kernel<{share},{waves},{D}{nt}>"
-    return f"attend_fast_kernel<{'float' if w.dtype == 'f32' else 'bf16'},{D},nt>"
+        if w.dtype == "bf16":
+            waves = 8 if share >= 8 and D != 256 else 4
+            return f"attend_group_mfma_kernel<{share},{waves},{D}{nt}>"
+        waves = 8 if share >= 8 else 4
+        return f"attend_group_f32_kernel<{share},{waves},{D}{nt}>"
+    row_bytes = D * (4 if w.dtype == "f32" else 2)
+    share = next(s for s in ((8, 4, 2, 1) if row_bytes == 512 else (16, 8, 4, 2, 1))
+                 if group % s == 0)
+    nt = ",nt" if group == share else ""
+    return f"attend_fast_kernel<{'float' if w.dtype == 'f32' else 'bf16'},{D}{nt}>"
 
 
 def prefill_bench(args, w, baseline):
