@@ -109,6 +109,9 @@ def parse():
                     help="waves per workgroup of the fast path (4, 8; 0 = per plan)")
     ap.add_argument("--merge-mode", type=int, default=2,
                     help="2: last-arriving chunk merges (default), 0: separate merge kernel")
+    ap.add_argument("--address-order", action="store_true",
+                    help="pool allocator leases pages in address order (PKV_POOL_ADDRESS_ORDER) "
+                         "instead of from the seeded shuffled free list")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's timed CPU work (all cores, then one)")
@@ -201,6 +204,8 @@ def main():
     d.k_storage, d.v_storage = kp.data_ptr(), vp.data_ptr()
     d.free_list_seed = w.seed
     d.num_kv_heads = Hkv
+    if args.address_order:
+        d.flags = pkv.PKV_POOL_ADDRESS_ORDER
     pool = pkv.pkv_pool_create(d)
     pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_MERGE_MODE, args.merge_mode)
     pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_WAVES, args.waves)
@@ -345,6 +350,8 @@ def main():
             "merge_mode": args.merge_mode,
             "waves_option": args.waves,
             "plan_chunks": chunks,
+            "page_allocator": ("address order" if args.address_order else "seeded shuffle")
+            if transactional else "synthetic shuffled page tables",
             "parallelism": "single GPU",
         },
         "roofline": {

@@ -35,6 +35,7 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "BAD_STATE", 3: "OUT_OF_PAGES
 PKV_DTYPE_F32 = 0
 PKV_DTYPE_BF16 = 1
 PKV_POOL_HOST_ONLY = 1
+PKV_POOL_ADDRESS_ORDER = 2
 
 
 class PkvError(RuntimeError):
@@ -455,7 +456,7 @@ def pkv_prefill_attention(pool: int, layer: int, page_table, pt_stride: int, sta
 
 
 __all__ = [n for n in list(globals()) if n.startswith("pkv_")] + [
-    "PkvError", "STATUS_NAMES", "PKV_DTYPE_F32", "PKV_DTYPE_BF16", "PKV_POOL_HOST_ONLY",
+    "PkvError", "STATUS_NAMES", "PKV_DTYPE_F32", "PKV_DTYPE_BF16", "PKV_POOL_HOST_ONLY", "PKV_POOL_ADDRESS_ORDER",
     "PKV_OPT_SPLIT_BLOCKS", "PKV_OPT_MERGE_MODE", "PKV_OPT_PROFILING", "PKV_OPT_WAVES", "PKV_OPT_VALIDATE", "PKV_MERGE_SEPARATE",
     "PKV_MERGE_LAST_ARRIVER", "LIB_PATH", "SIGNATURES", "PKV_NOALLOC_SCRATCH_BYTES",
     "PKV_NOALLOC_MAX_REQUESTS", "PKV_NOALLOC_MAX_CHUNKS", "PKV_NOALLOC_MAX_COUNTERS",

@@ -978,7 +978,8 @@ pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out) {
   if (d.head_width > 1024) return fail(PKV_ERR_INVALID_ARGUMENT, "head_width %d > 1024", d.head_width);
   if (d.kv_dtype != PKV_DTYPE_F32 && d.kv_dtype != PKV_DTYPE_BF16)
     return fail(PKV_ERR_INVALID_ARGUMENT, "unknown kv_dtype %d", d.kv_dtype);
-  if (d.flags & ~PKV_POOL_HOST_ONLY) return fail(PKV_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", d.flags);
+  if (d.flags & ~(PKV_POOL_HOST_ONLY | PKV_POOL_ADDRESS_ORDER))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", d.flags);
   if (!d.k_storage || !d.v_storage) return fail(PKV_ERR_INVALID_ARGUMENT, "null storage");
   if (!aligned16(d.k_storage) || !aligned16(d.v_storage))
     return fail(PKV_ERR_INVALID_ARGUMENT, "storage not 16-byte aligned");
@@ -1004,12 +1005,14 @@ pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out) {
     p->arena_stride = (int32_t)pages_per_cache;
     p->free_stack.resize(d.num_pages);
     for (int32_t i = 0; i < d.num_pages; ++i) p->free_stack[i] = i;
-    uint64_t s = d.free_list_seed;
-    for (int32_t i = d.num_pages - 1; i > 0; --i) {
-      const uint64_t j = ((splitmix_next(s) >> 32) * (uint64_t)(i + 1)) >> 32;
-      std::swap(p->free_stack[i], p->free_stack[(size_t)j]);
+    if (!(d.flags & PKV_POOL_ADDRESS_ORDER)) {
+      uint64_t s = d.free_list_seed;
+      for (int32_t i = d.num_pages - 1; i > 0; --i) {
+        const uint64_t j = ((splitmix_next(s) >> 32) * (uint64_t)(i + 1)) >> 32;
+        std::swap(p->free_stack[i], p->free_stack[(size_t)j]);
+      }
     }
-    std::reverse(p->free_stack.begin(), p->free_stack.end());  // first lease = first shuffled ID
+    std::reverse(p->free_stack.begin(), p->free_stack.end());  // first lease = first listed ID
     p->owner.assign(d.num_pages, kFree);
     p->refs.assign(d.num_pages, 0);
     p->free_slots.resize(d.max_caches);

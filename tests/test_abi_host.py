@@ -35,13 +35,13 @@ def test_every_declared_function_is_exported_and_bound():
 
 
 def make_pool(layers=2, heads=2, width=2, page=16, pages=8, ctx=64, caches=8, seed=1,
-              dtype=0, split=0):
+              dtype=0, split=0, flags=0):
     # host-only: the allocator and transaction run without device memory
     d = pkv.pkv_pool_desc_init()
     d.num_layers, d.num_heads, d.head_width = layers, heads, width
     d.page_size, d.num_pages, d.max_context = page, pages, ctx
     d.max_caches, d.kv_dtype, d.split_blocks = caches, dtype, split
-    d.flags = pkv.PKV_POOL_HOST_ONLY
+    d.flags = pkv.PKV_POOL_HOST_ONLY | flags
     d.k_storage = d.v_storage = FAKE
     d.free_list_seed = seed
     return pkv.pkv_pool_create(d)
@@ -118,6 +118,31 @@ def test_free_list_is_seeded_permutation_and_raw_lease():
         pkv.pkv_page_release(p2, g)
     pkv.pkv_pool_destroy(p)
     pkv.pkv_pool_destroy(p2)
+
+
+def test_address_order_flag_leases_consecutive_pages():
+    p = make_pool(pages=64, seed=11, flags=pkv.PKV_POOL_ADDRESS_ORDER)
+    a = pkv.pkv_cache_create(p, 64)
+    b = pkv.pkv_cache_create(p, 64)
+    pkv.pkv_cache_grow(a, 40)          # 3 pages
+    pkv.pkv_cache_grow(b, 17)          # 2 pages
+    assert pkv.pkv_cache_page_table(a) == [0, 1, 2]
+    assert pkv.pkv_cache_page_table(b) == [3, 4]
+    assert pkv.pkv_page_lease(p) == 5  # the seed plays no part
+    pkv.pkv_page_release(p, 5)
+    pkv.pkv_cache_reset(a)             # released pages come back last-in, first-out
+    got = [pkv.pkv_page_lease(p) for _ in range(4)]
+    assert sorted(got[:3]) == [0, 1, 2] and got[3] == 5
+    for g in got:
+        pkv.pkv_page_release(p, g)
+    pkv.pkv_cache_destroy(a)
+    pkv.pkv_cache_destroy(b)
+    pkv.pkv_pool_destroy(p)
+    d = pkv.pkv_pool_desc_init()       # unknown flag bits stay rejected
+    d.num_layers, d.num_heads, d.head_width, d.num_pages, d.max_context = 1, 1, 2, 4, 16
+    d.flags = pkv.PKV_POOL_HOST_ONLY | 4
+    d.k_storage = d.v_storage = FAKE
+    assert status_of(pkv.pkv_pool_create, d) == Status.INVALID_ARGUMENT
 
 
 def step(cache, layers, q=FAKE):
