@@ -69,7 +69,7 @@ def test_desc_defaults():
 
 @pytest.mark.parametrize("field,value", [("num_layers", 0), ("num_heads", -1), ("head_width", 0),
                                          ("head_width", 1025), ("page_size", 0),
-                                         ("max_context", 0), ("kv_dtype", 7), ("flags", 2),
+                                         ("max_context", 0), ("kv_dtype", 7), ("flags", 4),
                                          ("k_storage", None), ("v_storage", FAKE + 4),
                                          ("num_kv_heads", -1), ("num_kv_heads", 2),
                                          ("reserved", 1)])
