@@ -493,33 +493,36 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
   // kernel needs it (upload_plan_meta).
   const bool inline_plan = n <= pkv::kInlineReqs && (int64_t)items.size() <= pkv::kInlineItems;
   if (upload) {
-  const size_t part_floats = (size_t)slots * p->desc.num_heads * (p->desc.head_width + 2);
-  if (part_floats > pl->partials_cap) {
-    const size_t cap = std::max(part_floats, pl->partials_cap * 2);
-    void* d = nullptr;
-    if (hipMalloc(&d, cap * sizeof(float)) != hipSuccess)
-      return fail(PKV_ERR_ALLOC, "partials %zu floats", cap);
-    if (pl->d_partials) pl->retired_dev.push_back(pl->d_partials);
-    pl->d_partials = static_cast<float*>(d);
-    pl->partials_cap = cap;
-  }
-  const size_t counters = (size_t)n * p->desc.num_heads;
-  if (counters > pl->counters_cap) {
-    const size_t cap = std::max(counters, pl->counters_cap * 2);
-    void* d = nullptr;
-    if (hipMalloc(&d, cap * sizeof(int32_t)) != hipSuccess)
-      return fail(PKV_ERR_ALLOC, "merge counters %zu", cap);
-    // Zeroed on the stream of the launches that will use them.
-    if (pkv::launch_zero_i32(static_cast<int32_t*>(d), (int64_t)cap, stream) != hipSuccess) {
-      (void)hipFree(d);
-      return fail(PKV_ERR_DEVICE, "clearing the merge counters failed");
+    const size_t part_floats = (size_t)slots * p->desc.num_heads * (p->desc.head_width + 2);
+    if (part_floats > pl->partials_cap) {
+      const size_t cap = std::max(part_floats, pl->partials_cap * 2);
+      void* d = nullptr;
+      if (hipMalloc(&d, cap * sizeof(float)) != hipSuccess)
+        return fail(PKV_ERR_ALLOC, "partials %zu floats", cap);
+      if (pl->d_partials) pl->retired_dev.push_back(pl->d_partials);
+      pl->d_partials = static_cast<float*>(d);
+      pl->partials_cap = cap;
     }
-    if (pl->d_counters) pl->retired_dev.push_back(pl->d_counters);
-    pl->d_counters = static_cast<int32_t*>(d);
-    pl->counters_cap = cap;
+    const size_t counters = (size_t)n * p->desc.num_heads;
+    if (counters > pl->counters_cap) {
+      const size_t cap = std::max(counters, pl->counters_cap * 2);
+      void* d = nullptr;
+      if (hipMalloc(&d, cap * sizeof(int32_t)) != hipSuccess)
+        return fail(PKV_ERR_ALLOC, "merge counters %zu", cap);
+      // Zeroed on the stream of the launches that will use them.
+      if (pkv::launch_zero_i32(static_cast<int32_t*>(d), (int64_t)cap, stream) != hipSuccess) {
+        (void)hipFree(d);
+        return fail(PKV_ERR_DEVICE, "clearing the merge counters failed");
+      }
+      if (pl->d_counters) pl->retired_dev.push_back(pl->d_counters);
+      pl->d_counters = static_cast<int32_t*>(d);
+      pl->counters_cap = cap;
+    }
   }
-  }  // upload
 
+  // From here the plan holds the new work; it counts as built again only
+  // once the upload below has succeeded.
+  pl->built = false;
   pl->reqs = std::move(reqs);
   pl->items = std::move(items);
   pl->merge_list = std::move(merge_list);
@@ -768,6 +771,7 @@ pkv_status run_prefill_tiles(pkv_pool* p, int32_t n, const int32_t* rows, const 
     }
     pkv_status st = ensure_device(p, stream);
     if (st != PKV_OK) return st;
+    pl->built = false;  // the device copy is replaced below
     const MetaPart part{tiles.data(), tiles.size() * sizeof(PrefillTile)};
     if ((st = upload_meta(pl, &part, 1, stream)) != PKV_OK) return st;
     pl->key = std::move(key);
@@ -853,7 +857,7 @@ pkv_status run_prefill(pkv_pool* p, int32_t n, const int32_t* rows, const int32_
   pkv_status st = plan_build(pl, (int32_t)total, vrows.data(), vlens.data(), pt_stride, stream);
   if (st != PKV_OK) return st;
   if (!p->host_only) {
-      AttnArgs a = make_args(pl, layer, page_table, q, k, v, out, false);
+    AttnArgs a = make_args(pl, layer, page_table, q, k, v, out, false);
     PKV_HIP_TRY(pkv::launch_kv_append(a, p->desc.kv_dtype, (int32_t)total, stream));
   }
   // run_attention counts the decode-form K/V reads; this call counted its own
