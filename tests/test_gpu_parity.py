@@ -20,8 +20,9 @@ pytestmark = pytest.mark.gpu
 pkv = pytest.importorskip("paged_kv_cache_attention_amd")
 
 
-def _pool(w, kp, vp, split=0, seed=0, max_caches=0, max_context=None, merge=0):
+def _pool(w, kp, vp, split=0, seed=0, max_caches=0, max_context=None, merge=0, flags=0):
     d = pkv.pkv_pool_desc_init()
+    d.flags = flags
     d.num_layers, d.num_heads, d.head_width = w.layers, w.heads, w.head_width
     d.page_size, d.num_pages = w.page_size, w.num_pages
     d.max_context = max_context or w.pt_stride * w.page_size
@@ -354,14 +355,16 @@ def test_grouped_workgroup_waves(dtype, D, H, Hkv, waves, split):
 @pytest.mark.parametrize("dtype,D,H,Hkv", [("bf16", 128, 8, 2), ("f32", 64, 4, 1),
                                            ("f32", 40, 6, 3), ("bf16", 128, 32, 1),
                                            ("f32", 64, 12, 2)])
-def test_grouped_kv_heads_transactional(dtype, D, H, Hkv):
+@pytest.mark.parametrize("flags", [0, pkv.PKV_POOL_ADDRESS_ORDER])
+def test_grouped_kv_heads_transactional(dtype, D, H, Hkv, flags):
     """begin / batched append_and_attend / abort / commit on caches whose
-    pages hold H_kv heads; the aborted request retries with new rows."""
+    pages hold H_kv heads; the aborted request retries with new rows.  Also
+    with the address-order free list (the pages leased are 0, 1, 2, ...)."""
     lengths = np.array([1, 16, 17, 250, 600], dtype=np.int64)
     w = _small(f"gqa_txn_{dtype}", dtype, D, 16, lengths, heads=H, kv_heads=Hkv, layers=3,
                seed=37, extra_pages=20)
     kp, vp = device_pool(w)
-    pool = _pool(w, kp, vp, seed=9, max_caches=w.n, max_context=1024, merge=2)
+    pool = _pool(w, kp, vp, seed=9, max_caches=w.n, max_context=1024, merge=2, flags=flags)
     caches = [pkv.pkv_cache_create(pool, 1024) for _ in range(w.n)]
     prefix = w.lengths - 1
     for c, n in zip(caches, prefix.tolist()):
@@ -369,6 +372,9 @@ def test_grouped_kv_heads_transactional(dtype, D, H, Hkv):
     for c in caches:
         pkv.pkv_begin_token(c)
     tables = [pkv.pkv_cache_page_table(c) for c in caches]
+    if flags:
+        held = sorted(x for t in tables for x in t)
+        assert held == list(range(len(held)))
     aborted, abort_layer = 3, 1
     live = list(range(w.n))
     outs = {}
