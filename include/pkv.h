@@ -81,10 +81,9 @@ typedef enum pkv_dtype {
  * pages 0, 1, 2, ... (the first lease is page 0) instead of the seeded
  * shuffle, and free_list_seed is ignored.  A cache grown in one call, or
  * caches grown one after another, then hold runs of consecutive pages, so
- * the loads of one request touch few address-translation pages: this
- * matters when a pool's storage spans tens of gigabytes (many layers), where
- * translations of a layer do not survive until the next launch over it.
- * Pages released later are reused last-in, first-out as usual. */
+ * the loads of one request touch few address-translation pages (far fewer
+ * translation-cache misses on pools of many gigabytes).  Pages released
+ * later are reused last-in, first-out as usual. */
 #define PKV_POOL_ADDRESS_ORDER 2u
 
 typedef struct pkv_pool pkv_pool;
