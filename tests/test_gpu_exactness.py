@@ -248,6 +248,48 @@ def test_poisoned_tails_are_never_read(dtype, D, S, H, Hkv, split, merge, op):
     pkv.pkv_pool_destroy(pool)
 
 
+LONG_LENGTHS = [200003, 5, 70000, 131072]
+
+
+@pytest.mark.parametrize("dtype,D,S,H,Hkv", [("bf16", 128, 16, 4, 2), ("f32", 64, 16, 4, 4),
+                                             ("bf16", 128, 16, 32, 1)])
+@pytest.mark.parametrize("split,merge", [(0, 2), (0, 0), (-1, 2)])
+def test_very_long_contexts_closed_form(dtype, D, S, H, Hkv, split, merge):
+    """Contexts of up to 200,003 rows beside a short one.  The automatic plan
+    cuts the long ones into hundreds of chunks (up to 391 partials merged per
+    (request, head)); never splitting runs each on one workgroup.  q = 0 and
+    one-hot V rows give exact expected contexts (counts / t), and the slots
+    past each request's length hold NaN / Inf patterns."""
+    w = _workload("long_" + _name(dtype, D, S, H, Hkv), dtype, D, S, H, Hkv, LONG_LENGTHS,
+                  seed=71)
+    kp, vp = device_pool(w)
+    _one_hot_values(w, vp, w.lengths)
+    _poison_tails(w, kp, vp, w.lengths)
+    pool = _pool(w, kp, vp, split, merge)
+    plan = pkv.pkv_plan_create(pool)
+    pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
+    chunks = pkv.pkv_plan_num_chunks(plan)
+    if split == 0 and H == 4:
+        assert chunks > 300
+    if split == -1:
+        assert chunks == w.n
+    q = torch.zeros((w.n, H, D), dtype=kp.dtype, device="cuda")
+    out = torch.full((w.n, H, D), float("nan"), device="cuda")
+    pt = torch.from_numpy(w.page_tables.copy()).cuda()
+    pkv.pkv_plan_decode_attention(plan, 0, q, pt, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for r, t in enumerate(w.lengths.tolist()):
+        err = float(np.max(np.abs(got[r] - _expected_counts(w, r, t))))
+        worst = max(worst, err)
+        assert err <= EXACT, (r, t, err)
+    record_err(f"long contexts {_name(dtype, D, S, H, Hkv)} split {split} merge {merge} "
+               f"({chunks} chunks)", worst)
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(pool)
+
+
 PREFILL_FAMILIES = [
     ("bf16", 128, 16, 8, 2), ("bf16", 64, 16, 4, 4), ("bf16", 256, 16, 4, 1),
     ("bf16", 128, 32, 4, 4),
