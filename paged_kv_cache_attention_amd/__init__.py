@@ -456,8 +456,10 @@ def pkv_prefill_attention(pool: int, layer: int, page_table, pt_stride: int, sta
 
 
 __all__ = [n for n in list(globals()) if n.startswith("pkv_")] + [
-    "PkvError", "STATUS_NAMES", "PKV_DTYPE_F32", "PKV_DTYPE_BF16", "PKV_POOL_HOST_ONLY", "PKV_POOL_ADDRESS_ORDER",
-    "PKV_OPT_SPLIT_BLOCKS", "PKV_OPT_MERGE_MODE", "PKV_OPT_PROFILING", "PKV_OPT_WAVES", "PKV_OPT_VALIDATE", "PKV_MERGE_SEPARATE",
-    "PKV_MERGE_LAST_ARRIVER", "LIB_PATH", "SIGNATURES", "PKV_NOALLOC_SCRATCH_BYTES",
+    "PkvError", "STATUS_NAMES", "PKV_DTYPE_F32", "PKV_DTYPE_BF16",
+    "PKV_POOL_HOST_ONLY", "PKV_POOL_ADDRESS_ORDER",
+    "PKV_OPT_SPLIT_BLOCKS", "PKV_OPT_MERGE_MODE", "PKV_OPT_PROFILING", "PKV_OPT_WAVES",
+    "PKV_OPT_VALIDATE", "PKV_MERGE_SEPARATE", "PKV_MERGE_LAST_ARRIVER",
+    "LIB_PATH", "SIGNATURES", "PKV_NOALLOC_SCRATCH_BYTES",
     "PKV_NOALLOC_MAX_REQUESTS", "PKV_NOALLOC_MAX_CHUNKS", "PKV_NOALLOC_MAX_COUNTERS",
     "PKV_NOALLOC_MAX_PARTIAL_FLOATS"]
