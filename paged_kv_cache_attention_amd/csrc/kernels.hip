@@ -159,19 +159,21 @@ struct RowVec {
     for (int k = 0; k < kWords; ++k) v.w[k] = c ? a.w[k] : b.w[k];
     return v;
   }
-  // Buffer load at a lane byte offset (16-byte pieces are adjacent), with
-  // cache policy CP.
+  // Buffer load at a lane byte offset (16-byte pieces are adjacent) plus a
+  // wave-uniform offset `soff`, with cache policy CP.  The buffer's range
+  // check is not guaranteed to include `soff`, so a caller that relies on it
+  // to drop reads past the range passes the whole offset in `off`.
   template <int CP>
-  __device__ static inline RowVec load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __device__ static inline RowVec load(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff = 0) {
     RowVec v;
     if constexpr (VB == 8) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, CP);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, soff, CP);
       v.w[0] = x[0];
       v.w[1] = x[1];
     } else {
 #pragma unroll
       for (int h = 0; h < VB / 16; ++h) {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16 * h), 0, CP);
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16 * h), soff, CP);
 #pragma unroll
         for (int k = 0; k < 4; ++k) v.w[4 * h + k] = x[k];
       }
@@ -450,18 +452,34 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
     for (int e = 0; e < EPL; ++e) qf[j][e] *= a.scale_log2e;
   }
 
+  // With the fused append, the wave of each head group that takes the
+  // request's last block (the edge wave) substitutes the new row from the
+  // inputs there.  It loads that row now and parks it in LDS once the first
+  // K/V loads are issued, so no registers hold it through the block loop;
+  // head group 0's edge wave of tile 0 also writes it to its page slot.
+  const bool edge_wave = fused && sub == (last_blk - it.blk_begin) % WPG;
+  __shared__ __align__(16) uint32_t s_new[NG][2][LPR * Vec::kWords];
   Vec knew = Vec::zero(), vnew = Vec::zero();
-  if (fused && lane_on) {
+  if (edge_wave && lane_on) {
     knew = Vec::load(static_cast<const char*>(a.k_new) + kvrow_bytes + c * VB);
     vnew = Vec::load(static_cast<const char*>(a.v_new) + kvrow_bytes + c * VB);
-    if (wave == 0 && g == 0 && tile == 0) {
+  }
+  auto park_new_row = [&]() {
+    if (g == 0) {
+#pragma unroll
+      for (int k = 0; k < Vec::kWords; ++k) {
+        s_new[hg][0][c * Vec::kWords + k] = knew.w[k];
+        s_new[hg][1][c * Vec::kWords + k] = vnew.w[k];
+      }
+    }
+    if (hg == 0 && tile == 0 && g == 0 && lane_on) {
       const int pos = t - 1;
       const int64_t slot = (int64_t)pt[pos / S] * a.page_bytes + head_off +
                            (int64_t)(pos % S) * ROW_BYTES + c * VB;
       knew.store(a.k_layer + slot);
       vnew.store(a.v_layer + slot);
     }
-  }
+  };
 
   // Physical page of a wave-uniform block index (clamped into the request's
   // blocks so a look-ahead read past the end stays inside the table).
@@ -470,7 +488,11 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
     return pt[(b * kBlockRows) / S];
   };
   // Lane byte offsets inside a 16-row block: the block base is wave-uniform
-  // (scalar registers) and each load adds one unsigned 32-bit lane offset.
+  // (scalar registers) and each load adds an unsigned 32-bit lane offset.
+  // Whole rows stay inside the block, so load i passes its i * RPI rows as a
+  // scalar offset and one register serves all loads; padded rows read past
+  // the row into bytes the range check must drop at the block's end, so each
+  // load keeps its whole offset in a register.
   uint32_t lane_off[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) lane_off[i] = (uint32_t)((i * RPI + g) * ROW_BYTES + c * VB);
@@ -481,8 +503,13 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
     const auto rv = block_rsrc(a.v_layer + base, kBlockRows * ROW_BYTES);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      kk[i] = Vec::template load<CP>(rk, lane_off[i]);
-      vv[i] = Vec::template load<CP>(rv, lane_off[i]);
+      if constexpr (PAD) {
+        kk[i] = Vec::template load<CP>(rk, lane_off[i]);
+        vv[i] = Vec::template load<CP>(rv, lane_off[i]);
+      } else {
+        kk[i] = Vec::template load<CP>(rk, lane_off[0], i * RPI * ROW_BYTES);
+        vv[i] = Vec::template load<CP>(rv, lane_off[0], i * RPI * ROW_BYTES);
+      }
     }
   };
 
@@ -505,14 +532,23 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
     for (int i = 0; i < NI; ++i) valid[i] = true;
     if constexpr (edge) {
       // The request's last block: rows >= t are masked (their bytes may be
-      // anything), and with a fused append row t-1 comes from k_new/v_new.
+      // anything), and with a fused append row t-1 comes from k_new/v_new
+      // (parked in LDS by this wave).
+      Vec k_row = Vec::zero(), v_row = Vec::zero();
+      if (fused) {
+#pragma unroll
+        for (int k = 0; k < Vec::kWords; ++k) {
+          k_row.w[k] = s_new[hg][0][c * Vec::kWords + k];
+          v_row.w[k] = s_new[hg][1][c * Vec::kWords + k];
+        }
+      }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int row = b * kBlockRows + i * RPI + g;
         const bool is_new = fused && row == t - 1;
         valid[i] = row < t;
-        kk[i] = Vec::select(is_new, knew, kk[i]);
-        vv[i] = Vec::select(valid[i], Vec::select(is_new, vnew, vv[i]), Vec::zero());
+        kk[i] = Vec::select(is_new, k_row, kk[i]);
+        vv[i] = Vec::select(valid[i], Vec::select(is_new, v_row, vv[i]), Vec::zero());
       }
     }
     float s[HPW][NI];
@@ -579,6 +615,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_fast_kernel(AttnArgs a) {
       const int wave_last = first + ((end - 1 - first) / WPG) * WPG;
       Vec ka[NI], va[NI], kb[NI], vb[NI];
       load_block(first, page_of(first), ka, va);
+      if (edge_wave) park_new_row();
       int32_t p_next = page_of(min(first + WPG, wave_last));
       for (int b = first;; b += 2 * WPG) {
         const int b1 = b + WPG;
