@@ -107,8 +107,9 @@ def parse():
     ap.add_argument("--split-blocks", type=int, default=0)
     ap.add_argument("--waves", type=int, default=0,
                     help="waves per workgroup of the fast path (4, 8; 0 = per plan)")
-    ap.add_argument("--merge-mode", type=int, default=2,
-                    help="2: last-arriving chunk merges (default), 0: separate merge kernel")
+    ap.add_argument("--merge-mode", type=int, default=1,
+                    help="1: the library's choice per plan (default), 2: last-arriving chunk "
+                         "merges, 0: separate merge kernel")
     ap.add_argument("--address-order", action="store_true",
                     help="pool allocator leases pages in address order (PKV_POOL_ADDRESS_ORDER) "
                          "instead of from the seeded shuffled free list")

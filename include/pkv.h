@@ -162,9 +162,11 @@ typedef struct pkv_profile {
 /* Tunables of a pool (pkv_pool_set_option). */
 typedef enum pkv_option {
   PKV_OPT_SPLIT_BLOCKS = 1, /* as pkv_pool_desc.split_blocks                   */
-  PKV_OPT_MERGE_MODE = 2,   /* 2 (default): the last-arriving chunk merges
-                               inside the attention kernel; 0: a separate
-                               merge kernel after it                            */
+  PKV_OPT_MERGE_MODE = 2,   /* how split requests merge their chunks: 2: the
+                               last-arriving chunk merges inside the
+                               attention kernel; 0: a separate merge kernel
+                               after it; 1 (default): per plan, 0 when its
+                               launches read at least 1 GiB of K/V, else 2    */
   PKV_OPT_PROFILING = 3,    /* 1: record kernel timing events; 0: stop         */
   PKV_OPT_WAVES = 4,        /* waves per workgroup of the fast paths: 4, 8,
                                16 (the multi-head kernel for d_h <= 64; other

@@ -99,6 +99,7 @@ PKV_OPT_PROFILING = 3
 PKV_OPT_WAVES = 4
 PKV_OPT_VALIDATE = 5
 PKV_MERGE_SEPARATE = 0
+PKV_MERGE_AUTO = 1
 PKV_MERGE_LAST_ARRIVER = 2
 
 _P = ctypes.c_void_p
@@ -459,7 +460,7 @@ __all__ = [n for n in list(globals()) if n.startswith("pkv_")] + [
     "PkvError", "STATUS_NAMES", "PKV_DTYPE_F32", "PKV_DTYPE_BF16",
     "PKV_POOL_HOST_ONLY", "PKV_POOL_ADDRESS_ORDER",
     "PKV_OPT_SPLIT_BLOCKS", "PKV_OPT_MERGE_MODE", "PKV_OPT_PROFILING", "PKV_OPT_WAVES",
-    "PKV_OPT_VALIDATE", "PKV_MERGE_SEPARATE", "PKV_MERGE_LAST_ARRIVER",
+    "PKV_OPT_VALIDATE", "PKV_MERGE_SEPARATE", "PKV_MERGE_AUTO", "PKV_MERGE_LAST_ARRIVER",
     "LIB_PATH", "SIGNATURES", "PKV_NOALLOC_SCRATCH_BYTES",
     "PKV_NOALLOC_MAX_REQUESTS", "PKV_NOALLOC_MAX_CHUNKS", "PKV_NOALLOC_MAX_COUNTERS",
     "PKV_NOALLOC_MAX_PARTIAL_FLOATS"]

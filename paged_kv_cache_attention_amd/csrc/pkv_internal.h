@@ -135,7 +135,9 @@ enum class KernelPath { kFast, kGeneric };
 //             waits for them to complete before its relaxed counter
 //             increment, and the last arriver reads them with agent-scope
 //             atomic loads.  No L2 write-back or invalidate is needed.
-enum MergeMode : int32_t { kMergeSeparate = 0, kMergeLastArriver = 2 };
+//  kAuto:     a pool setting only -- each plan takes one of the two by the
+//             bytes its launches read (plan_merge_mode); kernels never see it.
+enum MergeMode : int32_t { kMergeSeparate = 0, kMergeAuto = 1, kMergeLastArriver = 2 };
 
 // Launchers (kernels.hip).  Each returns the hipError_t of the launch.
 hipError_t launch_attention(const AttnArgs& a, int dtype, int num_items, hipStream_t stream,

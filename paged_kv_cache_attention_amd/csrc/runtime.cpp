@@ -94,6 +94,7 @@ struct pkv_plan {
   int32_t total_splits = 0;
   int32_t num_split_reqs = 0;
   int32_t waves = 0;
+  int32_t merge_mode = pkv::kMergeLastArriver;  // as launched (never kMergeAuto)
   bool any_split = false;
   bool inline_plan = false;    // reqs/items go in the kernel arguments
   bool meta_uploaded = false;  // reqs/items/merge list are in d_meta
@@ -162,7 +163,7 @@ struct pkv_pool {
   pkv_plan call_plan;     // one-call batched forms
   pkv_plan prefill_plan;  // chunks of several rows per request
   pkv_counters counters{};
-  int32_t merge_mode = pkv::kMergeLastArriver;
+  int32_t merge_mode = pkv::kMergeAuto;  // the option; plans take plan_merge_mode()
   int32_t waves_option = 0;
   uint64_t opt_gen = 0;  // bumped by every option that changes a plan's shape
   bool profiling = false;
@@ -292,6 +293,24 @@ pkv_status flush_patches(pkv_pool* p, hipStream_t stream) {
 
 // Workgroup shape and split-K chunk size (in 16-row blocks) of a plan.
 //
+// The merge a plan's split requests use.  Automatic (the default): launches
+// that read at least kSeparateMergeBytes of K/V merge in a separate kernel,
+// smaller ones in place.  In place, each split chunk's last wave waits for its
+// partial stores and then for the counter's reply before it can leave, and
+// the last arrivers merge at the end of the launch; on long launches that
+// costs more than a second launch (32-layer bf16 step, 4.3 GB per launch:
+// 22.2 ms per step against 22.4-22.8 ms), while on short ones the second
+// launch dominates (12-layer float32 step, 88 MB per launch: a separate merge
+// adds ~4 us to each 21 us launch).
+constexpr uint64_t kSeparateMergeBytes = 1ull << 30;
+
+int32_t plan_merge_mode(const pkv_pool* p, uint64_t rows_attended) {
+  if (p->merge_mode != pkv::kMergeAuto) return p->merge_mode;
+  const uint64_t bytes = rows_attended * (uint64_t)p->desc.num_kv_heads * 2ull *
+                         (uint64_t)p->desc.head_width * p->elt;
+  return bytes >= kSeparateMergeBytes ? pkv::kMergeSeparate : pkv::kMergeLastArriver;
+}
+
 // Waves per workgroup: PKV_OPT_WAVES, or 0 to let the launcher choose per
 // kernel (four for the vector kernels, eight or sixteen for a small
 // multi-head batch as below; eight for the matrix-core kernel when a workgroup serves 8 or 16
@@ -529,7 +548,8 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
   pl->meta_uploaded = false;
   // The device copy is also made now when this pool's separate merge kernel
   // will need it, so a launch captured into a graph finds it there.
-  const bool need_meta = !inline_plan || (slots > 0 && p->merge_mode == pkv::kMergeSeparate);
+  const int32_t merge_mode = plan_merge_mode(p, rows_attended);
+  const bool need_meta = !inline_plan || (slots > 0 && merge_mode == pkv::kMergeSeparate);
   if (upload && need_meta && (st = upload_plan_meta(pl, stream)) != PKV_OK) return st;
   pl->key = std::move(key);
   pl->n = n;
@@ -538,6 +558,7 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
   pl->total_splits = slots;
   pl->num_split_reqs = (int32_t)pl->merge_list.size();
   pl->waves = choice.waves;
+  pl->merge_mode = merge_mode;
   pl->any_split = slots > 0;
   pl->inline_plan = inline_plan;
   pl->rows_attended = rows_attended;
@@ -554,6 +575,7 @@ struct PlanView {
   int32_t num_items;
   int32_t pt_stride;
   int32_t waves;
+  int32_t merge_mode;  // kMergeSeparate or kMergeLastArriver
   bool inline_plan;
   const char* d_meta;  // requests, then work items, then split requests
   float* d_partials;
@@ -578,7 +600,7 @@ AttnArgs make_args_view(const pkv_pool* p, const PlanView& v, int32_t layer,
   a.merge_count = v.d_counters;
   a.merge_reqs = reinterpret_cast<const int32_t*>(v.d_meta + (size_t)v.n * sizeof(ReqEntry) +
                                                   (size_t)v.num_items * sizeof(WorkItem));
-  a.merge_mode = p->merge_mode;
+  a.merge_mode = v.merge_mode;
   a.waves = v.waves;
   a.num_heads = p->desc.num_heads;
   a.num_kv_heads = p->desc.num_kv_heads;
@@ -600,8 +622,8 @@ AttnArgs make_args_view(const pkv_pool* p, const PlanView& v, int32_t layer,
 AttnArgs make_args(const pkv_plan* pl, int32_t layer, const int32_t* page_table,
                    const void* q, const void* k, const void* v, float* out, bool fuse) {
   const PlanView view{pl->reqs.data(), (int32_t)pl->reqs.size(), pl->items.data(),
-                      (int32_t)pl->items.size(), pl->pt_stride, pl->waves, pl->inline_plan,
-                      pl->d_meta, pl->d_partials, pl->d_counters};
+                      (int32_t)pl->items.size(), pl->pt_stride, pl->waves, pl->merge_mode,
+                      pl->inline_plan, pl->d_meta, pl->d_partials, pl->d_counters};
   return make_args_view(pl->pool, view, layer, page_table, q, k, v, out, fuse);
 }
 
@@ -698,7 +720,7 @@ pkv_status run_attention(pkv_plan* pl, int32_t layer, const int32_t* page_table,
     p->timed.push_back({e0, e1, pkv_pool::kTimedAttention});
     p->profile.algorithmic_bytes += launch_bytes(pl, fuse);
   }
-  if (pl->any_split && p->merge_mode == pkv::kMergeSeparate) {
+  if (pl->any_split && pl->merge_mode == pkv::kMergeSeparate) {
     // The merge kernel reads the plan from the device: an inline plan built
     // before the pool switched to this mode is copied there once, on the
     // stream ahead of the merge.
@@ -1079,7 +1101,8 @@ pkv_status pkv_pool_set_option(pkv_pool* p, int32_t option, int64_t value) {
       p->opt_gen += 1;
       return ok();
     case PKV_OPT_MERGE_MODE:
-      if (value != pkv::kMergeSeparate && value != pkv::kMergeLastArriver)
+      if (value != pkv::kMergeSeparate && value != pkv::kMergeAuto &&
+          value != pkv::kMergeLastArriver)
         return fail(PKV_ERR_INVALID_ARGUMENT, "merge mode %lld", (long long)value);
       p->merge_mode = (int32_t)value;
       p->opt_gen += 1;
@@ -1644,7 +1667,8 @@ pkv_status pkv_decode_attention_noalloc(pkv_pool* p, int32_t layer, int32_t n, c
   char* scratch = static_cast<char*>(base);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool inline_plan = n <= pkv::kInlineReqs && m <= pkv::kInlineItems;
-  const bool separate = slots > 0 && p->merge_mode == pkv::kMergeSeparate;
+  const int32_t merge_mode = plan_merge_mode(p, rows_attended);
+  const bool separate = slots > 0 && merge_mode == pkv::kMergeSeparate;
   char* d_meta = scratch + pkv::kScratchMetaOffset;
   if (!inline_plan || separate) {
     // one copy from fixed host memory: requests, work items, split requests
@@ -1658,7 +1682,7 @@ pkv_status pkv_decode_attention_noalloc(pkv_pool* p, int32_t layer, int32_t n, c
   int32_t* d_counters = reinterpret_cast<int32_t*>(scratch + pkv::kScratchCountersOffset);
   if (slots > 0 && !separate)  // the last-arriver merge counts from zero
     PKV_HIP_TRY(pkv::launch_zero_i32(d_counters, (int64_t)n * H, s));
-  const PlanView view{na_reqs, n, na_items, m, pt_stride, choice.waves, inline_plan, d_meta,
+  const PlanView view{na_reqs, n, na_items, m, pt_stride, choice.waves, merge_mode, inline_plan, d_meta,
                       reinterpret_cast<float*>(scratch + pkv::kScratchPartialsOffset),
                       d_counters};
   const AttnArgs a = make_args_view(p, view, layer, page_table, q, nullptr, nullptr, out, false);

@@ -396,6 +396,18 @@ def test_option_change_rebuilds_a_plan_with_the_same_lengths():
     pkv.pkv_pool_destroy(p)
 
 
+def test_merge_mode_option_values():
+    # 0 (separate), 1 (automatic, the default) and 2 (last arriver) are
+    # accepted; anything else is rejected
+    p = make_pool()
+    for v in (0, 1, 2):
+        pkv.pkv_pool_set_option(p, pkv.PKV_OPT_MERGE_MODE, v)
+    for v in (3, -1, 4):
+        assert status_of(pkv.pkv_pool_set_option, p, pkv.PKV_OPT_MERGE_MODE, v) == \
+            Status.INVALID_ARGUMENT
+    pkv.pkv_pool_destroy(p)
+
+
 def test_waves_option_values():
     # 0, 4, 8 and 16 are accepted; anything else is rejected and leaves the
     # option unchanged (16 explicit waves keep the finest default split)

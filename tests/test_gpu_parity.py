@@ -1007,19 +1007,27 @@ def test_plan_decode_replays_from_a_hip_graph(merge):
 
 @pytest.mark.parametrize("maker", [W.batch256_bf16, W.skewed64_bf16, W.batch256_gqa8_bf16,
                                    W.batch256_mqa_bf16])
-@pytest.mark.parametrize("merge", MERGES)
+@pytest.mark.parametrize("merge", MERGES + [pkv.PKV_MERGE_AUTO])
 def test_bf16_single_layer_full(maker, merge):
     w = maker()
     kp, vp = device_pool(w)
     pool = _pool(w, kp, vp, merge=merge)
     plan = pkv.pkv_plan_create(pool)
     pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
+    split = pkv.pkv_plan_num_chunks(plan) > w.n
     if w.lengths.max() > 4096:
-        assert pkv.pkv_plan_num_chunks(plan) > w.n   # long contexts are split
+        assert split   # long contexts are split
     qh = w.q(0)
     out = torch.empty((w.n, w.heads, w.head_width), device="cuda")
+    pkv.pkv_pool_set_option(pool, pkv.PKV_OPT_PROFILING, 1)
     pkv.pkv_plan_decode_attention(plan, 0, rows_to_device(qh, "bf16"), _pt_device(w), out)
     torch.cuda.synchronize()
+    prof = pkv.pkv_pool_get_profile(pool)
+    # a separate merge launch follows a split plan in mode 0, and in the
+    # automatic mode when the launch reads at least 1 GiB of K/V
+    separate = merge == pkv.PKV_MERGE_SEPARATE or (
+        merge == pkv.PKV_MERGE_AUTO and w.kv_bytes_per_layer() >= 1 << 30)
+    assert prof.merge_launches == (1 if split and separate else 0)
     assert torch.isfinite(out).all()
     kg, vg = GeneratorLayer(w, "k", 0), GeneratorLayer(w, "v", 0)
     kg.spot_check(w.page_tables[[0, w.n - 1], 0])

@@ -61,7 +61,7 @@ class Schedule:
         d.num_kv_heads = Hkv
         d.split_blocks = int(self.rng.choice([0, 1, 2]))
         self.pool = pkv.pkv_pool_create(d)
-        pkv.pkv_pool_set_option(self.pool, pkv.PKV_OPT_MERGE_MODE, int(self.rng.choice([0, 2])))
+        pkv.pkv_pool_set_option(self.pool, pkv.PKV_OPT_MERGE_MODE, int(self.rng.choice([0, 1, 2])))
         self.hist = {}    # cache -> per layer list of (k [Hkv, D], v) float64 rows
         self.worst = 0.0
         self.contexts = 0
