@@ -320,10 +320,28 @@ int32_t plan_merge_mode(const pkv_pool* p, uint64_t rows_attended) {
 // with few (request, head) pairs still fills the GPU and one long context
 // does not serialise on one workgroup; a batch that already has that many
 // pairs is not split.
+//
+// Such a launch runs its workgroups in several resident rounds, longest chunk
+// first, and ends as the last ones drain.  Its requests split into whole
+// chunks of `chunk` blocks with the remainder last (remainder_last), so the
+// chunks dispatched at the end are short: on the 32-layer bf16 step (128-block
+// chunks, requests of 97-161 blocks) that measured 695.7-697.0 us per launch in
+// six runs against 698-712 us with even chunks, whose runs often ended slower.
+// The other choices keep even chunks (the first blocks % nsplit take one block
+// more): a one-round launch ends with its longest workgroup, which even
+// chunks keep shortest.
 struct SplitChoice {
   int32_t chunk;
   int32_t waves;
+  bool remainder_last;
 };
+
+// Block range end of chunk s of a request of `blocks` blocks split nsplit ways
+// from b0 (the end of chunk s - 1).
+int32_t chunk_end(const SplitChoice& c, int32_t blocks, int32_t nsplit, int32_t s, int32_t b0) {
+  if (c.remainder_last) return std::min(b0 + c.chunk, blocks);
+  return b0 + blocks / nsplit + (s < blocks % nsplit ? 1 : 0);
+}
 
 SplitChoice choose_split(const pkv_pool* p, int32_t n, int64_t total_blocks) {
   // Work is counted in (block, query head) units: a workgroup serving a K/V
@@ -332,8 +350,8 @@ SplitChoice choose_split(const pkv_pool* p, int32_t n, int64_t total_blocks) {
   // publishes).
   const int64_t H = p->desc.num_heads;
   const int32_t waves = p->waves_option;
-  if (p->desc.split_blocks > 0) return {p->desc.split_blocks, waves};
-  if (p->desc.split_blocks < 0) return {std::numeric_limits<int32_t>::max(), waves};
+  if (p->desc.split_blocks > 0) return {p->desc.split_blocks, waves, false};
+  if (p->desc.split_blocks < 0) return {std::numeric_limits<int32_t>::max(), waves, false};
   constexpr int64_t kTargetChunks = 4096;
   const int64_t work = total_blocks * H;  // (block, head) units
   int64_t c = 8;
@@ -362,9 +380,10 @@ SplitChoice choose_split(const pkv_pool* p, int32_t n, int64_t total_blocks) {
   if (small_mha && p->desc.head_width <= 64 &&
       pkv::fast_width_native(p->desc.kv_dtype, p->desc.head_width) &&
       (total_blocks / 64 + n / 2) * H >= 256)
-    return {64, 16};
-  if (small_mha && (total_blocks / 32 + n / 2) * H >= 256) return {32, 8};
-  return {(int32_t)c, waves};
+    return {64, 16, false};
+  if (small_mha && (total_blocks / 32 + n / 2) * H >= 256) return {32, 8, false};
+  // Chunks above the minimum mean more (chunk, head) units than four rounds.
+  return {(int32_t)c, waves, c > 8};
 }
 
 // Frees the plan's buffers (at destroy: these frees wait for the device).
@@ -485,11 +504,9 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
     const int32_t nsplit = (int32_t)(((int64_t)blocks + chunk - 1) / chunk);
     reqs[r] = ReqEntry{rows[r], lens[r], nsplit, nsplit > 1 ? slots : -1};
     if (nsplit > 1) slots += nsplit;
-    // Even chunks: the first (blocks % nsplit) chunks take one block more.
-    const int32_t base = blocks / nsplit, extra = blocks % nsplit;
     int32_t b0 = 0;
     for (int32_t s = 0; s < nsplit; ++s) {
-      const int32_t b1 = b0 + base + (s < extra ? 1 : 0);
+      const int32_t b1 = chunk_end(choice, blocks, nsplit, s, b0);
       items.push_back(WorkItem{r, b0, b1, s, reqs[r]});
       b0 = b1;
     }
@@ -1637,10 +1654,9 @@ pkv_status pkv_decode_attention_noalloc(pkv_pool* p, int32_t layer, int32_t n, c
       slots += nsplit;
       na_merge[nmerge++] = r;
     }
-    const int32_t base = blocks / nsplit, extra = blocks % nsplit;
     int32_t b0 = 0;
     for (int32_t s = 0; s < nsplit; ++s) {
-      const int32_t b1 = b0 + base + (s < extra ? 1 : 0);
+      const int32_t b1 = chunk_end(choice, blocks, nsplit, s, b0);
       na_items[m++] = WorkItem{r, b0, b1, s, na_reqs[r]};
       b0 = b1;
     }
