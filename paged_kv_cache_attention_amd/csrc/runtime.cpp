@@ -356,6 +356,13 @@ SplitChoice choose_split(const pkv_pool* p, int32_t n, int64_t total_blocks) {
   const int64_t work = total_blocks * H;  // (block, head) units
   int64_t c = 8;
   while (c < 512 && c * kTargetChunks < work) c *= 2;
+  // A batch with at least kTargetChunks (request, head) pairs fills four
+  // rounds unsplit; its chunk only keeps the longest requests from ending the
+  // launch alone, so it is twice the average the loop above aims at.  The
+  // 32-layer bf16 step (requests of 97-161 blocks, average 128) then stays
+  // unsplit: 695-697 us per launch in every run on three boxes, where
+  // 128-block chunks ran at 690-697 on some boxes and 704-712 on another.
+  if ((int64_t)n * H >= kTargetChunks) c = std::min<int64_t>(2 * c, 512);
   // A small multi-head batch with enough (request, head) pairs for an
   // eight-wave workgroup on every CU: 32-block chunks over eight waves (four
   // blocks per wave) instead of 8-block chunks over four, so fewer requests
