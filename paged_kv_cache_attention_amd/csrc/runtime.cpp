@@ -324,12 +324,12 @@ int32_t plan_merge_mode(const pkv_pool* p, uint64_t rows_attended) {
 // Such a launch runs its workgroups in several resident rounds, longest chunk
 // first, and ends as the last ones drain.  Its requests split into whole
 // chunks of `chunk` blocks with the remainder last (remainder_last), so the
-// chunks dispatched at the end are short: on the 32-layer bf16 step (128-block
-// chunks, requests of 97-161 blocks) that measured 695.7-697.0 us per launch in
-// six runs against 698-712 us with even chunks, whose runs often ended slower.
-// The other choices keep even chunks (the first blocks % nsplit take one block
-// more): a one-round launch ends with its longest workgroup, which even
-// chunks keep shortest.
+// chunks dispatched at the end are short: on the 32-layer bf16 step split at
+// 128 blocks (requests of 97-161 blocks) that measured 695.7-697.0 us per
+// launch in six runs against 698-712 us with even chunks, whose runs often
+// ended slower (that step now runs unsplit, below).  The other choices keep
+// even chunks (the first blocks % nsplit take one block more): a one-round
+// launch ends with its longest workgroup, which even chunks keep shortest.
 struct SplitChoice {
   int32_t chunk;
   int32_t waves;
@@ -343,7 +343,7 @@ int32_t chunk_end(const SplitChoice& c, int32_t blocks, int32_t nsplit, int32_t 
   return b0 + blocks / nsplit + (s < blocks % nsplit ? 1 : 0);
 }
 
-SplitChoice choose_split(const pkv_pool* p, int32_t n, int64_t total_blocks) {
+SplitChoice choose_split(const pkv_pool* p, int32_t n, int64_t total_blocks, int32_t max_blocks) {
   // Work is counted in (block, query head) units: a workgroup serving a K/V
   // head does the work of its whole group, so grouped heads split like the
   // multi-head case (measured: splitting them further only adds partial
@@ -356,13 +356,14 @@ SplitChoice choose_split(const pkv_pool* p, int32_t n, int64_t total_blocks) {
   const int64_t work = total_blocks * H;  // (block, head) units
   int64_t c = 8;
   while (c < 512 && c * kTargetChunks < work) c *= 2;
-  // A batch with at least kTargetChunks (request, head) pairs fills four
-  // rounds unsplit; its chunk only keeps the longest requests from ending the
-  // launch alone, so it is twice the average the loop above aims at.  The
-  // 32-layer bf16 step (requests of 97-161 blocks, average 128) then stays
-  // unsplit: 695-697 us per launch in every run on three boxes, where
-  // 128-block chunks ran at 690-697 on some boxes and 704-712 on another.
-  if ((int64_t)n * H >= kTargetChunks) c = std::min<int64_t>(2 * c, 512);
+  // A batch of at least two resident rounds of (request, head) pairs whose
+  // longest request is at most twice the average keeps every request whole:
+  // no request can end the launch alone.  The 32-layer bf16 step (requests of
+  // 97-161 blocks) then runs unsplit, with or without its aborted requests:
+  // 695-697 us per launch in every run on three boxes, where 128-block
+  // chunks ran at 690-697 on some boxes and 704-712 on another.
+  if ((int64_t)n * H >= kTargetChunks / 2 && (int64_t)max_blocks * n <= 2 * total_blocks)
+    return {std::numeric_limits<int32_t>::max(), waves, false};
   // A small multi-head batch with enough (request, head) pairs for an
   // eight-wave workgroup on every CU: 32-block chunks over eight waves (four
   // blocks per wave) instead of 8-block chunks over four, so fewer requests
@@ -479,11 +480,14 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
   pkv_pool* p = pl->pool;
   const int64_t max_len = (int64_t)pt_stride * p->desc.page_size;
   int64_t total_blocks = 0;
+  int32_t max_blocks = 0;
   for (int32_t r = 0; r < n; ++r) {
     if (lens[r] < 1 || lens[r] > max_len)
       return fail(PKV_ERR_INVALID_ARGUMENT, "seq_lens[%d]=%d outside [1, %lld]", r, lens[r],
                   (long long)max_len);
-    total_blocks += (lens[r] + pkv::kBlockRows - 1) / pkv::kBlockRows;
+    const int32_t b = (lens[r] + pkv::kBlockRows - 1) / pkv::kBlockRows;
+    total_blocks += b;
+    max_blocks = std::max(max_blocks, b);
   }
   // The key holds the options generation too: a plan built before an option
   // changed its chunking or workgroup shape is rebuilt.
@@ -498,7 +502,7 @@ pkv_status plan_build(pkv_plan* pl, int32_t n, const int32_t* rows, const int32_
   pkv_status st = ensure_device(p, stream);
   if (st != PKV_OK) return st;
 
-  const SplitChoice choice = choose_split(p, n, total_blocks);
+  const SplitChoice choice = choose_split(p, n, total_blocks, max_blocks);
   const int32_t chunk = choice.chunk;
   const bool upload = !p->host_only;
   std::vector<ReqEntry> reqs(n);
@@ -1639,16 +1643,19 @@ pkv_status pkv_decode_attention_noalloc(pkv_pool* p, int32_t layer, int32_t n, c
                 "merge counters", n, (long long)H, PKV_NOALLOC_MAX_COUNTERS);
   const int64_t max_len = (int64_t)pt_stride * p->desc.page_size;
   int64_t total_blocks = 0;
+  int32_t max_blocks = 0;
   uint64_t rows_attended = 0;
   for (int32_t r = 0; r < n; ++r) {
     if (seq_lens[r] < 1 || seq_lens[r] > max_len)
       return fail(PKV_ERR_INVALID_ARGUMENT, "seq_lens[%d]=%d outside [1, %lld]", r, seq_lens[r],
                   (long long)max_len);
-    total_blocks += (seq_lens[r] + pkv::kBlockRows - 1) / pkv::kBlockRows;
+    const int32_t b = (seq_lens[r] + pkv::kBlockRows - 1) / pkv::kBlockRows;
+    total_blocks += b;
+    max_blocks = std::max(max_blocks, b);
     rows_attended += (uint64_t)seq_lens[r];
   }
   // The plan of pkv_decode_attention, built into the fixed arrays.
-  const SplitChoice choice = choose_split(p, n, total_blocks);
+  const SplitChoice choice = choose_split(p, n, total_blocks, max_blocks);
   int32_t m = 0, slots = 0, nmerge = 0;
   for (int32_t r = 0; r < n; ++r) {
     const int32_t blocks = (seq_lens[r] + pkv::kBlockRows - 1) / pkv::kBlockRows;
