@@ -309,6 +309,29 @@ def test_automatic_split_targets_4096_chunks():
     pkv.pkv_pool_destroy(p)
 
 
+def test_balanced_batch_of_two_rounds_stays_whole():
+    # 32 heads.  64 requests of 128 blocks: 2048 (request, head) pairs, the
+    # longest no more than twice the average -> every request whole (the
+    # work alone would ask for 64-block chunks, two per request).
+    p = make_pool(pages=4200, ctx=16 * 1024, heads=32)
+    plan = pkv.pkv_plan_create(p)
+    pkv.pkv_plan_build(plan, [16 * 128] * 64, 1024, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 64
+    # one request fewer: 2016 pairs -> the work's 64-block chunks
+    pkv.pkv_plan_build(plan, [16 * 128] * 63, 1024, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 63 * 2
+    # one request at three times the others (above twice the average):
+    # 270336 units -> 128-block chunks; the long request takes three
+    pkv.pkv_plan_build(plan, [16 * 128] * 63 + [16 * 384], 1024, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 63 + 3
+    # a fixed chunk size still applies
+    pkv.pkv_pool_set_option(p, pkv.PKV_OPT_SPLIT_BLOCKS, 64)
+    pkv.pkv_plan_build(plan, [16 * 128] * 64, 1024, stream=0)
+    assert pkv.pkv_plan_num_chunks(plan) == 64 * 2
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(p)
+
+
 def test_small_multihead_batch_takes_whole_requests_or_32_block_chunks():
     # 32 requests x 12 heads of width 64 (the vector fast kernel), 32 blocks
     # each: 12288 (block, head) units, the finest default split (8-block
