@@ -359,11 +359,14 @@ SplitChoice choose_split(const pkv_pool* p, int32_t n, int64_t total_blocks, int
   // A batch of at least two resident rounds of (request, head) pairs whose
   // longest request is at most twice the average keeps every request whole:
   // no request can end the launch alone.  The 32-layer bf16 step (requests of
-  // 97-161 blocks) then runs unsplit, with or without its aborted requests:
-  // 695-697 us per launch in every run on three boxes, where 128-block
-  // chunks ran at 690-697 on some boxes and 704-712 on another.
+  // 97-161 blocks) then runs unsplit, with or without its aborted requests,
+  // on eight-wave workgroups (multi-head; grouped kernels choose their own):
+  // 695-697 us per launch in all 21 runs on the boxes measured, where four
+  // waves landed there in 4 of 17 runs and at 704-710 us in the rest (two
+  // modes of the same pool, by physical placement), and 128-block chunks at
+  // 690-712.  The 256-request batch moved by 0.2%.
   if ((int64_t)n * H >= kTargetChunks / 2 && (int64_t)max_blocks * n <= 2 * total_blocks)
-    return {std::numeric_limits<int32_t>::max(), waves, false};
+    return {std::numeric_limits<int32_t>::max(), waves ? waves : 8, false};
   // A small multi-head batch with enough (request, head) pairs for an
   // eight-wave workgroup on every CU: 32-block chunks over eight waves (four
   // blocks per wave) instead of 8-block chunks over four, so fewer requests
