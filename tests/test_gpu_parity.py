@@ -1145,6 +1145,65 @@ def test_fullstep128_bf16_l32_transactional():
 
 
 # ------------------------------------------------------ randomized sweep --
+LARGE_PLANS = [
+    # dtype, d_h, H, H_kv, n, length recipe, op, merge; whole = requests kept whole
+    ("bf16", 128, 32, 32, 96, "balanced", "append", pkv.PKV_MERGE_AUTO, True),
+    ("f32", 64, 16, 16, 128, "one_long", "decode", pkv.PKV_MERGE_AUTO, False),
+    ("bf16", 128, 32, 8, 80, "log_uniform", "decode", pkv.PKV_MERGE_SEPARATE, False),
+    ("bf16", 256, 16, 16, 140, "balanced", "append", pkv.PKV_MERGE_LAST_ARRIVER, True),
+]
+
+
+@pytest.mark.parametrize("dtype,D,H,Hkv,n,recipe,op,merge,whole", LARGE_PLANS)
+def test_large_batch_plans(dtype, D, H, Hkv, n, recipe, op, merge, whole):
+    """Batches large enough for the plan's large-batch choices: a balanced
+    batch of two or more resident rounds keeps requests whole (eight-wave
+    workgroups on the multi-head kernel), one long request or log-uniform
+    lengths split into whole chunks with the remainder last.  Every context
+    against the oracle, appended rows bit-exact."""
+    rng = np.random.default_rng(4100 + D + H + n)
+    if recipe == "balanced":
+        lengths = rng.integers(600 if D == 128 else 200, 1200 if D == 128 else 400, size=n)
+    elif recipe == "one_long":
+        lengths = rng.integers(300, 600, size=n)
+        lengths[n // 3] = 4000
+    else:
+        lengths = np.minimum(6000, np.floor(16.0 * np.power(256.0, rng.random(n)))).astype(np.int64) + 1
+    w = _small(f"large_{recipe}_{dtype}_{D}", dtype, D, 16, lengths.astype(np.int64), heads=H,
+               kv_heads=Hkv if Hkv != H else 0, layers=1, seed=600 + n, extra_pages=8)
+    kp, vp = device_pool(w)
+    pool = _pool(w, kp, vp, merge=merge)
+    pt = _pt_device(w)
+    plan = pkv.pkv_plan_create(pool)
+    pkv.pkv_plan_build(plan, w.lengths.tolist(), w.pt_stride)
+    assert (pkv.pkv_plan_num_chunks(plan) == w.n) == whole
+    qh = w.q(0)
+    out = torch.empty((w.n, H, D), device="cuda")
+    worst = 0.0
+    if op == "decode":
+        pkv.pkv_plan_decode_attention(plan, 0, rows_to_device(qh, dtype), pt, out)
+        torch.cuda.synchronize()
+        for r in range(w.n):
+            err = max_err(out[r], _oracle_decode(w, 0, r, qh))
+            worst = max(worst, err)
+            assert err <= TOL[dtype], (r, int(w.lengths[r]))
+    else:
+        kh, vh = w.k_new(0), w.v_new(0)
+        pkv.pkv_plan_append_and_attend(plan, 0, pt, *(rows_to_device(x, dtype)
+                                                       for x in (qh, kh, vh)), out)
+        torch.cuda.synchronize()
+        for r in range(w.n):
+            t = int(w.lengths[r])
+            page, slot = w.page_tables[r][(t - 1) // 16], (t - 1) % 16
+            assert np.array_equal(to_bits(kp[0, page, :, slot, :], dtype), kh[r]), r
+            err = max_err(out[r], _oracle_decode(w, 0, r, qh, appended=(kh, vh)))
+            worst = max(worst, err)
+            assert err <= TOL[dtype], (r, t)
+    record_err(f"large plan {recipe} {dtype} d{D} H{H}/{Hkv}", worst)
+    pkv.pkv_plan_destroy(plan)
+    pkv.pkv_pool_destroy(pool)
+
+
 def _random_case(rng):
     dtype = ["f32", "bf16"][rng.integers(2)]
     D = int(rng.choice([64, 128, 40, 96, 32] if dtype == "f32" else [128, 128, 64, 80, 256]))
