@@ -383,12 +383,13 @@ __device__ inline GridUnit grid_unit(const AttnArgs& a) {
 
 // ---------------------------------------------------------------------------
 // Fast path: rows of 128, 256 or 512 bytes (bf16 d_h = 64, 128, 256; f32
-// d_h = 32, 64, 128), pages a multiple of 16 rows.  A workgroup of WAVES waves serves one (chunk, K/V
-// head) and the G query heads that share that K/V head: its waves form
-// WAVES/WPG head groups of HPW query heads each, and the WPG waves of a group
-// interleave the chunk's 16-row blocks, so each head group loads every K/V
-// byte of the chunk once for its HPW query heads (with one head group, once
-// for all G).  Multi-head attention is G = 1 (HPW = 1, WPG = WAVES).  A block is one contiguous 4 KiB slab of K and one of V.
+// d_h = 32, 64, 128), pages a multiple of 16 rows.  A workgroup of WAVES
+// waves serves one (chunk, K/V head) and the G query heads that share that
+// K/V head: its waves form WAVES/WPG head groups of HPW query heads each, and
+// the WPG waves of a group interleave the chunk's 16-row blocks, so each head
+// group loads every K/V byte of the chunk once for its HPW query heads (with
+// one head group, once for all G).  Multi-head attention is G = 1 (HPW = 1,
+// WPG = WAVES).  A block is one contiguous 4 KiB slab of K and one of V.
 // Lane (g, c): row i*4+g of each of the 4 loads, VB = row bytes / 16 bytes at
 // column c, so one load instruction reads four whole rows and the 16 lanes of
 // a DPP row hold one K/V row (512-byte rows take two 16-byte loads per lane).

@@ -1715,8 +1715,8 @@ pkv_status pkv_decode_attention_noalloc(pkv_pool* p, int32_t layer, int32_t n, c
   int32_t* d_counters = reinterpret_cast<int32_t*>(scratch + pkv::kScratchCountersOffset);
   if (slots > 0 && !separate)  // the last-arriver merge counts from zero
     PKV_HIP_TRY(pkv::launch_zero_i32(d_counters, (int64_t)n * H, s));
-  const PlanView view{na_reqs, n, na_items, m, pt_stride, choice.waves, merge_mode, inline_plan, d_meta,
-                      reinterpret_cast<float*>(scratch + pkv::kScratchPartialsOffset),
+  const PlanView view{na_reqs, n, na_items, m, pt_stride, choice.waves, merge_mode, inline_plan,
+                      d_meta, reinterpret_cast<float*>(scratch + pkv::kScratchPartialsOffset),
                       d_counters};
   const AttnArgs a = make_args_view(p, view, layer, page_table, q, nullptr, nullptr, out, false);
   PKV_HIP_TRY(pkv::launch_attention(a, p->desc.kv_dtype, m, s, nullptr));
