@@ -291,8 +291,6 @@ pkv_status flush_patches(pkv_pool* p, hipStream_t stream) {
   return PKV_OK;
 }
 
-// Workgroup shape and split-K chunk size (in 16-row blocks) of a plan.
-//
 // The merge a plan's split requests use.  Automatic (the default): launches
 // that read at least kSeparateMergeBytes of K/V merge in a separate kernel,
 // smaller ones in place.  In place, each split chunk's last wave waits for its
@@ -311,18 +309,21 @@ int32_t plan_merge_mode(const pkv_pool* p, uint64_t rows_attended) {
   return bytes >= kSeparateMergeBytes ? pkv::kMergeSeparate : pkv::kMergeLastArriver;
 }
 
+// Workgroup shape and split-K chunk size (in 16-row blocks) of a plan.
+//
 // Waves per workgroup: PKV_OPT_WAVES, or 0 to let the launcher choose per
 // kernel (four for the vector kernels, eight or sixteen for a small
-// multi-head batch as below; eight for the matrix-core kernel when a workgroup serves 8 or 16
-// query heads, whose requests then finish in half the block steps per wave).
+// multi-head batch and eight for a balanced batch kept whole, as below; eight
+// for the matrix-core kernel when a workgroup serves 8 or 16 query heads,
+// whose requests then finish in half the block steps per wave).
 // Requests split into chunks sized for about kTargetChunks (chunk, query
 // head) units -- four resident rounds of 256 CUs x 4 workgroups -- so a batch
 // with few (request, head) pairs still fills the GPU and one long context
-// does not serialise on one workgroup; a batch that already has that many
-// pairs is not split.
+// does not serialise on one workgroup; a balanced batch of two or more
+// resident rounds stays whole (below).
 //
-// Such a launch runs its workgroups in several resident rounds, longest chunk
-// first, and ends as the last ones drain.  Its requests split into whole
+// A split launch of more than four rounds runs its workgroups longest chunk
+// first and ends as the last ones drain.  Its requests split into whole
 // chunks of `chunk` blocks with the remainder last (remainder_last), so the
 // chunks dispatched at the end are short: on the 32-layer bf16 step split at
 // 128 blocks (requests of 97-161 blocks) that measured 695.7-697.0 us per
