@@ -74,6 +74,25 @@ __device__ inline int kv_byte(int row, int chunk) {
   return row * (2 * D) + ((chunk ^ (row & (D / 8 - 1))) << 4);
 }
 
+// V blocks at head width 128 take another swizzle: chunk c of row r sits at
+// position c ^ f(r), f(r) = 2 (r mod 8) + (r / 8 mod 2).  A transposing
+// value read serves each half wave (32 lanes) as eight consecutive rows
+// reading chunks 2 dt and 2 dt + 1 of each; with f these are 16 distinct
+// positions, which cover every bank once, where r mod 16 (K's swizzle) puts
+// rows r and r ^ 1 on the same two chunk positions (two-way bank conflicts,
+// two extra LDS cycles per read).  Other widths keep kv_byte's swizzle.
+template <int D>
+__device__ inline int v_swz(int row) {
+  if constexpr (D == 128)
+    return ((row & 7) << 1) | ((row >> 3) & 1);
+  else
+    return row & (D / 8 - 1);
+}
+template <int D>
+__device__ inline int v_byte(int row, int chunk) {
+  return row * (2 * D) + ((chunk ^ v_swz<D>(row)) << 4);
+}
+
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 // One 16-byte-per-lane buffer load straight into LDS: lane i's 16 bytes at
@@ -120,9 +139,10 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 // lane 4k + j/4 addresses, k = 0..3; lane i addressing key base + i/4, dims
 // 16 dt + 4 (i%4)..+3 then hands lane j the dim 16 dt + j of keys base..+3).
 // Each K or V fragment read from LDS feeds the MFMAs of both query sets.
-// Online softmax per query in log2 units; the running maximum is reduced
-// across the four lane groups with permlane swaps and moves lazily (only by
-// more than 2^8 in weight); the running sum comes from the matrix cores
+// Online softmax per query in log2 units; the running maximum moves lazily
+// (only by more than 2^8 in weight, decided by a vote over each lane's own
+// maxima) and only then is reduced across the four lane groups with permlane
+// swaps; the running sum comes from the matrix cores
 // (head width <= 128) or the same swaps (256).  The context accumulates in
 // the MFMA output layout (lane l: rows 4(l/16)..+3, column l%16 of each
 // 16-column tile), whose per-row scale factors come from the owning lanes by
@@ -157,7 +177,8 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
   constexpr int NC = D / 8;      // 16-byte chunks per row
   constexpr int RPI = 64 / NC;   // rows per 1 KiB staging load (4 or 8)
   constexpr int NPART = 64 / RPI / WAVES;  // staging loads per wave and block
-  // [buffer][0: K, 1: V][64 rows x 256 B], swizzled as kv_byte describes
+  // [buffer][0: K, 1: V][64 rows x 2 D bytes], swizzled as kv_byte (K) and
+  // v_byte (V) describe
   __shared__ __attribute__((aligned(16))) char sKV[2][2][kBlockKeys * kRowBytes];
 
   const int item = prefill_item();
@@ -225,10 +246,19 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
   auto stage = [&](int key0, int b) {
     if (key0 + kBlockKeys <= tile.key_end) {
       int32_t pg[NPART];
+      if constexpr (PAGE16 && RPI * WAVES == 16) {
+        // Part i's rows lie in page key0 / 16 + i (key0 is a multiple of 64
+        // and RPI * wave < 16): consecutive table entries, which the
+        // compiler fetches with one scalar load instead of one round trip
+        // per part.
 #pragma unroll
-      for (int i = 0; i < NPART; ++i) {
-        const int key = key0 + RPI * (WAVES * i + wave);
-        pg[i] = ptc[PAGE16 ? key >> 4 : key / S];
+        for (int i = 0; i < NPART; ++i) pg[i] = ptc[(key0 >> 4) + i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < NPART; ++i) {
+          const int key = key0 + RPI * (WAVES * i + wave);
+          pg[i] = ptc[PAGE16 ? key >> 4 : key / S];
+        }
       }
       const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(&sKV[b][0][0]);
       const uint32_t lds1 = (uint32_t)reinterpret_cast<uintptr_t>(&sKV[b][1][0]);
@@ -239,9 +269,11 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
         const int slot0 = PAGE16 ? key & 15 : key - (key / S) * S;
         const int64_t page = (int64_t)pg[i] * a.page_bytes + head_off;
         const int r = r0 + lrow;
-        const uint32_t voff = (slot0 + lrow) * kRowBytes + ((lpos ^ (r & (NC - 1))) << 4);
-        lds_dma16(a.k_layer + page, S * kRowBytes, voff, lds0 + r0 * kRowBytes);
-        lds_dma16(a.v_layer + page, S * kRowBytes, voff, lds1 + r0 * kRowBytes);
+        const uint32_t vrow_off = (slot0 + lrow) * kRowBytes;
+        lds_dma16(a.k_layer + page, S * kRowBytes, vrow_off + ((lpos ^ (r & (NC - 1))) << 4),
+                  lds0 + r0 * kRowBytes);
+        lds_dma16(a.v_layer + page, S * kRowBytes, vrow_off + ((lpos ^ v_swz<D>(r)) << 4),
+                  lds1 + r0 * kRowBytes);
       }
     } else {
       // Partial block: keys clamped to the last row the tile may read (the
@@ -254,9 +286,9 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
         const int page_idx = PAGE16 ? key >> 4 : key / S;
         const int slot = PAGE16 ? key & 15 : key - page_idx * S;
         const int64_t off = (int64_t)pt[page_idx] * a.page_bytes + head_off +
-                            (int64_t)slot * kRowBytes + ((lpos ^ (r & (NC - 1))) << 4);
-        kx[i] = *reinterpret_cast<const uint4*>(a.k_layer + off);
-        vx[i] = *reinterpret_cast<const uint4*>(a.v_layer + off);
+                            (int64_t)slot * kRowBytes;
+        kx[i] = *reinterpret_cast<const uint4*>(a.k_layer + off + ((lpos ^ (r & (NC - 1))) << 4));
+        vx[i] = *reinterpret_cast<const uint4*>(a.v_layer + off + ((lpos ^ v_swz<D>(r)) << 4));
       }
 #pragma unroll
       for (int i = 0; i < NPART; ++i) {
@@ -269,9 +301,19 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
   stage(0, 0);
 
   const int nblocks = (tile.key_end + kBlockKeys - 1) / kBlockKeys;
-  for (int kb = 0; kb < nblocks; ++kb) {
+  // Up to head width 128 blocks are taken in pairs, which makes the buffer
+  // index of each copy a constant: every LDS read address is then a
+  // loop-invariant lane offset plus an immediate (d_h 64: 630 -> 608 us,
+  // d_h 128: 1005 -> 1001 us on one box).  At 256 the pairs measured 8%
+  // slower (2375 -> 2565 us), and the index stays a run-time value.
+  constexpr int kPair = D == 256 ? 1 : 2;
+  for (int kp = 0; kp < nblocks; kp += kPair)
+#pragma unroll
+  for (int u = 0; u < kPair; ++u) {
+    const int kb = kp + u;
+    if (kb >= nblocks) break;
+    const int b = kPair == 2 ? u : kb & 1;
     const int key0 = kb * kBlockKeys;
-    const int b = kb & 1;
     // This wave's loads and stores into buffer b are complete; the barrier
     // then makes every wave's visible and ends all reads of buffer b ^ 1.
     __builtin_amdgcn_s_waitcnt(0);
@@ -317,8 +359,9 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
           for (int j = 0; j < 4; ++j)
             if (key0 + 16 * kt + 4 * g + j > my_pos[qs]) s[qs][kt][j] = -INFINITY;
     }
-    // Block maxima in scaled log2 units (the scale is positive, so the
-    // maximum of the raw products scales to the maximum of the scores).
+    // This lane's maxima over its 16 keys of the block, in scaled log2 units
+    // (the scale is positive, so the maximum of the raw products scales to
+    // the maximum of the scores).
     float cand[QS];
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) {
@@ -327,13 +370,17 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) mb = fmaxf(mb, s[qs][kt][j]);
-      cand[qs] = xor32_max(xor16_max(mb)) * a.scale_log2e;
+      cand[qs] = mb * a.scale_log2e;
     }
     // Lazy rescale: the running maxima move (and the context and sums are
     // rescaled) only when some query of the wave sees a block maximum more
     // than kSlack above its own; otherwise the weights exp2(s - m) stay at
     // most 2^kSlack, which float32 sums and bf16 weights carry exactly as
-    // well.  The first block always moves them from -inf.
+    // well.  The first block always moves them from -inf.  A query's block
+    // maximum is the largest of its four lanes' maxima, so the wave-wide
+    // vote over lane maxima decides the same; only then are the maxima
+    // reduced across the lane groups (every lane of a query then holds the
+    // same running maximum).
     constexpr float kSlack = 8.f;
     bool grow = false;
 #pragma unroll
@@ -341,7 +388,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
     if (__builtin_expect(__any(grow), 0)) {
 #pragma unroll
       for (int qs = 0; qs < QS; ++qs) {
-        const float mn = fmaxf(m[qs], cand[qs]);
+        const float mn = fmaxf(m[qs], xor32_max(xor16_max(cand[qs])));
         const float alpha = __builtin_amdgcn_exp2f(m[qs] - mn);
         l[qs] *= alpha;
         m[qs] = mn;
@@ -391,9 +438,9 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
         const int chunk = 2 * dt + ((ql & 3) >> 1);
         const int half = (ql & 1) * 8;
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(sV + kv_byte<D>(vrow, chunk) + half));
+            (lds_s16x4_t*)(sV + v_byte<D>(vrow, chunk) + half));
         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(sV + kv_byte<D>(vrow + 16, chunk) + half));
+            (lds_s16x4_t*)(sV + v_byte<D>(vrow + 16, chunk) + half));
         const bf16x8_t vf = __builtin_bit_cast(
             bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
