@@ -349,6 +349,18 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 2) void prefill_mfma_kernel(
 #pragma unroll
         for (int qs = 0; qs < QS; ++qs) s[qs][kt][j] = c[qs][j];
     }
+    // At head width 128 the scheduler is held to eight K reads ahead of the
+    // score products (it kept about four, waiting on the LDS five or six
+    // times per block): 1009 -> 1000 and 1027 -> 1014 us per launch in
+    // alternating runs on two boxes, in the same registers.
+    if constexpr (D == 128) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QS, 0);  // the products of one read
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // the next read
+      }
+    }
     // causal mask where the block reaches past this wave's first position
     if (key0 + kBlockKeys - 1 > wave_first_pos) {
 #pragma unroll
