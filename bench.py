@@ -73,11 +73,11 @@ MEASURED_TRAFFIC = {
     "batch256_mqa_bf16": {"source": "kernels.hip", "sha256_16": "5e8a45bd1180b636",
         "fetch_kib": 152515.3, "write_kib": 4096.0,
         "algorithmic_bytes": 309806592},
-    "prefill32_bf16": {"source": "prefill.hip", "sha256_16": "669cbf7f1b4068e5",
-        "fetch_kib": 751809.8, "write_kib": 518320.2,
+    "prefill32_bf16": {"source": "prefill.hip", "sha256_16": "c6bff56b4b013bd9",
+        "fetch_kib": 753658.9, "write_kib": 518320.2,
         "algorithmic_bytes": 1854562304},
-    "prefill32_fp32": {"source": "prefill.hip", "sha256_16": "669cbf7f1b4068e5",
-        "fetch_kib": 293532.5, "write_kib": 97857.0,
+    "prefill32_fp32": {"source": "prefill.hip", "sha256_16": "c6bff56b4b013bd9",
+        "fetch_kib": 281745.6, "write_kib": 97857.0,
         "algorithmic_bytes": 575582208},
 }
 
